@@ -1,0 +1,373 @@
+"""Python binding of libpagedkv: paged decode over a chunked-slab KV pool (MI355X).
+
+This is argument marshalling only.  Every step of the path (zero-filling new
+slabs, the write scatter, the gather, the decode attention and its combine)
+runs in the HIP kernels of ``libpagedkv.so``; torch supplies device memory and
+the current stream.  There is no CPU fallback: if the library is missing the
+import of :func:`lib` raises.
+
+Functions keep the C names without the ``pd_`` prefix (``pool_create``,
+``append_slab``, ``reserve_rows``, ``slab_for_row``, ``write_block``,
+``gather_visible``, ``decode_workspace_bytes``, ``paged_decode``,
+``pool_stats``, ``pool_check_error``).  :class:`SlabPool` bundles a pool with
+the torch tensors that back its slabs.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import List, Optional, Sequence
+
+import torch  # loads the HIP runtime that libpagedkv then shares
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpagedkv.so")
+
+FMT_FP16, FMT_BF16, FMT_K8V8, FMT_K8V4, FMT_K4V4 = 0, 1, 2, 3, 4
+FORMAT_NAMES = {"fp16": FMT_FP16, "bf16": FMT_BF16, "k8v8": FMT_K8V8, "k8v4": FMT_K8V4,
+                "k4v4": FMT_K4V4}
+
+DEVERR_WRITE_ROW, DEVERR_WRITE_SLOT, DEVERR_TABLE_ROW, DEVERR_LENGTH = 0x1, 0x2, 0x4, 0x8
+
+STATUS = {0: "PD_OK", -1: "PD_ERR_ARG", -2: "PD_ERR_RANGE", -3: "PD_ERR_CAPACITY",
+          -4: "PD_ERR_UNSUPPORTED", -5: "PD_ERR_HIP", -6: "PD_ERR_DEVICE"}
+
+
+class PagedKVError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS.get(status, status)}: {message}")
+        self.status = status
+
+
+class PoolDesc(ctypes.Structure):
+    _fields_ = [("n_layers", ctypes.c_int32), ("block_size", ctypes.c_int32),
+                ("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("slab_blocks", ctypes.c_int32), ("max_slabs", ctypes.c_int32),
+                ("format", ctypes.c_int32), ("hadamard_signs", ctypes.POINTER(ctypes.c_int8))]
+
+
+class PoolStats(ctypes.Structure):
+    _fields_ = [("n_slabs", ctypes.c_int64), ("slab_append_events", ctypes.c_int64),
+                ("capacity_rows", ctypes.c_int64), ("bytes_reserved", ctypes.c_int64),
+                ("bytes_copied_on_growth", ctypes.c_int64), ("k_slab_bytes", ctypes.c_int64),
+                ("v_slab_bytes", ctypes.c_int64), ("k_record_bytes", ctypes.c_int32),
+                ("v_record_bytes", ctypes.c_int32)]
+
+    def as_dict(self):
+        return {name: getattr(self, name) for name, _ in self._fields_}
+
+
+EXPORTS = [
+    "pd_version", "pd_last_error", "pd_record_bytes", "pd_pool_create", "pd_pool_destroy",
+    "pd_slab_bytes", "pd_append_slab", "pd_slabs_needed", "pd_reserve_rows", "pd_slab_for_row",
+    "pd_write_block", "pd_gather_visible", "pd_decode_workspace_bytes", "pd_paged_decode",
+    "pd_pool_stats", "pd_pool_check_error",
+]
+
+_lib_handle = None
+_vp, _i32, _i64, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+_p_i32 = ctypes.POINTER(ctypes.c_int32)
+_pp = ctypes.POINTER(ctypes.c_void_p)
+
+
+def _declare(lib):
+    sig = {
+        "pd_version": (_i32, []),
+        "pd_last_error": (ctypes.c_char_p, []),
+        "pd_record_bytes": (_i32, [_i32, _i32, _p_i32, _p_i32]),
+        "pd_pool_create": (_i32, [ctypes.POINTER(PoolDesc), ctypes.POINTER(_vp)]),
+        "pd_pool_destroy": (_i32, [_vp]),
+        "pd_slab_bytes": (_i32, [_vp, ctypes.POINTER(_sz), ctypes.POINTER(_sz)]),
+        "pd_append_slab": (_i32, [_vp, _pp, _pp, _vp, _p_i32]),
+        "pd_slabs_needed": (_i32, [_vp, _i64, _p_i32]),
+        "pd_reserve_rows": (_i32, [_vp, _i64, _pp, _pp, _i32, _vp, _p_i32]),
+        "pd_slab_for_row": (_i32, [_vp, _i32, _i64, _pp, _pp, _p_i32]),
+        "pd_write_block": (_i32, [_vp, _i32, _i32, _vp, _vp, _vp, _vp, _vp]),
+        "pd_gather_visible": (_i32, [_vp, _i32, _i32, _vp, _i32, _vp, _i32, _vp, _vp, _vp, _vp]),
+        "pd_decode_workspace_bytes": (_i32, [_vp, _i32, _i32, _i32, ctypes.POINTER(_sz)]),
+        "pd_paged_decode": (_i32, [_vp, _i32, _i32, _i32, _vp, _vp, _i32, _vp, _i32,
+                                   ctypes.c_float, _vp, _vp, _sz, _vp]),
+        "pd_pool_stats": (_i32, [_vp, ctypes.POINTER(PoolStats)]),
+        "pd_pool_check_error": (_i32, [_vp, _vp, _p_i32]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+
+
+def lib():
+    """The loaded libpagedkv (raises if it has not been built)."""
+    global _lib_handle
+    if _lib_handle is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m decode_memory_amd.build` (or __graft_entry__.build())")
+        handle = ctypes.CDLL(LIB_PATH, mode=ctypes.RTLD_GLOBAL)
+        _declare(handle)
+        _lib_handle = handle
+    return _lib_handle
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        raise PagedKVError(status, lib().pd_last_error().decode(errors="replace"))
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream=None) -> int:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def _ptr_array(tensors: Sequence[torch.Tensor]):
+    arr = (ctypes.c_void_p * max(1, len(tensors)))()
+    for i, t in enumerate(tensors):
+        arr[i] = t.data_ptr()
+    return arr
+
+
+def _require(t: torch.Tensor, name: str, dtype=None, numel=None):
+    if not t.is_cuda or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous device tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if numel is not None and t.numel() != numel:
+        raise ValueError(f"{name} must have {numel} elements, got {t.numel()}")
+
+
+# ---------------------------------------------------------------------------
+# thin wrappers, one per C entry point
+# ---------------------------------------------------------------------------
+
+def version() -> int:
+    return lib().pd_version()
+
+
+def record_bytes(fmt: int, head_dim: int):
+    k, v = ctypes.c_int32(), ctypes.c_int32()
+    _check(lib().pd_record_bytes(fmt, head_dim, ctypes.byref(k), ctypes.byref(v)))
+    return k.value, v.value
+
+
+def pool_create(n_layers, block_size, n_kv_heads, head_dim, slab_blocks, max_slabs, fmt,
+                hadamard_signs=None) -> int:
+    signs_buf = None
+    if hadamard_signs is not None:
+        vals = [int(x) for x in hadamard_signs]
+        signs_buf = (ctypes.c_int8 * len(vals))(*vals)
+    desc = PoolDesc(n_layers, block_size, n_kv_heads, head_dim, slab_blocks, max_slabs, fmt,
+                    ctypes.cast(signs_buf, ctypes.POINTER(ctypes.c_int8)) if signs_buf else None)
+    out = ctypes.c_void_p()
+    _check(lib().pd_pool_create(ctypes.byref(desc), ctypes.byref(out)))
+    return out.value
+
+
+def pool_destroy(pool: int) -> None:
+    _check(lib().pd_pool_destroy(pool))
+
+
+def slab_bytes(pool: int):
+    k, v = ctypes.c_size_t(), ctypes.c_size_t()
+    _check(lib().pd_slab_bytes(pool, ctypes.byref(k), ctypes.byref(v)))
+    return k.value, v.value
+
+
+def append_slab(pool: int, k_mem: Sequence[torch.Tensor], v_mem: Sequence[torch.Tensor],
+                stream=None) -> int:
+    idx = ctypes.c_int32(-1)
+    _check(lib().pd_append_slab(pool, _ptr_array(k_mem), _ptr_array(v_mem), _stream(stream),
+                                ctypes.byref(idx)))
+    return idx.value
+
+
+def slabs_needed(pool: int, rows_needed: int) -> int:
+    n = ctypes.c_int32()
+    _check(lib().pd_slabs_needed(pool, rows_needed, ctypes.byref(n)))
+    return n.value
+
+
+def reserve_rows(pool: int, rows_needed: int, k_mem, v_mem, n_slabs: int, stream=None) -> int:
+    n = ctypes.c_int32()
+    _check(lib().pd_reserve_rows(pool, rows_needed, _ptr_array(k_mem), _ptr_array(v_mem), n_slabs,
+                                 _stream(stream), ctypes.byref(n)))
+    return n.value
+
+
+def slab_for_row(pool: int, layer: int, row: int):
+    kb, vb, r = ctypes.c_void_p(), ctypes.c_void_p(), ctypes.c_int32()
+    _check(lib().pd_slab_for_row(pool, layer, row, ctypes.byref(kb), ctypes.byref(vb),
+                                 ctypes.byref(r)))
+    return kb.value, vb.value, r.value
+
+
+def write_block(pool: int, layer: int, rows: torch.Tensor, slots: torch.Tensor,
+                k_src: torch.Tensor, v_src: torch.Tensor, stream=None) -> None:
+    n = rows.numel()
+    _require(rows, "rows", torch.int32)
+    _require(slots, "slots", torch.int32, n)
+    _require(k_src, "k_src")
+    _require(v_src, "v_src")
+    _check(lib().pd_write_block(pool, layer, n, _ptr(rows), _ptr(slots), _ptr(k_src), _ptr(v_src),
+                                _stream(stream)))
+
+
+def gather_visible(pool: int, layer: int, block_table: torch.Tensor, lens: torch.Tensor,
+                   t_out: int, k_out: torch.Tensor, v_out: torch.Tensor,
+                   n_runs_out: Optional[torch.Tensor] = None, stream=None) -> None:
+    B, max_blocks = block_table.shape
+    _require(block_table, "block_table", torch.int32)
+    _require(lens, "lens", torch.int32, B)
+    _require(k_out, "k_out")
+    _require(v_out, "v_out")
+    if n_runs_out is not None:
+        _require(n_runs_out, "n_runs_out", torch.int32, B)
+    _check(lib().pd_gather_visible(pool, layer, B, _ptr(block_table), max_blocks, _ptr(lens), t_out,
+                                   _ptr(k_out), _ptr(v_out), _ptr(n_runs_out), _stream(stream)))
+
+
+def decode_workspace_bytes(pool: int, B: int, n_q_heads: int, max_len: int) -> int:
+    n = ctypes.c_size_t()
+    _check(lib().pd_decode_workspace_bytes(pool, B, n_q_heads, max_len, ctypes.byref(n)))
+    return n.value
+
+
+def paged_decode(pool: int, layer: int, q: torch.Tensor, block_table: torch.Tensor,
+                 lens: torch.Tensor, max_len: int, scale: float, out: torch.Tensor,
+                 workspace: torch.Tensor, stream=None) -> None:
+    B, n_q, _ = q.shape
+    _require(q, "q")
+    _require(block_table, "block_table", torch.int32)
+    _require(lens, "lens", torch.int32, B)
+    _require(out, "out", q.dtype, q.numel())
+    _require(workspace, "workspace")
+    if block_table.shape[0] != B:
+        raise ValueError("block_table rows must equal the batch size")
+    _check(lib().pd_paged_decode(pool, layer, B, n_q, _ptr(q), _ptr(block_table),
+                                 block_table.shape[1], _ptr(lens), max_len, float(scale), _ptr(out),
+                                 _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                 _stream(stream)))
+
+
+def pool_stats(pool: int) -> dict:
+    s = PoolStats()
+    _check(lib().pd_pool_stats(pool, ctypes.byref(s)))
+    return s.as_dict()
+
+
+def pool_check_error(pool: int, stream=None) -> int:
+    """Synchronise and return (and clear) the device error bits; never raises for them."""
+    bits = ctypes.c_int32(0)
+    st = lib().pd_pool_check_error(pool, _stream(stream), ctypes.byref(bits))
+    if st not in (0, -6):
+        _check(st)
+    return bits.value
+
+
+# ---------------------------------------------------------------------------
+# convenience: a pool whose slabs are torch tensors
+# ---------------------------------------------------------------------------
+
+class SlabPool:
+    """A chunked-slab pool plus the torch tensors that hold its slabs.
+
+    Slab memory is allocated here with torch (uninitialised; the library
+    zero-fills it on the current stream) and kept alive until close()."""
+
+    def __init__(self, n_layers: int, block_size: int, n_kv_heads: int, head_dim: int,
+                 slab_blocks: int, max_slabs: int, fmt="bf16", hadamard_signs=None,
+                 device="cuda"):
+        self.fmt = FORMAT_NAMES[fmt] if isinstance(fmt, str) else int(fmt)
+        self.n_layers, self.block_size, self.n_kv_heads = n_layers, block_size, n_kv_heads
+        self.head_dim, self.slab_blocks, self.max_slabs = head_dim, slab_blocks, max_slabs
+        self.device = torch.device(device)
+        with torch.cuda.device(self.device):
+            self.handle = pool_create(n_layers, block_size, n_kv_heads, head_dim, slab_blocks,
+                                      max_slabs, self.fmt, hadamard_signs)
+        self.k_slab_bytes, self.v_slab_bytes = slab_bytes(self.handle)
+        self.k_record_bytes, self.v_record_bytes = record_bytes(self.fmt, head_dim)
+        self.k_slabs: List[List[torch.Tensor]] = [[] for _ in range(n_layers)]
+        self.v_slabs: List[List[torch.Tensor]] = [[] for _ in range(n_layers)]
+
+    # dtype of q / outputs / 16-bit sources
+    @property
+    def dtype(self):
+        return torch.float16 if self.fmt == FMT_FP16 else torch.bfloat16
+
+    def _alloc(self, n: int):
+        ks = [torch.empty(self.k_slab_bytes, dtype=torch.uint8, device=self.device)
+              for _ in range(n * self.n_layers)]
+        vs = [torch.empty(self.v_slab_bytes, dtype=torch.uint8, device=self.device)
+              for _ in range(n * self.n_layers)]
+        return ks, vs
+
+    def _adopt(self, ks, vs, n):
+        for s in range(n):
+            for layer in range(self.n_layers):
+                self.k_slabs[layer].append(ks[s * self.n_layers + layer])
+                self.v_slabs[layer].append(vs[s * self.n_layers + layer])
+
+    def append_slab(self, stream=None) -> int:
+        ks, vs = self._alloc(1)
+        idx = append_slab(self.handle, ks, vs, stream)
+        self._adopt(ks, vs, 1)
+        return idx
+
+    def reserve_rows(self, rows_needed: int, stream=None) -> int:
+        n = slabs_needed(self.handle, rows_needed)
+        if n == 0:
+            return 0
+        ks, vs = self._alloc(n)
+        got = reserve_rows(self.handle, rows_needed, ks, vs, n, stream)
+        self._adopt(ks, vs, n)
+        return got
+
+    def slab_view(self, layer: int, slab: int, kv: str = "k") -> torch.Tensor:
+        """A slab as [slab_blocks, block_size, n_kv_heads, record_bytes] uint8."""
+        t = (self.k_slabs if kv == "k" else self.v_slabs)[layer][slab]
+        rec = self.k_record_bytes if kv == "k" else self.v_record_bytes
+        return t.view(self.slab_blocks, self.block_size, self.n_kv_heads, rec)
+
+    def slab_for_row(self, layer: int, row: int):
+        return slab_for_row(self.handle, layer, row)
+
+    def write_block(self, layer, rows, slots, k_src, v_src, stream=None):
+        write_block(self.handle, layer, rows, slots, k_src, v_src, stream)
+
+    def gather_visible(self, layer, block_table, lens, t_out, k_out, v_out, n_runs_out=None,
+                       stream=None):
+        gather_visible(self.handle, layer, block_table, lens, t_out, k_out, v_out, n_runs_out,
+                       stream)
+
+    def workspace(self, B: int, n_q_heads: int, max_len: int) -> torch.Tensor:
+        """A decode workspace for up to B sequences of at most max_len tokens."""
+        n = decode_workspace_bytes(self.handle, B, n_q_heads, max_len)
+        return torch.empty(max(n, 256), dtype=torch.uint8, device=self.device)
+
+    def paged_decode(self, layer, q, block_table, lens, max_len, scale, out, workspace,
+                     stream=None):
+        paged_decode(self.handle, layer, q, block_table, lens, max_len, scale, out, workspace,
+                     stream)
+
+    def stats(self) -> dict:
+        return pool_stats(self.handle)
+
+    def check_error(self, stream=None) -> int:
+        return pool_check_error(self.handle, stream)
+
+    def close(self) -> None:
+        if getattr(self, "handle", None):
+            pool_destroy(self.handle)
+            self.handle = None
+        self.k_slabs = [[] for _ in range(self.n_layers)]
+        self.v_slabs = [[] for _ in range(self.n_layers)]
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

@@ -1,0 +1,109 @@
+// Internal declarations shared by the host side of the library (pool.hip) and
+// the kernel translation units.  Not part of the C ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+
+#include "pagedkv.h"
+
+namespace pagedkv {
+
+// Everything a kernel needs to reach one layer's slabs.
+struct LayerView {
+  const void* const* k_tab;  // device: slab index -> K slab base
+  const void* const* v_tab;  // device: slab index -> V slab base
+  int32_t slab_blocks;       // rows per slab
+  int32_t block_size;        // tokens per row
+  int32_t n_kv;              // kv heads
+  int32_t k_rec;             // bytes per K token-head record
+  int32_t v_rec;             // bytes per V token-head record
+  int64_t capacity_rows;     // rows that exist (n_slabs * slab_blocks)
+  int32_t* err;              // device sticky error word
+};
+
+struct WriteArgs {
+  LayerView lv;
+  int32_t n;
+  const int32_t* rows;
+  const int32_t* slots;
+  const void* k_src;
+  const void* v_src;
+  // packed formats
+  int32_t head_dim;
+  int32_t k_bits, v_bits;
+  const float* signs;  // device [head_dim] of +-1 (packed only)
+  float inv_sqrt_d;
+};
+
+struct GatherArgs {
+  LayerView lv;
+  int32_t B;
+  const int32_t* table;
+  int32_t max_blocks;
+  const int32_t* lens;
+  int32_t t_out;
+  void* k_out;
+  void* v_out;
+  int32_t* n_runs_out;
+};
+
+struct DecodeArgs {
+  LayerView lv;
+  int32_t B;
+  int32_t n_q;
+  const void* q;
+  const int32_t* table;
+  int32_t max_blocks;
+  const int32_t* lens;
+  float scale_log2;      // scale * log2(e): scores live in the exp2 domain
+  void* out;
+  // Split partials: running-weighted V [B * n_q][n_split][D] at partials,
+  // then (max, sum) [B * n_q][n_split][2] at partials + ml_offset.
+  float* partials;
+  size_t ml_offset;      // floats
+  int32_t n_split;       // split s of a sequence takes logical blocks s, s + n_split, ...
+  int32_t blocks_per_split;  // most blocks any split takes (<= 64)
+  // packed formats
+  int32_t k_bits, v_bits;
+  const float* signs;
+  float inv_sqrt_d;
+};
+
+// Launchers (return the hipError_t of the launch; hipErrorInvalidValue when
+// no kernel exists for the shape).
+hipError_t launch_zero_fill(void* p, size_t bytes, hipStream_t s);
+hipError_t launch_write_block(const WriteArgs& a, int32_t format, hipStream_t s);
+hipError_t launch_gather(const GatherArgs& a, hipStream_t s);
+hipError_t launch_paged_decode_column(const DecodeArgs& a, bool bf16, int32_t head_dim,
+                                      int32_t group, hipStream_t s);
+hipError_t launch_paged_decode_row(const DecodeArgs& a, bool bf16, int32_t head_dim, int32_t group,
+                                   int hgw, hipStream_t s);
+hipError_t launch_decode_combine(const DecodeArgs& a, bool bf16, int32_t head_dim, hipStream_t s);
+hipError_t launch_paged_decode_packed(const DecodeArgs& a, int32_t head_dim, int32_t group,
+                                      hipStream_t s);
+bool packed_decode_available();
+// Row kernel: head groups per workgroup (0 = shape not supported) and kv
+// heads per workgroup.
+int row_kernel_kpl(int32_t n_kv, int32_t head_dim, int32_t group, int32_t block_size);
+int row_kernel_heads_per_workgroup(int32_t head_dim, int hgw);
+
+// Split policy shared by the workspace query and the launch.
+constexpr int kMaxBlocksPerSplit = 64;
+constexpr int kMaxSplits = 256;
+inline int64_t max_decode_len(int32_t block_size) {
+  return static_cast<int64_t>(kMaxBlocksPerSplit) * kMaxSplits * block_size;
+}
+struct SplitPlan {
+  int32_t n_split;
+  int32_t blocks_per_split;
+};
+// units: independent (sequence, head group) columns of work in the batch.
+SplitPlan plan_splits(long long units, int32_t max_len, int32_t block_size, int target_workgroups,
+                      int max_blocks_per_split);
+size_t decode_ml_offset(int32_t B, int32_t n_q, int32_t head_dim, const SplitPlan& plan);  // floats
+size_t decode_workspace_bytes(int32_t B, int32_t n_q, int32_t head_dim, const SplitPlan& plan);
+
+}  // namespace pagedkv

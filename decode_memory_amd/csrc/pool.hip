@@ -1,0 +1,548 @@
+// Host side of libpagedkv: the chunked-slab pool object, its device
+// slab-pointer tables, argument validation and kernel dispatch.
+//
+// mlxcel issue #235 ("perf(core): chunked slab storage for the paged pool to
+// eliminate growth reallocation entirely"), section "Proposed solution:
+// chunked slabs": per-layer vectors of fixed-size slabs replace the single
+// pool tensor; growth appends zeroed slabs (one per layer, since physical
+// row ids are shared by all layers) and is counted by a slab-append counter;
+// pool byte accounting sums over slabs; one slab_for_row helper is the only
+// place that maps a row to (slab, row_in_slab).
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "internal.h"
+
+using namespace pagedkv;
+
+// Workgroups a decode launch aims for (column kernel: 3 of 4 waves resident
+// per CU; row kernel: one workgroup of 8 waves per CU) and the row kernel's
+// largest split.
+#ifndef PAGEDKV_DECODE_TARGET_WG
+#define PAGEDKV_DECODE_TARGET_WG 768
+#endif
+#ifndef PAGEDKV_ROW_TARGET_WG
+#define PAGEDKV_ROW_TARGET_WG 256
+#endif
+#ifndef PAGEDKV_ROW_MAX_BLOCKS_PER_SPLIT
+#define PAGEDKV_ROW_MAX_BLOCKS_PER_SPLIT 32
+#endif
+
+struct pd_pool {
+  pd_pool_desc desc{};
+  int device = 0;
+  int32_t k_rec = 0, v_rec = 0;
+  int32_t k_bits = 16, v_bits = 16;
+  size_t k_slab_bytes = 0, v_slab_bytes = 0;
+  int64_t n_slabs = 0;
+  int64_t append_events = 0;
+  // tables: layer l uses [l * 2 * max_slabs, +max_slabs) for K and the next
+  // max_slabs entries for V.  The pinned host mirror is only ever appended
+  // to, so an asynchronous copy out of it never races a later update.
+  void** h_tables = nullptr;
+  void** d_tables = nullptr;
+  int32_t* d_err = nullptr;
+  float* d_signs = nullptr;  // packed: [head_dim] of +-1
+  float inv_sqrt_d = 1.f;
+};
+
+namespace {
+
+thread_local std::string g_last_error;
+
+pd_status fail(pd_status st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+pd_status fail(pd_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+pd_status hip_fail(hipError_t e, const char* what) {
+  return fail(PD_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool is_native(int32_t f) { return f == PD_FMT_FP16 || f == PD_FMT_BF16; }
+bool is_packed(int32_t f) { return f == PD_FMT_K8V8 || f == PD_FMT_K8V4 || f == PD_FMT_K4V4; }
+
+void format_bits(int32_t f, int32_t* kb, int32_t* vb) {
+  switch (f) {
+    case PD_FMT_K8V8: *kb = 8; *vb = 8; break;
+    case PD_FMT_K8V4: *kb = 8; *vb = 4; break;
+    case PD_FMT_K4V4: *kb = 4; *vb = 4; break;
+    default: *kb = 16; *vb = 16; break;
+  }
+}
+
+int32_t record_bytes_for(int32_t bits, int32_t d) {
+  if (bits == 16) return 2 * d;
+  return d * bits / 8 + (d / 32) * 8;  // codes + (scale, offset) per 32 values
+}
+
+LayerView layer_view(const pd_pool* p, int32_t layer) {
+  LayerView lv;
+  const int ms = p->desc.max_slabs;
+  lv.k_tab = const_cast<const void* const*>(p->d_tables + static_cast<size_t>(layer) * 2 * ms);
+  lv.v_tab = lv.k_tab + ms;
+  lv.slab_blocks = p->desc.slab_blocks;
+  lv.block_size = p->desc.block_size;
+  lv.n_kv = p->desc.n_kv_heads;
+  lv.k_rec = p->k_rec;
+  lv.v_rec = p->v_rec;
+  lv.capacity_rows = p->n_slabs * p->desc.slab_blocks;
+  lv.err = p->d_err;
+  return lv;
+}
+
+pd_status check_pool(const pd_pool* p) {
+  if (!p) return fail(PD_ERR_ARG, "pool is NULL");
+  return PD_OK;
+}
+
+pd_status check_layer(const pd_pool* p, int32_t layer) {
+  if (layer < 0 || layer >= p->desc.n_layers)
+    return fail(PD_ERR_RANGE, "layer %d outside [0, %d)", layer, p->desc.n_layers);
+  return PD_OK;
+}
+
+// Record `n` new slabs per layer (slab-major pointer arrays) after checks.
+pd_status append_slabs(pd_pool* p, int32_t n, void* const* k_mem, void* const* v_mem,
+                       hipStream_t stream) {
+  const int L = p->desc.n_layers;
+  if (n < 0) return fail(PD_ERR_ARG, "negative slab count");
+  if (n == 0) return PD_OK;
+  if (!k_mem || !v_mem) return fail(PD_ERR_ARG, "slab pointer arrays are NULL");
+  if (p->n_slabs + n > p->desc.max_slabs)
+    return fail(PD_ERR_CAPACITY, "pool holds %lld slabs, max_slabs is %d",
+                static_cast<long long>(p->n_slabs), p->desc.max_slabs);
+  for (int64_t i = 0; i < static_cast<int64_t>(n) * L; ++i) {
+    if (!k_mem[i] || !v_mem[i]) return fail(PD_ERR_ARG, "slab pointer %lld is NULL", (long long)i);
+    if ((reinterpret_cast<uintptr_t>(k_mem[i]) | reinterpret_cast<uintptr_t>(v_mem[i])) & 255)
+      return fail(PD_ERR_ARG, "slab pointer %lld is not 256-byte aligned", (long long)i);
+  }
+  hipError_t e = hipSetDevice(p->device);
+  if (e != hipSuccess) return hip_fail(e, "hipSetDevice");
+  // zero the new memory first; nothing is recorded until every launch is queued
+  for (int64_t i = 0; i < static_cast<int64_t>(n) * L; ++i) {
+    if ((e = launch_zero_fill(k_mem[i], p->k_slab_bytes, stream)) != hipSuccess)
+      return hip_fail(e, "zero fill");
+    if ((e = launch_zero_fill(v_mem[i], p->v_slab_bytes, stream)) != hipSuccess)
+      return hip_fail(e, "zero fill");
+  }
+  const int ms = p->desc.max_slabs;
+  for (int s = 0; s < n; ++s) {
+    const int64_t slab = p->n_slabs + s;
+    for (int l = 0; l < L; ++l) {
+      p->h_tables[static_cast<size_t>(l) * 2 * ms + slab] = k_mem[static_cast<size_t>(s) * L + l];
+      p->h_tables[static_cast<size_t>(l) * 2 * ms + ms + slab] = v_mem[static_cast<size_t>(s) * L + l];
+    }
+  }
+  // copy the new entries (one contiguous range per layer and K/V table)
+  for (int l = 0; l < L; ++l) {
+    for (int kv = 0; kv < 2; ++kv) {
+      const size_t base = static_cast<size_t>(l) * 2 * ms + kv * ms + p->n_slabs;
+      e = hipMemcpyAsync(p->d_tables + base, p->h_tables + base, sizeof(void*) * n,
+                         hipMemcpyHostToDevice, stream);
+      if (e != hipSuccess) {
+        for (int s = 0; s < n; ++s)  // roll the host mirror back: nothing recorded
+          for (int ll = 0; ll < L; ++ll)
+            for (int kk = 0; kk < 2; ++kk)
+              p->h_tables[static_cast<size_t>(ll) * 2 * ms + kk * ms + p->n_slabs + s] = nullptr;
+        return hip_fail(e, "table update");
+      }
+    }
+  }
+  p->n_slabs += n;
+  p->append_events += n;
+  return PD_OK;
+}
+
+}  // namespace
+
+namespace pagedkv {
+
+SplitPlan plan_splits(long long units, int32_t max_len, int32_t block_size, int target_workgroups,
+                      int max_blocks_per_split) {
+  // Enough splits of the token axis that about target_workgroups workgroups
+  // are launched; a split holds 1..max_blocks_per_split blocks (at most 64:
+  // the kernels keep one block address per lane of a wave) and there are at
+  // most kMaxSplits splits (the combine stages one weight per split in LDS).
+  // Split s takes logical blocks s, s + n_split, ... so the blocks read at
+  // any moment by the whole launch lie close together.
+  SplitPlan p{1, 1};
+  const int max_nb = max_len > 0 ? (max_len + block_size - 1) / block_size : 1;
+  long long want = units > 0 ? (target_workgroups + units - 1) / units : 1;
+  if (want < 1) want = 1;
+  if (want > max_nb) want = max_nb;
+  int bps = static_cast<int>((max_nb + want - 1) / want);
+  const int cap = max_blocks_per_split < kMaxBlocksPerSplit ? max_blocks_per_split : kMaxBlocksPerSplit;
+  if (bps > cap) bps = cap;
+  if ((max_nb + bps - 1) / bps > kMaxSplits) bps = (max_nb + kMaxSplits - 1) / kMaxSplits;
+  p.n_split = (max_nb + bps - 1) / bps;
+  p.blocks_per_split = (max_nb + p.n_split - 1) / p.n_split;
+  return p;
+}
+
+size_t decode_ml_offset(int32_t B, int32_t n_q, int32_t head_dim, const SplitPlan& plan) {
+  const size_t acc = static_cast<size_t>(B) * n_q * plan.n_split * head_dim;
+  return (acc + 63) / 64 * 64;  // 256-byte aligned
+}
+
+size_t decode_workspace_bytes(int32_t B, int32_t n_q, int32_t head_dim, const SplitPlan& plan) {
+  const size_t ml = static_cast<size_t>(B) * n_q * plan.n_split * 2;
+  return (decode_ml_offset(B, n_q, head_dim, plan) + ml) * sizeof(float);
+}
+
+}  // namespace pagedkv
+
+namespace {
+
+// Which decode kernel runs for a call, and how the token axis is split.
+struct DecodePlan {
+  int kind = 0;  // 0: column kernel, 1: row kernel, 2: packed kernel
+  int kpl = 0;   // row kernel: kv heads per lane group
+  SplitPlan split{1, 1};
+};
+
+bool make_decode_plan(const pd_pool* p, int32_t B, int32_t group, int32_t max_len, DecodePlan* out) {
+  const int32_t n_kv = p->desc.n_kv_heads, D = p->desc.head_dim, bs = p->desc.block_size;
+  const bool d_ok = D == 64 || D == 128 || D == 256;
+  const bool g_ok = group == 1 || group == 2 || group == 4 || group == 8;
+  if (!d_ok || !g_ok) return false;
+  DecodePlan plan;
+  long long units = static_cast<long long>(B) * n_kv;
+  int target = PAGEDKV_DECODE_TARGET_WG, max_bps = kMaxBlocksPerSplit;
+  if (is_native(p->desc.format)) {
+    if (bs != 16 && bs != 32 && bs != 64) return false;
+    plan.kpl = row_kernel_kpl(n_kv, D, group, bs);
+    if (plan.kpl > 0) {
+      plan.kind = 1;
+      units = static_cast<long long>(B) * (n_kv / row_kernel_heads_per_workgroup(D, plan.kpl));
+      target = PAGEDKV_ROW_TARGET_WG;
+      max_bps = PAGEDKV_ROW_MAX_BLOCKS_PER_SPLIT;
+    }
+  } else {
+    if (bs != 32 || !packed_decode_available()) return false;
+    plan.kind = 2;
+  }
+  plan.split = plan_splits(units, max_len, bs, target, max_bps);
+  *out = plan;
+  return true;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t pd_version(void) { return PD_VERSION; }
+
+const char* pd_last_error(void) { return g_last_error.c_str(); }
+
+pd_status pd_record_bytes(int32_t format, int32_t head_dim, int32_t* k_bytes, int32_t* v_bytes) {
+  if (!is_native(format) && !is_packed(format)) return fail(PD_ERR_ARG, "unknown format %d", format);
+  if (head_dim <= 0) return fail(PD_ERR_ARG, "head_dim must be positive");
+  int32_t kb, vb;
+  format_bits(format, &kb, &vb);
+  if (k_bytes) *k_bytes = record_bytes_for(kb, head_dim);
+  if (v_bytes) *v_bytes = record_bytes_for(vb, head_dim);
+  return PD_OK;
+}
+
+pd_status pd_pool_create(const pd_pool_desc* d, pd_pool** out) {
+  if (!d || !out) return fail(PD_ERR_ARG, "desc and out must not be NULL");
+  *out = nullptr;
+  if (d->n_layers < 1 || d->n_kv_heads < 1 || d->slab_blocks < 1 || d->max_slabs < 1 ||
+      d->block_size < 1)
+    return fail(PD_ERR_ARG, "n_layers, n_kv_heads, slab_blocks, max_slabs, block_size must be >= 1");
+  if (!is_native(d->format) && !is_packed(d->format))
+    return fail(PD_ERR_ARG, "unknown format %d", d->format);
+  if (d->head_dim != 64 && d->head_dim != 128 && d->head_dim != 256)
+    return fail(PD_ERR_UNSUPPORTED, "head_dim %d (supported: 64, 128, 256)", d->head_dim);
+  if (d->block_size != 16 && d->block_size != 32 && d->block_size != 64)
+    return fail(PD_ERR_UNSUPPORTED, "block_size %d (supported: 16, 32, 64)", d->block_size);
+  if (is_packed(d->format) && d->block_size != 32)
+    return fail(PD_ERR_UNSUPPORTED, "packed formats use block_size 32");
+  if (is_packed(d->format)) {
+    if (!d->hadamard_signs) return fail(PD_ERR_ARG, "packed formats need hadamard_signs");
+    for (int i = 0; i < d->head_dim; ++i)
+      if (d->hadamard_signs[i] != 1 && d->hadamard_signs[i] != -1)
+        return fail(PD_ERR_ARG, "hadamard_signs[%d] is %d, not +-1", i, d->hadamard_signs[i]);
+  }
+  const size_t table_entries = static_cast<size_t>(d->n_layers) * 2 * d->max_slabs;
+  if (table_entries > (size_t{1} << 28)) return fail(PD_ERR_ARG, "slab tables too large");
+
+  pd_pool* p = new pd_pool;
+  p->desc = *d;
+  p->desc.hadamard_signs = nullptr;
+  format_bits(d->format, &p->k_bits, &p->v_bits);
+  p->k_rec = record_bytes_for(p->k_bits, d->head_dim);
+  p->v_rec = record_bytes_for(p->v_bits, d->head_dim);
+  const size_t per = static_cast<size_t>(d->slab_blocks) * d->block_size * d->n_kv_heads;
+  p->k_slab_bytes = per * p->k_rec;
+  p->v_slab_bytes = per * p->v_rec;
+  p->inv_sqrt_d = static_cast<float>(1.0 / std::sqrt(static_cast<double>(d->head_dim)));
+
+  hipError_t e = hipGetDevice(&p->device);
+  if (e == hipSuccess) e = hipHostMalloc(reinterpret_cast<void**>(&p->h_tables),
+                                         table_entries * sizeof(void*), hipHostMallocDefault);
+  if (e == hipSuccess) {
+    std::memset(p->h_tables, 0, table_entries * sizeof(void*));
+    e = hipMalloc(reinterpret_cast<void**>(&p->d_tables), table_entries * sizeof(void*));
+  }
+  if (e == hipSuccess) e = hipMemset(p->d_tables, 0, table_entries * sizeof(void*));
+  if (e == hipSuccess) e = hipMalloc(reinterpret_cast<void**>(&p->d_err), 256);
+  if (e == hipSuccess) e = hipMemset(p->d_err, 0, 256);
+  if (e == hipSuccess && is_packed(d->format)) {
+    std::vector<float> s(d->head_dim);
+    for (int i = 0; i < d->head_dim; ++i) s[i] = static_cast<float>(d->hadamard_signs[i]);
+    e = hipMalloc(reinterpret_cast<void**>(&p->d_signs), sizeof(float) * d->head_dim);
+    if (e == hipSuccess)
+      e = hipMemcpy(p->d_signs, s.data(), sizeof(float) * d->head_dim, hipMemcpyHostToDevice);
+  }
+  if (e != hipSuccess) {
+    pd_pool_destroy(p);
+    return hip_fail(e, "pool_create");
+  }
+  *out = p;
+  return PD_OK;
+}
+
+pd_status pd_pool_destroy(pd_pool* p) {
+  if (!p) return PD_OK;
+  int cur = 0;
+  hipGetDevice(&cur);
+  hipSetDevice(p->device);
+  hipDeviceSynchronize();  // kernels may still read the tables
+  if (p->d_tables) hipFree(p->d_tables);
+  if (p->d_err) hipFree(p->d_err);
+  if (p->d_signs) hipFree(p->d_signs);
+  if (p->h_tables) hipHostFree(p->h_tables);
+  hipSetDevice(cur);
+  delete p;
+  return PD_OK;
+}
+
+pd_status pd_slab_bytes(const pd_pool* p, size_t* k_bytes, size_t* v_bytes) {
+  if (pd_status st = check_pool(p)) return st;
+  if (k_bytes) *k_bytes = p->k_slab_bytes;
+  if (v_bytes) *v_bytes = p->v_slab_bytes;
+  return PD_OK;
+}
+
+pd_status pd_append_slab(pd_pool* p, void* const* k_mem, void* const* v_mem, hipStream_t stream,
+                         int32_t* new_index) {
+  if (pd_status st = check_pool(p)) return st;
+  const int64_t idx = p->n_slabs;
+  if (pd_status st = append_slabs(p, 1, k_mem, v_mem, stream)) return st;
+  if (new_index) *new_index = static_cast<int32_t>(idx);
+  return PD_OK;
+}
+
+pd_status pd_slabs_needed(const pd_pool* p, int64_t rows_needed, int32_t* n_slabs) {
+  if (pd_status st = check_pool(p)) return st;
+  if (rows_needed < 0 || !n_slabs) return fail(PD_ERR_ARG, "rows_needed < 0 or n_slabs NULL");
+  const int64_t S = p->desc.slab_blocks;
+  const int64_t want = (rows_needed + S - 1) / S;
+  *n_slabs = static_cast<int32_t>(want > p->n_slabs ? want - p->n_slabs : 0);
+  return PD_OK;
+}
+
+pd_status pd_reserve_rows(pd_pool* p, int64_t rows_needed, void* const* k_mem, void* const* v_mem,
+                          int32_t n_slabs, hipStream_t stream, int32_t* n_appended) {
+  if (pd_status st = check_pool(p)) return st;
+  int32_t need = 0;
+  if (pd_status st = pd_slabs_needed(p, rows_needed, &need)) return st;
+  if (n_slabs != need)
+    return fail(PD_ERR_ARG, "reserve_rows(%lld) needs %d slabs, %d given",
+                static_cast<long long>(rows_needed), need, n_slabs);
+  if (pd_status st = append_slabs(p, need, k_mem, v_mem, stream)) return st;
+  if (n_appended) *n_appended = need;
+  return PD_OK;
+}
+
+pd_status pd_slab_for_row(const pd_pool* p, int32_t layer, int64_t row, void** k_base,
+                          void** v_base, int32_t* row_in_slab) {
+  if (pd_status st = check_pool(p)) return st;
+  if (pd_status st = check_layer(p, layer)) return st;
+  const int64_t S = p->desc.slab_blocks;
+  if (row < 0 || row >= p->n_slabs * S)
+    return fail(PD_ERR_RANGE, "row %lld outside [0, %lld)", static_cast<long long>(row),
+                static_cast<long long>(p->n_slabs * S));
+  const int64_t slab = row / S;
+  const size_t ms = p->desc.max_slabs;
+  if (k_base) *k_base = p->h_tables[layer * 2 * ms + slab];
+  if (v_base) *v_base = p->h_tables[layer * 2 * ms + ms + slab];
+  if (row_in_slab) *row_in_slab = static_cast<int32_t>(row % S);
+  return PD_OK;
+}
+
+pd_status pd_write_block(pd_pool* p, int32_t layer, int32_t n, const int32_t* rows,
+                         const int32_t* slots, const void* k_src, const void* v_src,
+                         hipStream_t stream) {
+  if (pd_status st = check_pool(p)) return st;
+  if (pd_status st = check_layer(p, layer)) return st;
+  if (n < 0) return fail(PD_ERR_ARG, "n < 0");
+  if (n == 0) return PD_OK;
+  if (!rows || !slots || !k_src || !v_src) return fail(PD_ERR_ARG, "NULL device pointer");
+  if ((reinterpret_cast<uintptr_t>(k_src) | reinterpret_cast<uintptr_t>(v_src)) & 15)
+    return fail(PD_ERR_ARG, "k_src and v_src must be 16-byte aligned");
+  WriteArgs a{};
+  a.lv = layer_view(p, layer);
+  a.n = n;
+  a.rows = rows;
+  a.slots = slots;
+  a.k_src = k_src;
+  a.v_src = v_src;
+  a.head_dim = p->desc.head_dim;
+  a.k_bits = p->k_bits;
+  a.v_bits = p->v_bits;
+  a.signs = p->d_signs;
+  a.inv_sqrt_d = p->inv_sqrt_d;
+  hipError_t e = launch_write_block(a, p->desc.format, stream);
+  if (e != hipSuccess) return hip_fail(e, "write_block launch");
+  return PD_OK;
+}
+
+pd_status pd_gather_visible(pd_pool* p, int32_t layer, int32_t B, const int32_t* block_table,
+                            int32_t max_blocks, const int32_t* lens, int32_t t_out, void* k_out,
+                            void* v_out, int32_t* n_runs_out, hipStream_t stream) {
+  if (pd_status st = check_pool(p)) return st;
+  if (pd_status st = check_layer(p, layer)) return st;
+  if (B < 0 || max_blocks < 1 || t_out < 0) return fail(PD_ERR_ARG, "B < 0, max_blocks < 1 or t_out < 0");
+  if (B == 0 || t_out == 0) return PD_OK;
+  if (!block_table || !lens || !k_out || !v_out) return fail(PD_ERR_ARG, "NULL device pointer");
+  if ((reinterpret_cast<uintptr_t>(k_out) | reinterpret_cast<uintptr_t>(v_out)) & 15)
+    return fail(PD_ERR_ARG, "outputs must be 16-byte aligned");
+  GatherArgs a{};
+  a.lv = layer_view(p, layer);
+  a.B = B;
+  a.table = block_table;
+  a.max_blocks = max_blocks;
+  a.lens = lens;
+  a.t_out = t_out;
+  a.k_out = k_out;
+  a.v_out = v_out;
+  a.n_runs_out = n_runs_out;
+  hipError_t e = launch_gather(a, stream);
+  if (e != hipSuccess) return hip_fail(e, "gather_visible launch");
+  return PD_OK;
+}
+
+pd_status pd_decode_workspace_bytes(const pd_pool* p, int32_t B, int32_t n_q_heads,
+                                    int32_t max_len, size_t* bytes) {
+  if (pd_status st = check_pool(p)) return st;
+  if (!bytes || B < 0 || max_len < 0 || n_q_heads < 1)
+    return fail(PD_ERR_ARG, "bytes NULL, B < 0, max_len < 0 or n_q_heads < 1");
+  const int32_t n_kv = p->desc.n_kv_heads;
+  if (n_q_heads % n_kv) return fail(PD_ERR_ARG, "n_q_heads %d not a multiple of n_kv_heads %d",
+                                    n_q_heads, n_kv);
+  if (static_cast<int64_t>(max_len) > max_decode_len(p->desc.block_size))
+    return fail(PD_ERR_UNSUPPORTED, "max_len %d beyond %lld", max_len,
+                static_cast<long long>(max_decode_len(p->desc.block_size)));
+  DecodePlan plan;
+  if (!make_decode_plan(p, B, n_q_heads / n_kv, max_len, &plan))
+    return fail(PD_ERR_UNSUPPORTED, "no decode kernel for format %d, head_dim %d, group %d",
+                p->desc.format, p->desc.head_dim, n_q_heads / n_kv);
+  *bytes = decode_workspace_bytes(B, n_q_heads, p->desc.head_dim, plan.split);
+  return PD_OK;
+}
+
+pd_status pd_paged_decode(pd_pool* p, int32_t layer, int32_t B, int32_t n_q_heads, const void* q,
+                          const int32_t* block_table, int32_t max_blocks, const int32_t* lens,
+                          int32_t max_len, float scale, void* out, void* workspace,
+                          size_t workspace_bytes, hipStream_t stream) {
+  if (pd_status st = check_pool(p)) return st;
+  if (pd_status st = check_layer(p, layer)) return st;
+  if (B < 0 || max_blocks < 1 || max_len < 0) return fail(PD_ERR_ARG, "B < 0, max_blocks < 1 or max_len < 0");
+  if (B == 0) return PD_OK;
+  const int32_t n_kv = p->desc.n_kv_heads;
+  if (n_q_heads < 1 || n_q_heads % n_kv)
+    return fail(PD_ERR_ARG, "n_q_heads %d not a positive multiple of n_kv_heads %d", n_q_heads, n_kv);
+  const int32_t group = n_q_heads / n_kv;
+  if (!q || !block_table || !lens || !out || !workspace) return fail(PD_ERR_ARG, "NULL device pointer");
+  if ((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(out)) & 15)
+    return fail(PD_ERR_ARG, "q and out must be 16-byte aligned");
+  if (reinterpret_cast<uintptr_t>(workspace) & 255) return fail(PD_ERR_ARG, "workspace not 256-byte aligned");
+  if (!(scale == scale) || std::isinf(scale)) return fail(PD_ERR_ARG, "scale is not finite");
+  // the split plan must not depend on data only the device knows
+  const int64_t cap_len = static_cast<int64_t>(max_blocks) * p->desc.block_size;
+  const int32_t plan_len = static_cast<int32_t>(max_len < cap_len ? max_len : cap_len);
+  if (static_cast<int64_t>(plan_len) > max_decode_len(p->desc.block_size))
+    return fail(PD_ERR_UNSUPPORTED, "max_len %d beyond %lld", plan_len,
+                static_cast<long long>(max_decode_len(p->desc.block_size)));
+  DecodePlan plan;
+  if (!make_decode_plan(p, B, group, plan_len, &plan))
+    return fail(PD_ERR_UNSUPPORTED, "no decode kernel for format %d, head_dim %d, group %d",
+                p->desc.format, p->desc.head_dim, group);
+  const size_t need = decode_workspace_bytes(B, n_q_heads, p->desc.head_dim, plan.split);
+  if (workspace_bytes < need)
+    return fail(PD_ERR_CAPACITY, "workspace %zu bytes, %zu needed", workspace_bytes, need);
+  DecodeArgs a{};
+  a.lv = layer_view(p, layer);
+  a.B = B;
+  a.n_q = n_q_heads;
+  a.q = q;
+  a.table = block_table;
+  a.max_blocks = max_blocks;
+  a.lens = lens;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.out = out;
+  a.partials = static_cast<float*>(workspace);
+  a.ml_offset = decode_ml_offset(B, n_q_heads, p->desc.head_dim, plan.split);
+  a.n_split = plan.split.n_split;
+  a.blocks_per_split = plan.split.blocks_per_split;
+  a.k_bits = p->k_bits;
+  a.v_bits = p->v_bits;
+  a.signs = p->d_signs;
+  a.inv_sqrt_d = p->inv_sqrt_d;
+  const bool bf16 = p->desc.format == PD_FMT_BF16;
+  const int32_t D = p->desc.head_dim;
+  hipError_t e;
+  switch (plan.kind) {
+    case 1: e = launch_paged_decode_row(a, bf16, D, group, plan.kpl, stream); break;
+    case 2: e = launch_paged_decode_packed(a, D, group, stream); break;
+    default: e = launch_paged_decode_column(a, bf16, D, group, stream); break;
+  }
+  if (e == hipSuccess && plan.kind != 2) e = launch_decode_combine(a, bf16, D, stream);
+  if (e == hipErrorInvalidValue) return fail(PD_ERR_UNSUPPORTED, "no decode kernel for this shape");
+  if (e != hipSuccess) return hip_fail(e, "paged_decode launch");
+  return PD_OK;
+}
+
+pd_status pd_pool_stats(const pd_pool* p, pd_stats* s) {
+  if (pd_status st = check_pool(p)) return st;
+  if (!s) return fail(PD_ERR_ARG, "stats is NULL");
+  s->n_slabs = p->n_slabs;
+  s->slab_append_events = p->append_events;
+  s->capacity_rows = p->n_slabs * p->desc.slab_blocks;
+  s->bytes_reserved = static_cast<int64_t>(p->desc.n_layers) * p->n_slabs *
+                      static_cast<int64_t>(p->k_slab_bytes + p->v_slab_bytes);
+  s->bytes_copied_on_growth = 0;
+  s->k_slab_bytes = static_cast<int64_t>(p->k_slab_bytes);
+  s->v_slab_bytes = static_cast<int64_t>(p->v_slab_bytes);
+  s->k_record_bytes = p->k_rec;
+  s->v_record_bytes = p->v_rec;
+  return PD_OK;
+}
+
+pd_status pd_pool_check_error(pd_pool* p, hipStream_t stream, int32_t* device_error) {
+  if (pd_status st = check_pool(p)) return st;
+  int32_t v = 0;
+  hipError_t e = hipMemcpyAsync(&v, p->d_err, sizeof v, hipMemcpyDeviceToHost, stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(stream);
+  if (e == hipSuccess && v) e = hipMemsetAsync(p->d_err, 0, sizeof v, stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) return hip_fail(e, "check_error");
+  if (device_error) *device_error = v;
+  if (v) return fail(PD_ERR_DEVICE, "device error bits 0x%x", v);
+  return PD_OK;
+}
+
+}  // extern "C"

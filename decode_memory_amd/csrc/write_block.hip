@@ -1,0 +1,216 @@
+// write_block: token-granular scatter of new K/V into the slab of their row,
+// and the zero fill that backs append_slab.
+//
+// mlxcel issue #235 ("perf(core): chunked slab storage for the paged pool to
+// eliminate growth reallocation entirely"), section "Proposed solution:
+// chunked slabs": growth appends a fresh zeros slab (touch point: no copy),
+// and write_block's update targets the row's slab instead of one pool tensor
+// (touch point 1).  Packed pools quantise here, once per fresh token
+// (mlx-swift-lm PR #142, "Add packed paged KV formats with bounded workspace
+// admission", section "Summary" and the "After" flowchart: "quantize fresh
+// K/V once"): K is rotated by H diag(sigma) / sqrt(D) with a fast
+// Walsh-Hadamard butterfly network, then each group of 32 values is mapped to
+// unsigned codes with an fp32 (scale, offset) pair.
+#include "device_common.h"
+#include "internal.h"
+
+namespace pagedkv {
+
+namespace {
+
+constexpr int kThreads = 256;
+
+__global__ __launch_bounds__(kThreads) void zero_fill_kernel(uint4* p, size_t n16) {
+  const size_t stride = static_cast<size_t>(gridDim.x) * kThreads;
+  for (size_t i = static_cast<size_t>(blockIdx.x) * kThreads + threadIdx.x; i < n16; i += stride)
+    p[i] = make_uint4(0, 0, 0, 0);
+}
+
+// True when (row, slot) lies inside the pool; otherwise flags the error word
+// (from the calling lane only) so the token can be skipped.
+__device__ __forceinline__ bool valid_target(const LayerView& lv, int32_t row, int32_t slot,
+                                             bool report) {
+  if (row < 0 || row >= lv.capacity_rows) {
+    if (report) set_error(lv.err, PD_DEVERR_WRITE_ROW);
+    return false;
+  }
+  if (slot < 0 || slot >= lv.block_size) {
+    if (report) set_error(lv.err, PD_DEVERR_WRITE_SLOT);
+    return false;
+  }
+  return true;
+}
+
+// Token index inside its slab (row_in_slab * block_size + slot) and the slab.
+__device__ __forceinline__ size_t token_in_slab(const LayerView& lv, int32_t row, int32_t slot,
+                                                int* slab) {
+  *slab = row / lv.slab_blocks;
+  return static_cast<size_t>(row - *slab * lv.slab_blocks) * lv.block_size + slot;
+}
+
+// 16-bit pools: one workgroup per token copies its n_kv records of K and V
+// (contiguous in the source and in the slab) as 16-byte vectors.
+__global__ __launch_bounds__(kThreads) void write_block_native_kernel(WriteArgs a) {
+  const size_t tok_bytes = static_cast<size_t>(a.lv.n_kv) * a.lv.k_rec;  // == V bytes
+  const int n16 = static_cast<int>(tok_bytes / 16);
+  for (int i = blockIdx.x; i < a.n; i += gridDim.x) {
+    const int32_t row = a.rows[i], slot = a.slots[i];
+    if (!valid_target(a.lv, row, slot, threadIdx.x == 0)) continue;
+    int slab;
+    const size_t tok = token_in_slab(a.lv, row, slot, &slab);
+    const uint4* ks = reinterpret_cast<const uint4*>(static_cast<const char*>(a.k_src) + i * tok_bytes);
+    const uint4* vs = reinterpret_cast<const uint4*>(static_cast<const char*>(a.v_src) + i * tok_bytes);
+    uint4* kd = reinterpret_cast<uint4*>(static_cast<char*>(const_cast<void*>(a.lv.k_tab[slab])) +
+                                         tok * tok_bytes);
+    uint4* vd = reinterpret_cast<uint4*>(static_cast<char*>(const_cast<void*>(a.lv.v_tab[slab])) +
+                                         tok * tok_bytes);
+    for (int j = threadIdx.x; j < n16; j += kThreads) {
+      kd[j] = ks[j];
+      vd[j] = vs[j];
+    }
+  }
+}
+
+// ---- packed pools -------------------------------------------------------------
+// One wave quantises one token-head vector (K or V).  Element e of the vector
+// lives in lane e % 64, register e / 64.
+
+template <int D>
+__device__ __forceinline__ void fwht_rotate(float (&x)[D / 64], const float* signs, int lane,
+                                            float inv_sqrt_d) {
+  constexpr int R = D / 64;
+#pragma unroll
+  for (int r = 0; r < R; ++r) x[r] *= signs[r * 64 + lane];  // exact sign flips
+  // stages h = 1 .. 32: partner in another lane
+#pragma unroll
+  for (int h = 1; h < 64 && h < D; h <<= 1) {
+    const bool upper = (lane & h) != 0;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const float other = __shfl_xor(x[r], h, kWave);
+      // pair (a, b) with a at the lower index: lower gets a + b, upper gets a - b
+      x[r] = upper ? __fsub_rn(other, x[r]) : __fadd_rn(x[r], other);
+    }
+  }
+  // stages h = 64 .. D/2: partner in another register of the same lane
+#pragma unroll
+  for (int hr = 1; hr < R; hr <<= 1) {
+    float y[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const float other = x[r ^ hr];
+      y[r] = (r & hr) ? __fsub_rn(other, x[r]) : __fadd_rn(x[r], other);
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r) x[r] = y[r];
+  }
+#pragma unroll
+  for (int r = 0; r < R; ++r) x[r] = __fmul_rn(x[r], inv_sqrt_d);
+}
+
+// Quantise the wave's vector in groups of 32 (half a wave per group and
+// register) and store codes + (scale, offset) records.
+template <int D>
+__device__ __forceinline__ void quantise_store(const float (&x)[D / 64], int bits, char* rec,
+                                               int lane) {
+  constexpr int R = D / 64;
+  const float levels = static_cast<float>((1 << bits) - 1);
+  const int payload = D * bits / 8;
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    float mn = x[r], mx = x[r];
+#pragma unroll
+    for (int m = 1; m < 32; m <<= 1) {
+      mn = fminf(mn, __shfl_xor(mn, m, kWave));
+      mx = fmaxf(mx, __shfl_xor(mx, m, kWave));
+    }
+    const float scale = __fdiv_rn(__fsub_rn(mx, mn), levels);
+    int code = 0;
+    if (scale != 0.f) {
+      float t = rintf(__fdiv_rn(__fsub_rn(x[r], mn), scale));
+      t = fminf(fmaxf(t, 0.f), levels);
+      code = static_cast<int>(t);
+    }
+    const int e = r * 64 + lane;  // element index
+    if (bits == 8) {
+      reinterpret_cast<uint8_t*>(rec)[e] = static_cast<uint8_t>(code);
+    } else {
+      const int hi = __shfl_xor(code, 1, kWave);
+      if ((lane & 1) == 0)
+        reinterpret_cast<uint8_t*>(rec)[e >> 1] = static_cast<uint8_t>((code & 15) | ((hi & 15) << 4));
+    }
+    if ((lane & 31) == 0) {
+      float* meta = reinterpret_cast<float*>(rec + payload) + 2 * (e / 32);
+      meta[0] = scale;
+      meta[1] = mn;
+    }
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(kThreads) void write_block_packed_kernel(WriteArgs a) {
+  constexpr int R = D / 64;
+  const int lane = threadIdx.x % kWave;
+  const int waves_per_grid = gridDim.x * (kThreads / kWave);
+  const int n_jobs = a.n * a.lv.n_kv * 2;  // (token, head, K|V)
+  for (int job = blockIdx.x * (kThreads / kWave) + threadIdx.x / kWave; job < n_jobs;
+       job += waves_per_grid) {
+    const int is_v = job & 1;
+    const int th = job >> 1;
+    const int i = th / a.lv.n_kv, head = th % a.lv.n_kv;
+    const int32_t row = a.rows[i], slot = a.slots[i];
+    if (!valid_target(a.lv, row, slot, lane == 0 && is_v == 0 && head == 0)) continue;
+    int slab;
+    const size_t tok = token_in_slab(a.lv, row, slot, &slab);
+    const uint16_t* src = static_cast<const uint16_t*>(is_v ? a.v_src : a.k_src) +
+                          (static_cast<size_t>(i) * a.lv.n_kv + head) * D;
+    float x[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) x[r] = bf16_lo(src[r * 64 + lane]);
+    const int rec_bytes = is_v ? a.lv.v_rec : a.lv.k_rec;
+    char* dst = static_cast<char*>(const_cast<void*>(is_v ? a.lv.v_tab[slab] : a.lv.k_tab[slab])) +
+                (tok * a.lv.n_kv + head) * rec_bytes;
+    if (!is_v) fwht_rotate<D>(x, a.signs, lane, a.inv_sqrt_d);
+    quantise_store<D>(x, is_v ? a.v_bits : a.k_bits, dst, lane);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_zero_fill(void* p, size_t bytes, hipStream_t s) {
+  const size_t n16 = bytes / 16;
+  if (n16 == 0) return hipSuccess;
+  size_t blocks = (n16 + kThreads - 1) / kThreads;
+  if (blocks > 4096) blocks = 4096;
+  hipLaunchKernelGGL(zero_fill_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, s,
+                     static_cast<uint4*>(p), n16);
+  return hipGetLastError();
+}
+
+hipError_t launch_write_block(const WriteArgs& a, int32_t format, hipStream_t s) {
+  if (a.n == 0) return hipSuccess;
+  if (format == PD_FMT_FP16 || format == PD_FMT_BF16) {
+    const int grid = a.n < 65536 ? a.n : 65536;
+    hipLaunchKernelGGL(write_block_native_kernel, dim3(grid), dim3(kThreads), 0, s, a);
+    return hipGetLastError();
+  }
+  const int jobs = a.n * a.lv.n_kv * 2;
+  int grid = (jobs + 3) / 4;
+  if (grid > 65536) grid = 65536;
+  switch (a.head_dim) {
+    case 64:
+      hipLaunchKernelGGL(write_block_packed_kernel<64>, dim3(grid), dim3(kThreads), 0, s, a);
+      break;
+    case 128:
+      hipLaunchKernelGGL(write_block_packed_kernel<128>, dim3(grid), dim3(kThreads), 0, s, a);
+      break;
+    case 256:
+      hipLaunchKernelGGL(write_block_packed_kernel<256>, dim3(grid), dim3(kThreads), 0, s, a);
+      break;
+    default:
+      return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace pagedkv

@@ -1,0 +1,261 @@
+/*
+ * pagedkv -- single-token paged decode attention over a chunked-slab KV pool,
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * The pool follows mlxcel issue #235 ("perf(core): chunked slab storage for
+ * the paged pool to eliminate growth reallocation entirely", section
+ * "Proposed solution: chunked slabs"): every layer keeps a growing list of
+ * fixed-size K slabs and V slabs, each slab shaped
+ *     [slab_blocks, block_size, n_kv_heads, record]
+ * where a record is one token-head vector.  Physical row r lives in slab
+ * r / slab_blocks at row r % slab_blocks.  Growth appends a zeroed slab and
+ * never copies.  Kernels reach a row through a per-layer device table of slab
+ * base pointers, so no single pool buffer exists and nothing is gathered
+ * before attention.
+ *
+ * Records:
+ *   PD_FMT_FP16, PD_FMT_BF16 : head_dim 16-bit values (2 * head_dim bytes).
+ *   PD_FMT_K8V8, PD_FMT_K8V4, PD_FMT_K4V4 (mlx-swift-lm PR #142, "Add packed
+ *   paged KV formats with bounded workspace admission", section "Summary"):
+ *   unsigned codes of the given bit width (8-bit: one byte per value; 4-bit:
+ *   value 2i in the low nibble of byte i), then one (fp32 scale, fp32 offset)
+ *   pair per group of 32 values, little endian; a value is code*scale+offset.
+ *   K is rotated by the fixed signed Hadamard basis H*diag(sigma)/sqrt(D)
+ *   before it is quantised; V is not rotated.  Packed pools take bf16 keys,
+ *   values and queries and produce bf16 outputs.
+ *
+ * Conventions for every call:
+ *   - Device memory is allocated by the caller (slabs, inputs, outputs,
+ *     workspace).  The library owns only its slab-pointer tables and a
+ *     4-byte device error word per pool.
+ *   - Pointers documented as "device" must be device-accessible memory of the
+ *     pool's device; "host" pointers are read before the call returns.
+ *   - All device work is enqueued on the caller's stream and is ordered by it;
+ *     no call below synchronises the host except pd_pool_check_error, and
+ *     none allocates device memory except pd_pool_create.
+ *   - Argument errors return a negative pd_status and enqueue nothing;
+ *     pd_last_error() then describes the problem (thread-local string).
+ *   - Data-dependent errors found by a kernel (a block-table row or a
+ *     write_block row/slot outside the pool, a sequence length the call
+ *     cannot hold) set a sticky bit in the pool's device error word; the
+ *     offending block or token is skipped (a bad length is clamped) and no
+ *     memory outside the pool, the inputs and the outputs is touched.  Read
+ *     and clear the word with pd_pool_check_error.
+ *   - One pool is used from one host thread at a time.
+ */
+#ifndef PAGEDKV_H
+#define PAGEDKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PD_VERSION 1
+
+typedef enum pd_status {
+  PD_OK = 0,
+  PD_ERR_ARG = -1,          /* invalid argument (null, negative, inconsistent) */
+  PD_ERR_RANGE = -2,        /* layer / row / size outside the pool             */
+  PD_ERR_CAPACITY = -3,     /* slab-pointer table full or workspace too small  */
+  PD_ERR_UNSUPPORTED = -4,  /* shape or format without a kernel                */
+  PD_ERR_HIP = -5,          /* a HIP runtime call failed                       */
+  PD_ERR_DEVICE = -6        /* a kernel reported a data-dependent error        */
+} pd_status;
+
+typedef enum pd_format {
+  PD_FMT_FP16 = 0,
+  PD_FMT_BF16 = 1,
+  PD_FMT_K8V8 = 2,
+  PD_FMT_K8V4 = 3,
+  PD_FMT_K4V4 = 4
+} pd_format;
+
+/* Device error word bits (pd_pool_check_error). */
+#define PD_DEVERR_WRITE_ROW   0x1  /* write_block: row outside [0, capacity_rows) */
+#define PD_DEVERR_WRITE_SLOT  0x2  /* write_block: slot outside [0, block_size)   */
+#define PD_DEVERR_TABLE_ROW   0x4  /* a block-table row outside the pool          */
+#define PD_DEVERR_LENGTH      0x8  /* lens[b] < 0, or beyond max_blocks*block_size,
+                                      t_out (gather) or max_len (decode)        */
+
+typedef struct pd_pool_desc {
+  int32_t n_layers;      /* >= 1                                                */
+  int32_t block_size;    /* tokens per block (row): 16, 32 or 64                */
+  int32_t n_kv_heads;    /* >= 1                                                */
+  int32_t head_dim;      /* 64, 128 or 256                                      */
+  int32_t slab_blocks;   /* POOL_SLAB_BLOCKS: rows per slab, >= 1               */
+  int32_t max_slabs;     /* capacity of the slab-pointer tables, >= 1           */
+  int32_t format;        /* pd_format                                           */
+  const int8_t* hadamard_signs; /* host, [head_dim] of +1/-1; packed formats
+                                   only (copied at create), else NULL           */
+} pd_pool_desc;
+
+typedef struct pd_stats {
+  int64_t n_slabs;                /* slabs per layer (same for K and V)         */
+  int64_t slab_append_events;     /* appends since create (one per new slab)    */
+  int64_t capacity_rows;          /* n_slabs * slab_blocks                      */
+  int64_t bytes_reserved;         /* n_layers * n_slabs * (K + V slab bytes)    */
+  int64_t bytes_copied_on_growth; /* always 0: growth never copies              */
+  int64_t k_slab_bytes;           /* bytes of one K slab of one layer           */
+  int64_t v_slab_bytes;           /* bytes of one V slab of one layer           */
+  int32_t k_record_bytes;         /* bytes of one K token-head record           */
+  int32_t v_record_bytes;         /* bytes of one V token-head record           */
+} pd_stats;
+
+typedef struct pd_pool pd_pool;
+
+/* Library version (PD_VERSION). */
+int32_t pd_version(void);
+
+/* Description of the last error on this thread ("" if none). */
+const char* pd_last_error(void);
+
+/* Bytes of one K and one V token-head record for a format and head_dim. */
+pd_status pd_record_bytes(int32_t format, int32_t head_dim, int32_t* k_bytes, int32_t* v_bytes);
+
+/*
+ * Create an empty pool (no slabs) on the current HIP device.
+ * mlxcel #235, "Proposed solution": per-layer slab vectors replace the single
+ * pool tensor.  Allocates the device slab-pointer tables
+ * (n_layers * 2 * max_slabs pointers) and the device error word.
+ * out: host, receives the handle.  Errors: PD_ERR_ARG, PD_ERR_UNSUPPORTED,
+ * PD_ERR_HIP.
+ */
+pd_status pd_pool_create(const pd_pool_desc* desc, pd_pool** out);
+
+/* Release the library's tables.  Slab memory stays the caller's.  Waits for
+ * the device to finish work that may still read the tables. */
+pd_status pd_pool_destroy(pd_pool* pool);
+
+/* Bytes of one K slab and one V slab of one layer
+ * (slab_blocks * block_size * n_kv_heads * record bytes); host outputs. */
+pd_status pd_slab_bytes(const pd_pool* pool, size_t* k_bytes, size_t* v_bytes);
+
+/*
+ * Append one slab to every layer.  mlxcel #235, "Proposed solution": growth
+ * appends a fresh zeros slab -- no copy, no free, no transient old+new pair.
+ * k_mem, v_mem: host arrays of n_layers device pointers, each to
+ * pd_slab_bytes() bytes (256-byte aligned) that the caller keeps alive until
+ * pd_pool_destroy.  The library zero-fills them on `stream`, records the
+ * pointers in its tables and increments slab_append_events.  All-or-nothing:
+ * on any error nothing is recorded.  new_index (host, optional) receives the
+ * new slab's index.  Errors: PD_ERR_ARG, PD_ERR_CAPACITY (table full),
+ * PD_ERR_HIP.
+ */
+pd_status pd_append_slab(pd_pool* pool, void* const* k_mem, void* const* v_mem,
+                         hipStream_t stream, int32_t* new_index);
+
+/* Number of slabs that pd_reserve_rows must append so that rows
+ * [0, rows_needed) exist (0 if they already do); host output. */
+pd_status pd_slabs_needed(const pd_pool* pool, int64_t rows_needed, int32_t* n_slabs);
+
+/*
+ * presize_for_span (mlxcel #235, "Proposed solution"): append as many slabs
+ * as a span needs in one step.  n_slabs must equal pd_slabs_needed(); k_mem
+ * and v_mem hold n_slabs * n_layers device pointers, slab-major
+ * (entry s * n_layers + layer).  All-or-nothing.  n_appended: host, optional.
+ */
+pd_status pd_reserve_rows(pd_pool* pool, int64_t rows_needed, void* const* k_mem,
+                          void* const* v_mem, int32_t n_slabs, hipStream_t stream,
+                          int32_t* n_appended);
+
+/*
+ * slab_for_row (mlxcel #235, "Proposed solution", touch point 7): the K and V
+ * slab base pointers (device addresses, host outputs) of the slab holding
+ * `row` in `layer`, and the row's index inside that slab.
+ * Errors: PD_ERR_RANGE if layer or row is outside the pool.
+ */
+pd_status pd_slab_for_row(const pd_pool* pool, int32_t layer, int64_t row, void** k_base,
+                          void** v_base, int32_t* row_in_slab);
+
+/*
+ * write_block (mlxcel #235, "Proposed solution", touch point 1): scatter new
+ * tokens into the slab of their row.  Token i goes to (rows[i], slots[i]) of
+ * `layer`, K and V.
+ *   rows, slots: device int32 [n].
+ *   k_src, v_src: device [n, n_kv_heads, head_dim], fp16/bf16 as the pool
+ *     format (packed formats: bf16; K is rotated and both are quantised here,
+ *     once, as mlx-swift-lm PR #142's "quantize fresh K/V once").
+ * A row outside [0, capacity_rows) or a slot outside [0, block_size) sets a
+ * device error bit and that token is skipped.  Two tokens with the same
+ * (row, slot) in one call give an unspecified winner.  n == 0 is a no-op.
+ */
+pd_status pd_write_block(pd_pool* pool, int32_t layer, int32_t n, const int32_t* rows,
+                         const int32_t* slots, const void* k_src, const void* v_src,
+                         hipStream_t stream);
+
+/*
+ * gather_visible (mlxcel #235, "Proposed solution", touch point 3): copy each
+ * sequence's visible K and V out of the pool into contiguous, transposed
+ * tensors.  The row list of a sequence is split into maximal same-slab runs
+ * in logical order; each run is read from its slab's base pointer.
+ *   block_table: device int32 [B, max_blocks]; entry (b, i) is the physical
+ *     row of logical block i of sequence b; entries past the sequence's block
+ *     count are ignored.
+ *   lens: device int32 [B], visible tokens per sequence, 0 <= lens[b] <= t_out
+ *     and <= max_blocks * block_size.
+ *   k_out, v_out: device [B, n_kv_heads, t_out, record] (record = head_dim
+ *     16-bit values, or the packed record bytes).  Positions >= lens[b] are
+ *     written as zero bytes.
+ *   n_runs_out: device int32 [B], optional (NULL): number of same-slab runs
+ *     of each sequence.
+ */
+pd_status pd_gather_visible(pd_pool* pool, int32_t layer, int32_t B, const int32_t* block_table,
+                            int32_t max_blocks, const int32_t* lens, int32_t t_out, void* k_out,
+                            void* v_out, int32_t* n_runs_out, hipStream_t stream);
+
+/*
+ * Workspace bytes that pd_paged_decode needs for B sequences, n_q_heads query
+ * heads and a longest sequence of at most max_len tokens (host output).
+ */
+pd_status pd_decode_workspace_bytes(const pd_pool* pool, int32_t B, int32_t n_q_heads,
+                                    int32_t max_len, size_t* bytes);
+
+/*
+ * paged_decode: attention of one query token per sequence over its visible
+ * tokens, read in place from the slabs.  mlxcel #2171 ("refactor: one KV
+ * storage abstraction with dense and paged backends", section "Proposed
+ * Solution"): attend(q, k, v, scale, mask) with one query token and no mask;
+ * query head h reads kv head h / (n_q_heads / n_kv_heads).
+ *   q: device [B, n_q_heads, head_dim], the pool's 16-bit dtype (bf16 for
+ *     packed pools; the kernel applies the Hadamard rotation itself).
+ *   block_table, lens: as pd_gather_visible; tokens >= lens[b] are not read.
+ *   max_len: host, >= max(lens); sizes the split of the token axis without a
+ *     host-device synchronisation.
+ *   scale: multiplies q.k (typically 1/sqrt(head_dim)).
+ *   out: device [B, n_q_heads, head_dim], same dtype as q, rounded to nearest
+ *     even once at the end.  A sequence with lens[b] == 0 gets zeros.
+ *   workspace: device, >= pd_decode_workspace_bytes(), 256-byte aligned; it
+ *     receives one partial (running max, sum, weighted V) per split of the
+ *     token axis and needs no initialisation.  Calls sharing a workspace must
+ *     be ordered (same stream).
+ * Two kernels run: the split kernel, then a combine kernel that merges the
+ * splits of each (sequence, kv head) in split order.
+ * The result is bit-identical from run to run and independent of which
+ * physical rows and slabs hold the data.
+ */
+pd_status pd_paged_decode(pd_pool* pool, int32_t layer, int32_t B, int32_t n_q_heads,
+                          const void* q, const int32_t* block_table, int32_t max_blocks,
+                          const int32_t* lens, int32_t max_len, float scale, void* out,
+                          void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Pool counters (host output).  mlxcel #235: slab-append counter and
+ * bytes_reserved summed over slabs. */
+pd_status pd_pool_stats(const pd_pool* pool, pd_stats* stats);
+
+/*
+ * Synchronise `stream`, then read and clear the pool's sticky device error
+ * word.  device_error (host, optional) receives the PD_DEVERR_* bits.
+ * Returns PD_ERR_DEVICE if any bit was set, else PD_OK.
+ */
+pd_status pd_pool_check_error(pd_pool* pool, hipStream_t stream, int32_t* device_error);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGEDKV_H */

@@ -1,0 +1,66 @@
+"""The C-ABI library loads, exports every declared entry point, and rejects
+bad arguments on the host before touching a device (CPU only)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import decode_memory_amd as pd
+from oracle.packed import record_bytes as oracle_record_bytes
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "pagedkv.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pd_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = declared_functions()
+    assert len(names) >= 16
+    lib = pd.lib()
+    for n in names:
+        assert hasattr(lib, n), n
+    assert sorted(pd.EXPORTS) == names
+
+
+def test_version_and_record_bytes():
+    assert pd.version() == 1
+    assert pd.record_bytes(pd.FMT_BF16, 128) == (256, 256)
+    assert pd.record_bytes(pd.FMT_FP16, 64) == (128, 128)
+    for fmt, (kb, vb) in {pd.FMT_K8V8: (8, 8), pd.FMT_K8V4: (8, 4), pd.FMT_K4V4: (4, 4)}.items():
+        for d in (64, 128, 256):
+            assert pd.record_bytes(fmt, d) == (oracle_record_bytes(d, kb), oracle_record_bytes(d, vb))
+    with pytest.raises(pd.PagedKVError) as e:
+        pd.record_bytes(9, 64)
+    assert e.value.status == -1
+
+
+@pytest.mark.parametrize("kwargs,status", [
+    (dict(head_dim=96), -4),                      # no kernel for this head_dim
+    (dict(block_size=24), -4),
+    (dict(fmt=7), -1),                            # unknown format
+    (dict(n_layers=0), -1),
+    (dict(slab_blocks=0), -1),
+    (dict(fmt=pd.FMT_K4V4, hadamard_signs=None), -1),   # packed needs signs
+    (dict(fmt=pd.FMT_K4V4, head_dim=64, hadamard_signs=[1, 0] * 32), -1),  # not +-1
+])
+def test_pool_create_validates_on_host(kwargs, status):
+    args = dict(n_layers=2, block_size=32, n_kv_heads=8, head_dim=128, slab_blocks=4,
+                max_slabs=8, fmt=pd.FMT_BF16, hadamard_signs=None)
+    args.update(kwargs)
+    with pytest.raises(pd.PagedKVError) as e:
+        pd.pool_create(**args)
+    assert e.value.status == status
+
+
+def test_null_pool_is_an_argument_error():
+    lib = pd.lib()
+    assert lib.pd_pool_stats(None, None) == -1
+    assert lib.pd_pool_destroy(None) == 0
+    assert lib.pd_write_block(None, 0, 0, None, None, None, None, None) == -1
+    assert b"NULL" in lib.pd_last_error()

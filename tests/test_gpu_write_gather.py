@@ -1,0 +1,157 @@
+"""write_block and gather_visible against the oracle's byte-level pool model:
+bit-exact slab contents, bit-exact gathered tensors, run counts (mlxcel #235,
+"Acceptance criteria": a multi-slab span round-trips byte-identically; gather
+over an interleaved block table is byte-identical)."""
+
+import numpy as np
+import pytest
+import torch
+
+import decode_memory_amd as pd
+from oracle.slab_pool import SlabPoolModel, records_from_u16
+from synth import WORKLOADS, make_block_table, monotone_rows, shuffled_rows, workload_lengths
+from tests.gpu_util import build_pool, from_device_bits, i32, to_device_bits, token_targets
+
+pytestmark = pytest.mark.gpu
+
+
+def _model_from(lengths, rows, n_layers, bs, S, n_kv, D, dtype, seed, cap):
+    """The oracle pool filled with the same tokens; built from the generators."""
+    m = SlabPoolModel(n_layers, bs, n_kv, 2 * D, 2 * D, S)
+    m.reserve_rows(cap)
+    return m
+
+
+def _fill_both(n_layers, lengths, rows, bs, S, n_kv, D, dtype, seed, cap=None):
+    used = [int(r.max()) + 1 for r in rows if len(r)]
+    cap = cap if cap is not None else max(used)
+    model = SlabPoolModel(n_layers, bs, n_kv, 2 * D, 2 * D, S)
+    model.reserve_rows(cap)
+
+    def on_layer(layer, ks, vs):
+        for b, n in enumerate(lengths):
+            if n:
+                r, s = token_targets(rows[b], int(n), bs)
+                model.write(layer, r, s, records_from_u16(ks[b]), records_from_u16(vs[b]))
+
+    pool = build_pool(n_layers, lengths, rows, bs, S, n_kv, D, dtype, seed, capacity_rows=cap,
+                      on_layer=on_layer)
+    return pool, model
+
+
+def _slab_bytes(pool, layer, kv):
+    slabs = pool.k_slabs if kv == "k" else pool.v_slabs
+    return torch.cat([s for s in slabs[layer]]).cpu().numpy()
+
+
+def _assert_slabs_equal(pool, model):
+    torch.cuda.synchronize()
+    for layer in range(model.n_layers):
+        for kv, slabs in (("k", model.k_slabs), ("v", model.v_slabs)):
+            expect = np.concatenate([s.reshape(-1) for s in slabs[layer]])
+            assert np.array_equal(_slab_bytes(pool, layer, kv), expect), (layer, kv)
+
+
+def _gather(pool, layer, table, lengths, t_out, rec):
+    B = len(lengths)
+    n_kv = pool.n_kv_heads
+    k = torch.full((B, n_kv, t_out, rec), 0x5A, dtype=torch.uint8, device="cuda")
+    v = torch.full((B, n_kv, t_out, rec), 0x5A, dtype=torch.uint8, device="cuda")
+    runs = torch.full((B,), -1, dtype=torch.int32, device="cuda")
+    pool.gather_visible(layer, i32(table), i32(lengths), t_out, k, v, runs)
+    torch.cuda.synchronize()
+    return k.cpu().numpy(), v.cpu().numpy(), runs.cpu().numpy()
+
+
+def test_tiny_multi_slab_span_write_and_gather():
+    w = WORKLOADS["tiny"]
+    lengths = [w.length]
+    rows = monotone_rows(lengths, w.block_size)
+    pool, model = _fill_both(1, lengths, rows, w.block_size, w.slab_blocks, w.n_kv_heads,
+                             w.head_dim, w.dtype, w.seed)
+    assert pool.stats()["n_slabs"] == 2
+    _assert_slabs_equal(pool, model)
+    table = make_block_table(rows)
+    k, v, runs = _gather(pool, 0, table, lengths, w.length, 2 * w.head_dim)
+    ek, ev = model.gather_batched(0, table, lengths, w.length)
+    assert np.array_equal(k, ek) and np.array_equal(v, ev)
+    assert list(runs) == [2]
+    assert pool.check_error() == 0
+    pool.close()
+
+
+@pytest.mark.parametrize("dtype,D,bs,S", [("bf16", 128, 32, 4), ("fp16", 64, 16, 3),
+                                           ("bf16", 256, 64, 5)])
+def test_interleaved_table_ragged_lengths(dtype, D, bs, S):
+    lengths = [0, 1, bs - 1, bs, bs + 1, 5 * bs + 7, 9 * bs]
+    rng = np.random.default_rng(D + bs)
+    rows, free, R = shuffled_rows(rng, lengths, bs, S, spare_rows=5)
+    n_layers, n_kv = 2, 4
+    pool, model = _fill_both(n_layers, lengths, rows, bs, S, n_kv, D, dtype, 17, cap=R)
+    _assert_slabs_equal(pool, model)
+    table = make_block_table(rows, max_blocks=max(len(r) for r in rows) + 2)
+    t_out = max(lengths) + 3                            # zero tail past every length
+    for layer in range(n_layers):
+        k, v, runs = _gather(pool, layer, table, lengths, t_out, 2 * D)
+        ek, ev = model.gather_batched(layer, table, lengths, t_out)
+        assert np.array_equal(k, ek) and np.array_equal(v, ev), layer
+        expect_runs = [len(model.split_runs(r)) for r in rows]
+        assert list(runs) == expect_runs
+    assert pool.check_error() == 0
+    pool.close()
+
+
+def test_fragmented_workload_gather_is_byte_identical():
+    """The fragmented pool's layout (64 sequences, shuffled free list) at a
+    reduced length so the host model stays small; runs ~ blocks per sequence."""
+    w = WORKLOADS["fragmented_64"]
+    lengths = (workload_lengths(w) // 16).astype(np.int64)
+    rng = np.random.default_rng(np.random.SeedSequence([w.seed, 1 << 23]))
+    rows, free, R = shuffled_rows(rng, lengths, w.block_size, w.slab_blocks)
+    pool, model = _fill_both(1, lengths, rows, w.block_size, w.slab_blocks, 2, w.head_dim,
+                             w.dtype, w.seed, cap=R)
+    table = make_block_table(rows)
+    k, v, runs = _gather(pool, 0, table, lengths, int(lengths.max()), 2 * w.head_dim)
+    ek, ev = model.gather_batched(0, table, lengths, int(lengths.max()))
+    assert np.array_equal(k, ek) and np.array_equal(v, ev)
+    expect_runs = [len(model.split_runs(r)) for r in rows]
+    assert list(runs) == expect_runs
+    nbs = [len(r) for r in rows]
+    assert sum(expect_runs) > 0.8 * sum(nbs)            # worst-case fragmentation
+    pool.close()
+
+
+def test_write_block_overwrites_and_rejects_out_of_range_targets():
+    bs, S, n_kv, D = 32, 2, 2, 64
+    pool = pd.SlabPool(1, bs, n_kv, D, S, 4, "bf16")
+    pool.reserve_rows(4)
+    src = torch.arange(3 * n_kv * D, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+    src = src.view(3, n_kv, D)
+    rows = i32([1, 99, 3])
+    slots = i32([5, 0, 31])
+    pool.write_block(0, rows, slots, src, src)
+    assert pool.check_error() == pd.DEVERR_WRITE_ROW
+    pool.write_block(0, i32([2]), i32([32]), src[:1].contiguous(), src[:1].contiguous())
+    assert pool.check_error() == pd.DEVERR_WRITE_SLOT
+    assert pool.check_error() == 0                      # cleared by the read
+    s0 = pool.slab_view(0, 0, "k").cpu().numpy()        # rows 0, 1
+    s1 = pool.slab_view(0, 1, "k").cpu().numpy()        # rows 2, 3
+    expect = from_device_bits(src).view(np.uint8).reshape(3, n_kv, 2 * D)
+    assert np.array_equal(s0[1, 5], expect[0]) and np.array_equal(s1[1, 31], expect[2])
+    assert not s1[0].any()                              # row 2 untouched (bad slot skipped)
+    # overwrite in place: last write wins
+    pool.write_block(0, i32([1]), i32([5]), src[2:3].contiguous(), src[2:3].contiguous())
+    torch.cuda.synchronize()
+    assert np.array_equal(pool.slab_view(0, 0, "k").cpu().numpy()[1, 5], expect[2])
+    pool.close()
+
+
+def test_gather_flags_rows_outside_the_pool():
+    bs, S, n_kv, D = 32, 2, 2, 64
+    pool = pd.SlabPool(1, bs, n_kv, D, S, 4, "bf16")
+    pool.reserve_rows(4)
+    table = np.array([[0, 7, 1]], np.int32)             # row 7 does not exist
+    k, v, runs = _gather(pool, 0, table, [70], 96, 2 * D)
+    assert pool.check_error() == pd.DEVERR_TABLE_ROW
+    assert not k[0, :, 32:64].any()                     # the bad block reads as zeros
+    pool.close()

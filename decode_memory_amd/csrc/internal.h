@@ -84,7 +84,7 @@ hipError_t launch_paged_decode_row(const DecodeArgs& a, bool bf16, int32_t head_
 hipError_t launch_decode_combine(const DecodeArgs& a, bool bf16, int32_t head_dim, hipStream_t s);
 hipError_t launch_paged_decode_packed(const DecodeArgs& a, int32_t head_dim, int32_t group,
                                       hipStream_t s);
-bool packed_decode_available();
+bool packed_decode_supported(int32_t n_kv, int32_t head_dim, int32_t group, int32_t block_size);
 // Row kernel: head groups per workgroup (0 = shape not supported) and kv
 // heads per workgroup.
 int row_kernel_kpl(int32_t n_kv, int32_t head_dim, int32_t group, int32_t block_size);

@@ -25,6 +25,9 @@ using namespace pagedkv;
 #ifndef PAGEDKV_DECODE_TARGET_WG
 #define PAGEDKV_DECODE_TARGET_WG 768
 #endif
+#ifndef PAGEDKV_PACKED_TARGET_WG
+#define PAGEDKV_PACKED_TARGET_WG 768
+#endif
 #ifndef PAGEDKV_ROW_TARGET_WG
 #define PAGEDKV_ROW_TARGET_WG 256
 #endif
@@ -229,8 +232,10 @@ bool make_decode_plan(const pd_pool* p, int32_t B, int32_t group, int32_t max_le
       max_bps = PAGEDKV_ROW_MAX_BLOCKS_PER_SPLIT;
     }
   } else {
-    if (bs != 32 || !packed_decode_available()) return false;
+    if (!packed_decode_supported(n_kv, D, group, bs)) return false;
     plan.kind = 2;
+    units = B;  // a packed workgroup covers every kv head of its sequence
+    target = PAGEDKV_PACKED_TARGET_WG;
   }
   plan.split = plan_splits(units, max_len, bs, target, max_bps);
   *out = plan;
@@ -510,7 +515,8 @@ pd_status pd_paged_decode(pd_pool* p, int32_t layer, int32_t B, int32_t n_q_head
     case 2: e = launch_paged_decode_packed(a, D, group, stream); break;
     default: e = launch_paged_decode_column(a, bf16, D, group, stream); break;
   }
-  if (e == hipSuccess && plan.kind != 2) e = launch_decode_combine(a, bf16, D, stream);
+  // packed pools produce bf16 outputs
+  if (e == hipSuccess) e = launch_decode_combine(a, bf16 || plan.kind == 2, D, stream);
   if (e == hipErrorInvalidValue) return fail(PD_ERR_UNSUPPORTED, "no decode kernel for this shape");
   if (e != hipSuccess) return hip_fail(e, "paged_decode launch");
   return PD_OK;

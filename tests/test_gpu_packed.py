@@ -1,0 +1,134 @@
+"""Packed KV formats on the device against the oracle (mlx-swift-lm PR #142,
+"Add packed paged KV formats with bounded workspace admission", section
+"Summary"): the quantising write_block produces the oracle's records byte for
+byte, gather_visible moves packed records bit-exactly, and paged_decode over
+the packed pages matches the oracle's fp64 attention over the same records
+(the oracle quantises the same bf16 inputs itself; nothing it reads comes
+from the device)."""
+
+import numpy as np
+import pytest
+import torch
+
+import decode_memory_amd as pd
+from oracle.packed import FORMATS, k_records, packed_decode_attention, record_bytes, v_records
+from oracle.slab_pool import SlabPoolModel
+from synth import (WORKLOADS, hadamard_signs, kv_bits_for_sequence, make_block_table,
+                   monotone_rows, q_bits, shuffled_rows)
+from tests.gpu_util import (assert_decode_close, from_device_bits, i32, to_device_bits,
+                            token_targets)
+
+pytestmark = pytest.mark.gpu
+
+BS = 32
+
+
+def _packed_pool(fmt, D, lengths, rows, seed, cap, n_kv=8, keep=None):
+    """Write every sequence through the quantising write_block; return the pool,
+    the oracle's records of the sequences in `keep` and the sign vector."""
+    kb, vb = FORMATS[fmt]
+    signs = hadamard_signs(seed, D)
+    pool = pd.SlabPool(1, BS, n_kv, D, 32, -(-cap // 32) + 2, fmt, hadamard_signs=signs)
+    pool.reserve_rows(cap)
+    recs = {}
+    for b, n in enumerate(lengths):
+        if n == 0:
+            continue
+        k, v = kv_bits_for_sequence(seed, 0, b, int(n), n_kv, D, "bf16")
+        r, s = token_targets(rows[b], int(n), BS)
+        pool.write_block(0, i32(r), i32(s), to_device_bits(k, "bf16"), to_device_bits(v, "bf16"))
+        if keep is None or b in keep:
+            recs[b] = (k_records(k, signs, kb), v_records(v, vb))
+    torch.cuda.synchronize()
+    return pool, recs, signs
+
+
+@pytest.mark.parametrize("fmt", ["k8v8", "k8v4", "k4v4"])
+@pytest.mark.parametrize("D", [64, 128, 256])
+def test_quantising_write_and_gather_are_bit_exact(fmt, D):
+    kb, vb = FORMATS[fmt]
+    lengths = [70, 1, 33, 0, 256]
+    rows, _, R = shuffled_rows(np.random.default_rng(D), lengths, BS, 32, spare_rows=2)
+    pool, recs, _ = _packed_pool(fmt, D, lengths, rows, 50 + D, R)
+    assert pool.k_record_bytes == record_bytes(D, kb) and pool.v_record_bytes == record_bytes(D, vb)
+    model = SlabPoolModel(1, BS, 8, record_bytes(D, kb), record_bytes(D, vb), 32)
+    model.reserve_rows(R)
+    for b, (kr, vr) in recs.items():
+        r, s = token_targets(rows[b], lengths[b], BS)
+        model.write(0, r, s, kr, vr)
+    for slab in range(model.n_slabs):
+        got_k = pool.slab_view(0, slab, "k").cpu().numpy()
+        got_v = pool.slab_view(0, slab, "v").cpu().numpy()
+        assert np.array_equal(got_k, model.k_slabs[0][slab]), (fmt, D, "K", slab)
+        assert np.array_equal(got_v, model.v_slabs[0][slab]), (fmt, D, "V", slab)
+    table = make_block_table(rows)
+    t_out = max(lengths)
+    gk = torch.empty((len(lengths), 8, t_out, pool.k_record_bytes), dtype=torch.uint8, device="cuda")
+    gv = torch.empty((len(lengths), 8, t_out, pool.v_record_bytes), dtype=torch.uint8, device="cuda")
+    pool.gather_visible(0, i32(table), i32(lengths), t_out, gk, gv)
+    ek, ev = model.gather_batched(0, table, lengths, t_out)
+    assert np.array_equal(gk.cpu().numpy(), ek) and np.array_equal(gv.cpu().numpy(), ev)
+    assert pool.check_error() == 0
+    pool.close()
+
+
+@pytest.mark.parametrize("fmt", ["k8v8", "k8v4", "k4v4"])
+@pytest.mark.parametrize("D,G", [(64, 4), (256, 4), (128, 2), (64, 1)])
+def test_packed_decode_matches_oracle(fmt, D, G):
+    lengths = [300, 1, 45, 0, 1024, 64]
+    rows, _, R = shuffled_rows(np.random.default_rng(D + G), lengths, BS, 32, spare_rows=2)
+    pool, recs, signs = _packed_pool(fmt, D, lengths, rows, 60 + D + G, R)
+    B = len(lengths)
+    q = q_bits(60 + D + G, 0, B, 8 * G, D, "bf16")
+    scale = 1.0 / np.sqrt(D)
+    kr = [recs[b][0] if b in recs else np.zeros((0, 8, pool.k_record_bytes), np.uint8) for b in range(B)]
+    vr = [recs[b][1] if b in recs else np.zeros((0, 8, pool.v_record_bytes), np.uint8) for b in range(B)]
+    ref = packed_decode_attention(q, kr, vr, signs, fmt, D, scale)
+    qd = to_device_bits(q, "bf16")
+    out = torch.empty_like(qd)
+    ws = pool.workspace(B, 8 * G, max(lengths))
+    pool.paged_decode(0, qd, i32(make_block_table(rows)), i32(lengths), max(lengths), scale, out, ws)
+    got = from_device_bits(out)
+    assert_decode_close(got, ref, "bf16", allow_output_rounding=True)
+    long = [b for b, n in enumerate(lengths) if n >= 300]
+    assert_decode_close(got[long], ref[long], "bf16")
+    assert not got[3].any()
+    assert pool.check_error() == 0
+    pool.close()
+
+
+@pytest.mark.parametrize("D", [64, 256])
+@pytest.mark.parametrize("fmt", ["k8v8", "k8v4", "k4v4"])
+def test_packed_workload_full_size_sampled(fmt, D):
+    """The packed workload at full size (16 x 16384 tokens, 8 kv heads, GQA 4):
+    every sequence is written and decoded on the device; the oracle checks the
+    records and outputs of sequences 0 and 15."""
+    w = WORKLOADS["packed_16x16k"]
+    lengths = [w.length] * w.batch
+    rows = monotone_rows(lengths, BS)
+    cap = int(rows[-1].max()) + 1
+    sample = (0, w.batch - 1)
+    pool, recs, signs = _packed_pool(fmt, D, lengths, rows, w.seed, cap, keep=sample)
+    q = q_bits(w.seed, 0, w.batch, w.n_q_heads, D, "bf16")
+    scale = 1.0 / np.sqrt(D)
+    qd = to_device_bits(q, "bf16")
+    out = torch.empty_like(qd)
+    table = make_block_table(rows)
+    ws = pool.workspace(w.batch, w.n_q_heads, w.length)
+    pool.paged_decode(0, qd, i32(table), i32(lengths), w.length, scale, out, ws)
+    got = from_device_bits(out)
+    # sampled records, through gather_visible of the sampled sequences
+    sub = table[list(sample)]
+    gk = torch.empty((2, 8, w.length, pool.k_record_bytes), dtype=torch.uint8, device="cuda")
+    gv = torch.empty((2, 8, w.length, pool.v_record_bytes), dtype=torch.uint8, device="cuda")
+    pool.gather_visible(0, i32(sub), i32([w.length] * 2), w.length, gk, gv)
+    gk, gv = gk.cpu().numpy(), gv.cpu().numpy()
+    for i, b in enumerate(sample):
+        assert np.array_equal(gk[i], recs[b][0].transpose(1, 0, 2)), (fmt, D, b)
+        assert np.array_equal(gv[i], recs[b][1].transpose(1, 0, 2)), (fmt, D, b)
+    ref = packed_decode_attention(q[list(sample)], [recs[b][0] for b in sample],
+                                  [recs[b][1] for b in sample], signs, fmt, D, scale)
+    err = assert_decode_close(got[list(sample)], ref, "bf16")
+    print(f"packed {fmt} D={D}: max-abs {err:.2e}")
+    assert pool.check_error() == 0
+    pool.close()

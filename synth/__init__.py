@@ -11,12 +11,14 @@ from .inputs import (  # noqa: F401
     Workload,
     bf16_bits_from_f32,
     bits_to_f32,
+    device_seed,
     f16_bits_from_f32,
     hadamard_signs,
     kv_bits_for_sequence,
     make_block_table,
     monotone_rows,
     normal_bits,
+    normal_device,
     q_bits,
     shuffled_rows,
     workload_lengths,

@@ -81,6 +81,25 @@ def q_bits(seed: int, layer: int, batch: int, n_q: int, head_dim: int, dtype: st
                        (batch, n_q, head_dim), dtype)
 
 
+def device_seed(key) -> int:
+    """Fold an integer tuple into one 63-bit seed for a device generator."""
+    state = np.random.SeedSequence(list(key)).generate_state(2, np.uint32)
+    return int((int(state[0]) << 31) ^ int(state[1])) & ((1 << 63) - 1)
+
+
+def normal_device(key, shape, dtype: str, device):
+    """N(0,1) samples drawn on the device with torch's seeded generator and
+    rounded to fp16/bf16 (torch's nearest-even cast).  Used for the 56 GiB
+    long-context workload, which is too large to generate on the host; a test
+    copies the sequences it checks back to the host for the oracle."""
+    import torch
+
+    g = torch.Generator(device=device)
+    g.manual_seed(device_seed(key))
+    x = torch.randn(shape, generator=g, device=device, dtype=torch.float32)
+    return x.to(torch.float16 if dtype == FP16 else torch.bfloat16)
+
+
 def hadamard_signs(seed: int, head_dim: int) -> np.ndarray:
     """The fixed +-1 sign vector of the signed Hadamard basis, int8 [D]."""
     rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, 1 << 21])))

@@ -14,10 +14,11 @@ KV, far more than the last-level cache, so every layer is read from HBM.
 
 Prints one JSON line.  `value` is the step's algorithmic HBM bytes (KV read
 by paged_decode, q in, out, block table, lens, plus write_block's bytes)
-divided by the measured step time; `roofline` is paged_decode alone: its
-algorithmic bytes per launch over its average launch duration, measured with
-HIP events recorded on the launch stream around every decode launch of the
-timed steps.  `cpu_baseline` times the CPU oracle (numpy, fp64) on a bounded
+divided by the measured step time; `roofline` is paged_decode's dominant kernel
+(the split stage): its algorithmic bytes per launch over its average launch
+duration, measured live with HIP events on the launch stream around 28-launch
+runs of that stage (the combine stage is timed the same way and reported
+beside).  `cpu_baseline` times the CPU oracle (numpy, fp64) on a bounded
 sample of the same workload.
 """
 
@@ -36,6 +37,38 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X published HBM3E bandwidth
+CALIB_COPY_BYTES = 256 << 20
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "paged_decode_qwen3_0p6b_8x4k_traffic.md")
+DECODE_SOURCES = ("paged_decode_row.hip", "device_common.h")
+
+
+def decode_source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for name in DECODE_SOURCES:
+        with open(os.path.join(ROOT, "decode_memory_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per paged_decode launch from the committed counter profile,
+    or None when the profile is missing or the kernel changed since."""
+    try:
+        text = open(TRAFFIC_PROFILE).read()
+    except OSError:
+        return None
+    fields = {}
+    for line in text.splitlines():
+        if line.startswith("- ") and ":" in line:
+            k, v = line[2:].split(":", 1)
+            fields[k.strip()] = v.strip().strip("`")
+    if fields.get("kernel_source_sha256") != decode_source_hash():
+        return None
+    try:
+        return int(fields["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def decode_bytes(lengths, n_kv, n_q, D, block_size, kv_bytes_per_token_head=None):
@@ -140,39 +173,50 @@ def main() -> int:
 
     stream = torch.cuda.current_stream()
 
-    def step(events=None):
+    def step():
         for layer in range(L):
             pool.write_block(layer, new_rows, new_slots, k_new[layer], v_new[layer])
-            if events is not None:
-                events[layer][0].record(stream)
             pool.paged_decode(layer, qs[layer], table, lens, n, w.scale, outs[layer], ws)
-            if events is not None:
-                events[layer][1].record(stream)
+
+    def stage_pass(stage):
+        for layer in range(L):
+            pool.paged_decode(layer, qs[layer], table, lens, n, w.scale, outs[layer], ws,
+                              stage=stage)
+
+    def timed(fn, reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / reps  # microseconds per call of fn
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
 
-    # timed region: exactly `steps` steps between two synchronised events
-    ev = [[[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(L)]
-          for _ in range(args.steps)]
-    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0.record(stream)
-    for k in range(args.steps):
-        step(ev[k])
-    t1.record(stream)
-    torch.cuda.synchronize()
-    step_ms = t0.elapsed_time(t1) / args.steps
-    decode_us = [e[0].elapsed_time(e[1]) * 1e3 for s in ev for e in s]
+    # timed region: exactly `steps` full steps between two synchronised events
+    step_ms = timed(step, args.steps) / 1e3
     if pool.check_error():
         raise RuntimeError("device error during the timed steps")
+
+    # per-kernel durations, live: the split stage (the dominant kernel) of all
+    # 28 layers back to back, then the combine stage, each between two events
+    for _ in range(2):
+        stage_pass("split")
+        stage_pass("combine")
+    split_us = timed(lambda: stage_pass("split"), args.steps) / L
+    combine_us = timed(lambda: stage_pass("combine"), args.steps) / L
+    stage_pass("split")
+    stage_pass("combine")
+    torch.cuda.synchronize()
 
     d_bytes = decode_bytes(lengths, n_kv, n_q, D, bs)
     w_bytes = write_bytes(B, n_kv, D)
     step_bytes = L * (d_bytes + w_bytes)
-    kernel_us = float(np.mean(decode_us))
-    achieved = d_bytes / (kernel_us * 1e-6) / 1e9
+    achieved = d_bytes / (split_us * 1e-6) / 1e9
 
     # gather_visible of one layer to contiguous [B, n_kv, T, D] (reported beside)
     gk = torch.empty((B, n_kv, n, D), dtype=torch.bfloat16, device=dev)
@@ -188,6 +232,14 @@ def main() -> int:
     torch.cuda.synchronize()
     g_us = g0.elapsed_time(g1) * 1e3 / g_iters
     g_bytes = 2 * 2 * B * n * n_kv * D * 2 + B * (n // bs) * 4
+
+    # A plain device copy of known size: the scale for HBM byte counters read
+    # by a profiler over this same run (outside every timed region).
+    calib = torch.empty(CALIB_COPY_BYTES, dtype=torch.uint8, device=dev)
+    calib_dst = torch.empty_like(calib)
+    calib_dst.copy_(calib)
+    torch.cuda.synchronize()
+    del calib, calib_dst
 
     result = {
         "metric": "paged_decode achieved HBM GB/s (% of peak) + KV tokens attended/sec",
@@ -209,10 +261,14 @@ def main() -> int:
         "pct_of_peak": round(100.0 * step_bytes / (step_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
         "kv_tokens_attended_per_s": round(sum(lengths) * L / (step_ms * 1e-3), 1),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel": "paged_decode_kernel<128,2,bf16,32>",
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic(),
+                     "kernel": "paged_decode_row_kernel<128,2,true,2> (split stage)",
+                     "kernel_source_sha256": decode_source_hash(),
                      "algorithmic_bytes_per_launch": d_bytes,
-                     "avg_launch_us": round(kernel_us, 3)},
+                     "avg_launch_us": round(split_us, 3)},
+        "paged_decode": {"split_us": round(split_us, 3), "combine_us": round(combine_us, 3),
+                         "achieved_gbs_both_stages": round(d_bytes / ((split_us + combine_us) * 1e-6) / 1e9, 1)},
         "write_block": {"bytes_per_launch": w_bytes},
         "gather_visible": {"us_per_layer": round(g_us, 2), "bytes_per_layer": g_bytes,
                            "achieved_gbs": round(g_bytes / (g_us * 1e-6) / 1e9, 1)},

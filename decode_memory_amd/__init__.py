@@ -62,7 +62,7 @@ EXPORTS = [
     "pd_version", "pd_last_error", "pd_record_bytes", "pd_pool_create", "pd_pool_destroy",
     "pd_slab_bytes", "pd_append_slab", "pd_slabs_needed", "pd_reserve_rows", "pd_slab_for_row",
     "pd_write_block", "pd_gather_visible", "pd_decode_workspace_bytes", "pd_paged_decode",
-    "pd_pool_stats", "pd_pool_check_error",
+    "pd_paged_decode_split", "pd_paged_decode_combine", "pd_pool_stats", "pd_pool_check_error",
 ]
 
 _lib_handle = None
@@ -88,6 +88,10 @@ def _declare(lib):
         "pd_decode_workspace_bytes": (_i32, [_vp, _i32, _i32, _i32, ctypes.POINTER(_sz)]),
         "pd_paged_decode": (_i32, [_vp, _i32, _i32, _i32, _vp, _vp, _i32, _vp, _i32,
                                    ctypes.c_float, _vp, _vp, _sz, _vp]),
+        "pd_paged_decode_split": (_i32, [_vp, _i32, _i32, _i32, _vp, _vp, _i32, _vp, _i32,
+                                         ctypes.c_float, _vp, _vp, _sz, _vp]),
+        "pd_paged_decode_combine": (_i32, [_vp, _i32, _i32, _i32, _vp, _vp, _i32, _vp, _i32,
+                                           ctypes.c_float, _vp, _vp, _sz, _vp]),
         "pd_pool_stats": (_i32, [_vp, ctypes.POINTER(PoolStats)]),
         "pd_pool_check_error": (_i32, [_vp, _vp, _p_i32]),
     }
@@ -238,7 +242,10 @@ def decode_workspace_bytes(pool: int, B: int, n_q_heads: int, max_len: int) -> i
 
 def paged_decode(pool: int, layer: int, q: torch.Tensor, block_table: torch.Tensor,
                  lens: torch.Tensor, max_len: int, scale: float, out: torch.Tensor,
-                 workspace: torch.Tensor, stream=None) -> None:
+                 workspace: torch.Tensor, stream=None, stage: str = "all") -> None:
+    """stage: "all" (pd_paged_decode), "split" or "combine" (its two stages)."""
+    fn = {"all": "pd_paged_decode", "split": "pd_paged_decode_split",
+          "combine": "pd_paged_decode_combine"}[stage]
     B, n_q, _ = q.shape
     _require(q, "q")
     _require(block_table, "block_table", torch.int32)
@@ -247,7 +254,7 @@ def paged_decode(pool: int, layer: int, q: torch.Tensor, block_table: torch.Tens
     _require(workspace, "workspace")
     if block_table.shape[0] != B:
         raise ValueError("block_table rows must equal the batch size")
-    _check(lib().pd_paged_decode(pool, layer, B, n_q, _ptr(q), _ptr(block_table),
+    _check(getattr(lib(), fn)(pool, layer, B, n_q, _ptr(q), _ptr(block_table),
                                  block_table.shape[1], _ptr(lens), max_len, float(scale), _ptr(out),
                                  _ptr(workspace), workspace.numel() * workspace.element_size(),
                                  _stream(stream)))
@@ -349,9 +356,9 @@ class SlabPool:
         return torch.empty(max(n, 256), dtype=torch.uint8, device=self.device)
 
     def paged_decode(self, layer, q, block_table, lens, max_len, scale, out, workspace,
-                     stream=None):
+                     stream=None, stage="all"):
         paged_decode(self.handle, layer, q, block_table, lens, max_len, scale, out, workspace,
-                     stream)
+                     stream, stage)
 
     def stats(self) -> dict:
         return pool_stats(self.handle)

@@ -459,10 +459,13 @@ pd_status pd_decode_workspace_bytes(const pd_pool* p, int32_t B, int32_t n_q_hea
   return PD_OK;
 }
 
-pd_status pd_paged_decode(pd_pool* p, int32_t layer, int32_t B, int32_t n_q_heads, const void* q,
-                          const int32_t* block_table, int32_t max_blocks, const int32_t* lens,
-                          int32_t max_len, float scale, void* out, void* workspace,
-                          size_t workspace_bytes, hipStream_t stream) {
+// Stages of paged_decode run by decode_call.
+static const int kStageSplit = 1, kStageCombine = 2;
+
+static pd_status decode_call(pd_pool* p, int32_t layer, int32_t B, int32_t n_q_heads, const void* q,
+                      const int32_t* block_table, int32_t max_blocks, const int32_t* lens,
+                      int32_t max_len, float scale, void* out, void* workspace,
+                      size_t workspace_bytes, hipStream_t stream, int stages) {
   if (pd_status st = check_pool(p)) return st;
   if (pd_status st = check_layer(p, layer)) return st;
   if (B < 0 || max_blocks < 1 || max_len < 0) return fail(PD_ERR_ARG, "B < 0, max_blocks < 1 or max_len < 0");
@@ -509,17 +512,44 @@ pd_status pd_paged_decode(pd_pool* p, int32_t layer, int32_t B, int32_t n_q_head
   a.inv_sqrt_d = p->inv_sqrt_d;
   const bool bf16 = p->desc.format == PD_FMT_BF16;
   const int32_t D = p->desc.head_dim;
-  hipError_t e;
-  switch (plan.kind) {
-    case 1: e = launch_paged_decode_row(a, bf16, D, group, plan.kpl, stream); break;
-    case 2: e = launch_paged_decode_packed(a, D, group, stream); break;
-    default: e = launch_paged_decode_column(a, bf16, D, group, stream); break;
+  hipError_t e = hipSuccess;
+  if (stages & kStageSplit) {
+    switch (plan.kind) {
+      case 1: e = launch_paged_decode_row(a, bf16, D, group, plan.kpl, stream); break;
+      case 2: e = launch_paged_decode_packed(a, D, group, stream); break;
+      default: e = launch_paged_decode_column(a, bf16, D, group, stream); break;
+    }
   }
   // packed pools produce bf16 outputs
-  if (e == hipSuccess) e = launch_decode_combine(a, bf16 || plan.kind == 2, D, stream);
+  if (e == hipSuccess && (stages & kStageCombine))
+    e = launch_decode_combine(a, bf16 || plan.kind == 2, D, stream);
   if (e == hipErrorInvalidValue) return fail(PD_ERR_UNSUPPORTED, "no decode kernel for this shape");
   if (e != hipSuccess) return hip_fail(e, "paged_decode launch");
   return PD_OK;
+}
+
+pd_status pd_paged_decode(pd_pool* p, int32_t layer, int32_t B, int32_t n_q_heads, const void* q,
+                          const int32_t* block_table, int32_t max_blocks, const int32_t* lens,
+                          int32_t max_len, float scale, void* out, void* workspace,
+                          size_t workspace_bytes, hipStream_t stream) {
+  return decode_call(p, layer, B, n_q_heads, q, block_table, max_blocks, lens, max_len, scale, out,
+                     workspace, workspace_bytes, stream, kStageSplit | kStageCombine);
+}
+
+pd_status pd_paged_decode_split(pd_pool* p, int32_t layer, int32_t B, int32_t n_q_heads,
+                                const void* q, const int32_t* block_table, int32_t max_blocks,
+                                const int32_t* lens, int32_t max_len, float scale, void* out,
+                                void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return decode_call(p, layer, B, n_q_heads, q, block_table, max_blocks, lens, max_len, scale, out,
+                     workspace, workspace_bytes, stream, kStageSplit);
+}
+
+pd_status pd_paged_decode_combine(pd_pool* p, int32_t layer, int32_t B, int32_t n_q_heads,
+                                  const void* q, const int32_t* block_table, int32_t max_blocks,
+                                  const int32_t* lens, int32_t max_len, float scale, void* out,
+                                  void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return decode_call(p, layer, B, n_q_heads, q, block_table, max_blocks, lens, max_len, scale, out,
+                     workspace, workspace_bytes, stream, kStageCombine);
 }
 
 pd_status pd_pool_stats(const pd_pool* p, pd_stats* s) {

@@ -243,6 +243,22 @@ pd_status pd_paged_decode(pd_pool* pool, int32_t layer, int32_t B, int32_t n_q_h
                           const int32_t* lens, int32_t max_len, float scale, void* out,
                           void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * The two stages of pd_paged_decode as separate calls, same arguments and
+ * checks: _split writes the per-split partials into the workspace, _combine
+ * merges them into `out`.  pd_paged_decode == _split then _combine on one
+ * stream.  For callers that place other work between the stages and for
+ * per-stage timing.
+ */
+pd_status pd_paged_decode_split(pd_pool* pool, int32_t layer, int32_t B, int32_t n_q_heads,
+                                const void* q, const int32_t* block_table, int32_t max_blocks,
+                                const int32_t* lens, int32_t max_len, float scale, void* out,
+                                void* workspace, size_t workspace_bytes, hipStream_t stream);
+pd_status pd_paged_decode_combine(pd_pool* pool, int32_t layer, int32_t B, int32_t n_q_heads,
+                                  const void* q, const int32_t* block_table, int32_t max_blocks,
+                                  const int32_t* lens, int32_t max_len, float scale, void* out,
+                                  void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* Pool counters (host output).  mlxcel #235: slab-append counter and
  * bytes_reserved summed over slabs. */
 pd_status pd_pool_stats(const pd_pool* pool, pd_stats* stats);

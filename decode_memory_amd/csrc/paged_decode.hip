@@ -294,9 +294,13 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(DecodeArgs a) {
   const float* acc = a.partials + static_cast<size_t>(hq) * n_split * D + d;
   const float* ml = a.partials + a.ml_offset;
 
+  // The first kChunk splits' values are loaded before the sequence length is
+  // known (they are in bounds of the workspace whatever it is); values of
+  // inactive splits are never used.
+  const int n_pre = min(n_split, kChunk);
   float v[kChunk];
 #pragma unroll
-  for (int k = 0; k < kChunk; ++k) v[k] = k < n_act ? acc[k * D] : 0.f;
+  for (int k = 0; k < kChunk; ++k) v[k] = (k < n_pre && hq < total) ? acc[k * D] : 0.f;
   for (int i = threadIdx.x; i < HPW * kMaxSplits; i += kThreads) {
     const int h = i / kMaxSplits, sp = i % kMaxSplits;
     const int hq2 = blockIdx.x * HPW + h;
@@ -328,7 +332,7 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(DecodeArgs a) {
   float A = 0.f;
 #pragma unroll
   for (int k = 0; k < kChunk; ++k)
-    if (k < n_act) A = fmaf(v[k], s_w[hloc][k], A);
+    A = (k < n_act) ? fmaf(v[k], s_w[hloc][k], A) : A;
   for (int sp = kChunk; sp < n_act; ++sp) A = fmaf(acc[sp * D], s_w[hloc][sp], A);
   static_cast<uint16_t*>(a.out)[static_cast<size_t>(hq) * D + d] = f32_to_out<BF16>(A * s_inv[hloc]);
 }

@@ -20,12 +20,18 @@
 // whole split, so the online softmax state (running max, sum and the lane's 8
 // output columns per query head) stays in the lane group: the only
 // cross-lane operation per token is the DPP reduction that finishes each dot
-// product.  Each wave keeps two tiles of K/V loads in flight (the next tile
-// is requested before the current one is consumed) and the kernel fits four
-// waves per SIMD, so a CU has about 256 KiB of reads outstanding -- what
-// HBM3E needs to run near its streaming rate.  The waves merge through LDS
-// and the workgroup writes one partial (max, sum, weighted V) per query head
-// and split; a combine kernel merges the splits.
+// product.  Each wave keeps PAGEDKV_ROW_TILES_IN_FLIGHT tiles of K/V loads in
+// flight (tile i + 2 is requested before tile i is consumed); with one
+// 8-wave workgroup per CU that is 128-192 KiB of reads outstanding per CU,
+// several times what HBM3E needs to run at its streaming rate.
+//
+// A block's address costs one dependent global read: the layer's slab
+// pointer tables are staged in LDS while the block-table reads are in
+// flight.  At the end each wave stages its state in LDS and the last wave of
+// each head group to finish merges the group's slices in slice order (so the
+// result does not depend on which wave that is) and writes one partial (max,
+// sum, weighted V) per query head and split; a combine kernel merges the
+// splits.
 #include "device_common.h"
 #include "internal.h"
 
@@ -39,16 +45,26 @@ namespace {
 #ifndef PAGEDKV_ROW_WAVES
 #define PAGEDKV_ROW_WAVES 8
 #endif
+// Most head groups (1 KiB of a token row each) one workgroup covers.
+#ifndef PAGEDKV_ROW_MAX_HEAD_GROUPS
+#define PAGEDKV_ROW_MAX_HEAD_GROUPS 4
+#endif
+#ifndef PAGEDKV_ROW_WAVES_PER_SIMD
+#define PAGEDKV_ROW_WAVES_PER_SIMD 2
+#endif
 
 constexpr int kRowWaves = PAGEDKV_ROW_WAVES;  // waves per workgroup
 constexpr int kRowThreads = kRowWaves * kWave;
 constexpr int kTile = 4;                     // tokens per wave per tile
 constexpr int kBuf = PAGEDKV_ROW_TILES_IN_FLIGHT;  // tiles a wave keeps in flight
 constexpr int kBS = 32;                      // tokens per block
+constexpr int kLdsSlabs = 2 * kRowThreads;   // slab pointers staged in LDS
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+// K/V bytes are read once per call: non-temporal loads keep them from
+// displacing the block tables, slab pointers and partials in L2.
 __device__ __forceinline__ uint4 gload16(const char* base, uint32_t off) {
-  const u32x4 v = *(const __attribute__((address_space(1))) u32x4*)(base + off);
+  const u32x4 v = __builtin_nontemporal_load((const __attribute__((address_space(1))) u32x4*)(base + off));
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
@@ -68,7 +84,7 @@ struct Tile {
 // D: head_dim, G: query heads per kv head, HGW: head groups (of HPL =
 // 64/(D/8) kv heads, one 1 KiB wave load per token) per workgroup.
 template <int D, int G, bool BF16, int HGW>
-__global__ __launch_bounds__(kRowThreads, 2) void paged_decode_row_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(kRowThreads, PAGEDKV_ROW_WAVES_PER_SIMD) void paged_decode_row_kernel(DecodeArgs a) {
   constexpr int LPT = D / 8;              // lanes per head vector (16 B each)
   constexpr int HPL = kWave / LPT;        // kv heads per wave load
   constexpr int HG = HPL * HGW;           // kv heads per workgroup
@@ -79,6 +95,9 @@ __global__ __launch_bounds__(kRowThreads, 2) void paged_decode_row_kernel(Decode
   __shared__ float s_m[kRowWaves][HPL * G];
   __shared__ float s_l[kRowWaves][HPL * G];
   __shared__ float s_acc[kRowWaves][HPL * G][D];
+  __shared__ uint64_t s_kt[kLdsSlabs];  // slab base pointers of the layer
+  __shared__ uint64_t s_vt[kLdsSlabs];
+  __shared__ int s_done[HGW];           // waves of each head group that finished
 
   const int lane = threadIdx.x % kWave;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -120,6 +139,33 @@ __global__ __launch_bounds__(kRowThreads, 2) void paged_decode_row_kernel(Decode
   const uint32_t tok_bytes = static_cast<uint32_t>(n_kv) * D * 2;
   const size_t row_bytes = static_cast<size_t>(kBS) * tok_bytes;
   const bool row_ok = row >= 0 && row < lv.capacity_rows;
+
+  // The layer's slab pointer tables go to LDS while the block-table reads
+  // are in flight, so a block's address costs one global read (its row), not
+  // two; slabs past kLdsSlabs are looked up in global memory.
+  {
+    const int n_slabs = static_cast<int>(lv.capacity_rows / lv.slab_blocks);
+    const int t0 = threadIdx.x, t1 = threadIdx.x + kRowThreads;
+    uint64_t k0 = 0, v0 = 0, k1 = 0, v1 = 0;
+    if (t0 < n_slabs && t0 < kLdsSlabs) {
+      k0 = reinterpret_cast<uint64_t>(lv.k_tab[t0]);
+      v0 = reinterpret_cast<uint64_t>(lv.v_tab[t0]);
+    }
+    if (t1 < n_slabs && t1 < kLdsSlabs) {
+      k1 = reinterpret_cast<uint64_t>(lv.k_tab[t1]);
+      v1 = reinterpret_cast<uint64_t>(lv.v_tab[t1]);
+    }
+    if (t0 < kLdsSlabs) {
+      s_kt[t0] = k0;
+      s_vt[t0] = v0;
+    }
+    if (t1 < kLdsSlabs) {
+      s_kt[t1] = k1;
+      s_vt[t1] = v1;
+    }
+    if (threadIdx.x < HGW) s_done[threadIdx.x] = 0;
+  }
+  __syncthreads();
   uint64_t kaddr = 0, vaddr = 0;
   {
     // a row outside the pool is read as row 0 of slab 0 and masked below
@@ -127,8 +173,13 @@ __global__ __launch_bounds__(kRowThreads, 2) void paged_decode_row_kernel(Decode
     const int slab = r / lv.slab_blocks;
     const size_t off = (r - slab * lv.slab_blocks) * row_bytes;
     if (lv.capacity_rows > 0) {
-      kaddr = reinterpret_cast<uint64_t>(lv.k_tab[slab]) + off;
-      vaddr = reinterpret_cast<uint64_t>(lv.v_tab[slab]) + off;
+      if (slab < kLdsSlabs) {
+        kaddr = s_kt[slab] + off;
+        vaddr = s_vt[slab] + off;
+      } else {
+        kaddr = reinterpret_cast<uint64_t>(lv.k_tab[slab]) + off;
+        vaddr = reinterpret_cast<uint64_t>(lv.v_tab[slab]) + off;
+      }
     }
   }
 
@@ -233,7 +284,10 @@ __global__ __launch_bounds__(kRowThreads, 2) void paged_decode_row_kernel(Decode
   }
 
   // Stage each wave's state in LDS (lane c of group lg holds columns
-  // c*8..c*8+7 of its kv head's query heads), then merge the slices.
+  // c*8..c*8+7 of its kv head's query heads).  The last wave of a head group
+  // to get here merges the group's slices in slice order -- the result does
+  // not depend on which wave that is -- and writes the partial; the others
+  // are done.
 #pragma unroll
   for (int jq = 0; jq < G; ++jq) {
     const int hq = lg * G + jq;
@@ -244,29 +298,38 @@ __global__ __launch_bounds__(kRowThreads, 2) void paged_decode_row_kernel(Decode
       s_l[wave][hq] = l[jq];
     }
   }
-  __syncthreads();
+  int arrived = 0;
+  if (lane == 0)
+    arrived = __hip_atomic_fetch_add(&s_done[hgw], 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_WORKGROUP);
+  arrived = __builtin_amdgcn_readfirstlane(arrived);
+  if (arrived != SLICES - 1) return;
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
 
   float* part_acc = a.partials;
   float* part_ml = a.partials + a.ml_offset;
-  for (int idx = threadIdx.x; idx < HGW * HPL * G * D; idx += kRowThreads) {
-    const int d = idx % D;
-    const int hq = (idx / D) % (HPL * G);
-    const int g2 = idx / (D * HPL * G);  // head group inside the workgroup
+#pragma unroll
+  for (int jq = 0; jq < G; ++jq) {
+    const int hq = lg * G + jq;
     float M = -INFINITY;
 #pragma unroll
-    for (int sl = 0; sl < SLICES; ++sl) M = fmaxf(M, s_m[sl * HGW + g2][hq]);
-    float L = 0.f, A = 0.f;
+    for (int sl = 0; sl < SLICES; ++sl) M = fmaxf(M, s_m[sl * HGW + hgw][hq]);
+    float L = 0.f, A[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) A[e] = 0.f;
 #pragma unroll
     for (int sl = 0; sl < SLICES; ++sl) {
-      const int wv = sl * HGW + g2;
+      const int wv = sl * HGW + hgw;
       const float mw = s_m[wv][hq];
       const float f = (mw == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mw - M);
       L = fmaf(s_l[wv][hq], f, L);
-      A = fmaf(s_acc[wv][hq][d], f, A);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) A[e] = fmaf(s_acc[wv][hq][c * 8 + e], f, A[e]);
     }
-    const size_t hs = (static_cast<size_t>(b) * a.n_q + (hset * HG + g2 * HPL) * G + hq) * n_split + s;
-    part_acc[hs * D + d] = A;
-    if (d == 0) {
+    const size_t hs = (static_cast<size_t>(b) * a.n_q + kvh * G + jq) * n_split + s;
+    float4* dst = reinterpret_cast<float4*>(part_acc + hs * D + c * 8);
+    dst[0] = make_float4(A[0], A[1], A[2], A[3]);
+    dst[1] = make_float4(A[4], A[5], A[6], A[7]);
+    if (c == 0) {
       part_ml[hs * 2] = M;
       part_ml[hs * 2 + 1] = L;
     }
@@ -318,9 +381,9 @@ int row_kernel_kpl(int32_t n_kv, int32_t head_dim, int32_t group, int32_t block_
   const int hpl = kWave / (head_dim / 8);
   if (n_kv % hpl) return 0;
   const int n_groups = n_kv / hpl;
-  for (int hgw : {4, 2, 1})  // whole token rows per workgroup where possible
-    if (hgw <= kRowWaves && kRowWaves % hgw == 0 && n_groups % hgw == 0 &&
-        (kRowWaves / hgw) * kTile <= kBS)
+  for (int hgw : {4, 2, 1})  // as many head groups per workgroup as allowed
+    if (hgw <= PAGEDKV_ROW_MAX_HEAD_GROUPS && hgw <= kRowWaves && kRowWaves % hgw == 0 &&
+        n_groups % hgw == 0 && (kRowWaves / hgw) * kTile <= kBS)
       return hgw;
   return 0;
 }

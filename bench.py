@@ -1,10 +1,10 @@
 #!/usr/bin/env python3
 """Benchmark of the paged-decode hot path on one MI355X.
 
-Workload: the qwen3-0.6b-shaped decode batch -- 28 layers, 8 sequences x 4096
-visible tokens, block 32, 32 blocks per slab, 16 query / 8 kv heads, head_dim
-128, bf16, N(0,1) K/V/Q from fixed seeds, rows allocated monotonically per
-sequence (4 same-slab runs each).
+Default workload: the qwen3-0.6b-shaped decode batch -- 28 layers, 8
+sequences x 4096 visible tokens, block 32, 32 blocks per slab, 16 query / 8
+kv heads, head_dim 128, bf16, N(0,1) K/V/Q from fixed seeds, rows allocated
+monotonically per sequence (4 same-slab runs each).
 
 A step is one decode step of the whole batch: for each of the 28 layers,
 write_block stores each sequence's newest token (position len-1) into its
@@ -16,10 +16,25 @@ Prints one JSON line.  `value` is the step's algorithmic HBM bytes (KV read
 by paged_decode, q in, out, block table, lens, plus write_block's bytes)
 divided by the measured step time; `roofline` is paged_decode's dominant kernel
 (the split stage): its algorithmic bytes per launch over its average launch
-duration, measured live with HIP events on the launch stream around 28-launch
-runs of that stage (the combine stage is timed the same way and reported
-beside).  `cpu_baseline` times the CPU oracle (numpy, fp64) on a bounded
-sample of the same workload.
+duration, measured live with HIP events on the launch stream around runs of
+that stage over every layer (the combine stage is timed the same way and
+reported beside).  `cpu_baseline` times the CPU oracle (numpy, fp64) on a
+bounded sample of the same workload.
+
+`--workload` selects one of the other workloads instead, each printed as its
+own JSON line of the same form:
+  fragmented_64      64 sequences of U{512..16384} tokens on rows popped from a
+                     shuffled free list; a step writes one new token per
+                     sequence (a fresh row at each block boundary) and decodes.
+  qwen3_1p7b_32x16k  28 layers x 32 sequences x 16384 tokens (56 GiB of KV); the
+                     same step as the default, plus gather_visible of a layer
+                     to [32, 8, 16384, 128] per tensor.
+  packed_16x16k      16 sequences x 16384 tokens, 8 kv / 32 q heads, head_dim 64
+                     and 256, bf16 and the packed formats K8V8, K8V4, K4V4;
+                     decode calls rotate over enough pool layers that the
+                     last-level cache cannot serve repeats.
+Their K/V come from the seeded device generator (the parity tests use the
+host generator at the same shapes).
 """
 
 from __future__ import annotations
@@ -40,6 +55,8 @@ HBM_PEAK_GBS = 8000.0  # MI355X published HBM3E bandwidth
 CALIB_COPY_BYTES = 256 << 20
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "paged_decode_qwen3_0p6b_8x4k_traffic.md")
 DECODE_SOURCES = ("paged_decode_row.hip", "device_common.h")
+METRIC = "paged_decode achieved HBM GB/s (% of peak) + KV tokens attended/sec"
+MALL_BYTES = 256 << 20  # last-level cache of the MI355X
 
 
 def decode_source_hash() -> str:
@@ -72,16 +89,28 @@ def measured_traffic():
 
 
 def decode_bytes(lengths, n_kv, n_q, D, block_size, kv_bytes_per_token_head=None):
-    """Algorithmic bytes of one paged_decode launch."""
+    """Algorithmic bytes of one paged_decode launch: K+V of the visible
+    tokens, q in, out, the block-table entries in use and the lengths."""
     kvb = 4 * D if kv_bytes_per_token_head is None else kv_bytes_per_token_head
     nb = sum(-(-int(n) // block_size) for n in lengths)
     B = len(lengths)
     return int(sum(lengths)) * n_kv * kvb + B * n_q * D * 2 * 2 + nb * 4 + 4 * B
 
 
-def write_bytes(n_tokens, n_kv, D):
-    """Algorithmic bytes of one write_block launch (read src, write slabs, rows, slots)."""
-    return n_tokens * n_kv * D * 2 * 2 * 2 + n_tokens * 8
+def write_bytes(n_tokens, n_kv, D, k_rec=None, v_rec=None):
+    """Algorithmic bytes of one write_block launch (read the 16-bit source,
+    write the records, rows, slots)."""
+    k_rec = 2 * D if k_rec is None else k_rec
+    v_rec = 2 * D if v_rec is None else v_rec
+    return n_tokens * n_kv * (2 * D * 2 + k_rec + v_rec) + n_tokens * 8
+
+
+def blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        return max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        return os.cpu_count()
 
 
 def cpu_baseline(w, target_s: float):
@@ -90,11 +119,6 @@ def cpu_baseline(w, target_s: float):
     from oracle.attention import decode_attention_bits
     from synth import kv_bits_for_sequence, q_bits
 
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    except Exception:  # pragma: no cover
-        cores = os.cpu_count()
     lengths = [w.length] * w.batch
     elapsed, layers = 0.0, 0
     while elapsed < target_s and layers < w.n_layers:
@@ -110,35 +134,104 @@ def cpu_baseline(w, target_s: float):
         "value": round(nbytes / elapsed / 1e9, 3),
         "unit": "GB/s",
         "tokens_attended_per_s": round(sum(lengths) * layers / elapsed, 1),
-        "cores": int(cores),
+        "cores": int(blas_threads()),
         "kind": "oracle",
         "sample": f"{layers} of {w.n_layers} layers of the same batch ({w.batch} x {w.length} "
                   f"tokens), numpy fp64 decode_attention, {elapsed:.1f} s",
     }
 
 
-def main() -> int:
-    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--cpu-seconds", type=float, default=10.0,
-                    help="CPU-oracle work to time for cpu_baseline (0 disables)")
-    args = ap.parse_args()
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: the paged-decode path here runs on a single "
-              "MI355X (a multi-GPU layout would shard sequences or kv heads with no exchange).",
-              file=sys.stderr)
-        return 2
+def cpu_baseline_sequences(w, lengths, target_s: float):
+    """The oracle's fp64 decode one sequence at a time (layer 0 of the
+    workload's seeded data), until about target_s seconds have been timed."""
+    from oracle.attention import decode_attention_bits
+    from synth import kv_bits_for_sequence, q_bits
 
-    import torch
+    q = q_bits(w.seed, 0, len(lengths), w.n_q_heads, w.head_dim, w.dtype)
+    elapsed, done = 0.0, []
+    for b, n in enumerate(lengths):
+        if elapsed >= target_s:
+            break
+        k, v = kv_bits_for_sequence(w.seed, 0, b, int(n), w.n_kv_heads, w.head_dim, w.dtype)
+        t0 = time.perf_counter()
+        decode_attention_bits(q[b:b + 1], [k], [v], w.dtype, w.scale)
+        elapsed += time.perf_counter() - t0
+        done.append(int(n))
+    nbytes = decode_bytes(done, w.n_kv_heads, w.n_q_heads, w.head_dim, w.block_size)
+    return {
+        "value": round(nbytes / elapsed / 1e9, 3),
+        "unit": "GB/s",
+        "tokens_attended_per_s": round(sum(done) / elapsed, 1),
+        "cores": int(blas_threads()),
+        "kind": "oracle",
+        "sample": f"{len(done)} of {len(lengths)} sequences of layer 0 ({sum(done)} tokens), "
+                  f"numpy fp64 decode_attention, {elapsed:.1f} s",
+    }
 
-    import decode_memory_amd as pd
+
+class Timer:
+    """Microseconds per call of fn, between two events recorded on the
+    stream the library launches on (torch's current stream)."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.stream = torch.cuda.current_stream()
+
+    def __call__(self, fn, reps):
+        torch = self.torch
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(self.stream)
+        for _ in range(reps):
+            fn()
+        e1.record(self.stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / reps
+
+
+def stage_times(timer, decode_call, layers, reps):
+    """Live per-launch durations of the split and combine stages: each stage
+    of every listed layer back to back, between two events."""
+    layers = list(layers)
+
+    def run(stage):
+        for layer in layers:
+            decode_call(layer, stage)
+    for _ in range(2):
+        run("split")
+        run("combine")
+    split_us = timer(lambda: run("split"), reps) / len(layers)
+    combine_us = timer(lambda: run("combine"), reps) / len(layers)
+    run("split")
+    run("combine")
+    return split_us, combine_us
+
+
+def roofline(d_bytes, split_us, kernel, traffic=None, bound="hbm"):
+    achieved = d_bytes / (split_us * 1e-6) / 1e9
+    return {"bound": bound, "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic, "kernel": kernel,
+            "algorithmic_bytes_per_launch": int(d_bytes), "avg_launch_us": round(split_us, 3)}
+
+
+def base_result(args, value, ms_per_step, dtype, config):
+    return {
+        "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": dtype,
+        "data": "synthetic", "config": config,
+    }
+
+
+# ---------------------------------------------------------------------------
+# default: the qwen3-0.6b-shaped batch
+# ---------------------------------------------------------------------------
+
+def run_qwen3_0p6b(args, torch, pd):
     from synth import WORKLOADS, kv_bits_for_sequence, make_block_table, monotone_rows, q_bits
 
     w = WORKLOADS["qwen3_0p6b_8x4k"]
     dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
     B, L, n, bs = w.batch, w.n_layers, w.length, w.block_size
     n_kv, n_q, D = w.n_kv_heads, w.n_q_heads, w.head_dim
     lengths = [n] * B
@@ -171,66 +264,38 @@ def main() -> int:
     if pool.check_error():
         raise RuntimeError("device error while filling the pool")
 
-    stream = torch.cuda.current_stream()
+    timer = Timer(torch)
 
     def step():
         for layer in range(L):
             pool.write_block(layer, new_rows, new_slots, k_new[layer], v_new[layer])
             pool.paged_decode(layer, qs[layer], table, lens, n, w.scale, outs[layer], ws)
 
-    def stage_pass(stage):
-        for layer in range(L):
-            pool.paged_decode(layer, qs[layer], table, lens, n, w.scale, outs[layer], ws,
-                              stage=stage)
-
-    def timed(fn, reps):
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        e0.record(stream)
-        for _ in range(reps):
-            fn()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) * 1e3 / reps  # microseconds per call of fn
+    def decode_call(layer, stage):
+        pool.paged_decode(layer, qs[layer], table, lens, n, w.scale, outs[layer], ws, stage=stage)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
 
     # timed region: exactly `steps` full steps between two synchronised events
-    step_ms = timed(step, args.steps) / 1e3
+    step_ms = timer(step, args.steps) / 1e3
     if pool.check_error():
         raise RuntimeError("device error during the timed steps")
 
-    # per-kernel durations, live: the split stage (the dominant kernel) of all
-    # 28 layers back to back, then the combine stage, each between two events
-    for _ in range(2):
-        stage_pass("split")
-        stage_pass("combine")
-    split_us = timed(lambda: stage_pass("split"), args.steps) / L
-    combine_us = timed(lambda: stage_pass("combine"), args.steps) / L
-    stage_pass("split")
-    stage_pass("combine")
-    torch.cuda.synchronize()
+    split_us, combine_us = stage_times(timer, decode_call, range(L), args.steps)
 
     d_bytes = decode_bytes(lengths, n_kv, n_q, D, bs)
     w_bytes = write_bytes(B, n_kv, D)
     step_bytes = L * (d_bytes + w_bytes)
-    achieved = d_bytes / (split_us * 1e-6) / 1e9
 
     # gather_visible of one layer to contiguous [B, n_kv, T, D] (reported beside)
     gk = torch.empty((B, n_kv, n, D), dtype=torch.bfloat16, device=dev)
     gv = torch.empty_like(gk)
     for _ in range(3):
         pool.gather_visible(0, table, lens, n, gk, gv)
-    g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    g_iters = 10
-    g0.record(stream)
-    for i in range(g_iters):
-        pool.gather_visible(i % L, table, lens, n, gk, gv)
-    g1.record(stream)
-    torch.cuda.synchronize()
-    g_us = g0.elapsed_time(g1) * 1e3 / g_iters
+    it = iter(range(1 << 30))
+    g_us = timer(lambda: pool.gather_visible(next(it) % L, table, lens, n, gk, gv), 10)
     g_bytes = 2 * 2 * B * n * n_kv * D * 2 + B * (n // bs) * 4
 
     # A plain device copy of known size: the scale for HBM byte counters read
@@ -241,43 +306,381 @@ def main() -> int:
     torch.cuda.synchronize()
     del calib, calib_dst
 
-    result = {
-        "metric": "paged_decode achieved HBM GB/s (% of peak) + KV tokens attended/sec",
-        "value": round(step_bytes / (step_ms * 1e-3) / 1e9, 2),
-        "unit": "GB/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(step_ms, 4),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic",
-        "config": {"workload": "qwen3-0.6b-shaped decode batch", "layers": L, "batch": B,
-                   "seq_len": n, "block_size": bs, "slab_blocks": w.slab_blocks,
-                   "n_q_heads": n_q, "n_kv_heads": n_kv, "head_dim": D,
-                   "row_layout": "monotone, 4 same-slab runs per sequence"},
-        "pct_of_peak": round(100.0 * step_bytes / (step_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
+    value = step_bytes / (step_ms * 1e-3) / 1e9
+    result = base_result(args, value, step_ms, "bf16", {
+        "workload": "qwen3-0.6b-shaped decode batch", "layers": L, "batch": B, "seq_len": n,
+        "block_size": bs, "slab_blocks": w.slab_blocks, "n_q_heads": n_q, "n_kv_heads": n_kv,
+        "head_dim": D, "row_layout": "monotone, 4 same-slab runs per sequence"})
+    rl = roofline(d_bytes, split_us, "paged_decode_row_kernel<128,2,true,2> (split stage)",
+                  measured_traffic())
+    rl["kernel_source_sha256"] = decode_source_hash()
+    result.update({
+        "pct_of_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
         "kv_tokens_attended_per_s": round(sum(lengths) * L / (step_ms * 1e-3), 1),
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": measured_traffic(),
-                     "kernel": "paged_decode_row_kernel<128,2,true,2> (split stage)",
-                     "kernel_source_sha256": decode_source_hash(),
-                     "algorithmic_bytes_per_launch": d_bytes,
-                     "avg_launch_us": round(split_us, 3)},
+        "roofline": rl,
         "paged_decode": {"split_us": round(split_us, 3), "combine_us": round(combine_us, 3),
                          "achieved_gbs_both_stages": round(d_bytes / ((split_us + combine_us) * 1e-6) / 1e9, 1)},
         "write_block": {"bytes_per_launch": w_bytes},
         "gather_visible": {"us_per_layer": round(g_us, 2), "bytes_per_layer": g_bytes,
                            "achieved_gbs": round(g_bytes / (g_us * 1e-6) / 1e9, 1)},
-    }
+    })
     pool.close()
+    result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds) if args.cpu_seconds > 0 else None
+    return result
+
+
+# ---------------------------------------------------------------------------
+# fragmented pool: 64 sequences, shuffled rows, one new token per step
+# ---------------------------------------------------------------------------
+
+def run_fragmented(args, torch, pd):
+    from synth import WORKLOADS, make_block_table, normal_device, q_bits, shuffled_rows, workload_lengths
+
+    w = WORKLOADS["fragmented_64"]
+    dev = torch.device("cuda:0")
+    B, bs, S = w.batch, w.block_size, w.slab_blocks
+    n_kv, n_q, D = w.n_kv_heads, w.n_q_heads, w.head_dim
+    lengths0 = [int(x) for x in workload_lengths(w)]
+    rng = np.random.default_rng(np.random.SeedSequence([w.seed, 1 << 23]))
+    rows, free, R = shuffled_rows(rng, lengths0, bs, S, spare_rows=64)
+    n_steps = args.warmup + args.steps
+
+    # every step's new rows, slots, tables and lengths, decided up front
+    rows = [list(r) for r in rows]
+    free = list(free)
+    grow = 0
+    step_rows, step_slots, step_lens = [], [], []
+    lens_now = list(lengths0)
+    for _ in range(n_steps):
+        r_s, s_s = [], []
+        for b in range(B):
+            pos = lens_now[b]
+            if pos % bs == 0:
+                if not free:  # the free list ran dry: one more slab of rows
+                    free = list(range(R + grow * S, R + (grow + 1) * S))
+                    grow += 1
+                rows[b].append(free.pop(0))
+            r_s.append(rows[b][pos // bs])
+            s_s.append(pos % bs)
+            lens_now[b] = pos + 1
+        step_rows.append(r_s)
+        step_slots.append(s_s)
+        step_lens.append(list(lens_now))
+    table = make_block_table([np.asarray(r, np.int32) for r in rows])
+    # the table of step i holds exactly the blocks in use after its write
+    tables = []
+    for i in range(n_steps):
+        t = table.copy()
+        for b in range(B):
+            t[b, -(-step_lens[i][b] // bs):] = -1
+        tables.append(torch.as_tensor(t, device=dev))
+    max_len = max(step_lens[-1])
+
+    pool = pd.SlabPool(1, bs, n_kv, D, S, -(-(R + grow * S) // S) + 1, "bf16", device=dev)
+    pool.reserve_rows(R + grow * S)
+    # fill: every sequence's first lengths0[b] tokens
+    all_r, all_s = [], []
+    for b in range(B):
+        t = np.arange(lengths0[b])
+        all_r.append(np.asarray(rows[b], np.int32)[t // bs])
+        all_s.append((t % bs).astype(np.int32))
+    all_r = torch.as_tensor(np.concatenate(all_r), device=dev)
+    all_s = torch.as_tensor(np.concatenate(all_s), device=dev)
+    n_tok = int(sum(lengths0))
+    k = normal_device((w.seed, 0, 0), (n_tok, n_kv, D), w.dtype, dev)
+    v = normal_device((w.seed, 0, 1), (n_tok, n_kv, D), w.dtype, dev)
+    pool.write_block(0, all_r, all_s, k, v)
+    del k, v
+    k_new = normal_device((w.seed, 1, 0), (n_steps, B, n_kv, D), w.dtype, dev)
+    v_new = normal_device((w.seed, 1, 1), (n_steps, B, n_kv, D), w.dtype, dev)
+    new_r = [torch.tensor(r, dtype=torch.int32, device=dev) for r in step_rows]
+    new_s = [torch.tensor(s, dtype=torch.int32, device=dev) for s in step_slots]
+    lens_d = [torch.tensor(x, dtype=torch.int32, device=dev) for x in step_lens]
+    q = torch.from_numpy(q_bits(w.seed, 0, B, n_q, D, w.dtype).view(np.int16)).to(dev).view(torch.bfloat16)
+    out = torch.empty_like(q)
+    ws = pool.workspace(B, n_q, max_len)
+    torch.cuda.synchronize()
+    if pool.check_error():
+        raise RuntimeError("device error while filling the pool")
+
+    timer = Timer(torch)
+    cur = [0]
+
+    def step():
+        i = cur[0]
+        pool.write_block(0, new_r[i], new_s[i], k_new[i], v_new[i])
+        pool.paged_decode(0, q, tables[i], lens_d[i], max_len, w.scale, out, ws)
+        cur[0] += 1
+
+    for _ in range(args.warmup):
+        step()
+    t_steps = timer(step, args.steps)
+    if pool.check_error():
+        raise RuntimeError("device error during the timed steps")
+    last = n_steps - 1
+    step_bytes = sum(decode_bytes(step_lens[i], n_kv, n_q, D, bs) + write_bytes(B, n_kv, D)
+                     for i in range(args.warmup, n_steps)) / args.steps
+
+    def decode_call(layer, stage):
+        pool.paged_decode(0, q, tables[last], lens_d[last], max_len, w.scale, out, ws, stage=stage)
+
+    split_us, combine_us = stage_times(timer, decode_call, [0], args.steps)
+    d_bytes = decode_bytes(step_lens[last], n_kv, n_q, D, bs)
+    stats = pool.stats()
+    pool.close()
+    value = step_bytes / (t_steps * 1e-6) / 1e9
+    result = base_result(args, value, t_steps / 1e3, "bf16", {
+        "workload": "fragmented pool, 64 sequences U{512..16384} tokens", "layers": 1, "batch": B,
+        "total_tokens": int(sum(step_lens[last])), "block_size": bs, "slab_blocks": S,
+        "n_q_heads": n_q, "n_kv_heads": n_kv, "head_dim": D,
+        "row_layout": "rows popped from a seeded shuffled free list"})
+    result.update({
+        "pct_of_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
+        "kv_tokens_attended_per_s": round(sum(step_lens[last]) / (t_steps * 1e-6), 1),
+        "roofline": roofline(d_bytes, split_us, "paged_decode_row_kernel<128,2,true,2> (split stage)"),
+        "paged_decode": {"split_us": round(split_us, 3), "combine_us": round(combine_us, 3)},
+        "pool": {"n_slabs": stats["n_slabs"], "slabs_appended_for_steps": grow},
+    })
+    result["cpu_baseline"] = (cpu_baseline_sequences(w, step_lens[last], args.cpu_seconds)
+                              if args.cpu_seconds > 0 else None)
+    return result
+
+
+# ---------------------------------------------------------------------------
+# long context: 28 layers x 32 sequences x 16384 tokens
+# ---------------------------------------------------------------------------
+
+def run_long_context(args, torch, pd):
+    from synth import WORKLOADS, make_block_table, monotone_rows, normal_device
+
+    w = WORKLOADS["qwen3_1p7b_32x16k"]
+    dev = torch.device("cuda:0")
+    B, L, n, bs, S = w.batch, w.n_layers, w.length, w.block_size, w.slab_blocks
+    n_kv, n_q, D = w.n_kv_heads, w.n_q_heads, w.head_dim
+    lengths = [n] * B
+    rows = monotone_rows(lengths, bs)
+    cap = int(rows[-1].max()) + 1
+    table = torch.as_tensor(make_block_table(rows), device=dev)
+    lens = torch.tensor(lengths, dtype=torch.int32, device=dev)
+    pool = pd.SlabPool(L, bs, n_kv, D, S, -(-cap // S) + 1, "bf16", device=dev)
+    pool.reserve_rows(cap)
+    t_tok = np.arange(n)
+    all_rows = torch.as_tensor(np.concatenate([r[t_tok // bs] for r in rows]).astype(np.int32), device=dev)
+    all_slots = torch.as_tensor(np.tile((t_tok % bs).astype(np.int32), B), device=dev)
+    new_rows = torch.as_tensor(np.array([r[(n - 1) // bs] for r in rows], np.int32), device=dev)
+    new_slots = torch.full((B,), (n - 1) % bs, dtype=torch.int32, device=dev)
+    qs, outs, k_new, v_new = [], [], [], []
+    for layer in range(L):
+        k = normal_device((w.seed, layer, 0), (B * n, n_kv, D), w.dtype, dev)
+        v = normal_device((w.seed, layer, 1), (B * n, n_kv, D), w.dtype, dev)
+        pool.write_block(layer, all_rows, all_slots, k, v)
+        k_new.append(k.view(B, n, n_kv, D)[:, n - 1].contiguous())
+        v_new.append(v.view(B, n, n_kv, D)[:, n - 1].contiguous())
+        del k, v
+        qs.append(normal_device((w.seed, layer, 2), (B, n_q, D), w.dtype, dev))
+        outs.append(torch.empty_like(qs[-1]))
+    ws = pool.workspace(B, n_q, n)
+    torch.cuda.synchronize()
+    if pool.check_error():
+        raise RuntimeError("device error while filling the pool")
+
+    timer = Timer(torch)
+
+    def step():
+        for layer in range(L):
+            pool.write_block(layer, new_rows, new_slots, k_new[layer], v_new[layer])
+            pool.paged_decode(layer, qs[layer], table, lens, n, w.scale, outs[layer], ws)
+
+    def decode_call(layer, stage):
+        pool.paged_decode(layer, qs[layer], table, lens, n, w.scale, outs[layer], ws, stage=stage)
+
+    for _ in range(args.warmup):
+        step()
+    step_ms = timer(step, args.steps) / 1e3
+    if pool.check_error():
+        raise RuntimeError("device error during the timed steps")
+    split_us, combine_us = stage_times(timer, decode_call, range(L), max(2, args.steps // 4))
+    d_bytes = decode_bytes(lengths, n_kv, n_q, D, bs)
+    step_bytes = L * (d_bytes + write_bytes(B, n_kv, D))
+
+    gk = torch.empty((B, n_kv, n, D), dtype=torch.bfloat16, device=dev)
+    gv = torch.empty_like(gk)
+    pool.gather_visible(0, table, lens, n, gk, gv)
+    it = iter(range(1 << 30))
+    g_us = timer(lambda: pool.gather_visible(next(it) % L, table, lens, n, gk, gv), 5)
+    g_bytes = 2 * 2 * B * n * n_kv * D * 2 + B * (n // bs) * 4
+    del gk, gv
+    pool.close()
+    value = step_bytes / (step_ms * 1e-3) / 1e9
+    result = base_result(args, value, step_ms, "bf16", {
+        "workload": "qwen3-1.7b-shaped long-context batch", "layers": L, "batch": B, "seq_len": n,
+        "block_size": bs, "slab_blocks": S, "n_q_heads": n_q, "n_kv_heads": n_kv, "head_dim": D,
+        "row_layout": "monotone"})
+    result.update({
+        "pct_of_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
+        "kv_tokens_attended_per_s": round(sum(lengths) * L / (step_ms * 1e-3), 1),
+        "roofline": roofline(d_bytes, split_us, "paged_decode_row_kernel<128,2,true,2> (split stage)"),
+        "paged_decode": {"split_us": round(split_us, 3), "combine_us": round(combine_us, 3)},
+        "gather_visible": {"us_per_layer": round(g_us, 2), "bytes_per_layer": g_bytes,
+                           "achieved_gbs": round(g_bytes / (g_us * 1e-6) / 1e9, 1),
+                           "pct_of_peak": round(100.0 * g_bytes / (g_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 2)},
+    })
     if args.cpu_seconds > 0:
-        result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+        result["cpu_baseline"] = cpu_baseline_sequences(w, [n] * B, args.cpu_seconds)
     else:
         result["cpu_baseline"] = None
+    return result
+
+
+# ---------------------------------------------------------------------------
+# packed formats: 16 sequences x 16384 tokens, head_dim 64 and 256
+# ---------------------------------------------------------------------------
+
+def run_packed(args, torch, pd):
+    from synth import WORKLOADS, hadamard_signs, make_block_table, monotone_rows, normal_device
+
+    w = WORKLOADS["packed_16x16k"]
+    dev = torch.device("cuda:0")
+    B, n, bs, S = w.batch, w.length, w.block_size, w.slab_blocks
+    n_kv, n_q = w.n_kv_heads, w.n_q_heads
+    lengths = [n] * B
+    rows = monotone_rows(lengths, bs)
+    cap = int(rows[-1].max()) + 1
+    table = torch.as_tensor(make_block_table(rows), device=dev)
+    lens = torch.tensor(lengths, dtype=torch.int32, device=dev)
+    t_tok = np.arange(n)
+    all_rows = torch.as_tensor(np.concatenate([r[t_tok // bs] for r in rows]).astype(np.int32), device=dev)
+    all_slots = torch.as_tensor(np.tile((t_tok % bs).astype(np.int32), B), device=dev)
+    timer = Timer(torch)
+    per, tot_bytes, tot_us = {}, 0, 0.0
+    for D in w.head_dims:
+        scale = 1.0 / float(np.sqrt(D))
+        for fmt in ("bf16",) + tuple(w.formats):
+            signs = hadamard_signs(w.seed, D) if fmt != "bf16" else None
+            k_rec, v_rec = pd.record_bytes(pd.FORMAT_NAMES[fmt], D)
+            kv_bytes = B * n * n_kv * (k_rec + v_rec)
+            copies = max(2, -(-3 * MALL_BYTES // kv_bytes))  # rotate past the last-level cache
+            pool = pd.SlabPool(copies, bs, n_kv, D, S, -(-cap // S) + 1, fmt, hadamard_signs=signs,
+                               device=dev)
+            pool.reserve_rows(cap)
+            for layer in range(copies):
+                k = normal_device((w.seed, D, layer, 0), (B * n, n_kv, D), "bf16", dev)
+                v = normal_device((w.seed, D, layer, 1), (B * n, n_kv, D), "bf16", dev)
+                pool.write_block(layer, all_rows, all_slots, k, v)
+                del k, v
+            q = normal_device((w.seed, D, 2), (B, n_q, D), "bf16", dev)
+            out = torch.empty_like(q)
+            ws = pool.workspace(B, n_q, n)
+            torch.cuda.synchronize()
+            if pool.check_error():
+                raise RuntimeError(f"device error while filling the {fmt} D={D} pool")
+            it = iter(range(1 << 30))
+
+            def call():
+                pool.paged_decode(next(it) % copies, q, table, lens, n, scale, out, ws)
+
+            for _ in range(args.warmup):
+                call()
+            us = timer(call, max(args.steps, copies))
+
+            def decode_call(layer, stage):
+                pool.paged_decode(layer, q, table, lens, n, scale, out, ws, stage=stage)
+
+            split_us, combine_us = stage_times(timer, decode_call, range(copies),
+                                               max(2, args.steps // copies))
+            if pool.check_error():
+                raise RuntimeError(f"device error during the {fmt} D={D} timing")
+            pool.close()
+            d_bytes = decode_bytes(lengths, n_kv, n_q, D, bs, k_rec + v_rec)
+            tot_bytes += d_bytes
+            tot_us += us
+            per[f"{fmt}_d{D}"] = {
+                "us_per_call": round(us, 2), "split_us": round(split_us, 2),
+                "combine_us": round(combine_us, 2), "kv_bytes": kv_bytes,
+                "algorithmic_bytes": d_bytes,
+                "split_gbs": round(d_bytes / (split_us * 1e-6) / 1e9, 1),
+                "split_pct_of_peak": round(100.0 * d_bytes / (split_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 2),
+                "call_gbs": round(d_bytes / (us * 1e-6) / 1e9, 1),
+                "kv_tokens_attended_per_s": round(B * n / (us * 1e-6), 1),
+                "pool_copies": copies,
+            }
+    value = tot_bytes / (tot_us * 1e-6) / 1e9
+    worst = min((k for k in per if not k.startswith("bf16")), key=lambda k: per[k]["split_gbs"])
+    result = base_result(args, value, tot_us / 1e3, "bf16 q, packed K/V, fp32 accumulate", {
+        "workload": "packed KV batch, 16 sequences x 16384 tokens", "layers": 1, "batch": B,
+        "seq_len": n, "block_size": bs, "slab_blocks": S, "n_q_heads": n_q, "n_kv_heads": n_kv,
+        "head_dims": list(w.head_dims), "formats": ["bf16"] + list(w.formats)})
+    p = per[worst]
+    result.update({
+        "pct_of_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
+        "kv_tokens_attended_per_s": round(len(per) * B * n / (tot_us * 1e-6), 1),
+        "roofline": {"bound": "hbm", "achieved": p["split_gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(p["split_gbs"] / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": f"paged_decode_packed_kernel ({worst}, split stage; the slowest packed case)",
+                     "algorithmic_bytes_per_launch": p["algorithmic_bytes"],
+                     "avg_launch_us": p["split_us"]},
+        "formats": per,
+    })
+    result["cpu_baseline"] = cpu_baseline_packed(w, args.cpu_seconds) if args.cpu_seconds > 0 else None
+    return result
+
+
+def cpu_baseline_packed(w, target_s):
+    """The oracle's packed decode (K4V4, head_dim 64) one sequence at a time."""
+    from oracle.packed import k_records, packed_decode_attention, record_bytes, v_records
+    from synth import hadamard_signs, kv_bits_for_sequence, q_bits
+
+    D = 64
+    signs = hadamard_signs(w.seed, D)
+    q = q_bits(w.seed, 0, w.batch, w.n_q_heads, D, "bf16")
+    elapsed, done = 0.0, 0
+    for b in range(w.batch):
+        if elapsed >= target_s:
+            break
+        k, v = kv_bits_for_sequence(w.seed, 0, b, w.length, w.n_kv_heads, D, "bf16")
+        kr, vr = k_records(k, signs, 4), v_records(v, 4)
+        t0 = time.perf_counter()
+        packed_decode_attention(q[b:b + 1], [kr], [vr], signs, "k4v4", D, 1.0 / np.sqrt(D))
+        elapsed += time.perf_counter() - t0
+        done += 1
+    rec = record_bytes(D, 4) * 2
+    nbytes = decode_bytes([w.length] * done, w.n_kv_heads, w.n_q_heads, D, w.block_size, rec)
+    return {"value": round(nbytes / elapsed / 1e9, 3), "unit": "GB/s",
+            "tokens_attended_per_s": round(done * w.length / elapsed, 1),
+            "cores": int(blas_threads()), "kind": "oracle",
+            "sample": f"{done} of {w.batch} sequences, K4V4 head_dim 64, numpy fp64 "
+                      f"packed_decode_attention, {elapsed:.1f} s"}
+
+
+RUNNERS = {
+    "qwen3_0p6b_8x4k": run_qwen3_0p6b,
+    "fragmented_64": run_fragmented,
+    "qwen3_1p7b_32x16k": run_long_context,
+    "packed_16x16k": run_packed,
+}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="CPU-oracle work to time for cpu_baseline (0 disables)")
+    ap.add_argument("--workload", default="qwen3_0p6b_8x4k", choices=sorted(RUNNERS))
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the paged-decode path here runs on a single "
+              "MI355X (a multi-GPU layout would shard sequences or kv heads with no exchange).",
+              file=sys.stderr)
+        return 2
+
+    import torch
+
+    import decode_memory_amd as pd
+
+    torch.cuda.set_device(torch.device("cuda:0"))
+    result = RUNNERS[args.workload](args, torch, pd)
     print(json.dumps(result), flush=True)
     return 0
 

@@ -11,13 +11,16 @@
 // store addresses, so every byte is read once and written once.
 //
 // Decomposition: one workgroup per (sequence, chunk of kChunk logical
-// blocks).  The workgroup splits its chunk into same-slab runs (a run that
-// crosses a chunk edge is continued by the neighbouring workgroup), resolves
-// each run's slab base pointer once, and copies the chunk's blocks in
+// blocks).  Lane i of the first wave resolves block i of the chunk: its row,
+// the row's slab and that slab's base pointer (blocks of one same-slab run
+// resolve to the same base).  The workgroup then copies the chunk's blocks in
 // logical order as 16-byte vectors: each block's source is one contiguous
 // row [block_size, n_kv, record]; the destination is n_kv contiguous pieces
-// of block_size records.  The first chunk's workgroup also counts the
-// sequence's runs over the whole row list for n_runs_out.
+// of block_size records.  Every thread issues kUnroll loads before it
+// stores, so a CU keeps enough reads in flight to stream at the HBM rate;
+// both sides are non-temporal, since each byte is touched once.  The first
+// chunk's workgroup also counts the sequence's runs over the whole row list
+// for n_runs_out.
 #include "device_common.h"
 #include "internal.h"
 
@@ -26,16 +29,19 @@ namespace pagedkv {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kChunk = 4;  // logical blocks per workgroup
+constexpr int kChunk = 2;   // logical blocks per workgroup
+constexpr int kUnroll = 16; // 16-byte loads in flight per thread
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(1))) u32x4 gu32x4;
 
 __device__ __forceinline__ int slab_of(int32_t row, const LayerView& lv) {
   return (row < 0 || row >= lv.capacity_rows) ? -1 : row / lv.slab_blocks;
 }
 
 __global__ __launch_bounds__(kThreads) void gather_kernel(GatherArgs a) {
-  __shared__ const char* s_kbase[kChunk];
-  __shared__ const char* s_vbase[kChunk];
-  __shared__ int s_row[kChunk];
+  __shared__ const char* s_ksrc[kChunk];  // source row of each block, null = zeros
+  __shared__ const char* s_vsrc[kChunk];
   __shared__ int s_runs[kThreads / kWave];
 
   const LayerView& lv = a.lv;
@@ -54,32 +60,28 @@ __global__ __launch_bounds__(kThreads) void gather_kernel(GatherArgs a) {
   }
   const int nb = (len + bs - 1) / bs;
   const int32_t* trow = a.table + static_cast<size_t>(b) * a.max_blocks;
+  const int n_kv = lv.n_kv;
+  const size_t k_row_bytes = static_cast<size_t>(bs) * n_kv * lv.k_rec;
+  const size_t v_row_bytes = static_cast<size_t>(bs) * n_kv * lv.v_rec;
 
-  // Run split of this chunk: a run starts at the chunk's first block or where
-  // the slab changes; its first block loads the slab base, later blocks of
-  // the run reuse it.
   const int blk0 = ch * kChunk;
-  if (threadIdx.x == 0) {
-    const char* kcur = nullptr;
-    const char* vcur = nullptr;
-    int prev_slab = -2;
-    for (int i = 0; i < kChunk; ++i) {
-      const int blk = blk0 + i;
-      int row = -1, slab = -1;
-      if (blk < nb) {
-        row = trow[blk];
-        slab = slab_of(row, lv);
-        if (slab < 0) set_error(lv.err, PD_DEVERR_TABLE_ROW);
+  if (threadIdx.x < kChunk) {
+    const int blk = blk0 + threadIdx.x;
+    const char* ks = nullptr;
+    const char* vs = nullptr;
+    if (blk < nb) {
+      const int row = trow[blk];
+      const int slab = slab_of(row, lv);
+      if (slab < 0) {
+        set_error(lv.err, PD_DEVERR_TABLE_ROW);
+      } else {
+        const size_t r = static_cast<size_t>(row - slab * lv.slab_blocks);
+        ks = static_cast<const char*>(lv.k_tab[slab]) + r * k_row_bytes;
+        vs = static_cast<const char*>(lv.v_tab[slab]) + r * v_row_bytes;
       }
-      if (slab >= 0 && slab != prev_slab) {
-        kcur = static_cast<const char*>(lv.k_tab[slab]);
-        vcur = static_cast<const char*>(lv.v_tab[slab]);
-      }
-      prev_slab = slab;
-      s_row[i] = slab >= 0 ? row - slab * lv.slab_blocks : -1;  // row in slab, -1 = zeros
-      s_kbase[i] = kcur;
-      s_vbase[i] = vcur;
     }
+    s_ksrc[threadIdx.x] = ks;
+    s_vsrc[threadIdx.x] = vs;
   }
 
   // Whole-sequence run count (first chunk only).
@@ -100,36 +102,43 @@ __global__ __launch_bounds__(kThreads) void gather_kernel(GatherArgs a) {
   }
   __syncthreads();
 
-  const int n_kv = lv.n_kv;
-  const int k_units = lv.k_rec / 16, v_units = lv.v_rec / 16;  // 16-byte units per record
-  const size_t k_row_bytes = static_cast<size_t>(bs) * n_kv * lv.k_rec;
-  const size_t v_row_bytes = static_cast<size_t>(bs) * n_kv * lv.v_rec;
   char* kout = static_cast<char*>(a.k_out);
   char* vout = static_cast<char*>(a.v_out);
-
   for (int i = 0; i < kChunk; ++i) {
     const int blk = blk0 + i;
     if (blk * bs >= a.t_out) break;
-    const int ris = s_row[i];
     // K then V: unit u of the row covers (slot, head, 16-byte piece)
     for (int pass = 0; pass < 2; ++pass) {
-      const int units = pass ? v_units : k_units;
       const int rec = pass ? lv.v_rec : lv.k_rec;
-      const char* src = (ris >= 0) ? (pass ? s_vbase[i] : s_kbase[i]) +
-                                         ris * (pass ? v_row_bytes : k_row_bytes)
-                                   : nullptr;
+      const int units = rec / 16;
+      const char* src = pass ? s_vsrc[i] : s_ksrc[i];
       char* dst = pass ? vout : kout;
       const int total_units = bs * n_kv * units;
-      for (int u = threadIdx.x; u < total_units; u += kThreads) {
-        const int piece = u % units;
-        const int head = (u / units) % n_kv;
-        const int slot = u / (units * n_kv);
-        const int t = blk * bs + slot;
-        if (t >= a.t_out) continue;
-        uint4 v = make_uint4(0, 0, 0, 0);
-        if (src && t < len) v = reinterpret_cast<const uint4*>(src)[u];
-        const size_t o = ((static_cast<size_t>(b) * n_kv + head) * a.t_out + t) * rec + piece * 16;
-        *reinterpret_cast<uint4*>(dst + o) = v;
+      // tokens of this block that exist in the output / are visible
+      const int t_end = min(bs, a.t_out - blk * bs);
+      const int t_vis = src ? max(0, min(bs, len - blk * bs)) : 0;
+      for (int u0 = threadIdx.x; u0 < total_units; u0 += kThreads * kUnroll) {
+        u32x4 v[kUnroll];
+#pragma unroll
+        for (int j = 0; j < kUnroll; ++j) {
+          const int u = u0 + j * kThreads;
+          const int slot = u / (units * n_kv);
+          v[j] = (u32x4){0u, 0u, 0u, 0u};
+          if (u < total_units && slot < t_vis)
+            v[j] = __builtin_nontemporal_load((const gu32x4*)src + u);
+        }
+#pragma unroll
+        for (int j = 0; j < kUnroll; ++j) {
+          const int u = u0 + j * kThreads;
+          const int piece = u % units;
+          const int head = (u / units) % n_kv;
+          const int slot = u / (units * n_kv);
+          if (u < total_units && slot < t_end) {
+            const size_t o = ((static_cast<size_t>(b) * n_kv + head) * a.t_out + blk * bs + slot) * rec +
+                             piece * 16;
+            __builtin_nontemporal_store(v[j], (gu32x4*)(dst + o));
+          }
+        }
       }
     }
   }

@@ -47,10 +47,11 @@ constexpr int kWaves = kThreads / kWave;
 constexpr int kMinWavesPerSimd = PAGEDKV_DECODE_WAVES_PER_SIMD;
 constexpr int kLoads = PAGEDKV_DECODE_LOADS;
 
-// 16-byte load from global memory at a uniform base plus a per-lane offset.
+// 16-byte load from global memory at a uniform base plus a per-lane offset;
+// non-temporal, since each K/V byte is read once per call.
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ uint4 gload16(const char* base, uint32_t off) {
-  const u32x4 v = *(const __attribute__((address_space(1))) u32x4*)(base + off);
+  const u32x4 v = __builtin_nontemporal_load((const __attribute__((address_space(1))) u32x4*)(base + off));
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 

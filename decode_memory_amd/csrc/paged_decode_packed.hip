@@ -14,7 +14,8 @@
 // axis) and every kv head; split s takes logical blocks s, s + n_split, ...
 // Packed records are short (48..320 bytes), so a tile of T tokens x n_kv
 // heads is first copied into LDS with 16-byte coalesced loads of whole token
-// rows (the rows of a block are contiguous in the slab), and the waves then
+// rows (the rows of a block are contiguous in the slab; the next tile's loads
+// are in flight while the current one is computed), and the waves then
 // read codes and group metadata from LDS in the layout the arithmetic wants:
 // a lane group of D/8 lanes owns one kv head, each lane 8 consecutive values
 // (one group of 32 spans 4 lanes).  The affine terms are folded so that each
@@ -35,6 +36,9 @@ namespace {
 constexpr int kPThreads = 256;
 constexpr int kPWaves = kPThreads / kWave;
 constexpr int kPBS = 32;
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(1))) u32x4 gu32x4;
 
 __device__ __forceinline__ const char* lane_ptr(uint64_t v, int j) {
   const uint32_t lo = __builtin_amdgcn_readlane(static_cast<uint32_t>(v), j);
@@ -89,8 +93,10 @@ __global__ __launch_bounds__(kPThreads) void paged_decode_packed_kernel(DecodeAr
   static_assert(kPWaves % NHS == 0 && T % SLICES == 0, "tile shape");
   static_assert(KTILE % 16 == 0 && VTILE % 16 == 0, "tile must be whole 16-byte units");
 
-  __shared__ __attribute__((aligned(16))) unsigned char s_k[KTILE];
-  __shared__ __attribute__((aligned(16))) unsigned char s_v[VTILE];
+  constexpr int KU = (KTILE / 16 + kPThreads - 1) / kPThreads;  // 16-byte units per thread
+  constexpr int VU = (VTILE / 16 + kPThreads - 1) / kPThreads;
+  __shared__ __attribute__((aligned(16))) unsigned char s_kbuf[2][KTILE];
+  __shared__ __attribute__((aligned(16))) unsigned char s_vbuf[2][VTILE];
   __shared__ float s_m[kPWaves][HPW * G];
   __shared__ float s_l[kPWaves][HPW * G];
   __shared__ float s_acc[kPWaves][HPW * G][D];
@@ -193,17 +199,45 @@ __global__ __launch_bounds__(kPThreads) void paged_decode_packed_kernel(DecodeAr
     for (int e = 0; e < 8; ++e) acc[j][e] = 0.f;
   }
 
+  // Tile i+1 is loaded into registers (non-temporal: read once) while tile i
+  // is computed from LDS; two LDS buffers, one barrier per tile.
+  u32x4 rk[KU], rv[VU];
+  auto fetch = [&](int i) {
+    const int jb = i / (kPBS / T);
+    const int t0 = (i % (kPBS / T)) * T;
+    const gu32x4* kb = (const gu32x4*)(lane_ptr(kaddr, jb) + static_cast<size_t>(t0) * NKV * KREC);
+    const gu32x4* vb = (const gu32x4*)(lane_ptr(vaddr, jb) + static_cast<size_t>(t0) * NKV * VREC);
+#pragma unroll
+    for (int j = 0; j < KU; ++j) {
+      const int u = threadIdx.x + j * kPThreads;
+      if (u < KTILE / 16) rk[j] = __builtin_nontemporal_load(kb + u);
+    }
+#pragma unroll
+    for (int j = 0; j < VU; ++j) {
+      const int u = threadIdx.x + j * kPThreads;
+      if (u < VTILE / 16) rv[j] = __builtin_nontemporal_load(vb + u);
+    }
+  };
+  if (n_tiles > 0) fetch(0);
   for (int i = 0; i < n_tiles; ++i) {
     const int jb = i / (kPBS / T);
     const int t0 = (i % (kPBS / T)) * T;  // first token of the tile in the block
     const int nt = ((ok_mask >> jb) & 1) ? min(kPBS, len - (s + jb * n_split) * kPBS) : 0;
-    const char* kb = lane_ptr(kaddr, jb) + static_cast<size_t>(t0) * NKV * KREC;
-    const char* vb = lane_ptr(vaddr, jb) + static_cast<size_t>(t0) * NKV * VREC;
-    __syncthreads();  // the previous tile's readers are done with the LDS
-    for (int u = threadIdx.x; u < KTILE / 16; u += kPThreads)
-      reinterpret_cast<uint4*>(s_k)[u] = reinterpret_cast<const uint4*>(kb)[u];
-    for (int u = threadIdx.x; u < VTILE / 16; u += kPThreads)
-      reinterpret_cast<uint4*>(s_v)[u] = reinterpret_cast<const uint4*>(vb)[u];
+    unsigned char* s_k = s_kbuf[i & 1];
+    unsigned char* s_v = s_vbuf[i & 1];
+    // buffer i&1 was last read in iteration i-2, before every wave passed
+    // the barrier of iteration i-1
+#pragma unroll
+    for (int j = 0; j < KU; ++j) {
+      const int u = threadIdx.x + j * kPThreads;
+      if (u < KTILE / 16) reinterpret_cast<u32x4*>(s_k)[u] = rk[j];
+    }
+#pragma unroll
+    for (int j = 0; j < VU; ++j) {
+      const int u = threadIdx.x + j * kPThreads;
+      if (u < VTILE / 16) reinterpret_cast<u32x4*>(s_v)[u] = rv[j];
+    }
+    if (i + 1 < n_tiles) fetch(i + 1);
     __syncthreads();
     if (t0 >= nt) continue;  // uniform: the whole tile is past the length
 

@@ -120,6 +120,22 @@ def test_gqa_heads_sharing_a_kv_head_with_equal_queries_agree():
     pool.close()
 
 
+def test_row_kernel_with_more_slabs_than_its_lds_table():
+    """The row kernel stages the first 1024 slab base pointers of a layer in
+    LDS and reads the rest from the pool's table in global memory: one-row
+    slabs and a shuffled free list put blocks in slabs on both sides."""
+    lengths = [20000, 9000, 5000, 1]
+    pool, table, refs, scale = _case(lengths, 8, 2, 128, "bf16", 32, 1, 31, layout="shuffled")
+    assert int(table.max()) >= 1024 and int(table[table >= 0].min()) < 1024
+    q, ref = refs[0]
+    out = run_decode(pool, 0, q, table, lengths, "bf16", scale)
+    err = assert_decode_close(out, ref, "bf16", allow_output_rounding=True)
+    assert_decode_close(out[:3], ref[:3], "bf16")
+    print(f"1068 one-row slabs: max-abs {err:.3e}")
+    assert pool.check_error() == 0
+    pool.close()
+
+
 def test_deterministic_and_independent_of_physical_layout():
     lengths = [1500, 333, 2048, 64]
     a = _case(lengths, 4, 2, 128, "bf16", 32, 32, 21, layout="monotone")

@@ -8,6 +8,7 @@ import of :func:`lib` raises.
 
 Functions keep the C names without the ``pd_`` prefix (``pool_create``,
 ``append_slab``, ``reserve_rows``, ``slab_for_row``, ``write_block``,
+``copy_on_write_block``,
 ``gather_visible``, ``decode_workspace_bytes``, ``paged_decode``,
 ``pool_stats``, ``pool_check_error``).  :class:`SlabPool` bundles a pool with
 the torch tensors that back its slabs.
@@ -61,7 +62,8 @@ class PoolStats(ctypes.Structure):
 EXPORTS = [
     "pd_version", "pd_last_error", "pd_record_bytes", "pd_pool_create", "pd_pool_destroy",
     "pd_slab_bytes", "pd_append_slab", "pd_slabs_needed", "pd_reserve_rows", "pd_slab_for_row",
-    "pd_write_block", "pd_gather_visible", "pd_decode_workspace_bytes", "pd_paged_decode",
+    "pd_write_block", "pd_copy_on_write_block", "pd_gather_visible", "pd_decode_workspace_bytes",
+    "pd_paged_decode",
     "pd_paged_decode_split", "pd_paged_decode_combine", "pd_pool_stats", "pd_pool_check_error",
 ]
 
@@ -84,6 +86,7 @@ def _declare(lib):
         "pd_reserve_rows": (_i32, [_vp, _i64, _pp, _pp, _i32, _vp, _p_i32]),
         "pd_slab_for_row": (_i32, [_vp, _i32, _i64, _pp, _pp, _p_i32]),
         "pd_write_block": (_i32, [_vp, _i32, _i32, _vp, _vp, _vp, _vp, _vp]),
+        "pd_copy_on_write_block": (_i32, [_vp, _i32, _vp, _vp, _vp]),
         "pd_gather_visible": (_i32, [_vp, _i32, _i32, _vp, _i32, _vp, _i32, _vp, _vp, _vp, _vp]),
         "pd_decode_workspace_bytes": (_i32, [_vp, _i32, _i32, _i32, ctypes.POINTER(_sz)]),
         "pd_paged_decode": (_i32, [_vp, _i32, _i32, _i32, _vp, _vp, _i32, _vp, _i32,
@@ -220,6 +223,15 @@ def write_block(pool: int, layer: int, rows: torch.Tensor, slots: torch.Tensor,
                                 _stream(stream)))
 
 
+def copy_on_write_block(pool: int, src_rows: torch.Tensor, dst_rows: torch.Tensor,
+                        stream=None) -> None:
+    """Copy block row src_rows[i] onto dst_rows[i] in every layer, K and V."""
+    n = src_rows.numel()
+    _require(src_rows, "src_rows", torch.int32)
+    _require(dst_rows, "dst_rows", torch.int32, n)
+    _check(lib().pd_copy_on_write_block(pool, n, _ptr(src_rows), _ptr(dst_rows), _stream(stream)))
+
+
 def gather_visible(pool: int, layer: int, block_table: torch.Tensor, lens: torch.Tensor,
                    t_out: int, k_out: torch.Tensor, v_out: torch.Tensor,
                    n_runs_out: Optional[torch.Tensor] = None, stream=None) -> None:
@@ -344,6 +356,9 @@ class SlabPool:
 
     def write_block(self, layer, rows, slots, k_src, v_src, stream=None):
         write_block(self.handle, layer, rows, slots, k_src, v_src, stream)
+
+    def copy_on_write_block(self, src_rows, dst_rows, stream=None):
+        copy_on_write_block(self.handle, src_rows, dst_rows, stream)
 
     def gather_visible(self, layer, block_table, lens, t_out, k_out, v_out, n_runs_out=None,
                        stream=None):

@@ -38,6 +38,19 @@ struct WriteArgs {
   float inv_sqrt_d;
 };
 
+struct CopyArgs {
+  const void* const* tables;  // device: [n_layers][2][max_slabs] slab bases
+  int32_t max_slabs;
+  int32_t n_layers;
+  int32_t slab_blocks;
+  int64_t capacity_rows;
+  int64_t row_bytes[2];       // bytes of one block row of K, of V
+  int32_t n;
+  const int32_t* src_rows;
+  const int32_t* dst_rows;
+  int32_t* err;
+};
+
 struct GatherArgs {
   LayerView lv;
   int32_t B;
@@ -76,6 +89,7 @@ struct DecodeArgs {
 // no kernel exists for the shape).
 hipError_t launch_zero_fill(void* p, size_t bytes, hipStream_t s);
 hipError_t launch_write_block(const WriteArgs& a, int32_t format, hipStream_t s);
+hipError_t launch_copy_block(const CopyArgs& a, hipStream_t s);
 hipError_t launch_gather(const GatherArgs& a, hipStream_t s);
 hipError_t launch_paged_decode_column(const DecodeArgs& a, bool bf16, int32_t head_dim,
                                       int32_t group, hipStream_t s);

@@ -415,6 +415,30 @@ pd_status pd_write_block(pd_pool* p, int32_t layer, int32_t n, const int32_t* ro
   return PD_OK;
 }
 
+pd_status pd_copy_on_write_block(pd_pool* p, int32_t n, const int32_t* src_rows,
+                                 const int32_t* dst_rows, hipStream_t stream) {
+  if (pd_status st = check_pool(p)) return st;
+  if (n < 0) return fail(PD_ERR_ARG, "n < 0");
+  if (n == 0) return PD_OK;
+  if (!src_rows || !dst_rows) return fail(PD_ERR_ARG, "NULL device pointer");
+  CopyArgs a{};
+  a.tables = const_cast<const void* const*>(p->d_tables);
+  a.max_slabs = p->desc.max_slabs;
+  a.n_layers = p->desc.n_layers;
+  a.slab_blocks = p->desc.slab_blocks;
+  a.capacity_rows = p->n_slabs * p->desc.slab_blocks;
+  const int64_t tok = static_cast<int64_t>(p->desc.block_size) * p->desc.n_kv_heads;
+  a.row_bytes[0] = tok * p->k_rec;
+  a.row_bytes[1] = tok * p->v_rec;
+  a.n = n;
+  a.src_rows = src_rows;
+  a.dst_rows = dst_rows;
+  a.err = p->d_err;
+  hipError_t e = launch_copy_block(a, stream);
+  if (e != hipSuccess) return hip_fail(e, "copy_on_write_block launch");
+  return PD_OK;
+}
+
 pd_status pd_gather_visible(pd_pool* p, int32_t layer, int32_t B, const int32_t* block_table,
                             int32_t max_blocks, const int32_t* lens, int32_t t_out, void* k_out,
                             void* v_out, int32_t* n_runs_out, hipStream_t stream) {

@@ -1,5 +1,6 @@
 // write_block: token-granular scatter of new K/V into the slab of their row,
-// and the zero fill that backs append_slab.
+// copy_on_write_block: whole-row copies between slabs, and the zero fill that
+// backs append_slab.
 //
 // mlxcel issue #235 ("perf(core): chunked slab storage for the paged pool to
 // eliminate growth reallocation entirely"), section "Proposed solution:
@@ -68,6 +69,43 @@ __global__ __launch_bounds__(kThreads) void write_block_native_kernel(WriteArgs 
       kd[j] = ks[j];
       vd[j] = vs[j];
     }
+  }
+}
+
+// copy_on_write_block (mlxcel #235, "Proposed solution", touch point 2): a
+// work unit is 4 KiB of one block row of one layer's K or V for one pair; a
+// workgroup copies it as one 16-byte vector per lane.  Rows of a block are
+// contiguous in their slab, so both sides are plain streams.
+constexpr int kCopyChunk = kThreads * 16;
+
+__global__ __launch_bounds__(kThreads) void copy_block_kernel(CopyArgs a) {
+  const int64_t max_row = a.row_bytes[0] > a.row_bytes[1] ? a.row_bytes[0] : a.row_bytes[1];
+  const int chunks = static_cast<int>((max_row + kCopyChunk - 1) / kCopyChunk);
+  const long long units = static_cast<long long>(a.n) * a.n_layers * 2 * chunks;
+  for (long long u = blockIdx.x; u < units; u += gridDim.x) {
+    const int c = static_cast<int>(u % chunks);
+    long long r = u / chunks;
+    const int kv = static_cast<int>(r % 2);
+    r /= 2;
+    const int layer = static_cast<int>(r % a.n_layers);
+    const int i = static_cast<int>(r / a.n_layers);
+    const int32_t src = a.src_rows[i], dst = a.dst_rows[i];
+    const bool src_ok = src >= 0 && src < a.capacity_rows;
+    const bool dst_ok = dst >= 0 && dst < a.capacity_rows;
+    if (!src_ok || !dst_ok) {
+      // reported once per pair
+      if (threadIdx.x == 0 && c == 0 && kv == 0 && layer == 0)
+        set_error(a.err, src_ok ? PD_DEVERR_WRITE_ROW : PD_DEVERR_TABLE_ROW);
+      continue;
+    }
+    const int64_t bytes = a.row_bytes[kv];
+    const int64_t off = static_cast<int64_t>(c) * kCopyChunk + threadIdx.x * 16;
+    if (off >= bytes) continue;
+    const void* const* tab = a.tables + (static_cast<size_t>(layer) * 2 + kv) * a.max_slabs;
+    const int ss = src / a.slab_blocks, ds = dst / a.slab_blocks;
+    const char* from = static_cast<const char*>(tab[ss]) + (src - ss * a.slab_blocks) * bytes;
+    char* to = static_cast<char*>(const_cast<void*>(tab[ds])) + (dst - ds * a.slab_blocks) * bytes;
+    *reinterpret_cast<uint4*>(to + off) = *reinterpret_cast<const uint4*>(from + off);
   }
 }
 
@@ -184,6 +222,16 @@ hipError_t launch_zero_fill(void* p, size_t bytes, hipStream_t s) {
   if (blocks > 4096) blocks = 4096;
   hipLaunchKernelGGL(zero_fill_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, s,
                      static_cast<uint4*>(p), n16);
+  return hipGetLastError();
+}
+
+hipError_t launch_copy_block(const CopyArgs& a, hipStream_t s) {
+  const int64_t max_row = a.row_bytes[0] > a.row_bytes[1] ? a.row_bytes[0] : a.row_bytes[1];
+  const long long units = static_cast<long long>(a.n) * a.n_layers * 2 *
+                          ((max_row + kCopyChunk - 1) / kCopyChunk);
+  const int grid = static_cast<int>(units < 4096 ? units : 4096);
+  if (grid == 0) return hipSuccess;
+  hipLaunchKernelGGL(copy_block_kernel, dim3(grid), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 

@@ -189,6 +189,26 @@ pd_status pd_write_block(pd_pool* pool, int32_t layer, int32_t n, const int32_t*
                          hipStream_t stream);
 
 /*
+ * copy_on_write_block (mlxcel #235, "Proposed solution", touch point 2):
+ * copy whole block rows inside the pool.  For each i, row dst_rows[i] of
+ * every layer, K and V, receives the bytes of row src_rows[i]: the source
+ * slice comes from the source row's slab and lands in the destination row's
+ * slab, through the same row mapping as every other call.  This is the
+ * block-level step of copy-on-write: a block shared by several sequences
+ * (a common prefix) is duplicated into a row the caller has taken from its
+ * free list before one sequence writes into it.  Packed pools copy records
+ * byte for byte (no requantisation).
+ *   n: number of pairs (>= 0); src_rows, dst_rows: device int32 [n].
+ *   Destination rows must be distinct and must not appear among the source
+ *   rows of the same call; otherwise the result is unspecified.
+ * A pair with a source row outside [0, capacity_rows) sets
+ * PD_DEVERR_TABLE_ROW, one with a destination row outside it sets
+ * PD_DEVERR_WRITE_ROW, and that pair is skipped.  n == 0 is a no-op.
+ */
+pd_status pd_copy_on_write_block(pd_pool* pool, int32_t n, const int32_t* src_rows,
+                                 const int32_t* dst_rows, hipStream_t stream);
+
+/*
  * gather_visible (mlxcel #235, "Proposed solution", touch point 3): copy each
  * sequence's visible K and V out of the pool into contiguous, transposed
  * tensors.  The row list of a sequence is split into maximal same-slab runs

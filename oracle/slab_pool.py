@@ -11,6 +11,9 @@ chunked slabs":
 * growth appends a fresh zero slab (to every layer, since row ids are shared
   by all layers) and never copies; a counter counts append events;
 * write_block assigns into the row's slab;
+* copy_on_write_block (touch point 2) copies a whole block row, every layer,
+  K and V: the source bytes come from the source row's slab and land in the
+  destination row's slab;
 * gather_visible splits a sequence's block-table rows into maximal same-slab
   runs in logical order, takes each run from its slab, concatenates the runs
   and then reshapes, slices to the visible length and transposes.
@@ -101,6 +104,21 @@ class SlabPoolModel:
             ks, vs, r = self.slab_for_row(layer, int(row))
             ks[r, int(slot)] = k_records[i]
             vs[r, int(slot)] = v_records[i]
+
+    def copy_block(self, src_rows: Sequence[int], dst_rows: Sequence[int]) -> None:
+        """Copy block row src_rows[i] onto dst_rows[i] in every layer, K and V.
+
+        All source rows are read before any destination is written."""
+        pairs = [(int(s), int(d)) for s, d in zip(src_rows, dst_rows)]
+        for layer in range(self.n_layers):
+            saved = []
+            for src, _ in pairs:
+                ks, vs, r = self.slab_for_row(layer, src)
+                saved.append((ks[r].copy(), vs[r].copy()))
+            for (_, dst), (kb, vb) in zip(pairs, saved):
+                kd, vd, r = self.slab_for_row(layer, dst)
+                kd[r] = kb
+                vd[r] = vb
 
     # -- reads ------------------------------------------------------------
     def split_runs(self, rows: Sequence[int]) -> List[Tuple[int, int, int]]:

@@ -155,3 +155,69 @@ def test_gather_flags_rows_outside_the_pool():
     assert pool.check_error() == pd.DEVERR_TABLE_ROW
     assert not k[0, :, 32:64].any()                     # the bad block reads as zeros
     pool.close()
+
+
+def _copy_pairs(rows, R, rng, n_pairs):
+    """Source rows among those in use, destinations among the free rows."""
+    used = np.unique(np.concatenate([r for r in rows if len(r)]))
+    free = np.setdiff1d(np.arange(R), used)
+    src = rng.choice(used, size=n_pairs, replace=False).astype(np.int32)
+    dst = rng.choice(free, size=n_pairs, replace=False).astype(np.int32)
+    return src, dst
+
+
+def test_copy_on_write_block_matches_the_oracle():
+    """copy_on_write_block over 3 layers of a fragmented bf16 pool: every
+    slab equals the oracle's after the copies, sources that cross slabs
+    included; pairs with a row outside the pool are skipped and flagged."""
+    lengths = [300, 77, 1000, 32, 5]
+    bs, S, n_kv, D = 32, 4, 8, 128
+    rows, _, R = shuffled_rows(np.random.default_rng(3), lengths, bs, S, spare_rows=12)
+    pool, model = _fill_both(3, lengths, rows, bs, S, n_kv, D, "bf16", 71, cap=R)
+    src, dst = _copy_pairs(rows, R, np.random.default_rng(4), 10)
+    assert len({int(s) // S for s in src}) > 1 and any(s // S != d // S for s, d in zip(src, dst))
+    pool.copy_on_write_block(i32(src), i32(dst))
+    model.copy_block(src, dst)
+    _assert_slabs_equal(pool, model)
+    assert pool.check_error() == 0
+    # a source past the pool and a negative destination: skipped, both flagged
+    bad_src = np.array([R + 3, int(src[0])], np.int32)
+    bad_dst = np.array([int(dst[1]), -1], np.int32)
+    pool.copy_on_write_block(i32(bad_src), i32(bad_dst))
+    err = pool.check_error()
+    assert err & pd.DEVERR_TABLE_ROW and err & pd.DEVERR_WRITE_ROW
+    _assert_slabs_equal(pool, model)                      # nothing was written
+    pool.close()
+
+
+@pytest.mark.parametrize("fmt,D", [("k4v4", 64), ("k8v4", 256)])
+def test_copy_on_write_block_moves_packed_records(fmt, D):
+    """Packed pools: the copy moves records byte for byte (no requantisation);
+    the oracle quantises the same bf16 inputs itself."""
+    from oracle.packed import FORMATS, k_records, record_bytes, v_records
+    from synth import hadamard_signs, kv_bits_for_sequence
+    kb, vb = FORMATS[fmt]
+    lengths = [200, 64, 33]
+    bs, S, n_kv = 32, 4, 8
+    rows, _, R = shuffled_rows(np.random.default_rng(D), lengths, bs, S, spare_rows=8)
+    signs = hadamard_signs(90 + D, D)
+    pool = pd.SlabPool(2, bs, n_kv, D, S, -(-R // S) + 2, fmt, hadamard_signs=signs)
+    pool.reserve_rows(R)
+    model = SlabPoolModel(2, bs, n_kv, record_bytes(D, kb), record_bytes(D, vb), S)
+    model.reserve_rows(R)
+    for layer in range(2):
+        for b, n in enumerate(lengths):
+            k, v = kv_bits_for_sequence(90 + D, layer, b, n, n_kv, D, "bf16")
+            r, s = token_targets(rows[b], n, bs)
+            pool.write_block(layer, i32(r), i32(s), to_device_bits(k, "bf16"), to_device_bits(v, "bf16"))
+            model.write(layer, r, s, k_records(k, signs, kb), v_records(v, vb))
+    src, dst = _copy_pairs(rows, R, np.random.default_rng(D + 1), 5)
+    pool.copy_on_write_block(i32(src), i32(dst))
+    model.copy_block(src, dst)
+    torch.cuda.synchronize()
+    for layer in range(2):
+        for slab in range(model.n_slabs):
+            assert np.array_equal(pool.slab_view(layer, slab, "k").cpu().numpy(), model.k_slabs[layer][slab])
+            assert np.array_equal(pool.slab_view(layer, slab, "v").cpu().numpy(), model.v_slabs[layer][slab])
+    assert pool.check_error() == 0
+    pool.close()

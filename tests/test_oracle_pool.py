@@ -185,3 +185,55 @@ def test_u16_record_views_round_trip():
     r = records_from_u16(x)
     assert r.shape == (2, 3, 8) and r[0, 0, 0] == 0 and r[0, 0, 2] == (997 & 0xFF)
     assert np.array_equal(u16_from_records(r), x)
+
+
+def test_copy_on_write_block_shares_then_isolates_a_block():
+    """Touch point 2 of the chunked-slab proposal: copy_on_write_block takes
+    the source slice from the source row's slab.  A sequence that takes a
+    copy of another's last (partial) block in a different slab gathers
+    byte-identically to the original; a later write into the copy leaves the
+    original untouched, and no other row of any layer changes."""
+    S, bs, n_kv, D = 4, 8, 2, 16
+    pool = SlabPoolModel(2, bs, n_kv, 2 * D, 2 * D, S)
+    pool.reserve_rows(16)
+    rows_a = np.array([1, 6, 9, 2], np.int32)              # slabs 0, 1, 2, 0
+    n = 29
+    ks, vs = [], []
+    for layer in range(2):
+        k, v = kv_bits_for_sequence(13, layer, 0, n, n_kv, D, "bf16")
+        _fill(pool, layer, rows_a, k, v)
+        ks.append(k)
+        vs.append(v)
+    before = [[s.copy() for s in pool.k_slabs[l] + pool.v_slabs[l]] for l in range(2)]
+    pool.copy_block([2], [13])                             # row 13 is in slab 3
+    rows_b = np.array([1, 6, 9, 13], np.int32)
+    for layer in range(2):
+        after = pool.k_slabs[layer] + pool.v_slabs[layer]
+        for i, (x, y) in enumerate(zip(before[layer], after)):
+            if i % pool.n_slabs == 3:                      # K and V slab 3: only row 1 changed
+                assert np.array_equal(np.delete(x, 1, axis=0), np.delete(y, 1, axis=0))
+            else:
+                assert np.array_equal(x, y)
+        gk, gv = pool.gather(layer, rows_b, n)
+        assert np.array_equal(u16_from_records(gk), _dense_reference(ks[layer]))
+        assert np.array_equal(u16_from_records(gv), _dense_reference(vs[layer]))
+    # sequence B appends token 29 into its own copy of the block
+    new = np.full((1, n_kv, 2 * D), 0xAB, np.uint8)
+    pool.write(0, [13], [n % bs], new, new)
+    gk_a, _ = pool.gather(0, rows_a, n)
+    gk_b, _ = pool.gather(0, rows_b, n + 1)
+    assert np.array_equal(u16_from_records(gk_a), _dense_reference(ks[0]))
+    assert np.array_equal(gk_b[:, :n], gk_a) and (gk_b[:, n] == 0xAB).all()
+
+
+def test_copy_block_reads_every_source_before_writing():
+    """Several pairs in one call: each destination gets its source as it was
+    before the call (brute force over a tiny pool)."""
+    pool = SlabPoolModel(1, 2, 1, 4, 4, 2)
+    pool.reserve_rows(6)
+    for row in range(6):
+        rec = np.full((1, 1, 4), row + 1, np.uint8)
+        pool.write(0, [row, row], [0, 1], np.repeat(rec, 2, 0), np.repeat(rec, 2, 0))
+    pool.copy_block([0, 3, 5], [4, 1, 2])
+    got = [int(pool.slab_for_row(0, r)[0][pool.slab_for_row(0, r)[2]][0, 0, 0]) for r in range(6)]
+    assert got == [1, 4, 6, 4, 1, 6]

@@ -12,9 +12,11 @@ row's slab, then paged_decode attends over all len tokens.  Inputs are
 resident in HBM before timing starts.  The 28-layer step touches 3.5 GiB of
 KV, far more than the last-level cache, so every layer is read from HBM.
 
-Prints one JSON line.  `value` is the step's algorithmic HBM bytes (KV read
-by paged_decode, q in, out, block table, lens, plus write_block's bytes)
-divided by the measured step time; `roofline` is paged_decode's dominant kernel
+The timed step is captured once into a HIP graph and replayed, as a serving
+loop would run it (every replay is checked bit-equal to the eager step, whose
+time is reported beside).  Prints one JSON line.  `value` is the step's
+algorithmic HBM bytes (KV read by paged_decode, q in, out, block table, lens,
+plus write_block's bytes) divided by the measured step time; `roofline` is paged_decode's dominant kernel
 (the split stage): its algorithmic bytes per launch over its average launch
 duration, measured live with HIP events on the launch stream around runs of
 that stage over every layer (the combine stage is timed the same way and
@@ -189,10 +191,52 @@ class Timer:
         return e0.elapsed_time(e1) * 1e3 / reps
 
 
-def stage_times(timer, decode_call, layers, reps):
-    """Live per-launch durations of the split and combine stages: each stage
-    of every listed layer back to back, between two events."""
+class Graph:
+    """fn captured once into a HIP graph (torch.cuda.CUDAGraph; the library
+    launches on the capturing stream, which torch makes current) and replayed
+    on the current stream.  fn must not allocate or synchronise."""
+
+    def __init__(self, torch, fn):
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            fn()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        self.graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(self.graph):
+            fn()
+        torch.cuda.synchronize()
+
+    def __call__(self):
+        self.graph.replay()
+
+
+def check_graph_replays(torch, step, graph, outs, rounds=2):
+    """Every replay of the captured step gives the eager step's outputs, bit
+    for bit, with eager work and synchronisations between the replays."""
+    for _ in range(rounds):
+        step()
+        torch.cuda.synchronize()
+        eager = [o.clone() for o in outs]
+        for o in outs:
+            o.zero_()
+        graph()
+        torch.cuda.synchronize()
+        if not all(torch.equal(a, b) for a, b in zip(eager, outs)):
+            raise RuntimeError("a graph replay of the decode step differs from the eager step")
+
+
+def stage_times(timer, decode_call, layers, reps, torch=None):
+    """Per-launch durations of the split and combine stages: each stage of
+    every listed layer back to back (the list repeated to at least 16
+    launches), between two events on the launch stream.  The split stage is
+    launched eagerly (it runs far longer than the host takes to issue it).
+    With torch given, the combine run is captured into a HIP graph and
+    replayed, so that host launch overhead does not count: issued from
+    Python, the short combine would be timed at the rate Python can issue it."""
     layers = list(layers)
+    layers = layers * max(1, -(-16 // len(layers)))
 
     def run(stage):
         for layer in layers:
@@ -200,8 +244,14 @@ def stage_times(timer, decode_call, layers, reps):
     for _ in range(2):
         run("split")
         run("combine")
+    # the split stage is timed before any graph is captured: the launches
+    # right after a capture run slower for a while
     split_us = timer(lambda: run("split"), reps) / len(layers)
-    combine_us = timer(lambda: run("combine"), reps) / len(layers)
+    combine_fn = lambda: run("combine")  # noqa: E731
+    if torch is not None:
+        combine_fn = Graph(torch, combine_fn)
+        combine_fn()
+    combine_us = timer(combine_fn, reps) / len(layers)
     run("split")
     run("combine")
     return split_us, combine_us
@@ -277,13 +327,20 @@ def run_qwen3_0p6b(args, torch, pd):
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    # per-stage launch durations first, right after the warm-up steps
+    split_us, combine_us = stage_times(timer, decode_call, range(L), args.steps, torch)
 
+    # The step as a serving loop runs it: captured once into a HIP graph and
+    # replayed (28 x write_block + split + combine, no host work per launch).
+    graph = Graph(torch, step)
+    check_graph_replays(torch, step, graph, outs)
+    for _ in range(args.warmup):
+        graph()
     # timed region: exactly `steps` full steps between two synchronised events
-    step_ms = timer(step, args.steps) / 1e3
+    step_ms = timer(graph, args.steps) / 1e3
     if pool.check_error():
         raise RuntimeError("device error during the timed steps")
-
-    split_us, combine_us = stage_times(timer, decode_call, range(L), args.steps)
+    eager_ms = timer(step, args.steps) / 1e3
 
     d_bytes = decode_bytes(lengths, n_kv, n_q, D, bs)
     w_bytes = write_bytes(B, n_kv, D)
@@ -318,6 +375,8 @@ def run_qwen3_0p6b(args, torch, pd):
         "pct_of_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
         "kv_tokens_attended_per_s": round(sum(lengths) * L / (step_ms * 1e-3), 1),
         "roofline": rl,
+        "step_timing": "HIP graph of the 28-layer step, replayed; every replay checked bit-equal to the eager step",
+        "eager_ms_per_step": round(eager_ms, 4),
         "paged_decode": {"split_us": round(split_us, 3), "combine_us": round(combine_us, 3),
                          "achieved_gbs_both_stages": round(d_bytes / ((split_us + combine_us) * 1e-6) / 1e9, 1)},
         "write_block": {"bytes_per_launch": w_bytes},
@@ -424,7 +483,7 @@ def run_fragmented(args, torch, pd):
     def decode_call(layer, stage):
         pool.paged_decode(0, q, tables[last], lens_d[last], max_len, w.scale, out, ws, stage=stage)
 
-    split_us, combine_us = stage_times(timer, decode_call, [0], args.steps)
+    split_us, combine_us = stage_times(timer, decode_call, [0], args.steps, torch)
     d_bytes = decode_bytes(step_lens[last], n_kv, n_q, D, bs)
     stats = pool.stats()
     pool.close()
@@ -496,10 +555,15 @@ def run_long_context(args, torch, pd):
 
     for _ in range(args.warmup):
         step()
-    step_ms = timer(step, args.steps) / 1e3
+    torch.cuda.synchronize()
+    eager_ms = timer(step, max(2, args.steps // 4)) / 1e3
+    graph = Graph(torch, step)
+    check_graph_replays(torch, step, graph, outs, rounds=1)
+    graph()
+    step_ms = timer(graph, args.steps) / 1e3
     if pool.check_error():
         raise RuntimeError("device error during the timed steps")
-    split_us, combine_us = stage_times(timer, decode_call, range(L), max(2, args.steps // 4))
+    split_us, combine_us = stage_times(timer, decode_call, range(L), max(2, args.steps // 4), torch)
     d_bytes = decode_bytes(lengths, n_kv, n_q, D, bs)
     step_bytes = L * (d_bytes + write_bytes(B, n_kv, D))
 
@@ -520,6 +584,8 @@ def run_long_context(args, torch, pd):
         "pct_of_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
         "kv_tokens_attended_per_s": round(sum(lengths) * L / (step_ms * 1e-3), 1),
         "roofline": roofline(d_bytes, split_us, "paged_decode_row_kernel<128,2,true,2> (split stage)"),
+        "step_timing": "HIP graph of the 28-layer step, replayed; replays checked bit-equal to the eager step",
+        "eager_ms_per_step": round(eager_ms, 4),
         "paged_decode": {"split_us": round(split_us, 3), "combine_us": round(combine_us, 3)},
         "gather_visible": {"us_per_layer": round(g_us, 2), "bytes_per_layer": g_bytes,
                            "achieved_gbs": round(g_bytes / (g_us * 1e-6) / 1e9, 1),
@@ -587,7 +653,7 @@ def run_packed(args, torch, pd):
                 pool.paged_decode(layer, q, table, lens, n, scale, out, ws, stage=stage)
 
             split_us, combine_us = stage_times(timer, decode_call, range(copies),
-                                               max(2, args.steps // copies))
+                                               max(2, args.steps // copies), torch)
             if pool.check_error():
                 raise RuntimeError(f"device error during the {fmt} D={D} timing")
             pool.close()

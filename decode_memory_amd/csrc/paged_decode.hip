@@ -23,9 +23,11 @@
 //
 // A second kernel combines the splits of each (sequence, kv head) in split
 // order, so the result does not depend on timing.  (Merging inside the split
-// kernel through an arrival counter would need an agent-scope release fence
-// per workgroup, and on this GPU such a fence writes back the whole L2 of
-// the XCD; a kernel boundary gives the same visibility once per launch.)
+// kernel through an arrival counter needs the partials to cross XCDs within
+// the launch: with an agent-scope release fence per workgroup, which writes
+// back the XCD's whole L2, or with device-scope write-through stores; the
+// latter works but the last workgroup of a sequence then pulls every split's
+// partial through one CU, which costs as much as this launch.)
 #include "device_common.h"
 #include "internal.h"
 
@@ -265,77 +267,94 @@ __global__ __launch_bounds__(kThreads, kMinWavesPerSimd) void paged_decode_kerne
   }
 }
 
-// Split-K combine.  A workgroup owns 256/D (sequence, query head) pairs.  It
-// stages every active split's (max, sum) in LDS while each thread already
-// loads the weighted-V values of its output column for up to kChunk splits,
-// so the pass costs about one memory latency; one wave per query head turns
-// the maxima into split weights (exp2(m_s - M) / sum), and every thread sums
+// Split-K combine.  One wave owns 64 output columns of one (sequence, query
+// head): lane j holds column j of the chunk.  Everything it needs is
+// requested at once -- the (max, sum) of every active split (one per lane,
+// coalesced) and its column of the first kCChunk splits' weighted V -- so the
+// pass costs about one memory round trip and has no LDS or barrier.  The
+// maxima are reduced across the wave (a fixed butterfly), each split's weight
+// exp2(m_s - M) is broadcast from the lane that holds it, and every lane sums
 // its column in split order -- the result does not depend on timing -- and
 // rounds once to the q dtype.  Empty sequences get zeros.
+constexpr int kCChunk = 32;                 // splits whose values a lane holds at once
+constexpr int kCWaves = 4;                  // waves per combine workgroup
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = kWave / 2; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = kWave / 2; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
 template <int D, bool BF16>
-__global__ __launch_bounds__(kThreads) void combine_kernel(DecodeArgs a) {
-  constexpr int HPW = kThreads / D;  // query heads per workgroup
-  constexpr int kChunk = 32;         // splits whose values a thread holds at once
-  __shared__ float s_w[HPW][kMaxSplits];
-  __shared__ float s_l[HPW][kMaxSplits];
-  __shared__ float s_inv[HPW];
-  const int hloc = __builtin_amdgcn_readfirstlane(threadIdx.x / D);
-  const int d = threadIdx.x % D;
+__global__ __launch_bounds__(kCWaves * kWave) void combine_kernel(DecodeArgs a) {
+  constexpr int CH = D / kWave;  // 64-column chunks per query head
+  constexpr int KM = kMaxSplits / kWave;
+  const int lane = threadIdx.x % kWave;
+  const int item = blockIdx.x * kCWaves + __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int total = a.B * a.n_q;
+  if (item >= total * CH) return;
+  const int hq = item / CH;                 // (sequence, query head) index
+  const int col = (item % CH) * kWave + lane;
   const int n_split = a.n_split;
   const int BS = a.lv.block_size;
   const int cap_len = min(a.max_blocks, n_split * a.blocks_per_split) * BS;
-  auto active = [&](int hq) {
-    int len = a.lens[hq / a.n_q];
-    len = len < 0 ? 0 : (len > cap_len ? cap_len : len);
-    return min(n_split, (len + BS - 1) / BS);
-  };
-  const int total = a.B * a.n_q;
-  const int hq = blockIdx.x * HPW + hloc;  // (sequence, query head) index
-  const int n_act = hq < total ? active(hq) : 0;
-  const float* acc = a.partials + static_cast<size_t>(hq) * n_split * D + d;
-  const float* ml = a.partials + a.ml_offset;
+  int len = a.lens[hq / a.n_q];
+  len = len < 0 ? 0 : (len > cap_len ? cap_len : len);
+  const int n_act = min(n_split, (len + BS - 1) / BS);
+  uint16_t* out = static_cast<uint16_t*>(a.out) + static_cast<size_t>(hq) * D + col;
 
-  // The first kChunk splits' values are loaded before the sequence length is
-  // known (they are in bounds of the workspace whatever it is); values of
-  // inactive splits are never used.
-  const int n_pre = min(n_split, kChunk);
-  float v[kChunk];
+  const float* acc = a.partials + static_cast<size_t>(hq) * n_split * D + col;
+  const float2* ml = reinterpret_cast<const float2*>(a.partials + a.ml_offset) +
+                     static_cast<size_t>(hq) * n_split;
+  // requests first: the first kCChunk splits' values (in bounds of the
+  // workspace whatever the length is; inactive splits are never used) and
+  // the (max, sum) pairs, one split per lane
+  float v[kCChunk];
 #pragma unroll
-  for (int k = 0; k < kChunk; ++k) v[k] = (k < n_pre && hq < total) ? acc[k * D] : 0.f;
-  for (int i = threadIdx.x; i < HPW * kMaxSplits; i += kThreads) {
-    const int h = i / kMaxSplits, sp = i % kMaxSplits;
-    const int hq2 = blockIdx.x * HPW + h;
-    if (hq2 < total && sp < active(hq2)) {
-      const size_t at = (static_cast<size_t>(hq2) * n_split + sp) * 2;
-      s_w[h][sp] = ml[at];
-      s_l[h][sp] = ml[at + 1];
-    }
+  for (int k = 0; k < kCChunk; ++k) v[k] = k < n_split ? acc[static_cast<size_t>(k) * D] : 0.f;
+  float mm[KM], ll[KM];
+#pragma unroll
+  for (int k = 0; k < KM; ++k) {
+    const int sp = lane + k * kWave;
+    const float2 x = sp < n_act ? ml[sp] : make_float2(-INFINITY, 0.f);
+    mm[k] = x.x;
+    ll[k] = x.y;
   }
-  __syncthreads();
-  if (d < kWave) {  // the first wave of each head computes the split weights
-    const int lane = d;
-    float M = -INFINITY;
-    for (int sp = lane; sp < n_act; sp += kWave) M = fmaxf(M, s_w[hloc][sp]);
-    for (int o = kWave / 2; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, kWave));
-    float L = 0.f;
-    for (int sp = lane; sp < n_act; sp += kWave) {
-      const float m = s_w[hloc][sp];
-      // a split whose rows were all rejected carries (-inf, 0, 0)
-      const float f = (m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m - M);
-      s_w[hloc][sp] = f;
-      L = fmaf(s_l[hloc][sp], f, L);
-    }
-    for (int o = kWave / 2; o >= 1; o >>= 1) L += __shfl_xor(L, o, kWave);
-    if (lane == 0) s_inv[hloc] = L > 0.f ? 1.f / L : 0.f;
+  if (n_act == 0) {
+    *out = 0;
+    return;
   }
-  __syncthreads();
-  if (hq >= total) return;
+  float M = mm[0];
+#pragma unroll
+  for (int k = 1; k < KM; ++k) M = fmaxf(M, mm[k]);
+  M = wave_max(M);
+  float L = 0.f;
+#pragma unroll
+  for (int k = 0; k < KM; ++k) {
+    // a split whose rows were all rejected carries (-inf, 0, 0)
+    mm[k] = (mm[k] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mm[k] - M);
+    L = fmaf(ll[k], mm[k], L);
+  }
+  L = wave_sum(L);
+  // weight of split sp: mm[sp / 64] of lane sp % 64
+  auto weight = [&](int sp) {
+    float w = 0.f;
+#pragma unroll
+    for (int k = 0; k < KM; ++k)
+      if (sp / kWave == k) w = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, mm[k]), sp % kWave));
+    return w;
+  };
   float A = 0.f;
 #pragma unroll
-  for (int k = 0; k < kChunk; ++k)
-    A = (k < n_act) ? fmaf(v[k], s_w[hloc][k], A) : A;
-  for (int sp = kChunk; sp < n_act; ++sp) A = fmaf(acc[sp * D], s_w[hloc][sp], A);
-  static_cast<uint16_t*>(a.out)[static_cast<size_t>(hq) * D + d] = f32_to_out<BF16>(A * s_inv[hloc]);
+  for (int k = 0; k < kCChunk; ++k)
+    if (k < n_act) A = fmaf(v[k], weight(k), A);
+  for (int sp = kCChunk; sp < n_act; ++sp) A = fmaf(acc[static_cast<size_t>(sp) * D], weight(sp), A);
+  *out = f32_to_out<BF16>(A * (L > 0.f ? 1.f / L : 0.f));
 }
 
 template <int D, int G, bool BF16, int BS>
@@ -348,9 +367,9 @@ hipError_t launch_typed(const DecodeArgs& a, hipStream_t s) {
 
 template <int D, bool BF16>
 hipError_t launch_combine_typed(const DecodeArgs& a, hipStream_t s) {
-  const long long outs = static_cast<long long>(a.B) * a.n_q * D;
-  const int grid = static_cast<int>((outs + kThreads - 1) / kThreads);
-  hipLaunchKernelGGL((combine_kernel<D, BF16>), dim3(grid), dim3(kThreads), 0, s, a);
+  const long long waves = static_cast<long long>(a.B) * a.n_q * (D / kWave);
+  const int grid = static_cast<int>((waves + kCWaves - 1) / kCWaves);
+  hipLaunchKernelGGL((combine_kernel<D, BF16>), dim3(grid), dim3(kCWaves * kWave), 0, s, a);
   return hipGetLastError();
 }
 

@@ -59,12 +59,35 @@ class PoolStats(ctypes.Structure):
         return {name: getattr(self, name) for name, _ in self._fields_}
 
 
+class StorageIdentity(ctypes.Structure):
+    """pd_storage_identity: 48 bytes, little endian."""
+    _fields_ = [("magic", ctypes.c_uint32), ("layout", ctypes.c_uint32), ("format", ctypes.c_int32),
+                ("n_layers", ctypes.c_int32), ("block_size", ctypes.c_int32),
+                ("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("k_record_bytes", ctypes.c_int32), ("v_record_bytes", ctypes.c_int32),
+                ("group_size", ctypes.c_int32), ("signs_hash", ctypes.c_uint64)]
+
+    def as_dict(self):
+        return {name: getattr(self, name) for name, _ in self._fields_}
+
+    def to_bytes(self) -> bytes:
+        return bytes(self)
+
+    @classmethod
+    def from_bytes(cls, b: bytes) -> "StorageIdentity":
+        if len(b) != ctypes.sizeof(cls):
+            raise ValueError(f"a storage identity is {ctypes.sizeof(cls)} bytes, got {len(b)}")
+        return cls.from_buffer_copy(b)
+
+
 EXPORTS = [
     "pd_version", "pd_last_error", "pd_record_bytes", "pd_pool_create", "pd_pool_destroy",
     "pd_slab_bytes", "pd_append_slab", "pd_slabs_needed", "pd_reserve_rows", "pd_slab_for_row",
     "pd_write_block", "pd_copy_on_write_block", "pd_gather_visible", "pd_decode_workspace_bytes",
     "pd_paged_decode",
     "pd_paged_decode_split", "pd_paged_decode_combine", "pd_pool_stats", "pd_pool_check_error",
+    "pd_signs_hash", "pd_storage_identity_of", "pd_identity_check", "pd_block_bytes",
+    "pd_export_blocks", "pd_import_blocks",
 ]
 
 _lib_handle = None
@@ -97,6 +120,12 @@ def _declare(lib):
                                            ctypes.c_float, _vp, _vp, _sz, _vp]),
         "pd_pool_stats": (_i32, [_vp, ctypes.POINTER(PoolStats)]),
         "pd_pool_check_error": (_i32, [_vp, _vp, _p_i32]),
+        "pd_signs_hash": (_i32, [ctypes.POINTER(ctypes.c_int8), _i32, ctypes.POINTER(ctypes.c_uint64)]),
+        "pd_storage_identity_of": (_i32, [_vp, ctypes.POINTER(StorageIdentity)]),
+        "pd_identity_check": (_i32, [_vp, ctypes.POINTER(StorageIdentity)]),
+        "pd_block_bytes": (_i32, [_vp, ctypes.POINTER(_sz)]),
+        "pd_export_blocks": (_i32, [_vp, _i32, _vp, _vp, _sz, _vp]),
+        "pd_import_blocks": (_i32, [_vp, ctypes.POINTER(StorageIdentity), _i32, _vp, _vp, _sz, _vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -232,6 +261,75 @@ def copy_on_write_block(pool: int, src_rows: torch.Tensor, dst_rows: torch.Tenso
     _check(lib().pd_copy_on_write_block(pool, n, _ptr(src_rows), _ptr(dst_rows), _stream(stream)))
 
 
+def signs_hash(signs: Sequence[int]) -> int:
+    """FNV-1a 64 of the Hadamard sign bytes (host only)."""
+    arr = (ctypes.c_int8 * max(1, len(signs)))(*[int(x) for x in signs])
+    h = ctypes.c_uint64(0)
+    _check(lib().pd_signs_hash(arr, len(signs), ctypes.byref(h)))
+    return h.value
+
+
+def storage_identity(pool: int) -> StorageIdentity:
+    out = StorageIdentity()
+    _check(lib().pd_storage_identity_of(pool, ctypes.byref(out)))
+    return out
+
+
+def identity_check(pool: int, identity: StorageIdentity) -> None:
+    """Raises PagedKVError (status -7) when blocks of `identity` cannot be
+    imported into the pool."""
+    _check(lib().pd_identity_check(pool, ctypes.byref(identity)))
+
+
+def block_bytes(pool: int) -> int:
+    n = _sz(0)
+    _check(lib().pd_block_bytes(pool, ctypes.byref(n)))
+    return n.value
+
+
+def export_blocks(pool: int, rows: torch.Tensor, dst: torch.Tensor, stream=None) -> None:
+    _require(rows, "rows", torch.int32)
+    _require(dst, "dst")
+    _check(lib().pd_export_blocks(pool, rows.numel(), _ptr(rows), _ptr(dst),
+                                  dst.numel() * dst.element_size(), _stream(stream)))
+
+
+def import_blocks(pool: int, identity: StorageIdentity, rows: torch.Tensor, src: torch.Tensor,
+                  stream=None) -> None:
+    _require(rows, "rows", torch.int32)
+    _require(src, "src")
+    _check(lib().pd_import_blocks(pool, ctypes.byref(identity), rows.numel(), _ptr(rows), _ptr(src),
+                                  src.numel() * src.element_size(), _stream(stream)))
+
+
+CHECKPOINT_MAGIC = b"PDKVBLK1"
+
+
+def write_checkpoint(path: str, identity: StorageIdentity, payload: torch.Tensor) -> None:
+    """A block checkpoint file: 8-byte magic, the 48-byte storage identity,
+    the block count (int64 little endian), then the exported bytes."""
+    data = payload.contiguous().view(torch.uint8).cpu().numpy().tobytes()
+    n = len(data) // max(1, block_bytes_of(identity))
+    with open(path, "wb") as f:
+        f.write(CHECKPOINT_MAGIC + identity.to_bytes() + int(n).to_bytes(8, "little") + data)
+
+
+def read_checkpoint_header(path: str):
+    """(identity, n_blocks) of a block checkpoint, reading only its header."""
+    size = len(CHECKPOINT_MAGIC) + ctypes.sizeof(StorageIdentity) + 8
+    with open(path, "rb") as f:
+        head = f.read(size)
+    if len(head) != size or not head.startswith(CHECKPOINT_MAGIC):
+        raise ValueError(f"{path} is not a block checkpoint")
+    ident = StorageIdentity.from_bytes(head[len(CHECKPOINT_MAGIC):-8])
+    return ident, int.from_bytes(head[-8:], "little")
+
+
+def block_bytes_of(identity: StorageIdentity) -> int:
+    return (identity.n_layers * identity.block_size * identity.n_kv_heads *
+            (identity.k_record_bytes + identity.v_record_bytes))
+
+
 def gather_visible(pool: int, layer: int, block_table: torch.Tensor, lens: torch.Tensor,
                    t_out: int, k_out: torch.Tensor, v_out: torch.Tensor,
                    n_runs_out: Optional[torch.Tensor] = None, stream=None) -> None:
@@ -359,6 +457,43 @@ class SlabPool:
 
     def copy_on_write_block(self, src_rows, dst_rows, stream=None):
         copy_on_write_block(self.handle, src_rows, dst_rows, stream)
+
+    def storage_identity(self) -> StorageIdentity:
+        return storage_identity(self.handle)
+
+    def export_blocks(self, rows: torch.Tensor, stream=None) -> torch.Tensor:
+        """The bytes of block rows `rows`, every layer: uint8 [n, block_bytes]."""
+        dst = torch.empty((rows.numel(), block_bytes(self.handle)), dtype=torch.uint8, device=self.device)
+        export_blocks(self.handle, rows, dst, stream)
+        return dst
+
+    def import_blocks(self, identity: StorageIdentity, rows: torch.Tensor, payload: torch.Tensor,
+                      stream=None) -> None:
+        import_blocks(self.handle, identity, rows, payload, stream)
+
+    def save_checkpoint(self, path: str, rows: torch.Tensor) -> None:
+        payload = self.export_blocks(rows)
+        torch.cuda.synchronize(self.device)
+        write_checkpoint(path, self.storage_identity(), payload)
+
+    def restore_checkpoint(self, path: str, rows: torch.Tensor) -> None:
+        """Restore a block checkpoint into rows `rows`.  The storage identity
+        is checked before anything is allocated: a mismatch raises
+        PagedKVError (status -7) with the pool and the device untouched.
+        Then the rows are reserved (growth by slab append) and written."""
+        ident, n = read_checkpoint_header(path)
+        identity_check(self.handle, ident)
+        if rows.numel() != n:
+            raise ValueError(f"the checkpoint holds {n} blocks, {rows.numel()} rows given")
+        size = len(CHECKPOINT_MAGIC) + ctypes.sizeof(StorageIdentity) + 8
+        with open(path, "rb") as f:
+            f.seek(size)
+            data = f.read()
+        import numpy as np
+        payload = torch.from_numpy(np.frombuffer(data, dtype=np.uint8).copy()).to(self.device)
+        if n:
+            self.reserve_rows(int(rows.max().item()) + 1)
+        import_blocks(self.handle, ident, rows, payload)
 
     def gather_visible(self, layer, block_table, lens, t_out, k_out, v_out, n_runs_out=None,
                        stream=None):

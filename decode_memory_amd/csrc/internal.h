@@ -38,7 +38,11 @@ struct WriteArgs {
   float inv_sqrt_d;
 };
 
-struct CopyArgs {
+// Whole block rows moved between two pool rows (copy_on_write_block), from
+// pool rows to a contiguous buffer (export_blocks) or back (import_blocks).
+// Buffer layout: [n][n_layers][K row bytes, V row bytes].
+enum RowMoveMode { kMoveCopy = 0, kMoveExport = 1, kMoveImport = 2 };
+struct RowMoveArgs {
   const void* const* tables;  // device: [n_layers][2][max_slabs] slab bases
   int32_t max_slabs;
   int32_t n_layers;
@@ -46,8 +50,10 @@ struct CopyArgs {
   int64_t capacity_rows;
   int64_t row_bytes[2];       // bytes of one block row of K, of V
   int32_t n;
-  const int32_t* src_rows;
-  const int32_t* dst_rows;
+  const int32_t* src_rows;    // copy, export
+  const int32_t* dst_rows;    // copy, import
+  const char* src_buf;        // import
+  char* dst_buf;              // export
   int32_t* err;
 };
 
@@ -89,7 +95,7 @@ struct DecodeArgs {
 // no kernel exists for the shape).
 hipError_t launch_zero_fill(void* p, size_t bytes, hipStream_t s);
 hipError_t launch_write_block(const WriteArgs& a, int32_t format, hipStream_t s);
-hipError_t launch_copy_block(const CopyArgs& a, hipStream_t s);
+hipError_t launch_row_move(const RowMoveArgs& a, int mode, hipStream_t s);
 hipError_t launch_gather(const GatherArgs& a, hipStream_t s);
 hipError_t launch_paged_decode_column(const DecodeArgs& a, bool bf16, int32_t head_dim,
                                       int32_t group, hipStream_t s);

@@ -50,6 +50,7 @@ struct pd_pool {
   void** d_tables = nullptr;
   int32_t* d_err = nullptr;
   float* d_signs = nullptr;  // packed: [head_dim] of +-1
+  uint64_t signs_hash = 0;   // packed: pd_signs_hash of the signs
   float inv_sqrt_d = 1.f;
 };
 
@@ -305,6 +306,7 @@ pd_status pd_pool_create(const pd_pool_desc* d, pd_pool** out) {
   if (e == hipSuccess) e = hipMalloc(reinterpret_cast<void**>(&p->d_err), 256);
   if (e == hipSuccess) e = hipMemset(p->d_err, 0, 256);
   if (e == hipSuccess && is_packed(d->format)) {
+    pd_signs_hash(d->hadamard_signs, d->head_dim, &p->signs_hash);
     std::vector<float> s(d->head_dim);
     for (int i = 0; i < d->head_dim; ++i) s[i] = static_cast<float>(d->hadamard_signs[i]);
     e = hipMalloc(reinterpret_cast<void**>(&p->d_signs), sizeof(float) * d->head_dim);
@@ -415,13 +417,12 @@ pd_status pd_write_block(pd_pool* p, int32_t layer, int32_t n, const int32_t* ro
   return PD_OK;
 }
 
-pd_status pd_copy_on_write_block(pd_pool* p, int32_t n, const int32_t* src_rows,
-                                 const int32_t* dst_rows, hipStream_t stream) {
-  if (pd_status st = check_pool(p)) return st;
-  if (n < 0) return fail(PD_ERR_ARG, "n < 0");
-  if (n == 0) return PD_OK;
-  if (!src_rows || !dst_rows) return fail(PD_ERR_ARG, "NULL device pointer");
-  CopyArgs a{};
+}  // extern "C"
+
+namespace {
+
+RowMoveArgs row_move_args(const pd_pool* p, int32_t n) {
+  RowMoveArgs a{};
   a.tables = const_cast<const void* const*>(p->d_tables);
   a.max_slabs = p->desc.max_slabs;
   a.n_layers = p->desc.n_layers;
@@ -431,11 +432,130 @@ pd_status pd_copy_on_write_block(pd_pool* p, int32_t n, const int32_t* src_rows,
   a.row_bytes[0] = tok * p->k_rec;
   a.row_bytes[1] = tok * p->v_rec;
   a.n = n;
+  a.err = p->d_err;
+  return a;
+}
+
+size_t block_bytes(const pd_pool* p) {
+  return static_cast<size_t>(p->desc.n_layers) * p->desc.block_size * p->desc.n_kv_heads *
+         static_cast<size_t>(p->k_rec + p->v_rec);
+}
+
+void identity_of(const pd_pool* p, pd_storage_identity* id) {
+  std::memset(id, 0, sizeof *id);
+  id->magic = PD_IDENTITY_MAGIC;
+  id->layout = PD_IDENTITY_LAYOUT;
+  id->format = p->desc.format;
+  id->n_layers = p->desc.n_layers;
+  id->block_size = p->desc.block_size;
+  id->n_kv_heads = p->desc.n_kv_heads;
+  id->head_dim = p->desc.head_dim;
+  id->k_record_bytes = p->k_rec;
+  id->v_record_bytes = p->v_rec;
+  id->group_size = is_packed(p->desc.format) ? 32 : 0;
+  id->signs_hash = p->signs_hash;
+}
+
+}  // namespace
+
+extern "C" {
+
+pd_status pd_copy_on_write_block(pd_pool* p, int32_t n, const int32_t* src_rows,
+                                 const int32_t* dst_rows, hipStream_t stream) {
+  if (pd_status st = check_pool(p)) return st;
+  if (n < 0) return fail(PD_ERR_ARG, "n < 0");
+  if (n == 0) return PD_OK;
+  if (!src_rows || !dst_rows) return fail(PD_ERR_ARG, "NULL device pointer");
+  RowMoveArgs a = row_move_args(p, n);
   a.src_rows = src_rows;
   a.dst_rows = dst_rows;
-  a.err = p->d_err;
-  hipError_t e = launch_copy_block(a, stream);
+  hipError_t e = launch_row_move(a, kMoveCopy, stream);
   if (e != hipSuccess) return hip_fail(e, "copy_on_write_block launch");
+  return PD_OK;
+}
+
+pd_status pd_signs_hash(const int8_t* signs, int32_t n, uint64_t* hash) {
+  if (!hash || n < 0 || (n > 0 && !signs)) return fail(PD_ERR_ARG, "signs NULL, n < 0 or hash NULL");
+  uint64_t h = 0xcbf29ce484222325ull;  // FNV-1a 64 offset basis
+  for (int32_t i = 0; i < n; ++i) {
+    h ^= static_cast<uint8_t>(signs[i]);
+    h *= 0x100000001b3ull;             // FNV-1a 64 prime
+  }
+  *hash = h;
+  return PD_OK;
+}
+
+pd_status pd_storage_identity_of(const pd_pool* p, pd_storage_identity* id) {
+  if (pd_status st = check_pool(p)) return st;
+  if (!id) return fail(PD_ERR_ARG, "id is NULL");
+  identity_of(p, id);
+  return PD_OK;
+}
+
+pd_status pd_identity_check(const pd_pool* p, const pd_storage_identity* id) {
+  if (pd_status st = check_pool(p)) return st;
+  if (!id) return fail(PD_ERR_ARG, "id is NULL");
+  pd_storage_identity mine;
+  identity_of(p, &mine);
+#define PD_FIELD(f)                                                                            \
+  if (id->f != mine.f)                                                                         \
+    return fail(PD_ERR_IDENTITY, "storage identity differs in " #f ": blocks have %lld, pool has %lld", \
+                static_cast<long long>(id->f), static_cast<long long>(mine.f));
+  PD_FIELD(magic)
+  PD_FIELD(layout)
+  PD_FIELD(format)
+  PD_FIELD(n_layers)
+  PD_FIELD(block_size)
+  PD_FIELD(n_kv_heads)
+  PD_FIELD(head_dim)
+  PD_FIELD(k_record_bytes)
+  PD_FIELD(v_record_bytes)
+  PD_FIELD(group_size)
+  PD_FIELD(signs_hash)
+#undef PD_FIELD
+  return PD_OK;
+}
+
+pd_status pd_block_bytes(const pd_pool* p, size_t* bytes) {
+  if (pd_status st = check_pool(p)) return st;
+  if (!bytes) return fail(PD_ERR_ARG, "bytes is NULL");
+  *bytes = block_bytes(p);
+  return PD_OK;
+}
+
+pd_status pd_export_blocks(pd_pool* p, int32_t n, const int32_t* rows, void* dst, size_t dst_bytes,
+                           hipStream_t stream) {
+  if (pd_status st = check_pool(p)) return st;
+  if (n < 0) return fail(PD_ERR_ARG, "n < 0");
+  if (n == 0) return PD_OK;
+  if (!rows || !dst) return fail(PD_ERR_ARG, "NULL device pointer");
+  if (reinterpret_cast<uintptr_t>(dst) & 15) return fail(PD_ERR_ARG, "dst must be 16-byte aligned");
+  if (dst_bytes < static_cast<size_t>(n) * block_bytes(p))
+    return fail(PD_ERR_CAPACITY, "dst holds %zu bytes, %zu needed", dst_bytes,
+                static_cast<size_t>(n) * block_bytes(p));
+  RowMoveArgs a = row_move_args(p, n);
+  a.src_rows = rows;
+  a.dst_buf = static_cast<char*>(dst);
+  hipError_t e = launch_row_move(a, kMoveExport, stream);
+  if (e != hipSuccess) return hip_fail(e, "export_blocks launch");
+  return PD_OK;
+}
+
+pd_status pd_import_blocks(pd_pool* p, const pd_storage_identity* id, int32_t n, const int32_t* rows,
+                           const void* src, size_t src_bytes, hipStream_t stream) {
+  if (pd_status st = pd_identity_check(p, id)) return st;
+  if (n < 0) return fail(PD_ERR_ARG, "n < 0");
+  if (n == 0) return PD_OK;
+  if (!rows || !src) return fail(PD_ERR_ARG, "NULL device pointer");
+  if (reinterpret_cast<uintptr_t>(src) & 15) return fail(PD_ERR_ARG, "src must be 16-byte aligned");
+  if (src_bytes < static_cast<size_t>(n) * block_bytes(p))
+    return fail(PD_ERR_CAPACITY, "src holds %zu bytes, %zu needed", src_bytes,
+                static_cast<size_t>(n) * block_bytes(p));
+  RowMoveArgs a = row_move_args(p, n);
+  a.dst_rows = rows;
+  a.src_buf = static_cast<const char*>(src);
+  hipError_t e = launch_row_move(a, kMoveImport, stream);
+  if (e != hipSuccess) return hip_fail(e, "import_blocks launch");
   return PD_OK;
 }
 

@@ -1,6 +1,6 @@
-// write_block: token-granular scatter of new K/V into the slab of their row,
-// copy_on_write_block: whole-row copies between slabs, and the zero fill that
-// backs append_slab.
+// write_block: token-granular scatter of new K/V into the slab of their row;
+// whole-row moves (copy_on_write_block, block export and import); and the
+// zero fill that backs append_slab.
 //
 // mlxcel issue #235 ("perf(core): chunked slab storage for the paged pool to
 // eliminate growth reallocation entirely"), section "Proposed solution:
@@ -72,15 +72,31 @@ __global__ __launch_bounds__(kThreads) void write_block_native_kernel(WriteArgs 
   }
 }
 
-// copy_on_write_block (mlxcel #235, "Proposed solution", touch point 2): a
-// work unit is 4 KiB of one block row of one layer's K or V for one pair; a
-// workgroup copies it as one 16-byte vector per lane.  Rows of a block are
-// contiguous in their slab, so both sides are plain streams.
-constexpr int kCopyChunk = kThreads * 16;
+// Whole block rows, every layer, K and V: copy_on_write_block (mlxcel #235,
+// "Proposed solution", touch point 2: the source slice comes from the source
+// row's slab), and the serde block-content extraction and restore path
+// (touch point 6: per-block reads and writes localise to the row's slab
+// through the same mapping).  A work unit is 4 KiB of one block row of one
+// layer's K or V for one block; a workgroup moves it as one 16-byte vector
+// per lane.  The rows of a block are contiguous in their slab, so both sides
+// are plain streams.
+constexpr int kMoveChunk = kThreads * 16;
 
-__global__ __launch_bounds__(kThreads) void copy_block_kernel(CopyArgs a) {
+__device__ __forceinline__ char* pool_row(const RowMoveArgs& a, int layer, int kv, int32_t row) {
+  const void* const* tab = a.tables + (static_cast<size_t>(layer) * 2 + kv) * a.max_slabs;
+  const int slab = row / a.slab_blocks;
+  return static_cast<char*>(const_cast<void*>(tab[slab])) + (row - slab * a.slab_blocks) * a.row_bytes[kv];
+}
+
+__device__ __forceinline__ size_t buf_offset(const RowMoveArgs& a, int i, int layer, int kv) {
+  return (static_cast<size_t>(i) * a.n_layers + layer) * (a.row_bytes[0] + a.row_bytes[1]) +
+         (kv ? a.row_bytes[0] : 0);
+}
+
+template <int MODE>
+__global__ __launch_bounds__(kThreads) void row_move_kernel(RowMoveArgs a) {
   const int64_t max_row = a.row_bytes[0] > a.row_bytes[1] ? a.row_bytes[0] : a.row_bytes[1];
-  const int chunks = static_cast<int>((max_row + kCopyChunk - 1) / kCopyChunk);
+  const int chunks = static_cast<int>((max_row + kMoveChunk - 1) / kMoveChunk);
   const long long units = static_cast<long long>(a.n) * a.n_layers * 2 * chunks;
   for (long long u = blockIdx.x; u < units; u += gridDim.x) {
     const int c = static_cast<int>(u % chunks);
@@ -89,23 +105,39 @@ __global__ __launch_bounds__(kThreads) void copy_block_kernel(CopyArgs a) {
     r /= 2;
     const int layer = static_cast<int>(r % a.n_layers);
     const int i = static_cast<int>(r / a.n_layers);
-    const int32_t src = a.src_rows[i], dst = a.dst_rows[i];
-    const bool src_ok = src >= 0 && src < a.capacity_rows;
-    const bool dst_ok = dst >= 0 && dst < a.capacity_rows;
-    if (!src_ok || !dst_ok) {
-      // reported once per pair
-      if (threadIdx.x == 0 && c == 0 && kv == 0 && layer == 0)
-        set_error(a.err, src_ok ? PD_DEVERR_WRITE_ROW : PD_DEVERR_TABLE_ROW);
-      continue;
-    }
+    const bool report = threadIdx.x == 0 && c == 0 && kv == 0 && layer == 0;  // once per block
     const int64_t bytes = a.row_bytes[kv];
-    const int64_t off = static_cast<int64_t>(c) * kCopyChunk + threadIdx.x * 16;
-    if (off >= bytes) continue;
-    const void* const* tab = a.tables + (static_cast<size_t>(layer) * 2 + kv) * a.max_slabs;
-    const int ss = src / a.slab_blocks, ds = dst / a.slab_blocks;
-    const char* from = static_cast<const char*>(tab[ss]) + (src - ss * a.slab_blocks) * bytes;
-    char* to = static_cast<char*>(const_cast<void*>(tab[ds])) + (dst - ds * a.slab_blocks) * bytes;
-    *reinterpret_cast<uint4*>(to + off) = *reinterpret_cast<const uint4*>(from + off);
+    const int64_t off = static_cast<int64_t>(c) * kMoveChunk + threadIdx.x * 16;
+    const bool lane_in = off < bytes;
+    if constexpr (MODE == kMoveCopy) {
+      const int32_t src = a.src_rows[i], dst = a.dst_rows[i];
+      const bool src_ok = src >= 0 && src < a.capacity_rows;
+      const bool dst_ok = dst >= 0 && dst < a.capacity_rows;
+      if (!src_ok || !dst_ok) {
+        if (report) set_error(a.err, src_ok ? PD_DEVERR_WRITE_ROW : PD_DEVERR_TABLE_ROW);
+        continue;
+      }
+      if (lane_in)
+        *reinterpret_cast<uint4*>(pool_row(a, layer, kv, dst) + off) =
+            *reinterpret_cast<const uint4*>(pool_row(a, layer, kv, src) + off);
+    } else if constexpr (MODE == kMoveExport) {
+      const int32_t src = a.src_rows[i];
+      const bool ok = src >= 0 && src < a.capacity_rows;
+      if (!ok && report) set_error(a.err, PD_DEVERR_TABLE_ROW);
+      if (lane_in)
+        *reinterpret_cast<uint4*>(a.dst_buf + buf_offset(a, i, layer, kv) + off) =
+            ok ? *reinterpret_cast<const uint4*>(pool_row(a, layer, kv, src) + off)
+               : make_uint4(0, 0, 0, 0);
+    } else {
+      const int32_t dst = a.dst_rows[i];
+      if (dst < 0 || dst >= a.capacity_rows) {
+        if (report) set_error(a.err, PD_DEVERR_WRITE_ROW);
+        continue;
+      }
+      if (lane_in)
+        *reinterpret_cast<uint4*>(pool_row(a, layer, kv, dst) + off) =
+            *reinterpret_cast<const uint4*>(a.src_buf + buf_offset(a, i, layer, kv) + off);
+    }
   }
 }
 
@@ -225,13 +257,18 @@ hipError_t launch_zero_fill(void* p, size_t bytes, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_copy_block(const CopyArgs& a, hipStream_t s) {
+hipError_t launch_row_move(const RowMoveArgs& a, int mode, hipStream_t s) {
   const int64_t max_row = a.row_bytes[0] > a.row_bytes[1] ? a.row_bytes[0] : a.row_bytes[1];
   const long long units = static_cast<long long>(a.n) * a.n_layers * 2 *
-                          ((max_row + kCopyChunk - 1) / kCopyChunk);
+                          ((max_row + kMoveChunk - 1) / kMoveChunk);
   const int grid = static_cast<int>(units < 4096 ? units : 4096);
   if (grid == 0) return hipSuccess;
-  hipLaunchKernelGGL(copy_block_kernel, dim3(grid), dim3(kThreads), 0, s, a);
+  switch (mode) {
+    case kMoveCopy: hipLaunchKernelGGL(row_move_kernel<kMoveCopy>, dim3(grid), dim3(kThreads), 0, s, a); break;
+    case kMoveExport: hipLaunchKernelGGL(row_move_kernel<kMoveExport>, dim3(grid), dim3(kThreads), 0, s, a); break;
+    case kMoveImport: hipLaunchKernelGGL(row_move_kernel<kMoveImport>, dim3(grid), dim3(kThreads), 0, s, a); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

@@ -64,7 +64,8 @@ typedef enum pd_status {
   PD_ERR_CAPACITY = -3,     /* slab-pointer table full or workspace too small  */
   PD_ERR_UNSUPPORTED = -4,  /* shape or format without a kernel                */
   PD_ERR_HIP = -5,          /* a HIP runtime call failed                       */
-  PD_ERR_DEVICE = -6        /* a kernel reported a data-dependent error        */
+  PD_ERR_DEVICE = -6,       /* a kernel reported a data-dependent error        */
+  PD_ERR_IDENTITY = -7      /* block bytes of another storage identity         */
 } pd_status;
 
 typedef enum pd_format {
@@ -105,6 +106,32 @@ typedef struct pd_stats {
   int32_t k_record_bytes;         /* bytes of one K token-head record           */
   int32_t v_record_bytes;         /* bytes of one V token-head record           */
 } pd_stats;
+
+/*
+ * Storage identity: everything the bytes of a block depend on.  Blocks
+ * exported from one pool can be imported into another only when their
+ * identities are equal (mlx-swift-lm PR #142, section "Summary": resident
+ * reuse and complete checkpoints preserve packed bytes and reject
+ * incompatible storage identities before allocation; the "After" flowchart:
+ * exact packed checkpoint with format identity).  48 bytes, little endian,
+ * no padding; the slab geometry (slab_blocks, max_slabs) is not part of it:
+ * a block is a row, wherever its slab is.
+ */
+#define PD_IDENTITY_MAGIC 0x564B4450u /* bytes "PDKV" */
+#define PD_IDENTITY_LAYOUT 1u          /* record layout described at the top */
+typedef struct pd_storage_identity {
+  uint32_t magic;           /* PD_IDENTITY_MAGIC                                */
+  uint32_t layout;          /* PD_IDENTITY_LAYOUT                               */
+  int32_t format;           /* pd_format                                        */
+  int32_t n_layers;
+  int32_t block_size;
+  int32_t n_kv_heads;
+  int32_t head_dim;
+  int32_t k_record_bytes;
+  int32_t v_record_bytes;
+  int32_t group_size;       /* values per (scale, offset) pair: 32 packed, 0     */
+  uint64_t signs_hash;      /* packed: pd_signs_hash of the Hadamard signs; 0   */
+} pd_storage_identity;
 
 typedef struct pd_pool pd_pool;
 
@@ -278,6 +305,57 @@ pd_status pd_paged_decode_combine(pd_pool* pool, int32_t layer, int32_t B, int32
                                   const void* q, const int32_t* block_table, int32_t max_blocks,
                                   const int32_t* lens, int32_t max_len, float scale, void* out,
                                   void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Block serialisation (mlxcel #235, "Proposed solution", touch point 6: serde
+ * block-content extraction and the restore path read and write each block in
+ * the row's slab through the same row mapping).
+ *
+ * pd_signs_hash: FNV-1a, 64 bit (offset basis 0xcbf29ce484222325, prime
+ * 0x100000001b3) over the n sign bytes as stored (+1 -> 0x01, -1 -> 0xFF).
+ * Host only; needs no device.
+ */
+pd_status pd_signs_hash(const int8_t* signs, int32_t n, uint64_t* hash);
+
+/* The pool's storage identity (host output). */
+pd_status pd_storage_identity_of(const pd_pool* pool, pd_storage_identity* id);
+
+/*
+ * PD_OK when blocks of identity `id` (host) can be imported into `pool`;
+ * otherwise PD_ERR_IDENTITY, and pd_last_error() names the first field that
+ * differs.  Host only: call it before allocating anything for a restore.
+ */
+pd_status pd_identity_check(const pd_pool* pool, const pd_storage_identity* id);
+
+/* Bytes of one exported block: n_layers * block_size * n_kv_heads *
+ * (k_record_bytes + v_record_bytes) (host output). */
+pd_status pd_block_bytes(const pd_pool* pool, size_t* bytes);
+
+/*
+ * export_blocks: the bytes of block rows rows[0..n), every layer, into a
+ * contiguous buffer laid out [n][n_layers][K row, V row], where a K (V) row
+ * is the block's [block_size, n_kv_heads, record] bytes exactly as stored.
+ *   rows: device int32 [n]; dst: device, >= n * pd_block_bytes() bytes,
+ *   16-byte aligned.
+ * A row outside [0, capacity_rows) sets PD_DEVERR_TABLE_ROW and its slot of
+ * dst is zero-filled.  n == 0 is a no-op.
+ */
+pd_status pd_export_blocks(pd_pool* pool, int32_t n, const int32_t* rows, void* dst,
+                           size_t dst_bytes, hipStream_t stream);
+
+/*
+ * import_blocks: the restore path.  `id` (host) is the identity the bytes
+ * were exported under; it is checked first, and a mismatch returns
+ * PD_ERR_IDENTITY and enqueues nothing.  Then block i of src (layout as
+ * pd_export_blocks) is written into row rows[i] of every layer, K and V.
+ *   rows: device int32 [n], distinct; src: device, >= n * pd_block_bytes()
+ *   bytes, 16-byte aligned.
+ * A row outside [0, capacity_rows) sets PD_DEVERR_WRITE_ROW and that block is
+ * skipped.  n == 0 is a no-op (after the identity check).
+ */
+pd_status pd_import_blocks(pd_pool* pool, const pd_storage_identity* id, int32_t n,
+                           const int32_t* rows, const void* src, size_t src_bytes,
+                           hipStream_t stream);
 
 /* Pool counters (host output).  mlxcel #235: slab-append counter and
  * bytes_reserved summed over slabs. */

@@ -14,6 +14,9 @@ chunked slabs":
 * copy_on_write_block (touch point 2) copies a whole block row, every layer,
   K and V: the source bytes come from the source row's slab and land in the
   destination row's slab;
+* serde (touch point 6) extracts a block's bytes from the row's slab, every
+  layer, and the restore path writes them back into a row's slab; blocks are
+  laid out [n][n_layers][K row, V row];
 * gather_visible splits a sequence's block-table rows into maximal same-slab
   runs in logical order, takes each run from its slab, concatenates the runs
   and then reshapes, slices to the visible length and transposes.
@@ -120,6 +123,30 @@ class SlabPoolModel:
                 kd[r] = kb
                 vd[r] = vb
 
+    def export_blocks(self, rows: Sequence[int]) -> np.ndarray:
+        """uint8 [n, n_layers * (K row + V row)]: each block's rows, layer by
+        layer, K then V, exactly as stored."""
+        out = []
+        for row in rows:
+            parts = []
+            for layer in range(self.n_layers):
+                ks, vs, r = self.slab_for_row(layer, int(row))
+                parts += [ks[r].reshape(-1), vs[r].reshape(-1)]
+            out.append(np.concatenate(parts))
+        return np.stack(out) if out else np.zeros((0, 0), np.uint8)
+
+    def import_blocks(self, rows: Sequence[int], data: np.ndarray) -> None:
+        """Inverse of export_blocks: block i of data into row rows[i]."""
+        kb = self.block_size * self.n_kv_heads * self.k_rec
+        vb = self.block_size * self.n_kv_heads * self.v_rec
+        for i, row in enumerate(rows):
+            at = 0
+            for layer in range(self.n_layers):
+                ks, vs, r = self.slab_for_row(layer, int(row))
+                ks[r] = data[i, at:at + kb].reshape(ks[r].shape)
+                vs[r] = data[i, at + kb:at + kb + vb].reshape(vs[r].shape)
+                at += kb + vb
+
     # -- reads ------------------------------------------------------------
     def split_runs(self, rows: Sequence[int]) -> List[Tuple[int, int, int]]:
         """Maximal same-slab runs of a row list, in logical order.
@@ -178,3 +205,19 @@ def u16_from_records(rec: np.ndarray) -> np.ndarray:
     """Inverse of records_from_u16."""
     rec = np.ascontiguousarray(rec, dtype=np.uint8)
     return rec.view(np.uint16).reshape(rec.shape[:-1] + (rec.shape[-1] // 2,))
+
+
+def fnv1a64(data: bytes) -> int:
+    """FNV-1a, 64 bit: start from the offset basis 14695981039346656037; for
+    each byte, xor it in, then multiply by the prime 1099511628211 mod 2^64.
+    Serves as the storage identity's fingerprint of the Hadamard signs."""
+    h = 14695981039346656037
+    for byte in data:
+        h ^= byte
+        h = (h * 1099511628211) % (1 << 64)
+    return h
+
+
+def signs_fingerprint(signs) -> int:
+    """fnv1a64 of the sign vector as stored: +1 -> 0x01, -1 -> 0xFF."""
+    return fnv1a64(bytes((int(x) & 0xFF) for x in signs))

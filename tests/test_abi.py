@@ -64,3 +64,27 @@ def test_null_pool_is_an_argument_error():
     assert lib.pd_pool_destroy(None) == 0
     assert lib.pd_write_block(None, 0, 0, None, None, None, None, None) == -1
     assert b"NULL" in lib.pd_last_error()
+
+
+def test_signs_hash_is_fnv1a_of_the_sign_bytes():
+    """pd_signs_hash (host only) against the oracle's FNV-1a over the stored
+    sign bytes; a flipped sign changes it."""
+    from oracle.slab_pool import signs_fingerprint
+    from synth import hadamard_signs
+    for D in (64, 128, 256):
+        s = [int(x) for x in hadamard_signs(5, D)]
+        assert pd.signs_hash(s) == signs_fingerprint(s)
+        t = list(s)
+        t[D // 2] = -t[D // 2]
+        assert pd.signs_hash(t) != pd.signs_hash(s)
+    assert pd.signs_hash([]) == 0xCBF29CE484222325
+
+
+def test_storage_identity_is_48_packed_bytes():
+    assert ctypes.sizeof(pd.StorageIdentity) == 48
+    ident = pd.StorageIdentity(magic=0x564B4450, layout=1, format=4, n_layers=2, block_size=32,
+                               n_kv_heads=8, head_dim=64, k_record_bytes=48, v_record_bytes=48,
+                               group_size=32, signs_hash=123)
+    b = ident.to_bytes()
+    assert b[:4] == b"PDKV" and len(b) == 48
+    assert pd.StorageIdentity.from_bytes(b).as_dict() == ident.as_dict()

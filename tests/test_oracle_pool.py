@@ -237,3 +237,45 @@ def test_copy_block_reads_every_source_before_writing():
     pool.copy_block([0, 3, 5], [4, 1, 2])
     got = [int(pool.slab_for_row(0, r)[0][pool.slab_for_row(0, r)[2]][0, 0, 0]) for r in range(6)]
     assert got == [1, 4, 6, 4, 1, 6]
+
+
+def test_fnv1a64_published_vectors():
+    """The storage identity fingerprints the Hadamard signs with FNV-1a 64;
+    its published test values pin the oracle's implementation."""
+    from oracle.slab_pool import fnv1a64
+    assert fnv1a64(b"") == 0xCBF29CE484222325
+    assert fnv1a64(b"a") == 0xAF63DC4C8601EC8C
+    assert fnv1a64(b"foobar") == 0x85944171F73967E8
+
+
+def test_block_export_is_the_dense_tokens_and_round_trips():
+    """Serde touch point of the chunked-slab proposal: a block's exported
+    bytes are its tokens' records (every layer, K then V), here checked
+    against the dense sequence itself; importing them into other rows of a
+    pool with another slab size gathers the same sequence byte for byte."""
+    bs, n_kv, D = 8, 2, 16
+    a = SlabPoolModel(2, bs, n_kv, 2 * D, 2 * D, 4)
+    a.reserve_rows(12)
+    rows_a = np.array([5, 0, 11], np.int32)
+    n = 20
+    dense = []
+    for layer in range(2):
+        k, v = kv_bits_for_sequence(17, layer, 0, n, n_kv, D, "bf16")
+        _fill(a, layer, rows_a, k, v)
+        dense.append((k, v))
+    blob = a.export_blocks(rows_a)
+    rec = 2 * D
+    assert blob.shape == (3, 2 * 2 * bs * n_kv * rec)
+    # block 1 (tokens 8..15), layer 1, V: the dense tokens' bytes in order
+    row_bytes = bs * n_kv * rec
+    at = (2 + 1) * row_bytes
+    expect = records_from_u16(dense[1][1][8:16]).reshape(-1)
+    assert np.array_equal(blob[1, at:at + row_bytes], expect)
+    b = SlabPoolModel(2, bs, n_kv, 2 * D, 2 * D, 3)
+    b.reserve_rows(9)
+    rows_b = np.array([8, 1, 4], np.int32)
+    b.import_blocks(rows_b, blob)
+    for layer in range(2):
+        for (ga, gb) in zip(a.gather(layer, rows_a, n), b.gather(layer, rows_b, n)):
+            assert np.array_equal(ga, gb)
+    assert np.array_equal(b.export_blocks(rows_b), blob)

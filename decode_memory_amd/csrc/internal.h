@@ -105,6 +105,10 @@ hipError_t launch_decode_combine(const DecodeArgs& a, bool bf16, int32_t head_di
 hipError_t launch_paged_decode_packed(const DecodeArgs& a, int32_t head_dim, int32_t group,
                                       hipStream_t s);
 bool packed_decode_supported(int32_t n_kv, int32_t head_dim, int32_t group, int32_t block_size);
+hipError_t launch_paged_decode_packed_mfma(const DecodeArgs& a, int32_t head_dim, int32_t group,
+                                           hipStream_t s);
+bool packed_mfma_supported(int32_t n_kv, int32_t head_dim, int32_t group, int32_t block_size);
+int packed_mfma_target_workgroups(int32_t head_dim);
 // Row kernel: head groups per workgroup (0 = shape not supported) and kv
 // heads per workgroup.
 int row_kernel_kpl(int32_t n_kv, int32_t head_dim, int32_t group, int32_t block_size);

@@ -1,0 +1,421 @@
+// paged_decode for packed pools (K8/V8, K8/V4, K4/V4) on the gfx950 matrix
+// cores.
+//
+// Operation (mlx-swift-lm PR #142, "Add packed paged KV formats with bounded
+// workspace admission", section "Summary" and the "After" flowchart): direct
+// attention over the packed pages.  Keys were rotated by a fixed signed
+// Hadamard basis before they were quantised, so the query gets the same
+// rotation (q'.k' = q.k); values are stored unrotated.  A token-head record is
+// its codes (8-bit bytes, or 4-bit nibbles with value 2i in the low nibble of
+// byte i) followed by one (fp32 scale, fp32 offset) per group of 32 values; a
+// value is code * scale + offset.  Per group g of a key,
+//   q'.k = scale_g * sum_{i in g} q'_i c_i + offset_g * sum_{i in g} q'_i,
+// and per group of a value
+//   sum_t p_t v_t = sum_t (p_t scale_t) c_t + sum_t p_t offset_t.
+// The code sums are matrix products with small integer operands, which the
+// MFMA units take exactly in f16; q' and p * scale go in as f16 and the
+// products accumulate in fp32.
+//
+// Decomposition.  A workgroup owns (sequence, split of the token axis) and
+// all 8 kv heads, one wave per kv head; split s takes logical blocks s, s +
+// n_split, ...  Whole token rows of a block (every head, K and V) are staged
+// in LDS with 16-byte coalesced loads, the next stage's loads in flight in
+// registers while the current one is computed.  A wave works through its
+// head's tokens 16 at a time:
+//   scores: one 16x16x32 product per group of 32 values, A = q' (query head
+//     j in row 4j, other rows zero), B = the 16 tokens' codes of the group;
+//     the score of (query head j, token n) lands in lane n + 16 j, so the
+//     online softmax runs on every lane and its reductions over tokens are
+//     16-lane DPP row operations;
+//   values: p * scale * 1024 goes through a small per-wave LDS area into the
+//     A operand of 4x4x4 products (16 independent blocks per instruction:
+//     4 query heads x 4 tokens times 4 tokens x 4 dimensions), so lane l
+//     accumulates value dimension 64 i + l of every query head in its four
+//     registers; the B operand is that dimension of 4 tokens, read byte by
+//     byte from the staged rows; the offsets add sum_t p_t offset_t per group.
+// Codes become f16 exactly: a byte placed under the exponent bits 0x64 is
+// 1024 + code, and one packed f16 add of -1024 leaves the code.
+// Partials go to the same workspace layout as the 16-bit kernels and the same
+// combine kernel merges them.
+#include "device_common.h"
+#include "internal.h"
+
+namespace pagedkv {
+
+namespace {
+
+constexpr int kPWaves = 8;  // one wave per kv head; packed pools have 8
+constexpr int kPThreads = kPWaves * kWave;
+constexpr int kPBS = 32;    // tokens per block
+constexpr int kSub = 16;    // tokens per MFMA sub-tile
+constexpr float kPScale = 1024.f;  // p * scale travels as (p * scale * 1024) in f16
+
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+typedef float f4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(1))) u32x4 gu32x4;
+
+template <int D, int KB, int VB>
+struct PShape {
+  static constexpr int NG = D / 32;                    // groups of 32 values
+  static constexpr int KCODE = D * KB / 8, VCODE = D * VB / 8;
+  static constexpr int KREC = KCODE + NG * 8, VREC = VCODE + NG * 8;
+  static constexpr int KROW = 8 * KREC, VROW = 8 * VREC;  // one token, every head
+  // LDS pitch of a staged token row: 16 bytes of padding spread the rows of
+  // consecutive tokens over the banks
+  static constexpr int PK = KROW + 16, PV = VROW + 16;
+  // tokens per stage (inside one block): 32 while a stage is at most 48 KiB
+  static constexpr int T = (KROW + VROW) * kPBS <= 48 * 1024 ? 32 : 16;
+  static constexpr int KU = T * KROW / 16, VU = T * VROW / 16;  // 16-byte units
+  static constexpr int UPT = (KU + VU + kPThreads - 1) / kPThreads;
+  static constexpr int STAGE = T * (PK + PV);
+  static_assert(KREC % 16 == 0 && VREC % 16 == 0, "records are whole 16-byte units");
+};
+
+// Waves per SIMD the launch asks for: two workgroups per CU where the
+// registers allow it.
+template <int D>
+constexpr int kPMinWaves = D <= 64 ? 4 : 2;
+
+__device__ __forceinline__ const char* lane_ptr(uint64_t v, int j) {
+  const uint32_t lo = __builtin_amdgcn_readlane(static_cast<uint32_t>(v), j);
+  const uint32_t hi = __builtin_amdgcn_readlane(static_cast<uint32_t>(v >> 32), j);
+  return reinterpret_cast<const char*>((static_cast<uint64_t>(hi) << 32) | lo);
+}
+
+// Two bytes of w (selected by SEL) as an f16 pair holding the byte values:
+// each byte is placed under the exponent bits 0x64 (the f16 1024 + byte) and
+// 1024 is subtracted, exactly.
+__device__ __forceinline__ uint32_t bytes_to_f16x2(uint32_t w, uint32_t sel) {
+  const uint32_t biased = __builtin_amdgcn_perm(0x64646464u, w, sel);
+  const h2 x = __builtin_bit_cast(h2, biased) - h2{static_cast<_Float16>(1024.f), static_cast<_Float16>(1024.f)};
+  return __builtin_bit_cast(uint32_t, x);
+}
+constexpr uint32_t kSelB01 = 0x04010400u;  // bytes 0, 1 -> (lo, hi) halves
+constexpr uint32_t kSelB23 = 0x04030402u;  // bytes 2, 3
+
+// B operand of a score product: 8 codes of one token and group as f16, in
+// the element order the A operand (q') uses.  8-bit codes: values 0..7 of
+// the k-block in order; 4-bit codes: values 0, 2, 4, 6, 1, 3, 5, 7.
+template <int KB>
+__device__ __forceinline__ h8 key_codes(const unsigned char* p) {
+  uint32_t r[4];
+  if constexpr (KB == 8) {
+    const uint2 w = *reinterpret_cast<const uint2*>(p);
+    r[0] = bytes_to_f16x2(w.x, kSelB01);
+    r[1] = bytes_to_f16x2(w.x, kSelB23);
+    r[2] = bytes_to_f16x2(w.y, kSelB01);
+    r[3] = bytes_to_f16x2(w.y, kSelB23);
+  } else {
+    const uint32_t w = *reinterpret_cast<const uint32_t*>(p);
+    const uint32_t lo = w & 0x0f0f0f0fu, hi = (w >> 4) & 0x0f0f0f0fu;
+    r[0] = bytes_to_f16x2(lo, kSelB01);
+    r[1] = bytes_to_f16x2(lo, kSelB23);
+    r[2] = bytes_to_f16x2(hi, kSelB01);
+    r[3] = bytes_to_f16x2(hi, kSelB23);
+  }
+  return __builtin_bit_cast(h8, r);
+}
+
+template <int KB>
+__device__ __forceinline__ int key_value_index(int e) {  // value of element e in its k-block
+  if constexpr (KB == 8) return e;
+  else return e < 4 ? 2 * e : 2 * (e - 4) + 1;
+}
+
+// Code of value dimension d of one staged V record.
+template <int VB>
+__device__ __forceinline__ uint32_t value_code(const unsigned char* rec, int d) {
+  if constexpr (VB == 8) return rec[d];
+  else return (rec[d >> 1] >> ((d & 1) * 4)) & 0xfu;
+}
+
+__device__ __forceinline__ float row_max16(float v) {
+  v = fmaxf(v, dpp<kDppXor1>(v));
+  v = fmaxf(v, dpp<kDppXor2>(v));
+  v = fmaxf(v, dpp<kDppHalfMirror>(v));
+  v = fmaxf(v, dpp<kDppMirror>(v));
+  return v;
+}
+
+template <int D, int KB, int VB, int G>
+__global__ __launch_bounds__(kPThreads, kPMinWaves<D>) void paged_decode_packed_mfma_kernel(DecodeArgs a) {
+  using S = PShape<D, KB, VB>;
+  constexpr int NG = S::NG, T = S::T, PK = S::PK, PV = S::PV;
+  constexpr int KREC = S::KREC, VREC = S::VREC, KROW = S::KROW, VROW = S::VROW;
+  constexpr int NV = D / 64;  // value chunks of 64 dimensions (one per lane)
+  constexpr int AUX = (G * D > NG * 4 * kSub) ? G * D : NG * 4 * kSub;  // floats per wave
+  static_assert(G <= 4, "query heads of a kv head take rows 0, 4, 8, 12");
+
+  __shared__ __attribute__((aligned(16))) unsigned char s_stage[S::STAGE];
+  __shared__ __attribute__((aligned(16))) float s_aux[kPWaves][AUX];  // q' transform, then p^T
+  __shared__ float s_qs[kPWaves][G * NG];  // sum of q' per (query head, group)
+
+  const int lane = threadIdx.x % kWave;
+  const int h = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // kv head of this wave
+  const int n = lane % kSub;   // token (scores), dimension (values), row (A operands)
+  const int J = lane / kSub;   // query head of the score layout; k-block of the operands
+
+  const LayerView& lv = a.lv;
+  const int n_split = a.n_split;
+  const int w = xcd_work_id(blockIdx.x, gridDim.x);
+  if (w >= a.B * n_split) return;
+  const int s = w % n_split;
+  const int b = w / n_split;
+  const int32_t* trow = a.table + static_cast<size_t>(b) * a.max_blocks;
+
+  int len = a.lens[b];
+  int row = -1;
+  {
+    const int blk = s + lane * n_split;
+    if (lane < a.blocks_per_split && blk < a.max_blocks) row = trow[blk];
+  }
+  const int cap_len = min(a.max_blocks, n_split * a.blocks_per_split) * kPBS;
+  if (len < 0 || len > cap_len) {
+    if (threadIdx.x == 0 && s == 0) set_error(lv.err, PD_DEVERR_LENGTH);
+    len = len < 0 ? 0 : cap_len;
+  }
+  const int nb = (len + kPBS - 1) / kPBS;
+  if (s >= nb) return;  // inactive split (uniform over the workgroup)
+  const int nblk = (nb - s + n_split - 1) / n_split;
+  const bool row_ok = row >= 0 && row < lv.capacity_rows;
+  const uint64_t ok_mask = __ballot(row_ok);
+  if (h == 0 && lane < nblk && !row_ok) set_error(lv.err, PD_DEVERR_TABLE_ROW);
+  uint64_t kaddr = 0, vaddr = 0;
+  if (lv.capacity_rows > 0) {
+    const int r = row_ok ? row : 0;  // rows outside the pool read row 0 and are masked
+    const int slab = r / lv.slab_blocks;
+    const size_t in_slab = static_cast<size_t>(r - slab * lv.slab_blocks);
+    kaddr = reinterpret_cast<uint64_t>(lv.k_tab[slab]) + in_slab * kPBS * KROW;
+    vaddr = reinterpret_cast<uint64_t>(lv.v_tab[slab]) + in_slab * kPBS * VROW;
+  }
+  constexpr int SPB = kPBS / T;  // stages per block
+  const int n_stages = lv.capacity_rows > 0 ? nblk * SPB : 0;
+
+  // Stage loads: unit u < KU is 16 bytes of the K rows, the rest of the V rows.
+  u32x4 rg[S::UPT];
+  auto fetch = [&](int i) {
+    const int jb = i / SPB, t0 = (i % SPB) * T;
+    const char* kb = lane_ptr(kaddr, jb) + static_cast<size_t>(t0) * KROW;
+    const char* vb = lane_ptr(vaddr, jb) + static_cast<size_t>(t0) * VROW;
+#pragma unroll
+    for (int r = 0; r < S::UPT; ++r) {
+      const int u = threadIdx.x + r * kPThreads;
+      if (u < S::KU) rg[r] = __builtin_nontemporal_load((const gu32x4*)(kb + static_cast<size_t>(u) * 16));
+      else if (u < S::KU + S::VU)
+        rg[r] = __builtin_nontemporal_load((const gu32x4*)(vb + static_cast<size_t>(u - S::KU) * 16));
+    }
+  };
+  if (n_stages > 0) fetch(0);
+
+  // ---- query: widen, signs, fp32 Walsh-Hadamard transform (per wave, LDS) --
+  float* sq = s_aux[h];
+  {
+    const uint16_t* q = static_cast<const uint16_t*>(a.q) + (static_cast<size_t>(b) * a.n_q + h * G) * D;
+    for (int i = lane; i < G * D; i += kWave)
+      sq[i] = __uint_as_float(static_cast<uint32_t>(q[i]) << 16) * a.signs[i % D];
+  }
+  __syncthreads();
+  for (int hh = 1; hh < D; hh <<= 1) {
+    for (int i = lane; i < G * D / 2; i += kWave) {
+      const int j = i / (D / 2), p = i % (D / 2);
+      const int i0 = j * D + (p / hh) * 2 * hh + (p % hh);
+      const float x = sq[i0], y = sq[i0 + hh];
+      sq[i0] = x + y;
+      sq[i0 + hh] = x - y;
+    }
+    __syncthreads();
+  }
+  const float qs = a.inv_sqrt_d * a.scale_log2;  // scores live in the exp2 domain
+  // A operands of the score products: row m = n holds query head m / 4 when
+  // m % 4 == 0 (rows of absent query heads and the rest are zero), k-block J
+  h8 aq[NG];
+  {
+    const bool live = (n % 4) == 0 && n / 4 < G;
+    const int jq = live ? n / 4 : 0;
+#pragma unroll
+    for (int g = 0; g < NG; ++g)
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        aq[g][e] = static_cast<_Float16>(live ? sq[jq * D + g * 32 + J * 8 + key_value_index<KB>(e)] * qs : 0.f);
+  }
+  // sum of q' over each group: one lane per (query head, group) into LDS,
+  // then each lane takes those of query head J of the score layout
+  for (int i = lane; i < G * NG; i += kWave) {
+    const float* src = sq + (i / NG) * D + (i % NG) * 32;
+    float acc = 0.f;
+#pragma unroll 8
+    for (int k = 0; k < 32; ++k) acc += src[k];
+    s_qs[h][i] = acc * qs;
+  }
+  __syncthreads();  // the per-wave area is reused for p^T below
+  float qsum[NG];
+#pragma unroll
+  for (int g = 0; g < NG; ++g) qsum[g] = J < G ? s_qs[h][J * NG + g] : 0.f;
+
+  float m_run = -INFINITY, l_run = 0.f, bias[NG];
+  f4 acc[NV];  // lane l: dimension 64 i + l, register r: query head r
+#pragma unroll
+  for (int g = 0; g < NG; ++g) bias[g] = 0.f;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) acc[i] = f4{0.f, 0.f, 0.f, 0.f};
+  float* sp = s_aux[h];  // p * scale * 1024: [group][query head][token of the sub-tile]
+
+  for (int i = 0; i < n_stages; ++i) {
+    __syncthreads();  // every wave is done with the previous stage
+#pragma unroll
+    for (int r = 0; r < S::UPT; ++r) {
+      const int u = threadIdx.x + r * kPThreads;
+      if (u < S::KU) {
+        const int t = u / (KROW / 16), c = u % (KROW / 16);
+        *reinterpret_cast<u32x4*>(s_stage + t * PK + c * 16) = rg[r];
+      } else if (u < S::KU + S::VU) {
+        const int v = u - S::KU;
+        const int t = v / (VROW / 16), c = v % (VROW / 16);
+        *reinterpret_cast<u32x4*>(s_stage + T * PK + t * PV + c * 16) = rg[r];
+      }
+    }
+    if (i + 1 < n_stages) fetch(i + 1);
+    __syncthreads();  // stage i is in LDS
+
+    const int jb = i / SPB, t0 = (i % SPB) * T;
+    const int nt = ((ok_mask >> jb) & 1) ? min(kPBS, len - (s + jb * n_split) * kPBS) : 0;
+#pragma unroll
+    for (int sub = 0; sub < T / kSub; ++sub) {
+      const int lt0 = sub * kSub;  // first token of the sub-tile in the stage
+      if (t0 + lt0 >= nt) break;   // uniform: the rest of the stage is past the length
+
+      // scores: lane (n, J) = (token n, query head J)
+      const unsigned char* krow = s_stage + (lt0 + n) * PK + h * KREC;
+      float sv = 0.f;
+#pragma unroll
+      for (int g = 0; g < NG; ++g) {
+        const h8 bk = key_codes<KB>(krow + g * (32 * KB / 8) + J * KB);
+        const f4 c = __builtin_amdgcn_mfma_f32_16x16x32_f16(aq[g], bk, f4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+        const float2 km = *reinterpret_cast<const float2*>(krow + S::KCODE + 8 * g);
+        sv = fmaf(c[0], km.x, fmaf(km.y, qsum[g], sv));
+      }
+      const bool tv = J < G && t0 + lt0 + n < nt;
+      const float sc = tv ? sv : -INFINITY;
+      const float m_new = fmaxf(m_run, row_max16(sc));  // -inf while nothing is visible
+      const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+      const float p = (sc == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(sc - m_new);
+      m_run = m_new;
+      l_run = fmaf(l_run, alpha, p);
+      // value metadata of token n; invisible tokens add nothing even if it is garbage
+      const unsigned char* vrow = s_stage + T * PK + (lt0 + n) * PV + h * VREC;
+#pragma unroll
+      for (int g = 0; g < NG; ++g) {
+        const float2 vm = *reinterpret_cast<const float2*>(vrow + S::VCODE + 8 * g);
+        bias[g] = fmaf(bias[g], alpha, tv ? p * vm.y : 0.f);
+        sp[(g * 4 + J) * kSub + n] = tv ? p * vm.x * kPScale : 0.f;
+      }
+      if (__ballot(alpha != 1.f)) {
+        // alpha of query head r is uniform over score row r
+#pragma unroll
+        for (int r = 0; r < G; ++r) {
+          const float ar = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, alpha), kSub * r));
+#pragma unroll
+          for (int i = 0; i < NV; ++i) acc[i][r] *= ar;
+        }
+      }
+      __builtin_amdgcn_wave_barrier();
+      // values: block lane / 4 of a 4x4x4 product; A row lane % 4 is query
+      // head lane % 4, B/C column is dimension 64 i + lane
+      const int qa = lane % 4;
+#pragma unroll
+      for (int tq = 0; tq < kSub / 4; ++tq) {
+        const unsigned char* vtok = s_stage + T * PK + (lt0 + 4 * tq) * PV + h * VREC;
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+          const int d = 64 * i + lane;
+          const int g = d / 32;
+          float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
+          if (qa < G) x = *reinterpret_cast<const float4*>(sp + (g * 4 + qa) * kSub + 4 * tq);
+          const h4 ap = {static_cast<_Float16>(x.x), static_cast<_Float16>(x.y), static_cast<_Float16>(x.z),
+                         static_cast<_Float16>(x.w)};
+          const uint32_t c0 = value_code<VB>(vtok, d), c1 = value_code<VB>(vtok + PV, d);
+          const uint32_t c2 = value_code<VB>(vtok + 2 * PV, d), c3 = value_code<VB>(vtok + 3 * PV, d);
+          const uint32_t u2[2] = {bytes_to_f16x2(c0 | (c1 << 8), kSelB01), bytes_to_f16x2(c2 | (c3 << 8), kSelB01)};
+          acc[i] = __builtin_amdgcn_mfma_f32_4x4x4f16(ap, __builtin_bit_cast(h4, u2), acc[i], 0, 0, 0);
+        }
+        // keep each token quad's loads next to their products (bounds the
+        // registers the scheduler would otherwise spend hoisting them)
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      __builtin_amdgcn_wave_barrier();
+    }
+  }
+
+  // partials: (max, sum) and the group offsets' sums are uniform over score
+  // row r; lane l holds dimension 64 i + l of query head r in register r
+  const float l_tot = group_sum<kSub>(l_run);
+  float btot[NG];
+#pragma unroll
+  for (int g = 0; g < NG; ++g) btot[g] = group_sum<kSub>(bias[g]);
+#pragma unroll
+  for (int r = 0; r < G; ++r) {
+    const size_t hs = (static_cast<size_t>(b) * a.n_q + h * G + r) * n_split + s;
+    float* part_acc = a.partials + hs * D;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int d = 64 * i + lane;
+      const float b_lo = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, btot[2 * i]), kSub * r));
+      const float b_hi = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, btot[2 * i + 1]), kSub * r));
+      part_acc[d] = fmaf(acc[i][r], 1.f / kPScale, lane < 32 ? b_lo : b_hi);
+    }
+    if (lane == kSub * r) {
+      a.partials[a.ml_offset + hs * 2] = m_run;
+      a.partials[a.ml_offset + hs * 2 + 1] = l_tot;
+    }
+  }
+}
+
+template <int D, int KB, int VB, int G>
+hipError_t launch_mfma(const DecodeArgs& a, hipStream_t s) {
+  const int grid = round_up(a.B * a.n_split, kXcds);
+  hipLaunchKernelGGL((paged_decode_packed_mfma_kernel<D, KB, VB, G>), dim3(grid), dim3(kPThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+template <int D, int KB, int VB>
+hipError_t mfma_by_group(const DecodeArgs& a, int group, hipStream_t s) {
+  switch (group) {
+    case 1: return launch_mfma<D, KB, VB, 1>(a, s);
+    case 2: return launch_mfma<D, KB, VB, 2>(a, s);
+    case 4: return launch_mfma<D, KB, VB, 4>(a, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <int KB, int VB>
+hipError_t mfma_by_dim(const DecodeArgs& a, int head_dim, int group, hipStream_t s) {
+  switch (head_dim) {
+    case 64: return mfma_by_group<64, KB, VB>(a, group, s);
+    case 128: return mfma_by_group<128, KB, VB>(a, group, s);
+    case 256: return mfma_by_group<256, KB, VB>(a, group, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+bool packed_mfma_supported(int32_t n_kv, int32_t head_dim, int32_t group, int32_t block_size) {
+  return n_kv == kPWaves && block_size == kPBS && (head_dim == 64 || head_dim == 128 || head_dim == 256) &&
+         (group == 1 || group == 2 || group == 4);
+}
+
+// Workgroups a launch aims for: two per CU where a workgroup's registers allow it.
+int packed_mfma_target_workgroups(int32_t head_dim) { return head_dim <= 64 ? 512 : 256; }
+
+hipError_t launch_paged_decode_packed_mfma(const DecodeArgs& a, int32_t head_dim, int32_t group,
+                                           hipStream_t s) {
+  if (a.k_bits == 8 && a.v_bits == 8) return mfma_by_dim<8, 8>(a, head_dim, group, s);
+  if (a.k_bits == 8 && a.v_bits == 4) return mfma_by_dim<8, 4>(a, head_dim, group, s);
+  if (a.k_bits == 4 && a.v_bits == 4) return mfma_by_dim<4, 4>(a, head_dim, group, s);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace pagedkv

@@ -28,6 +28,10 @@ using namespace pagedkv;
 #ifndef PAGEDKV_PACKED_TARGET_WG
 #define PAGEDKV_PACKED_TARGET_WG 768
 #endif
+// Packed pools decode on the matrix cores (0: the VALU kernel).
+#ifndef PAGEDKV_PACKED_MFMA
+#define PAGEDKV_PACKED_MFMA 1
+#endif
 #ifndef PAGEDKV_ROW_TARGET_WG
 #define PAGEDKV_ROW_TARGET_WG 256
 #endif
@@ -210,7 +214,7 @@ namespace {
 
 // Which decode kernel runs for a call, and how the token axis is split.
 struct DecodePlan {
-  int kind = 0;  // 0: column kernel, 1: row kernel, 2: packed kernel
+  int kind = 0;  // 0: column kernel, 1: row kernel, 2: packed kernel, 3: packed MFMA kernel
   int kpl = 0;   // row kernel: kv heads per lane group
   SplitPlan split{1, 1};
 };
@@ -232,10 +236,14 @@ bool make_decode_plan(const pd_pool* p, int32_t B, int32_t group, int32_t max_le
       target = PAGEDKV_ROW_TARGET_WG;
       max_bps = PAGEDKV_ROW_MAX_BLOCKS_PER_SPLIT;
     }
+  } else if (PAGEDKV_PACKED_MFMA && packed_mfma_supported(n_kv, D, group, bs)) {
+    plan.kind = 3;
+    units = B;  // a packed workgroup covers every kv head of its sequence
+    target = packed_mfma_target_workgroups(D);
   } else {
     if (!packed_decode_supported(n_kv, D, group, bs)) return false;
     plan.kind = 2;
-    units = B;  // a packed workgroup covers every kv head of its sequence
+    units = B;
     target = PAGEDKV_PACKED_TARGET_WG;
   }
   plan.split = plan_splits(units, max_len, bs, target, max_bps);
@@ -661,12 +669,13 @@ static pd_status decode_call(pd_pool* p, int32_t layer, int32_t B, int32_t n_q_h
     switch (plan.kind) {
       case 1: e = launch_paged_decode_row(a, bf16, D, group, plan.kpl, stream); break;
       case 2: e = launch_paged_decode_packed(a, D, group, stream); break;
+      case 3: e = launch_paged_decode_packed_mfma(a, D, group, stream); break;
       default: e = launch_paged_decode_column(a, bf16, D, group, stream); break;
     }
   }
   // packed pools produce bf16 outputs
   if (e == hipSuccess && (stages & kStageCombine))
-    e = launch_decode_combine(a, bf16 || plan.kind == 2, D, stream);
+    e = launch_decode_combine(a, bf16 || plan.kind >= 2, D, stream);
   if (e == hipErrorInvalidValue) return fail(PD_ERR_UNSUPPORTED, "no decode kernel for this shape");
   if (e != hipSuccess) return hip_fail(e, "paged_decode launch");
   return PD_OK;

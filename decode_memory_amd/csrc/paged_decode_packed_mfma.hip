@@ -30,9 +30,11 @@
 //   values: p * scale * 1024 goes through a small per-wave LDS area into the
 //     A operand of 4x4x4 products (16 independent blocks per instruction:
 //     4 query heads x 4 tokens times 4 tokens x 4 dimensions), so lane l
-//     accumulates value dimension 64 i + l of every query head in its four
-//     registers; the B operand is that dimension of 4 tokens, read byte by
-//     byte from the staged rows; the offsets add sum_t p_t offset_t per group.
+//     accumulates one value dimension of every query head in its four
+//     registers per 64 dimensions; the B operand is that dimension of 4
+//     tokens, read byte by byte from the staged rows (4-bit codes: one byte
+//     feeds the two dimensions of its nibbles); the offsets add
+//     sum_t p_t offset_t per group.
 // Codes become f16 exactly: a byte placed under the exponent bits 0x64 is
 // 1024 + code, and one packed f16 add of -1024 leaves the code.
 // Partials go to the same workspace layout as the 16-bit kernels and the same
@@ -125,11 +127,15 @@ __device__ __forceinline__ int key_value_index(int e) {  // value of element e i
   else return e < 4 ? 2 * e : 2 * (e - 4) + 1;
 }
 
-// Code of value dimension d of one staged V record.
-template <int VB>
-__device__ __forceinline__ uint32_t value_code(const unsigned char* rec, int d) {
-  if constexpr (VB == 8) return rec[d];
-  else return (rec[d >> 1] >> ((d & 1) * 4)) & 0xfu;
+// Value dimension that accumulator i of lane l holds.  8-bit codes: 64 i +
+// l.  4-bit codes: lanes take code bytes, whose two nibbles are dimensions
+// 2 byte and 2 byte + 1 -- with 64 dimensions byte l % 32 and nibble l / 32,
+// otherwise byte l + 64 (i / 2) and nibble i % 2.
+template <int VB, int NV>
+__device__ __forceinline__ int vdim(int i, int lane) {
+  if constexpr (VB == 8) return 64 * i + lane;
+  else if constexpr (NV == 1) return 2 * (lane % 32) + lane / 32;
+  else return 2 * (lane + 64 * (i / 2)) + (i % 2);
 }
 
 __device__ __forceinline__ float row_max16(float v) {
@@ -145,7 +151,7 @@ __global__ __launch_bounds__(kPThreads, kPMinWaves<D>) void paged_decode_packed_
   using S = PShape<D, KB, VB>;
   constexpr int NG = S::NG, T = S::T, PK = S::PK, PV = S::PV;
   constexpr int KREC = S::KREC, VREC = S::VREC, KROW = S::KROW, VROW = S::VROW;
-  constexpr int NV = D / 64;  // value chunks of 64 dimensions (one per lane)
+  constexpr int NV = D / 64;  // value accumulators (64 dimensions each, one per lane)
   constexpr int AUX = (G * D > NG * 4 * kSub) ? G * D : NG * 4 * kSub;  // floats per wave
   static_assert(G <= 4, "query heads of a kv head take rows 0, 4, 8, 12");
 
@@ -261,7 +267,8 @@ __global__ __launch_bounds__(kPThreads, kPMinWaves<D>) void paged_decode_packed_
   for (int g = 0; g < NG; ++g) bias[g] = 0.f;
 #pragma unroll
   for (int i = 0; i < NV; ++i) acc[i] = f4{0.f, 0.f, 0.f, 0.f};
-  float* sp = s_aux[h];  // p * scale * 1024: [group][query head][token of the sub-tile]
+  // p * scale * 1024 as f16: [group][query head][token of the sub-tile]
+  _Float16* sp = reinterpret_cast<_Float16*>(s_aux[h]);
 
   for (int i = 0; i < n_stages; ++i) {
     __syncthreads();  // every wave is done with the previous stage
@@ -310,7 +317,7 @@ __global__ __launch_bounds__(kPThreads, kPMinWaves<D>) void paged_decode_packed_
       for (int g = 0; g < NG; ++g) {
         const float2 vm = *reinterpret_cast<const float2*>(vrow + S::VCODE + 8 * g);
         bias[g] = fmaf(bias[g], alpha, tv ? p * vm.y : 0.f);
-        sp[(g * 4 + J) * kSub + n] = tv ? p * vm.x * kPScale : 0.f;
+        sp[(g * 4 + J) * kSub + n] = static_cast<_Float16>(tv ? p * vm.x * kPScale : 0.f);
       }
       if (__ballot(alpha != 1.f)) {
         // alpha of query head r is uniform over score row r
@@ -323,23 +330,48 @@ __global__ __launch_bounds__(kPThreads, kPMinWaves<D>) void paged_decode_packed_
       }
       __builtin_amdgcn_wave_barrier();
       // values: block lane / 4 of a 4x4x4 product; A row lane % 4 is query
-      // head lane % 4, B/C column is dimension 64 i + lane
+      // head lane % 4; the B/C column of lane l is dimension vdim(i, l)
       const int qa = lane % 4;
 #pragma unroll
       for (int tq = 0; tq < kSub / 4; ++tq) {
         const unsigned char* vtok = s_stage + T * PK + (lt0 + 4 * tq) * PV + h * VREC;
+        if constexpr (VB == 8) {
 #pragma unroll
-        for (int i = 0; i < NV; ++i) {
-          const int d = 64 * i + lane;
-          const int g = d / 32;
-          float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
-          if (qa < G) x = *reinterpret_cast<const float4*>(sp + (g * 4 + qa) * kSub + 4 * tq);
-          const h4 ap = {static_cast<_Float16>(x.x), static_cast<_Float16>(x.y), static_cast<_Float16>(x.z),
-                         static_cast<_Float16>(x.w)};
-          const uint32_t c0 = value_code<VB>(vtok, d), c1 = value_code<VB>(vtok + PV, d);
-          const uint32_t c2 = value_code<VB>(vtok + 2 * PV, d), c3 = value_code<VB>(vtok + 3 * PV, d);
-          const uint32_t u2[2] = {bytes_to_f16x2(c0 | (c1 << 8), kSelB01), bytes_to_f16x2(c2 | (c3 << 8), kSelB01)};
-          acc[i] = __builtin_amdgcn_mfma_f32_4x4x4f16(ap, __builtin_bit_cast(h4, u2), acc[i], 0, 0, 0);
+          for (int i = 0; i < NV; ++i) {
+            const int d = 64 * i + lane;
+            const h4 ap = qa < G ? *reinterpret_cast<const h4*>(sp + (d / 32 * 4 + qa) * kSub + 4 * tq) : h4{};
+            const uint32_t c0 = vtok[d], c1 = vtok[PV + d], c2 = vtok[2 * PV + d], c3 = vtok[3 * PV + d];
+            const uint32_t u2[2] = {bytes_to_f16x2(c0 | (c1 << 8), kSelB01), bytes_to_f16x2(c2 | (c3 << 8), kSelB01)};
+            acc[i] = __builtin_amdgcn_mfma_f32_4x4x4f16(ap, __builtin_bit_cast(h4, u2), acc[i], 0, 0, 0);
+          }
+        } else if constexpr (NV == 1) {
+          // 4-bit codes, 64 dimensions: lane l takes code byte l % 32 of the 4
+          // tokens and its low (l < 32) or high nibble: dimension vdim(0, l)
+          const int bi = lane % 32;
+          const h4 ap = qa < G ? *reinterpret_cast<const h4*>(sp + (bi / 16 * 4 + qa) * kSub + 4 * tq) : h4{};
+          const uint32_t w = vtok[bi] | (static_cast<uint32_t>(vtok[PV + bi]) << 8) |
+                             (static_cast<uint32_t>(vtok[2 * PV + bi]) << 16) |
+                             (static_cast<uint32_t>(vtok[3 * PV + bi]) << 24);
+          const uint32_t v = (w >> (4 * (lane / 32))) & 0x0f0f0f0fu;
+          const uint32_t u2[2] = {bytes_to_f16x2(v, kSelB01), bytes_to_f16x2(v, kSelB23)};
+          acc[0] = __builtin_amdgcn_mfma_f32_4x4x4f16(ap, __builtin_bit_cast(h4, u2), acc[0], 0, 0, 0);
+        } else {
+          // 4-bit codes: lane l takes code byte l + 64 k of the 4 tokens, whose
+          // low nibbles are dimension 2 (l + 64 k) and high nibbles the next
+          // one -- two products (accumulators 2k, 2k + 1), one A operand
+#pragma unroll
+          for (int k = 0; k < NV / 2; ++k) {
+            const int bi = lane + 64 * k;
+            const h4 ap = qa < G ? *reinterpret_cast<const h4*>(sp + (bi / 16 * 4 + qa) * kSub + 4 * tq) : h4{};
+            const uint32_t w = vtok[bi] | (static_cast<uint32_t>(vtok[PV + bi]) << 8) |
+                               (static_cast<uint32_t>(vtok[2 * PV + bi]) << 16) |
+                               (static_cast<uint32_t>(vtok[3 * PV + bi]) << 24);
+            const uint32_t lo = w & 0x0f0f0f0fu, hi = (w >> 4) & 0x0f0f0f0fu;
+            const uint32_t ul[2] = {bytes_to_f16x2(lo, kSelB01), bytes_to_f16x2(lo, kSelB23)};
+            const uint32_t uh[2] = {bytes_to_f16x2(hi, kSelB01), bytes_to_f16x2(hi, kSelB23)};
+            acc[2 * k] = __builtin_amdgcn_mfma_f32_4x4x4f16(ap, __builtin_bit_cast(h4, ul), acc[2 * k], 0, 0, 0);
+            acc[2 * k + 1] = __builtin_amdgcn_mfma_f32_4x4x4f16(ap, __builtin_bit_cast(h4, uh), acc[2 * k + 1], 0, 0, 0);
+          }
         }
         // keep each token quad's loads next to their products (bounds the
         // registers the scheduler would otherwise spend hoisting them)
@@ -359,12 +391,17 @@ __global__ __launch_bounds__(kPThreads, kPMinWaves<D>) void paged_decode_packed_
   for (int r = 0; r < G; ++r) {
     const size_t hs = (static_cast<size_t>(b) * a.n_q + h * G + r) * n_split + s;
     float* part_acc = a.partials + hs * D;
+    float bq[NG];  // the group offsets' sums of query head r
+#pragma unroll
+    for (int g = 0; g < NG; ++g)
+      bq[g] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, btot[g]), kSub * r));
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
-      const int d = 64 * i + lane;
-      const float b_lo = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, btot[2 * i]), kSub * r));
-      const float b_hi = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, btot[2 * i + 1]), kSub * r));
-      part_acc[d] = fmaf(acc[i][r], 1.f / kPScale, lane < 32 ? b_lo : b_hi);
+      const int d = vdim<VB, NV>(i, lane);
+      float bsel = 0.f;
+#pragma unroll
+      for (int g = 0; g < NG; ++g) bsel = d / 32 == g ? bq[g] : bsel;
+      part_acc[d] = fmaf(acc[i][r], 1.f / kPScale, bsel);
     }
     if (lane == kSub * r) {
       a.partials[a.ml_offset + hs * 2] = m_run;

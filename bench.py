@@ -230,11 +230,10 @@ def check_graph_replays(torch, step, graph, outs, rounds=2):
 def stage_times(timer, decode_call, layers, reps, torch=None):
     """Per-launch durations of the split and combine stages: each stage of
     every listed layer back to back (the list repeated to at least 16
-    launches), between two events on the launch stream.  The split stage is
-    launched eagerly (it runs far longer than the host takes to issue it).
-    With torch given, the combine run is captured into a HIP graph and
-    replayed, so that host launch overhead does not count: issued from
-    Python, the short combine would be timed at the rate Python can issue it."""
+    launches), between two events on the launch stream.  With torch given,
+    the combine run is captured into a HIP graph and replayed, so that host
+    launch overhead does not count: issued from Python, the short combine
+    would be timed at the rate the host can issue it."""
     layers = list(layers)
     layers = layers * max(1, -(-16 // len(layers)))
 
@@ -244,13 +243,17 @@ def stage_times(timer, decode_call, layers, reps, torch=None):
     for _ in range(2):
         run("split")
         run("combine")
-    # the split stage is timed before any graph is captured: the launches
-    # right after a capture run slower for a while
+    # The split stage is launched eagerly, as a serving loop issues it: it
+    # runs far longer than the host takes to issue it (except under a
+    # profiler's per-dispatch overhead), and graph replays add gaps of their
+    # own between kernels.  It is timed before any graph is captured: the
+    # launches right after a capture run slower for a while.
     split_us = timer(lambda: run("split"), reps) / len(layers)
     combine_fn = lambda: run("combine")  # noqa: E731
     if torch is not None:
         combine_fn = Graph(torch, combine_fn)
-        combine_fn()
+        for _ in range(4):
+            combine_fn()
     combine_us = timer(combine_fn, reps) / len(layers)
     run("split")
     run("combine")
@@ -682,7 +685,7 @@ def run_packed(args, torch, pd):
         "kv_tokens_attended_per_s": round(len(per) * B * n / (tot_us * 1e-6), 1),
         "roofline": {"bound": "hbm", "achieved": p["split_gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(p["split_gbs"] / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel": f"paged_decode_packed_kernel ({worst}, split stage; the slowest packed case)",
+                     "kernel": f"paged_decode_packed_mfma_kernel ({worst}, split stage; the slowest packed case)",
                      "algorithmic_bytes_per_launch": p["algorithmic_bytes"],
                      "avg_launch_us": p["split_us"]},
         "formats": per,

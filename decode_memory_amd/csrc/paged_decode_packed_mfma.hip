@@ -46,6 +46,16 @@ namespace pagedkv {
 
 namespace {
 
+#ifndef PAGEDKV_PMFMA_STAGE_KIB
+#define PAGEDKV_PMFMA_STAGE_KIB 48
+#endif
+#ifndef PAGEDKV_PMFMA_TARGET_WG_SMALL
+#define PAGEDKV_PMFMA_TARGET_WG_SMALL 512
+#endif
+#ifndef PAGEDKV_PMFMA_TARGET_WG
+#define PAGEDKV_PMFMA_TARGET_WG 256
+#endif
+
 constexpr int kPWaves = 8;  // one wave per kv head; packed pools have 8
 constexpr int kPThreads = kPWaves * kWave;
 constexpr int kPBS = 32;    // tokens per block
@@ -68,8 +78,9 @@ struct PShape {
   // LDS pitch of a staged token row: 16 bytes of padding spread the rows of
   // consecutive tokens over the banks
   static constexpr int PK = KROW + 16, PV = VROW + 16;
-  // tokens per stage (inside one block): 32 while a stage is at most 48 KiB
-  static constexpr int T = (KROW + VROW) * kPBS <= 48 * 1024 ? 32 : 16;
+  // tokens per stage (inside one block): 32 while a stage is at most
+  // PAGEDKV_PMFMA_STAGE_KIB
+  static constexpr int T = (KROW + VROW) * kPBS <= PAGEDKV_PMFMA_STAGE_KIB * 1024 ? 32 : 16;
   static constexpr int KU = T * KROW / 16, VU = T * VROW / 16;  // 16-byte units
   static constexpr int UPT = (KU + VU + kPThreads - 1) / kPThreads;
   static constexpr int STAGE = T * (PK + PV);
@@ -445,7 +456,9 @@ bool packed_mfma_supported(int32_t n_kv, int32_t head_dim, int32_t group, int32_
 }
 
 // Workgroups a launch aims for: two per CU where a workgroup's registers allow it.
-int packed_mfma_target_workgroups(int32_t head_dim) { return head_dim <= 64 ? 512 : 256; }
+int packed_mfma_target_workgroups(int32_t head_dim) {
+  return head_dim <= 64 ? PAGEDKV_PMFMA_TARGET_WG_SMALL : PAGEDKV_PMFMA_TARGET_WG;
+}
 
 hipError_t launch_paged_decode_packed_mfma(const DecodeArgs& a, int32_t head_dim, int32_t group,
                                            hipStream_t s) {

@@ -31,6 +31,9 @@ own JSON line of the same form:
   qwen3_1p7b_32x16k  28 layers x 32 sequences x 16384 tokens (56 GiB of KV); the
                      same step as the default, plus gather_visible of a layer
                      to [32, 8, 16384, 128] per tensor.
+  footprint_8x4k     8 distinct ~4.2k-token prompts prefilled one after another
+                     (qwen3-0.6b KV shape): peak HBM of the slab pool over the
+                     dense backend's (its own metric; lower is better).
   packed_16x16k      16 sequences x 16384 tokens, 8 kv / 32 q heads, head_dim 64
                      and 256, bf16 and the packed formats K8V8, K8V4, K4V4;
                      decode calls rotate over enough pool layers that the
@@ -694,6 +697,102 @@ def run_packed(args, torch, pd):
     return result
 
 
+# ---------------------------------------------------------------------------
+# footprint: 8 sequential distinct ~4.2k-token prefills, slab pool vs dense
+# ---------------------------------------------------------------------------
+
+def run_footprint(args, torch, pd):
+    """Peak HBM of the KV cache over 8 distinct prompts of ~4.2k tokens
+    prefilled one after another (qwen3-0.6b KV shape, 28 layers): the slab
+    pool, which grows by appending slabs as each prompt extends it, against
+    the dense backend, which holds each sequence in K/V tensors of exactly
+    its length.  Both phases write the same tokens from the same transient
+    per-layer sources; peaks come from the torch allocator."""
+    from synth import WORKLOADS, normal_device, workload_lengths
+
+    w = WORKLOADS["footprint_8x4k"]
+    dev = torch.device("cuda:0")
+    L, bs, S, n_kv, D = w.n_layers, w.block_size, w.slab_blocks, w.n_kv_heads, w.head_dim
+    lengths = [int(x) for x in workload_lengths(w)]
+    token_bytes = L * n_kv * D * 2 * 2  # K + V, every layer
+
+    def measure(fn):
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        torch.cuda.reset_peak_memory_stats()
+        base_a, base_r = torch.cuda.memory_allocated(), torch.cuda.memory_reserved()
+        t0 = time.perf_counter()
+        keep = fn()
+        torch.cuda.synchronize()
+        dt = time.perf_counter() - t0
+        peak_a = torch.cuda.max_memory_allocated() - base_a
+        peak_r = torch.cuda.max_memory_reserved() - base_r
+        return keep, peak_a, peak_r, dt
+
+    def source(i, layer, n):
+        return (normal_device((w.seed, layer, i, 0), (n, n_kv, D), w.dtype, dev),
+                normal_device((w.seed, layer, i, 1), (n, n_kv, D), w.dtype, dev))
+
+    def dense():
+        cache = []
+        for i, n in enumerate(lengths):
+            k = torch.empty((L, n, n_kv, D), dtype=torch.bfloat16, device=dev)
+            v = torch.empty_like(k)
+            for layer in range(L):
+                ks, vs = source(i, layer, n)
+                k[layer].copy_(ks)
+                v[layer].copy_(vs)
+                del ks, vs
+            cache.append((k, v))
+        return cache
+
+    def slab():
+        pool = pd.SlabPool(L, bs, n_kv, D, S, 64, "bf16", device=dev)
+        rows = 0
+        for i, n in enumerate(lengths):
+            nb = -(-n // bs)
+            pool.reserve_rows(rows + nb)  # presize for the span: whole slabs appended
+            t = np.arange(n)
+            r = torch.as_tensor((rows + t // bs).astype(np.int32), device=dev)
+            sl = torch.as_tensor((t % bs).astype(np.int32), device=dev)
+            for layer in range(L):
+                ks, vs = source(i, layer, n)
+                pool.write_block(layer, r, sl, ks, vs)
+                del ks, vs
+            rows += nb
+        return pool
+
+    cache, dense_a, dense_r, dense_s = measure(dense)
+    dense_storage = sum(k.numel() * 2 * 2 for k, _ in cache)
+    del cache
+    pool, slab_a, slab_r, slab_s = measure(slab)
+    if pool.check_error():
+        raise RuntimeError("device error during the prefills")
+    st = pool.stats()
+    pool.close()
+    del pool
+    ratio = slab_r / dense_r
+    result = {
+        "metric": "peak KV-cache HBM of 8 sequential distinct ~4.2k-token prefills, slab pool / dense",
+        "value": round(ratio, 4), "unit": "x", "n_gpus": 1, "steps": 1, "warmup": 0,
+        "ms_per_step": round(slab_s * 1e3, 2), "higher_is_better": False, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "footprint: 8 distinct prompts U{4096..4300} tokens, prefilled one after another",
+                   "layers": L, "block_size": bs, "slab_blocks": S, "n_kv_heads": n_kv, "head_dim": D,
+                   "lengths": lengths},
+        "dense": {"storage_bytes": dense_storage, "peak_allocated_bytes": dense_a,
+                  "peak_reserved_bytes": dense_r},
+        "slab_pool": {"bytes_reserved": st["bytes_reserved"], "n_slabs": st["n_slabs"],
+                      "slab_append_events": st["slab_append_events"],
+                      "bytes_copied_on_growth": st["bytes_copied_on_growth"],
+                      "peak_allocated_bytes": slab_a, "peak_reserved_bytes": slab_r},
+        "ratio_reserved": round(ratio, 4), "ratio_allocated": round(slab_a / dense_a, 4),
+        "gate": "within about 1.15x of the dense backend",
+        "token_bytes_all_layers": token_bytes,
+    }
+    return result
+
+
 def cpu_baseline_packed(w, target_s):
     """The oracle's packed decode (K4V4, head_dim 64) one sequence at a time."""
     from oracle.packed import k_records, packed_decode_attention, record_bytes, v_records
@@ -726,6 +825,7 @@ RUNNERS = {
     "fragmented_64": run_fragmented,
     "qwen3_1p7b_32x16k": run_long_context,
     "packed_16x16k": run_packed,
+    "footprint_8x4k": run_footprint,
 }
 
 

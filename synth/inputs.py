@@ -222,6 +222,11 @@ WORKLOADS = {
         block_size=32, slab_blocks=32, n_q_heads=16, n_kv_heads=8, head_dim=128,
         dtype=BF16, layout="monotone",
         notes="long context; gather_visible to [B, 8, 16384, 128]"),
+    "footprint_8x4k": Workload(
+        name="footprint_8x4k", seed=6, n_layers=28, batch=8, length_range=(4096, 4300),
+        block_size=32, slab_blocks=32, n_q_heads=16, n_kv_heads=8, head_dim=128,
+        dtype=BF16, layout="monotone",
+        notes="8 distinct ~4.2k-token prompts prefilled one after another; the pool grows each time"),
     "packed_16x16k": Workload(
         name="packed_16x16k", seed=5, n_layers=1, batch=16, length=16384,
         block_size=32, slab_blocks=32, n_q_heads=32, n_kv_heads=8, head_dim=64,

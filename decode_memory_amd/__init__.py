@@ -80,6 +80,11 @@ class StorageIdentity(ctypes.Structure):
         return cls.from_buffer_copy(b)
 
 
+class DenseDesc(ctypes.Structure):
+    """pd_dense_desc."""
+    _fields_ = [("format", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32)]
+
+
 EXPORTS = [
     "pd_version", "pd_last_error", "pd_record_bytes", "pd_pool_create", "pd_pool_destroy",
     "pd_slab_bytes", "pd_append_slab", "pd_slabs_needed", "pd_reserve_rows", "pd_slab_for_row",
@@ -87,7 +92,7 @@ EXPORTS = [
     "pd_paged_decode",
     "pd_paged_decode_split", "pd_paged_decode_combine", "pd_pool_stats", "pd_pool_check_error",
     "pd_signs_hash", "pd_storage_identity_of", "pd_identity_check", "pd_block_bytes",
-    "pd_export_blocks", "pd_import_blocks",
+    "pd_export_blocks", "pd_import_blocks", "pd_dense_workspace_bytes", "pd_dense_decode",
 ]
 
 _lib_handle = None
@@ -126,6 +131,9 @@ def _declare(lib):
         "pd_block_bytes": (_i32, [_vp, ctypes.POINTER(_sz)]),
         "pd_export_blocks": (_i32, [_vp, _i32, _vp, _vp, _sz, _vp]),
         "pd_import_blocks": (_i32, [_vp, ctypes.POINTER(StorageIdentity), _i32, _vp, _vp, _sz, _vp]),
+        "pd_dense_workspace_bytes": (_i32, [ctypes.POINTER(DenseDesc), _i32, _i32, _i32, ctypes.POINTER(_sz)]),
+        "pd_dense_decode": (_i32, [ctypes.POINTER(DenseDesc), _i32, _i32, _vp, _vp, _vp, _vp, _i32,
+                                   ctypes.c_float, _vp, _vp, _sz, _vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -300,6 +308,40 @@ def import_blocks(pool: int, identity: StorageIdentity, rows: torch.Tensor, src:
     _require(src, "src")
     _check(lib().pd_import_blocks(pool, ctypes.byref(identity), rows.numel(), _ptr(rows), _ptr(src),
                                   src.numel() * src.element_size(), _stream(stream)))
+
+
+def dense_workspace_bytes(fmt, n_kv_heads: int, head_dim: int, B: int, n_q_heads: int,
+                          max_len: int) -> int:
+    desc = DenseDesc(FORMAT_NAMES[fmt] if isinstance(fmt, str) else int(fmt), n_kv_heads, head_dim)
+    n = _sz(0)
+    _check(lib().pd_dense_workspace_bytes(ctypes.byref(desc), B, n_q_heads, max_len, ctypes.byref(n)))
+    return n.value
+
+
+def dense_decode(q: torch.Tensor, k_seqs: Sequence[torch.Tensor], v_seqs: Sequence[torch.Tensor],
+                 lens: torch.Tensor, max_len: int, scale: float, out: torch.Tensor,
+                 workspace: torch.Tensor, stream=None) -> None:
+    """Decode over per-sequence contiguous K/V [len_b, n_kv, D] (the dense
+    backend): bit-identical to paged_decode over the same tokens."""
+    B, n_q, D = q.shape
+    n_kv = k_seqs[0].shape[1] if B else 1
+    fmt = FMT_FP16 if q.dtype == torch.float16 else FMT_BF16
+    desc = DenseDesc(fmt, n_kv, D)
+    _require(q, "q")
+    _require(out, "out")
+    _require(lens, "lens", torch.int32, B)
+    for t in list(k_seqs) + list(v_seqs):
+        _require(t, "k/v sequence")
+    ptrs = torch.tensor([t.data_ptr() for t in k_seqs] + [t.data_ptr() for t in v_seqs],
+                        dtype=torch.int64, device=q.device)
+    _check(lib().pd_dense_decode(ctypes.byref(desc), B, n_q, _ptr(q), ptrs.data_ptr(),
+                                 ptrs.data_ptr() + 8 * B, _ptr(lens), max_len, float(scale), _ptr(out),
+                                 _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                 _stream(stream)))
+    if stream is not None:
+        # the pointer array is freed on return; the allocator reuses it only
+        # after work already queued on the streams it was used on
+        ptrs.record_stream(stream)
 
 
 CHECKPOINT_MAGIC = b"PDKVBLK1"

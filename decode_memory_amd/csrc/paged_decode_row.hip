@@ -117,7 +117,9 @@ __global__ __launch_bounds__(kRowThreads, PAGEDKV_ROW_WAVES_PER_SIMD) void paged
   const int hset = bh % n_sets;
   const int b = bh / n_sets;
   const int kvh = hset * HG + hgw * HPL + lg;  // this lane group's kv head
-  const int32_t* trow = a.table + static_cast<size_t>(b) * a.max_blocks;
+  // without a block table (dense sequences) block j of sequence b is row
+  // b * slab_blocks + j
+  const int32_t* trow = a.table ? a.table + static_cast<size_t>(b) * a.max_blocks : nullptr;
 
   // Independent loads first: the length, the rows of this split's blocks
   // (split s takes logical blocks s, s + n_split, ...; one per lane), the
@@ -126,7 +128,7 @@ __global__ __launch_bounds__(kRowThreads, PAGEDKV_ROW_WAVES_PER_SIMD) void paged
   int row = -1;
   {
     const int blk = s + lane * n_split;
-    if (lane < a.blocks_per_split && blk < a.max_blocks) row = trow[blk];
+    if (lane < a.blocks_per_split && blk < a.max_blocks) row = trow ? trow[blk] : b * lv.slab_blocks + blk;
   }
   uint4 qv[G];
   {

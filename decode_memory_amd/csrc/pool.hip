@@ -219,15 +219,18 @@ struct DecodePlan {
   SplitPlan split{1, 1};
 };
 
-bool make_decode_plan(const pd_pool* p, int32_t B, int32_t group, int32_t max_len, DecodePlan* out) {
-  const int32_t n_kv = p->desc.n_kv_heads, D = p->desc.head_dim, bs = p->desc.block_size;
+// The kernel and split of the token axis for a call; it depends only on the
+// storage shape and (B, group, max_len), so a dense call and a paged call of
+// the same shape run the same arithmetic in the same order.
+bool make_decode_plan_for(int32_t format, int32_t n_kv, int32_t D, int32_t bs, int32_t B,
+                          int32_t group, int32_t max_len, DecodePlan* out) {
   const bool d_ok = D == 64 || D == 128 || D == 256;
   const bool g_ok = group == 1 || group == 2 || group == 4 || group == 8;
   if (!d_ok || !g_ok) return false;
   DecodePlan plan;
   long long units = static_cast<long long>(B) * n_kv;
   int target = PAGEDKV_DECODE_TARGET_WG, max_bps = kMaxBlocksPerSplit;
-  if (is_native(p->desc.format)) {
+  if (is_native(format)) {
     if (bs != 16 && bs != 32 && bs != 64) return false;
     plan.kpl = row_kernel_kpl(n_kv, D, group, bs);
     if (plan.kpl > 0) {
@@ -249,6 +252,11 @@ bool make_decode_plan(const pd_pool* p, int32_t B, int32_t group, int32_t max_le
   plan.split = plan_splits(units, max_len, bs, target, max_bps);
   *out = plan;
   return true;
+}
+
+bool make_decode_plan(const pd_pool* p, int32_t B, int32_t group, int32_t max_len, DecodePlan* out) {
+  return make_decode_plan_for(p->desc.format, p->desc.n_kv_heads, p->desc.head_dim, p->desc.block_size,
+                              B, group, max_len, out);
 }
 
 }  // namespace
@@ -703,6 +711,89 @@ pd_status pd_paged_decode_combine(pd_pool* p, int32_t layer, int32_t B, int32_t 
                                   void* workspace, size_t workspace_bytes, hipStream_t stream) {
   return decode_call(p, layer, B, n_q_heads, q, block_table, max_blocks, lens, max_len, scale, out,
                      workspace, workspace_bytes, stream, kStageCombine);
+}
+
+namespace {
+
+constexpr int32_t kDenseBlock = 32;  // dense sequences are read as 32-token block rows
+
+pd_status dense_plan(const pd_dense_desc* d, int32_t B, int32_t n_q_heads, int32_t max_len,
+                     DecodePlan* plan) {
+  if (!d) return fail(PD_ERR_ARG, "desc is NULL");
+  if (!is_native(d->format)) return fail(PD_ERR_UNSUPPORTED, "dense decode takes fp16 or bf16");
+  if (d->n_kv_heads < 1 || n_q_heads < 1 || n_q_heads % d->n_kv_heads)
+    return fail(PD_ERR_ARG, "n_q_heads %d not a positive multiple of n_kv_heads %d", n_q_heads,
+                d->n_kv_heads);
+  if (B < 0 || max_len < 0) return fail(PD_ERR_ARG, "B < 0 or max_len < 0");
+  if (static_cast<int64_t>(max_len) > max_decode_len(kDenseBlock))
+    return fail(PD_ERR_UNSUPPORTED, "max_len %d beyond %lld", max_len,
+                static_cast<long long>(max_decode_len(kDenseBlock)));
+  const int32_t group = n_q_heads / d->n_kv_heads;
+  if (!make_decode_plan_for(d->format, d->n_kv_heads, d->head_dim, kDenseBlock, B, group, max_len, plan) ||
+      plan->kind != 1)
+    return fail(PD_ERR_UNSUPPORTED,
+                "dense decode needs the row kernel's shapes (n_kv_heads * head_dim * 2 a multiple of "
+                "1024 bytes, head_dim 64/128/256, group 1/2/4/8); got n_kv %d, head_dim %d, group %d",
+                d->n_kv_heads, d->head_dim, group);
+  return PD_OK;
+}
+
+}  // namespace
+
+pd_status pd_dense_workspace_bytes(const pd_dense_desc* d, int32_t B, int32_t n_q_heads,
+                                   int32_t max_len, size_t* bytes) {
+  if (!bytes) return fail(PD_ERR_ARG, "bytes is NULL");
+  DecodePlan plan;
+  if (pd_status st = dense_plan(d, B, n_q_heads, max_len, &plan)) return st;
+  *bytes = decode_workspace_bytes(B, n_q_heads, d->head_dim, plan.split);
+  return PD_OK;
+}
+
+pd_status pd_dense_decode(const pd_dense_desc* d, int32_t B, int32_t n_q_heads, const void* q,
+                          const void* const* k_seqs, const void* const* v_seqs, const int32_t* lens,
+                          int32_t max_len, float scale, void* out, void* workspace,
+                          size_t workspace_bytes, hipStream_t stream) {
+  DecodePlan plan;
+  if (pd_status st = dense_plan(d, B, n_q_heads, max_len, &plan)) return st;
+  if (B == 0) return PD_OK;
+  if (!q || !k_seqs || !v_seqs || !lens || !out || !workspace) return fail(PD_ERR_ARG, "NULL device pointer");
+  if ((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(out)) & 15)
+    return fail(PD_ERR_ARG, "q and out must be 16-byte aligned");
+  if (reinterpret_cast<uintptr_t>(workspace) & 255) return fail(PD_ERR_ARG, "workspace not 256-byte aligned");
+  if (!(scale == scale) || std::isinf(scale)) return fail(PD_ERR_ARG, "scale is not finite");
+  const size_t need = decode_workspace_bytes(B, n_q_heads, d->head_dim, plan.split);
+  if (workspace_bytes < need)
+    return fail(PD_ERR_CAPACITY, "workspace %zu bytes, %zu needed", workspace_bytes, need);
+  const int32_t max_blocks = max_len > 0 ? (max_len + kDenseBlock - 1) / kDenseBlock : 1;
+  DecodeArgs a{};
+  // sequence b is "slab" b whose rows are its consecutive 32-token blocks;
+  // with no block table, block j of sequence b is row b * max_blocks + j
+  a.lv.k_tab = k_seqs;
+  a.lv.v_tab = v_seqs;
+  a.lv.slab_blocks = max_blocks;
+  a.lv.block_size = kDenseBlock;
+  a.lv.n_kv = d->n_kv_heads;
+  a.lv.k_rec = a.lv.v_rec = 2 * d->head_dim;
+  a.lv.capacity_rows = static_cast<int64_t>(B) * max_blocks;
+  a.lv.err = nullptr;
+  a.B = B;
+  a.n_q = n_q_heads;
+  a.q = q;
+  a.table = nullptr;
+  a.max_blocks = max_blocks;
+  a.lens = lens;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.out = out;
+  a.partials = static_cast<float*>(workspace);
+  a.ml_offset = decode_ml_offset(B, n_q_heads, d->head_dim, plan.split);
+  a.n_split = plan.split.n_split;
+  a.blocks_per_split = plan.split.blocks_per_split;
+  const bool bf16 = d->format == PD_FMT_BF16;
+  const int32_t group = n_q_heads / d->n_kv_heads;
+  hipError_t e = launch_paged_decode_row(a, bf16, d->head_dim, group, plan.kpl, stream);
+  if (e == hipSuccess) e = launch_decode_combine(a, bf16, d->head_dim, stream);
+  if (e != hipSuccess) return hip_fail(e, "dense_decode launch");
+  return PD_OK;
 }
 
 pd_status pd_pool_stats(const pd_pool* p, pd_stats* s) {

@@ -291,6 +291,40 @@ pd_status pd_paged_decode(pd_pool* pool, int32_t layer, int32_t B, int32_t n_q_h
                           void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * Dense decode: the same attention as pd_paged_decode over per-sequence
+ * contiguous K/V, with no pool.  mlxcel #2171 ("refactor: one KV storage
+ * abstraction with dense and paged backends", section "Proposed Solution":
+ * dense and paged backends behind one attend(q, k, v, scale, mask); section
+ * "Acceptance Criteria": dense and paged results identical under a
+ * deterministic mode).
+ *   desc: host; format PD_FMT_FP16 or PD_FMT_BF16, n_kv_heads, head_dim.
+ *   k_seqs, v_seqs: device arrays [B] of device pointers; sequence b's K (V)
+ *     is [lens[b], n_kv_heads, head_dim] contiguous and 16-byte aligned: the
+ *     pool's block-row layout without the pool.
+ *   q, lens, max_len, scale, out, workspace: as pd_paged_decode; the
+ *     workspace size comes from pd_dense_workspace_bytes.
+ * The kernels and the split of the token axis are those of a 16-bit pool of
+ * block_size 32 with the same (B, n_q_heads, max_len), so the output is bit
+ * for bit that of pd_paged_decode over the same tokens, wherever the pool
+ * keeps them.  Shapes: those of the row kernel (n_kv_heads * head_dim * 2 a
+ * multiple of 1024 bytes; head_dim 64, 128, 256; group 1, 2, 4, 8), else
+ * PD_ERR_UNSUPPORTED.  There is no device error word: a length beyond
+ * max_len is clamped to it.
+ */
+typedef struct pd_dense_desc {
+  int32_t format;      /* PD_FMT_FP16 or PD_FMT_BF16 */
+  int32_t n_kv_heads;
+  int32_t head_dim;
+} pd_dense_desc;
+
+pd_status pd_dense_workspace_bytes(const pd_dense_desc* desc, int32_t B, int32_t n_q_heads,
+                                   int32_t max_len, size_t* bytes);
+pd_status pd_dense_decode(const pd_dense_desc* desc, int32_t B, int32_t n_q_heads, const void* q,
+                          const void* const* k_seqs, const void* const* v_seqs,
+                          const int32_t* lens, int32_t max_len, float scale, void* out,
+                          void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
  * The two stages of pd_paged_decode as separate calls, same arguments and
  * checks: _split writes the per-split partials into the workspace, _combine
  * merges them into `out`.  pd_paged_decode == _split then _combine on one

@@ -312,6 +312,8 @@ def run_qwen3_0p6b(args, torch, pd):
         pool.write_block(layer, all_rows, all_slots, kd, vd)
         k_new.append(kd.view(B, n, n_kv, D)[:, n - 1].contiguous())
         v_new.append(vd.view(B, n, n_kv, D)[:, n - 1].contiguous())
+        if layer == L - 1:
+            prefill_src = (kd, vd)  # kept for the prefill-size write_block timing
         del kd, vd
         qs.append(dev_bits(q_bits(w.seed, layer, B, n_q, D, w.dtype)))
         outs.append(torch.empty_like(qs[-1]))
@@ -352,6 +354,15 @@ def run_qwen3_0p6b(args, torch, pd):
     w_bytes = write_bytes(B, n_kv, D)
     step_bytes = L * (d_bytes + w_bytes)
 
+    # write_block of a whole layer's prefill (8 x 4096 tokens; it rewrites the
+    # same values), reported beside: K and V read from the sources, written
+    # into their rows' slabs, plus the rows and slots
+    for _ in range(2):
+        pool.write_block(L - 1, all_rows, all_slots, *prefill_src)
+    wb_us = timer(lambda: pool.write_block(L - 1, all_rows, all_slots, *prefill_src), 5)
+    wb_bytes = 2 * 2 * B * n * n_kv * D * 2 + B * n * 8
+    del prefill_src
+
     # gather_visible of one layer to contiguous [B, n_kv, T, D] (reported beside)
     gk = torch.empty((B, n_kv, n, D), dtype=torch.bfloat16, device=dev)
     gv = torch.empty_like(gk)
@@ -385,7 +396,9 @@ def run_qwen3_0p6b(args, torch, pd):
         "eager_ms_per_step": round(eager_ms, 4),
         "paged_decode": {"split_us": round(split_us, 3), "combine_us": round(combine_us, 3),
                          "achieved_gbs_both_stages": round(d_bytes / ((split_us + combine_us) * 1e-6) / 1e9, 1)},
-        "write_block": {"bytes_per_launch": w_bytes},
+        "write_block": {"decode_step_bytes_per_launch": w_bytes,
+                        "prefill_layer_us": round(wb_us, 2), "prefill_layer_bytes": wb_bytes,
+                        "prefill_layer_gbs": round(wb_bytes / (wb_us * 1e-6) / 1e9, 1)},
         "gather_visible": {"us_per_layer": round(g_us, 2), "bytes_per_layer": g_bytes,
                            "achieved_gbs": round(g_bytes / (g_us * 1e-6) / 1e9, 1)},
     })
@@ -639,7 +652,13 @@ def run_packed(args, torch, pd):
                 k = normal_device((w.seed, D, layer, 0), (B * n, n_kv, D), "bf16", dev)
                 v = normal_device((w.seed, D, layer, 1), (B * n, n_kv, D), "bf16", dev)
                 pool.write_block(layer, all_rows, all_slots, k, v)
-                del k, v
+                if layer < copies - 1:
+                    del k, v
+            # the write of a whole layer (16 x 16384 tokens; packed formats
+            # rotate K and quantise K and V here), rewriting the same values
+            wb_us = timer(lambda: pool.write_block(copies - 1, all_rows, all_slots, k, v), 3)
+            wb_bytes = 2 * B * n * n_kv * D * 2 + kv_bytes + B * n * 8
+            del k, v
             q = normal_device((w.seed, D, 2), (B, n_q, D), "bf16", dev)
             out = torch.empty_like(q)
             ws = pool.workspace(B, n_q, n)
@@ -675,6 +694,8 @@ def run_packed(args, torch, pd):
                 "call_gbs": round(d_bytes / (us * 1e-6) / 1e9, 1),
                 "kv_tokens_attended_per_s": round(B * n / (us * 1e-6), 1),
                 "pool_copies": copies,
+                "write_block_us": round(wb_us, 2), "write_block_bytes": wb_bytes,
+                "write_block_gbs": round(wb_bytes / (wb_us * 1e-6) / 1e9, 1),
             }
     value = tot_bytes / (tot_us * 1e-6) / 1e9
     worst = min((k for k in per if not k.startswith("bf16")), key=lambda k: per[k]["split_gbs"])

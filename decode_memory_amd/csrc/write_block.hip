@@ -142,106 +142,125 @@ __global__ __launch_bounds__(kThreads) void row_move_kernel(RowMoveArgs a) {
 }
 
 // ---- packed pools -------------------------------------------------------------
-// One wave quantises one token-head vector (K or V).  Element e of the vector
-// lives in lane e % 64, register e / 64.
+// A lane holds 8 consecutive values of a vector (one token-head of K or V),
+// D/8 lanes hold the vector, and a wave works on 64/(D/8) vectors at once.
+// Jobs are ordered all K vectors first, then all V vectors, so a wave rarely
+// mixes the two.
 
+// Rotate a K vector: x' = H diag(sigma) x / sqrt(D), with H the Sylvester
+// Hadamard matrix applied as the butterfly network h = 1, 2, ..., D/2, each
+// pair (a, b) -> (a + b, a - b) in fp32 (the lower index gets a + b), then
+// one multiply by 1/sqrt(D).  Stages h < 8 pair values inside a lane, the
+// others pair lanes c and c ^ (h / 8) of the vector's lane group.
 template <int D>
-__device__ __forceinline__ void fwht_rotate(float (&x)[D / 64], const float* signs, int lane,
-                                            float inv_sqrt_d) {
-  constexpr int R = D / 64;
+__device__ __forceinline__ void fwht_rotate8(float (&x)[8], const float* signs, int c,
+                                             float inv_sqrt_d) {
+  constexpr int LPT = D / 8;
 #pragma unroll
-  for (int r = 0; r < R; ++r) x[r] *= signs[r * 64 + lane];  // exact sign flips
-  // stages h = 1 .. 32: partner in another lane
+  for (int e = 0; e < 8; ++e) x[e] *= signs[8 * c + e];  // exact sign flips
 #pragma unroll
-  for (int h = 1; h < 64 && h < D; h <<= 1) {
-    const bool upper = (lane & h) != 0;
+  for (int h = 1; h < 8; h <<= 1) {
+    float y[8];
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const float other = __shfl_xor(x[r], h, kWave);
-      // pair (a, b) with a at the lower index: lower gets a + b, upper gets a - b
-      x[r] = upper ? __fsub_rn(other, x[r]) : __fadd_rn(x[r], other);
-    }
-  }
-  // stages h = 64 .. D/2: partner in another register of the same lane
+    for (int e = 0; e < 8; ++e) y[e] = (e & h) ? __fsub_rn(x[e ^ h], x[e]) : __fadd_rn(x[e], x[e ^ h]);
 #pragma unroll
-  for (int hr = 1; hr < R; hr <<= 1) {
-    float y[R];
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const float other = x[r ^ hr];
-      y[r] = (r & hr) ? __fsub_rn(other, x[r]) : __fadd_rn(x[r], other);
-    }
-#pragma unroll
-    for (int r = 0; r < R; ++r) x[r] = y[r];
+    for (int e = 0; e < 8; ++e) x[e] = y[e];
   }
 #pragma unroll
-  for (int r = 0; r < R; ++r) x[r] = __fmul_rn(x[r], inv_sqrt_d);
-}
-
-// Quantise the wave's vector in groups of 32 (half a wave per group and
-// register) and store codes + (scale, offset) records.
-template <int D>
-__device__ __forceinline__ void quantise_store(const float (&x)[D / 64], int bits, char* rec,
-                                               int lane) {
-  constexpr int R = D / 64;
-  const float levels = static_cast<float>((1 << bits) - 1);
-  const int payload = D * bits / 8;
+  for (int hl = 1; hl < LPT; hl <<= 1) {
+    const bool upper = (c & hl) != 0;
 #pragma unroll
-  for (int r = 0; r < R; ++r) {
-    float mn = x[r], mx = x[r];
-#pragma unroll
-    for (int m = 1; m < 32; m <<= 1) {
-      mn = fminf(mn, __shfl_xor(mn, m, kWave));
-      mx = fmaxf(mx, __shfl_xor(mx, m, kWave));
-    }
-    const float scale = __fdiv_rn(__fsub_rn(mx, mn), levels);
-    int code = 0;
-    if (scale != 0.f) {
-      float t = rintf(__fdiv_rn(__fsub_rn(x[r], mn), scale));
-      t = fminf(fmaxf(t, 0.f), levels);
-      code = static_cast<int>(t);
-    }
-    const int e = r * 64 + lane;  // element index
-    if (bits == 8) {
-      reinterpret_cast<uint8_t*>(rec)[e] = static_cast<uint8_t>(code);
-    } else {
-      const int hi = __shfl_xor(code, 1, kWave);
-      if ((lane & 1) == 0)
-        reinterpret_cast<uint8_t*>(rec)[e >> 1] = static_cast<uint8_t>((code & 15) | ((hi & 15) << 4));
-    }
-    if ((lane & 31) == 0) {
-      float* meta = reinterpret_cast<float*>(rec + payload) + 2 * (e / 32);
-      meta[0] = scale;
-      meta[1] = mn;
+    for (int e = 0; e < 8; ++e) {
+      const float other = __shfl_xor(x[e], hl, kWave);
+      x[e] = upper ? __fsub_rn(other, x[e]) : __fadd_rn(x[e], other);
     }
   }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) x[e] = __fmul_rn(x[e], inv_sqrt_d);
 }
 
 template <int D>
 __global__ __launch_bounds__(kThreads) void write_block_packed_kernel(WriteArgs a) {
-  constexpr int R = D / 64;
+  constexpr int LPT = D / 8;        // lanes per vector
+  constexpr int VPW = kWave / LPT;  // vectors per wave
   const int lane = threadIdx.x % kWave;
-  const int waves_per_grid = gridDim.x * (kThreads / kWave);
-  const int n_jobs = a.n * a.lv.n_kv * 2;  // (token, head, K|V)
-  for (int job = blockIdx.x * (kThreads / kWave) + threadIdx.x / kWave; job < n_jobs;
-       job += waves_per_grid) {
-    const int is_v = job & 1;
-    const int th = job >> 1;
+  const int c = lane % LPT;         // values 8c .. 8c+7 of the vector
+  const int n_vec = a.n * a.lv.n_kv;  // K vectors; as many V vectors follow
+  const int waves = gridDim.x * (kThreads / kWave);
+  for (int w0 = (blockIdx.x * (kThreads / kWave) + threadIdx.x / kWave) * VPW; w0 < 2 * n_vec;
+       w0 += waves * VPW) {
+    const int job = w0 + lane / LPT;
+    const bool live = job < 2 * n_vec;
+    const bool is_v = job >= n_vec;
+    const int th = is_v ? job - n_vec : job;
     const int i = th / a.lv.n_kv, head = th % a.lv.n_kv;
-    const int32_t row = a.rows[i], slot = a.slots[i];
-    if (!valid_target(a.lv, row, slot, lane == 0 && is_v == 0 && head == 0)) continue;
-    int slab;
-    const size_t tok = token_in_slab(a.lv, row, slot, &slab);
-    const uint16_t* src = static_cast<const uint16_t*>(is_v ? a.v_src : a.k_src) +
-                          (static_cast<size_t>(i) * a.lv.n_kv + head) * D;
-    float x[R];
+    bool ok = false;
+    int slab = 0;
+    size_t tok = 0;
+    if (live) {
+      const int32_t row = a.rows[i], slot = a.slots[i];
+      ok = valid_target(a.lv, row, slot, c == 0 && !is_v && head == 0);
+      if (ok) tok = token_in_slab(a.lv, row, slot, &slab);
+    }
+    float x[8];
+    {
+      uint4 u = make_uint4(0, 0, 0, 0);
+      if (ok) {
+        const uint16_t* src = static_cast<const uint16_t*>(is_v ? a.v_src : a.k_src) +
+                              static_cast<size_t>(th) * D + 8 * c;
+        u = *reinterpret_cast<const uint4*>(src);
+      }
+      widen8<true>(u, x);
+    }
+    // every lane takes part in the cross-lane stages; V vectors keep x
+    if (__ballot(live && !is_v)) {
+      float y[8];
 #pragma unroll
-    for (int r = 0; r < R; ++r) x[r] = bf16_lo(src[r * 64 + lane]);
+      for (int e = 0; e < 8; ++e) y[e] = x[e];
+      fwht_rotate8<D>(y, a.signs, c, a.inv_sqrt_d);
+      if (!is_v) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = y[e];
+      }
+    }
+    // group of 32 values = 4 lanes: min and max in the lane, then across them
+    float mn = x[0], mx = x[0];
+#pragma unroll
+    for (int e = 1; e < 8; ++e) {
+      mn = fminf(mn, x[e]);
+      mx = fmaxf(mx, x[e]);
+    }
+    mn = fminf(mn, dpp<kDppXor1>(mn));
+    mx = fmaxf(mx, dpp<kDppXor1>(mx));
+    mn = fminf(mn, dpp<kDppXor2>(mn));
+    mx = fmaxf(mx, dpp<kDppXor2>(mx));
+    const int bits = is_v ? a.v_bits : a.k_bits;
+    const float levels = static_cast<float>((1 << bits) - 1);
+    const float scale = __fdiv_rn(__fsub_rn(mx, mn), levels);
+    uint32_t code[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float t = 0.f;
+      if (scale != 0.f) t = fminf(fmaxf(rintf(__fdiv_rn(__fsub_rn(x[e], mn), scale)), 0.f), levels);
+      code[e] = static_cast<uint32_t>(t);
+    }
+    if (!ok) continue;
     const int rec_bytes = is_v ? a.lv.v_rec : a.lv.k_rec;
-    char* dst = static_cast<char*>(const_cast<void*>(is_v ? a.lv.v_tab[slab] : a.lv.k_tab[slab])) +
+    char* rec = static_cast<char*>(const_cast<void*>(is_v ? a.lv.v_tab[slab] : a.lv.k_tab[slab])) +
                 (tok * a.lv.n_kv + head) * rec_bytes;
-    if (!is_v) fwht_rotate<D>(x, a.signs, lane, a.inv_sqrt_d);
-    quantise_store<D>(x, is_v ? a.v_bits : a.k_bits, dst, lane);
+    if (bits == 8) {
+      *reinterpret_cast<uint2*>(rec + 8 * c) =
+          make_uint2(code[0] | (code[1] << 8) | (code[2] << 16) | (code[3] << 24),
+                     code[4] | (code[5] << 8) | (code[6] << 16) | (code[7] << 24));
+    } else {
+      *reinterpret_cast<uint32_t*>(rec + 4 * c) =
+          (code[0] | (code[1] << 4)) | ((code[2] | (code[3] << 4)) << 8) |
+          ((code[4] | (code[5] << 4)) << 16) | ((code[6] | (code[7] << 4)) << 24);
+    }
+    if ((c & 3) == 0) {
+      float* meta = reinterpret_cast<float*>(rec + D * bits / 8) + 2 * (c / 4);
+      *reinterpret_cast<float2*>(meta) = make_float2(scale, mn);
+    }
   }
 }
 
@@ -279,8 +298,8 @@ hipError_t launch_write_block(const WriteArgs& a, int32_t format, hipStream_t s)
     hipLaunchKernelGGL(write_block_native_kernel, dim3(grid), dim3(kThreads), 0, s, a);
     return hipGetLastError();
   }
-  const int jobs = a.n * a.lv.n_kv * 2;
-  int grid = (jobs + 3) / 4;
+  const long long waves = (2LL * a.n * a.lv.n_kv * (a.head_dim / 8) + kWave - 1) / kWave;
+  long long grid = (waves + kThreads / kWave - 1) / (kThreads / kWave);
   if (grid > 65536) grid = 65536;
   switch (a.head_dim) {
     case 64:

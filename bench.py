@@ -64,10 +64,10 @@ METRIC = "paged_decode achieved HBM GB/s (% of peak) + KV tokens attended/sec"
 MALL_BYTES = 256 << 20  # last-level cache of the MI355X
 
 
-def decode_source_hash() -> str:
+def decode_source_hash(sources=DECODE_SOURCES) -> str:
     import hashlib
     h = hashlib.sha256()
-    for name in DECODE_SOURCES:
+    for name in sources:
         with open(os.path.join(ROOT, "decode_memory_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -89,6 +89,31 @@ def measured_traffic():
         return None
     try:
         return int(fields["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+PACKED_TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "paged_decode_packed_16x16k_traffic.md")
+PACKED_SOURCES = ("paged_decode_packed_mfma.hip", "device_common.h")
+
+
+def measured_packed_traffic(case: str):
+    """HBM bytes per launch of the packed decode kernel for `case` (e.g.
+    "k4v4_d64") from the committed counter profile, or None when the profile
+    is missing or the kernel changed since."""
+    try:
+        text = open(PACKED_TRAFFIC_PROFILE).read()
+    except OSError:
+        return None
+    fields = {}
+    for line in text.splitlines():
+        if line.startswith("- ") and ":" in line:
+            k, v = line[2:].split(":", 1)
+            fields[k.strip()] = v.strip().strip("`")
+    if fields.get("kernel_source_sha256") != decode_source_hash(PACKED_SOURCES):
+        return None
+    try:
+        return int(fields[f"hbm_bytes_per_launch {case}"])
     except (KeyError, ValueError):
         return None
 
@@ -708,7 +733,8 @@ def run_packed(args, torch, pd):
         "pct_of_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
         "kv_tokens_attended_per_s": round(len(per) * B * n / (tot_us * 1e-6), 1),
         "roofline": {"bound": "hbm", "achieved": p["split_gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(p["split_gbs"] / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(p["split_gbs"] / HBM_PEAK_GBS, 4),
+                     "traffic": measured_packed_traffic(worst),
                      "kernel": f"paged_decode_packed_mfma_kernel ({worst}, split stage; the slowest packed case)",
                      "algorithmic_bytes_per_launch": p["algorithmic_bytes"],
                      "avg_launch_us": p["split_us"]},

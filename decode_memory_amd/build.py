@@ -20,7 +20,7 @@ LIB = os.path.join(HERE, "libpagedkv.so")
 OBJ_DIR = os.path.join(HERE, "_build")
 
 SOURCES = ["pool.hip", "write_block.hip", "gather_visible.hip", "paged_decode.hip",
-           "paged_decode_row.hip", "paged_decode_packed.hip", "paged_decode_packed_mfma.hip"]
+           "paged_decode_row.hip", "paged_decode_packed_mfma.hip"]
 
 HIPCC_FLAGS = [
     "-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950",

@@ -102,9 +102,6 @@ hipError_t launch_paged_decode_column(const DecodeArgs& a, bool bf16, int32_t he
 hipError_t launch_paged_decode_row(const DecodeArgs& a, bool bf16, int32_t head_dim, int32_t group,
                                    int hgw, hipStream_t s);
 hipError_t launch_decode_combine(const DecodeArgs& a, bool bf16, int32_t head_dim, hipStream_t s);
-hipError_t launch_paged_decode_packed(const DecodeArgs& a, int32_t head_dim, int32_t group,
-                                      hipStream_t s);
-bool packed_decode_supported(int32_t n_kv, int32_t head_dim, int32_t group, int32_t block_size);
 hipError_t launch_paged_decode_packed_mfma(const DecodeArgs& a, int32_t head_dim, int32_t group,
                                            hipStream_t s);
 bool packed_mfma_supported(int32_t n_kv, int32_t head_dim, int32_t group, int32_t block_size);

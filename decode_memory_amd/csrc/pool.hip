@@ -25,13 +25,6 @@ using namespace pagedkv;
 #ifndef PAGEDKV_DECODE_TARGET_WG
 #define PAGEDKV_DECODE_TARGET_WG 768
 #endif
-#ifndef PAGEDKV_PACKED_TARGET_WG
-#define PAGEDKV_PACKED_TARGET_WG 768
-#endif
-// Packed pools decode on the matrix cores (0: the VALU kernel).
-#ifndef PAGEDKV_PACKED_MFMA
-#define PAGEDKV_PACKED_MFMA 1
-#endif
 #ifndef PAGEDKV_ROW_TARGET_WG
 #define PAGEDKV_ROW_TARGET_WG 256
 #endif
@@ -214,7 +207,7 @@ namespace {
 
 // Which decode kernel runs for a call, and how the token axis is split.
 struct DecodePlan {
-  int kind = 0;  // 0: column kernel, 1: row kernel, 2: packed kernel, 3: packed MFMA kernel
+  int kind = 0;  // 0: column kernel, 1: row kernel, 2: packed (matrix-core) kernel
   int kpl = 0;   // row kernel: kv heads per lane group
   SplitPlan split{1, 1};
 };
@@ -239,15 +232,11 @@ bool make_decode_plan_for(int32_t format, int32_t n_kv, int32_t D, int32_t bs, i
       target = PAGEDKV_ROW_TARGET_WG;
       max_bps = PAGEDKV_ROW_MAX_BLOCKS_PER_SPLIT;
     }
-  } else if (PAGEDKV_PACKED_MFMA && packed_mfma_supported(n_kv, D, group, bs)) {
-    plan.kind = 3;
+  } else {
+    if (!packed_mfma_supported(n_kv, D, group, bs)) return false;
+    plan.kind = 2;
     units = B;  // a packed workgroup covers every kv head of its sequence
     target = packed_mfma_target_workgroups(D);
-  } else {
-    if (!packed_decode_supported(n_kv, D, group, bs)) return false;
-    plan.kind = 2;
-    units = B;
-    target = PAGEDKV_PACKED_TARGET_WG;
   }
   plan.split = plan_splits(units, max_len, bs, target, max_bps);
   *out = plan;
@@ -676,8 +665,7 @@ static pd_status decode_call(pd_pool* p, int32_t layer, int32_t B, int32_t n_q_h
   if (stages & kStageSplit) {
     switch (plan.kind) {
       case 1: e = launch_paged_decode_row(a, bf16, D, group, plan.kpl, stream); break;
-      case 2: e = launch_paged_decode_packed(a, D, group, stream); break;
-      case 3: e = launch_paged_decode_packed_mfma(a, D, group, stream); break;
+      case 2: e = launch_paged_decode_packed_mfma(a, D, group, stream); break;
       default: e = launch_paged_decode_column(a, bf16, D, group, stream); break;
     }
   }

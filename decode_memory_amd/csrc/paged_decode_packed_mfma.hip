@@ -36,7 +36,12 @@
 //     feeds the two dimensions of its nibbles); the offsets add
 //     sum_t p_t offset_t per group.
 // Codes become f16 exactly: a byte placed under the exponent bits 0x64 is
-// 1024 + code, and one packed f16 add of -1024 leaves the code.
+// 1024 + byte.  Key products take these biased codes as they are and drop
+// 1024 * sum(q') per group afterwards; value codes get one packed f16 add of
+// -1024 first (their sums run over the whole split, where the cancellation
+// would cost accuracy).  A 4-bit high nibble is taken in place, as 16 * code,
+// and scaled back by an exact power of two (keys: in q', values: in the
+// accumulator).
 // Partials go to the same workspace layout as the 16-bit kernels and the same
 // combine kernel merges them.
 #include "device_common.h"
@@ -59,12 +64,14 @@ namespace {
 constexpr int kPWaves = 8;  // one wave per kv head; packed pools have 8
 constexpr int kPThreads = kPWaves * kWave;
 constexpr int kPBS = 32;    // tokens per block
+constexpr int kPLdsSlabs = kPThreads;  // slab pointers staged in LDS
 constexpr int kSub = 16;    // tokens per MFMA sub-tile
 constexpr float kPScale = 1024.f;  // p * scale travels as (p * scale * 1024) in f16
 
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 typedef _Float16 h4 __attribute__((ext_vector_type(4)));
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+typedef unsigned short us2 __attribute__((ext_vector_type(2)));
 typedef float f4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(1))) u32x4 gu32x4;
@@ -92,42 +99,78 @@ struct PShape {
 template <int D>
 constexpr int kPMinWaves = D <= 64 ? 4 : 2;
 
+// N 32-bit words at p (aligned to min(4 N, 16) bytes) with the widest loads.
+template <int N>
+__device__ __forceinline__ void load_words(const void* p, uint32_t (&w)[N]) {
+  if constexpr (N % 4 == 0) {
+#pragma unroll
+    for (int k = 0; k < N / 4; ++k) {
+      const uint4 x = reinterpret_cast<const uint4*>(p)[k];
+      w[4 * k] = x.x;
+      w[4 * k + 1] = x.y;
+      w[4 * k + 2] = x.z;
+      w[4 * k + 3] = x.w;
+    }
+  } else if constexpr (N == 2) {
+    const uint2 x = *reinterpret_cast<const uint2*>(p);
+    w[0] = x.x;
+    w[1] = x.y;
+  } else {
+    static_assert(N == 1, "1, 2 or a multiple of 4 words");
+    w[0] = *reinterpret_cast<const uint32_t*>(p);
+  }
+}
+
 __device__ __forceinline__ const char* lane_ptr(uint64_t v, int j) {
   const uint32_t lo = __builtin_amdgcn_readlane(static_cast<uint32_t>(v), j);
   const uint32_t hi = __builtin_amdgcn_readlane(static_cast<uint32_t>(v >> 32), j);
   return reinterpret_cast<const char*>((static_cast<uint64_t>(hi) << 32) | lo);
 }
 
-// Two bytes of w (selected by SEL) as an f16 pair holding the byte values:
-// each byte is placed under the exponent bits 0x64 (the f16 1024 + byte) and
-// 1024 is subtracted, exactly.
-__device__ __forceinline__ uint32_t bytes_to_f16x2(uint32_t w, uint32_t sel) {
-  const uint32_t biased = __builtin_amdgcn_perm(0x64646464u, w, sel);
-  const h2 x = __builtin_bit_cast(h2, biased) - h2{static_cast<_Float16>(1024.f), static_cast<_Float16>(1024.f)};
-  return __builtin_bit_cast(uint32_t, x);
+// Two bytes of w (selected by SEL) as the f16 pair (1024 + byte): each byte
+// is placed under the exponent bits 0x64.
+__device__ __forceinline__ uint32_t bytes_biased(uint32_t w, uint32_t sel) {
+  return __builtin_amdgcn_perm(0x64646464u, w, sel);
 }
 constexpr uint32_t kSelB01 = 0x04010400u;  // bytes 0, 1 -> (lo, hi) halves
 constexpr uint32_t kSelB23 = 0x04030402u;  // bytes 2, 3
+constexpr uint32_t kBias2 = 0x64006400u;   // f16 pair (1024, 1024)
 
-// B operand of a score product: 8 codes of one token and group as f16, in
-// the element order the A operand (q') uses.  8-bit codes: values 0..7 of
-// the k-block in order; 4-bit codes: values 0, 2, 4, 6, 1, 3, 5, 7.
+// An f16 pair (1024 + x, 1024 + y) less 1024 each, exactly.
+__device__ __forceinline__ uint32_t unbias(uint32_t v) {
+  const h2 x = __builtin_bit_cast(h2, v) - h2{static_cast<_Float16>(1024.f), static_cast<_Float16>(1024.f)};
+  return __builtin_bit_cast(uint32_t, x);
+}
+
+// Byte c of the 4 token rows at p, PITCH apart, as two 16-bit pairs
+// (token 0 | token 1 << 16, token 2 | token 3 << 16).
+template <int PITCH>
+__device__ __forceinline__ void byte_column(const unsigned char* p, uint32_t& x01, uint32_t& x23) {
+  const us2 a{p[0], p[PITCH]}, b{p[2 * PITCH], p[3 * PITCH]};
+  x01 = __builtin_bit_cast(uint32_t, a);
+  x23 = __builtin_bit_cast(uint32_t, b);
+}
+
+// B operand of a score product: 8 codes of one token and group as biased
+// f16, in the element order the A operand (q') uses.  8-bit codes: 1024 +
+// value e of the k-block; 4-bit codes: 1024 + values 0, 2, 4, 6 (low
+// nibbles), then 1024 + 16 * values 1, 3, 5, 7 (high nibbles in place).
 template <int KB>
 __device__ __forceinline__ h8 key_codes(const unsigned char* p) {
   uint32_t r[4];
   if constexpr (KB == 8) {
     const uint2 w = *reinterpret_cast<const uint2*>(p);
-    r[0] = bytes_to_f16x2(w.x, kSelB01);
-    r[1] = bytes_to_f16x2(w.x, kSelB23);
-    r[2] = bytes_to_f16x2(w.y, kSelB01);
-    r[3] = bytes_to_f16x2(w.y, kSelB23);
+    r[0] = bytes_biased(w.x, kSelB01);
+    r[1] = bytes_biased(w.x, kSelB23);
+    r[2] = bytes_biased(w.y, kSelB01);
+    r[3] = bytes_biased(w.y, kSelB23);
   } else {
     const uint32_t w = *reinterpret_cast<const uint32_t*>(p);
-    const uint32_t lo = w & 0x0f0f0f0fu, hi = (w >> 4) & 0x0f0f0f0fu;
-    r[0] = bytes_to_f16x2(lo, kSelB01);
-    r[1] = bytes_to_f16x2(lo, kSelB23);
-    r[2] = bytes_to_f16x2(hi, kSelB01);
-    r[3] = bytes_to_f16x2(hi, kSelB23);
+    const uint32_t lo = w & 0x0f0f0f0fu, hi = w & 0xf0f0f0f0u;
+    r[0] = bytes_biased(lo, kSelB01);
+    r[1] = bytes_biased(lo, kSelB23);
+    r[2] = bytes_biased(hi, kSelB01);
+    r[3] = bytes_biased(hi, kSelB23);
   }
   return __builtin_bit_cast(h8, r);
 }
@@ -136,6 +179,11 @@ template <int KB>
 __device__ __forceinline__ int key_value_index(int e) {  // value of element e in its k-block
   if constexpr (KB == 8) return e;
   else return e < 4 ? 2 * e : 2 * (e - 4) + 1;
+}
+// q' factor of value v of a group (4-bit high nibbles enter as 16 * code)
+template <int KB>
+__device__ __forceinline__ float key_q_factor(int v) {
+  return (KB == 4 && (v & 1)) ? 0.0625f : 1.f;
 }
 
 // Value dimension that accumulator i of lane l holds.  8-bit codes: 64 i +
@@ -147,6 +195,13 @@ __device__ __forceinline__ int vdim(int i, int lane) {
   if constexpr (VB == 8) return 64 * i + lane;
   else if constexpr (NV == 1) return 2 * (lane % 32) + lane / 32;
   else return 2 * (lane + 64 * (i / 2)) + (i % 2);
+}
+// Scale that brings accumulator i of lane l back to sum_t p_t s_t c_t: the
+// 1024 of p * scale, and 16 more for a 4-bit high nibble taken in place.
+template <int VB, int NV>
+__device__ __forceinline__ float vacc_scale(int i, int lane) {
+  const bool high = VB == 4 && (NV == 1 ? lane >= 32 : (i % 2) == 1);
+  return high ? 1.f / (16.f * kPScale) : 1.f / kPScale;
 }
 
 __device__ __forceinline__ float row_max16(float v) {
@@ -169,6 +224,9 @@ __global__ __launch_bounds__(kPThreads, kPMinWaves<D>) void paged_decode_packed_
   __shared__ __attribute__((aligned(16))) unsigned char s_stage[S::STAGE];
   __shared__ __attribute__((aligned(16))) float s_aux[kPWaves][AUX];  // q' transform, then p^T
   __shared__ float s_qs[kPWaves][G * NG];  // sum of q' per (query head, group)
+  __shared__ float s_kb[kPWaves][G * NG];  // 1024 * sum of the f16 A operand, likewise
+  __shared__ uint64_t s_kt[kPLdsSlabs];    // slab base pointers of the layer
+  __shared__ uint64_t s_vt[kPLdsSlabs];
 
   const int lane = threadIdx.x % kWave;
   const int h = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // kv head of this wave
@@ -183,11 +241,22 @@ __global__ __launch_bounds__(kPThreads, kPMinWaves<D>) void paged_decode_packed_
   const int b = w / n_split;
   const int32_t* trow = a.table + static_cast<size_t>(b) * a.max_blocks;
 
+  // Independent loads first: the length, the rows of this split's blocks (one
+  // per lane), this wave's query heads and the signs.  Lane l holds query
+  // values [l EPL, (l + 1) EPL) of the wave's [G][D] query.
   int len = a.lens[b];
   int row = -1;
   {
     const int blk = s + lane * n_split;
     if (lane < a.blocks_per_split && blk < a.max_blocks) row = trow[blk];
+  }
+  constexpr int EPL = G * D / kWave;
+  uint32_t qw[(EPL + 1) / 2], sgw[EPL];  // bf16 pairs (one value: the low half); signs
+  {
+    const uint16_t* q = static_cast<const uint16_t*>(a.q) + (static_cast<size_t>(b) * a.n_q + h * G) * D + lane * EPL;
+    if constexpr (EPL == 1) qw[0] = q[0];
+    else load_words<EPL / 2>(q, qw);
+    load_words<EPL>(a.signs + (lane * EPL) % D, sgw);
   }
   const int cap_len = min(a.max_blocks, n_split * a.blocks_per_split) * kPBS;
   if (len < 0 || len > cap_len) {
@@ -197,6 +266,21 @@ __global__ __launch_bounds__(kPThreads, kPMinWaves<D>) void paged_decode_packed_
   const int nb = (len + kPBS - 1) / kPBS;
   if (s >= nb) return;  // inactive split (uniform over the workgroup)
   const int nblk = (nb - s + n_split - 1) / n_split;
+  // The layer's slab pointer tables go to LDS while the row reads are in
+  // flight, so a block's address costs one dependent global read (its row),
+  // not two; slabs past kPLdsSlabs are looked up in global memory.
+  {
+    const int n_slabs = static_cast<int>(lv.capacity_rows / lv.slab_blocks);
+    const int t = threadIdx.x;
+    uint64_t kt = 0, vt = 0;
+    if (t < n_slabs) {
+      kt = reinterpret_cast<uint64_t>(lv.k_tab[t]);
+      vt = reinterpret_cast<uint64_t>(lv.v_tab[t]);
+    }
+    s_kt[t] = kt;
+    s_vt[t] = vt;
+  }
+  __syncthreads();
   const bool row_ok = row >= 0 && row < lv.capacity_rows;
   const uint64_t ok_mask = __ballot(row_ok);
   if (h == 0 && lane < nblk && !row_ok) set_error(lv.err, PD_DEVERR_TABLE_ROW);
@@ -205,8 +289,10 @@ __global__ __launch_bounds__(kPThreads, kPMinWaves<D>) void paged_decode_packed_
     const int r = row_ok ? row : 0;  // rows outside the pool read row 0 and are masked
     const int slab = r / lv.slab_blocks;
     const size_t in_slab = static_cast<size_t>(r - slab * lv.slab_blocks);
-    kaddr = reinterpret_cast<uint64_t>(lv.k_tab[slab]) + in_slab * kPBS * KROW;
-    vaddr = reinterpret_cast<uint64_t>(lv.v_tab[slab]) + in_slab * kPBS * VROW;
+    const uint64_t kbase = slab < kPLdsSlabs ? s_kt[slab] : reinterpret_cast<uint64_t>(lv.k_tab[slab]);
+    const uint64_t vbase = slab < kPLdsSlabs ? s_vt[slab] : reinterpret_cast<uint64_t>(lv.v_tab[slab]);
+    kaddr = kbase + in_slab * kPBS * KROW;
+    vaddr = vbase + in_slab * kPBS * VROW;
   }
   constexpr int SPB = kPBS / T;  // stages per block
   const int n_stages = lv.capacity_rows > 0 ? nblk * SPB : 0;
@@ -229,10 +315,10 @@ __global__ __launch_bounds__(kPThreads, kPMinWaves<D>) void paged_decode_packed_
 
   // ---- query: widen, signs, fp32 Walsh-Hadamard transform (per wave, LDS) --
   float* sq = s_aux[h];
-  {
-    const uint16_t* q = static_cast<const uint16_t*>(a.q) + (static_cast<size_t>(b) * a.n_q + h * G) * D;
-    for (int i = lane; i < G * D; i += kWave)
-      sq[i] = __uint_as_float(static_cast<uint32_t>(q[i]) << 16) * a.signs[i % D];
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) {
+    const uint32_t qb = (e % 2) ? qw[e / 2] & 0xffff0000u : qw[e / 2] << 16;
+    sq[lane * EPL + e] = __uint_as_float(qb) * __uint_as_float(sgw[e]);
   }
   __syncthreads();
   for (int hh = 1; hh < D; hh <<= 1) {
@@ -256,21 +342,33 @@ __global__ __launch_bounds__(kPThreads, kPMinWaves<D>) void paged_decode_packed_
     for (int g = 0; g < NG; ++g)
 #pragma unroll
       for (int e = 0; e < 8; ++e)
-        aq[g][e] = static_cast<_Float16>(live ? sq[jq * D + g * 32 + J * 8 + key_value_index<KB>(e)] * qs : 0.f);
+      for (int e = 0; e < 8; ++e) {
+        const int v = J * 8 + key_value_index<KB>(e);
+        aq[g][e] = static_cast<_Float16>(live ? sq[jq * D + g * 32 + v] * qs * key_q_factor<KB>(v) : 0.f);
+      }
   }
-  // sum of q' over each group: one lane per (query head, group) into LDS,
-  // then each lane takes those of query head J of the score layout
+  // per (query head, group), one lane each, into LDS: the sum of q' (offset
+  // term) and 1024 times the sum of the A operand's f16 values (the bias the
+  // biased key codes add); each lane then takes those of query head J of the
+  // score layout
   for (int i = lane; i < G * NG; i += kWave) {
     const float* src = sq + (i / NG) * D + (i % NG) * 32;
-    float acc = 0.f;
+    float acc = 0.f, ab = 0.f;
 #pragma unroll 8
-    for (int k = 0; k < 32; ++k) acc += src[k];
+    for (int k = 0; k < 32; ++k) {
+      acc += src[k];
+      ab += static_cast<float>(static_cast<_Float16>(src[k] * qs * key_q_factor<KB>(k)));
+    }
     s_qs[h][i] = acc * qs;
+    s_kb[h][i] = ab * 1024.f;
   }
   __syncthreads();  // the per-wave area is reused for p^T below
-  float qsum[NG];
+  float qsum[NG], kbias[NG];
 #pragma unroll
-  for (int g = 0; g < NG; ++g) qsum[g] = J < G ? s_qs[h][J * NG + g] : 0.f;
+  for (int g = 0; g < NG; ++g) {
+    qsum[g] = J < G ? s_qs[h][J * NG + g] : 0.f;
+    kbias[g] = J < G ? s_kb[h][J * NG + g] : 0.f;
+  }
 
   float m_run = -INFINITY, l_run = 0.f, bias[NG];
   f4 acc[NV];  // lane l: dimension 64 i + l, register r: query head r
@@ -313,7 +411,7 @@ __global__ __launch_bounds__(kPThreads, kPMinWaves<D>) void paged_decode_packed_
         const h8 bk = key_codes<KB>(krow + g * (32 * KB / 8) + J * KB);
         const f4 c = __builtin_amdgcn_mfma_f32_16x16x32_f16(aq[g], bk, f4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
         const float2 km = *reinterpret_cast<const float2*>(krow + S::KCODE + 8 * g);
-        sv = fmaf(c[0], km.x, fmaf(km.y, qsum[g], sv));
+        sv = fmaf(c[0] - kbias[g], km.x, fmaf(km.y, qsum[g], sv));
       }
       const bool tv = J < G && t0 + lt0 + n < nt;
       const float sc = tv ? sv : -INFINITY;
@@ -322,13 +420,14 @@ __global__ __launch_bounds__(kPThreads, kPMinWaves<D>) void paged_decode_packed_
       const float p = (sc == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(sc - m_new);
       m_run = m_new;
       l_run = fmaf(l_run, alpha, p);
+      const float pk = p * kPScale;
       // value metadata of token n; invisible tokens add nothing even if it is garbage
       const unsigned char* vrow = s_stage + T * PK + (lt0 + n) * PV + h * VREC;
 #pragma unroll
       for (int g = 0; g < NG; ++g) {
         const float2 vm = *reinterpret_cast<const float2*>(vrow + S::VCODE + 8 * g);
         bias[g] = fmaf(bias[g], alpha, tv ? p * vm.y : 0.f);
-        sp[(g * 4 + J) * kSub + n] = static_cast<_Float16>(tv ? p * vm.x * kPScale : 0.f);
+        sp[(g * 4 + J) * kSub + n] = static_cast<_Float16>(tv ? pk * vm.x : 0.f);
       }
       if (__ballot(alpha != 1.f)) {
         // alpha of query head r is uniform over score row r
@@ -341,8 +440,11 @@ __global__ __launch_bounds__(kPThreads, kPMinWaves<D>) void paged_decode_packed_
       }
       __builtin_amdgcn_wave_barrier();
       // values: block lane / 4 of a 4x4x4 product; A row lane % 4 is query
-      // head lane % 4; the B/C column of lane l is dimension vdim(i, l)
+      // head lane % 4 (rows of absent query heads hold zeros); the B/C column
+      // of lane l is dimension vdim(i, l)
       const int qa = lane % 4;
+      // 4-bit codes, 64 dimensions: the nibble of this lane, in place
+      const uint32_t nib_mask = lane < 32 ? 0x000f000fu : 0x00f000f0u;
 #pragma unroll
       for (int tq = 0; tq < kSub / 4; ++tq) {
         const unsigned char* vtok = s_stage + T * PK + (lt0 + 4 * tq) * PV + h * VREC;
@@ -350,21 +452,20 @@ __global__ __launch_bounds__(kPThreads, kPMinWaves<D>) void paged_decode_packed_
 #pragma unroll
           for (int i = 0; i < NV; ++i) {
             const int d = 64 * i + lane;
-            const h4 ap = qa < G ? *reinterpret_cast<const h4*>(sp + (d / 32 * 4 + qa) * kSub + 4 * tq) : h4{};
-            const uint32_t c0 = vtok[d], c1 = vtok[PV + d], c2 = vtok[2 * PV + d], c3 = vtok[3 * PV + d];
-            const uint32_t u2[2] = {bytes_to_f16x2(c0 | (c1 << 8), kSelB01), bytes_to_f16x2(c2 | (c3 << 8), kSelB01)};
+            const h4 ap = *reinterpret_cast<const h4*>(sp + (d / 32 * 4 + qa) * kSub + 4 * tq);
+            uint32_t x01, x23;
+            byte_column<PV>(vtok + d, x01, x23);
+            const uint32_t u2[2] = {unbias(x01 | kBias2), unbias(x23 | kBias2)};
             acc[i] = __builtin_amdgcn_mfma_f32_4x4x4f16(ap, __builtin_bit_cast(h4, u2), acc[i], 0, 0, 0);
           }
         } else if constexpr (NV == 1) {
           // 4-bit codes, 64 dimensions: lane l takes code byte l % 32 of the 4
           // tokens and its low (l < 32) or high nibble: dimension vdim(0, l)
           const int bi = lane % 32;
-          const h4 ap = qa < G ? *reinterpret_cast<const h4*>(sp + (bi / 16 * 4 + qa) * kSub + 4 * tq) : h4{};
-          const uint32_t w = vtok[bi] | (static_cast<uint32_t>(vtok[PV + bi]) << 8) |
-                             (static_cast<uint32_t>(vtok[2 * PV + bi]) << 16) |
-                             (static_cast<uint32_t>(vtok[3 * PV + bi]) << 24);
-          const uint32_t v = (w >> (4 * (lane / 32))) & 0x0f0f0f0fu;
-          const uint32_t u2[2] = {bytes_to_f16x2(v, kSelB01), bytes_to_f16x2(v, kSelB23)};
+          const h4 ap = *reinterpret_cast<const h4*>(sp + (bi / 16 * 4 + qa) * kSub + 4 * tq);
+          uint32_t x01, x23;
+          byte_column<PV>(vtok + bi, x01, x23);
+          const uint32_t u2[2] = {unbias((x01 & nib_mask) | kBias2), unbias((x23 & nib_mask) | kBias2)};
           acc[0] = __builtin_amdgcn_mfma_f32_4x4x4f16(ap, __builtin_bit_cast(h4, u2), acc[0], 0, 0, 0);
         } else {
           // 4-bit codes: lane l takes code byte l + 64 k of the 4 tokens, whose
@@ -373,13 +474,11 @@ __global__ __launch_bounds__(kPThreads, kPMinWaves<D>) void paged_decode_packed_
 #pragma unroll
           for (int k = 0; k < NV / 2; ++k) {
             const int bi = lane + 64 * k;
-            const h4 ap = qa < G ? *reinterpret_cast<const h4*>(sp + (bi / 16 * 4 + qa) * kSub + 4 * tq) : h4{};
-            const uint32_t w = vtok[bi] | (static_cast<uint32_t>(vtok[PV + bi]) << 8) |
-                               (static_cast<uint32_t>(vtok[2 * PV + bi]) << 16) |
-                               (static_cast<uint32_t>(vtok[3 * PV + bi]) << 24);
-            const uint32_t lo = w & 0x0f0f0f0fu, hi = (w >> 4) & 0x0f0f0f0fu;
-            const uint32_t ul[2] = {bytes_to_f16x2(lo, kSelB01), bytes_to_f16x2(lo, kSelB23)};
-            const uint32_t uh[2] = {bytes_to_f16x2(hi, kSelB01), bytes_to_f16x2(hi, kSelB23)};
+            const h4 ap = *reinterpret_cast<const h4*>(sp + (bi / 16 * 4 + qa) * kSub + 4 * tq);
+            uint32_t x01, x23;
+            byte_column<PV>(vtok + bi, x01, x23);
+            const uint32_t ul[2] = {unbias((x01 & 0x000f000fu) | kBias2), unbias((x23 & 0x000f000fu) | kBias2)};
+            const uint32_t uh[2] = {unbias((x01 & 0x00f000f0u) | kBias2), unbias((x23 & 0x00f000f0u) | kBias2)};
             acc[2 * k] = __builtin_amdgcn_mfma_f32_4x4x4f16(ap, __builtin_bit_cast(h4, ul), acc[2 * k], 0, 0, 0);
             acc[2 * k + 1] = __builtin_amdgcn_mfma_f32_4x4x4f16(ap, __builtin_bit_cast(h4, uh), acc[2 * k + 1], 0, 0, 0);
           }
@@ -412,7 +511,7 @@ __global__ __launch_bounds__(kPThreads, kPMinWaves<D>) void paged_decode_packed_
       float bsel = 0.f;
 #pragma unroll
       for (int g = 0; g < NG; ++g) bsel = d / 32 == g ? bq[g] : bsel;
-      part_acc[d] = fmaf(acc[i][r], 1.f / kPScale, bsel);
+      part_acc[d] = fmaf(acc[i][r], vacc_scale<VB, NV>(i, lane), bsel);
     }
     if (lane == kSub * r) {
       a.partials[a.ml_offset + hs * 2] = m_run;

@@ -23,12 +23,13 @@ pytestmark = pytest.mark.gpu
 BS = 32
 
 
-def _packed_pool(fmt, D, lengths, rows, seed, cap, n_kv=8, keep=None):
+def _packed_pool(fmt, D, lengths, rows, seed, cap, n_kv=8, keep=None, slab_blocks=32):
     """Write every sequence through the quantising write_block; return the pool,
     the oracle's records of the sequences in `keep` and the sign vector."""
     kb, vb = FORMATS[fmt]
     signs = hadamard_signs(seed, D)
-    pool = pd.SlabPool(1, BS, n_kv, D, 32, -(-cap // 32) + 2, fmt, hadamard_signs=signs)
+    pool = pd.SlabPool(1, BS, n_kv, D, slab_blocks, -(-cap // slab_blocks) + 2, fmt,
+                       hadamard_signs=signs)
     pool.reserve_rows(cap)
     recs = {}
     for b, n in enumerate(lengths):
@@ -93,6 +94,33 @@ def test_packed_decode_matches_oracle(fmt, D, G):
     long = [b for b, n in enumerate(lengths) if n >= 300]
     assert_decode_close(got[long], ref[long], "bf16")
     assert not got[3].any()
+    assert pool.check_error() == 0
+    pool.close()
+
+
+@pytest.mark.parametrize("fmt,D,G", [("k8v4", 64, 4), ("k4v4", 256, 2)])
+def test_packed_decode_with_more_slabs_than_its_lds_table(fmt, D, G):
+    """The packed kernel stages the first 512 slab base pointers of a layer in
+    LDS and reads the rest from the pool's table in global memory: one-row
+    slabs and a shuffled free list put blocks in slabs on both sides."""
+    lengths = [12000, 5000, 3000, 1]
+    rows, _, R = shuffled_rows(np.random.default_rng(7 + D), lengths, BS, 1, spare_rows=8)
+    table = make_block_table(rows)
+    assert int(table.max()) >= 512 and int(table[table >= 0].min()) < 512
+    pool, recs, signs = _packed_pool(fmt, D, lengths, rows, 90 + D, R, slab_blocks=1)
+    B = len(lengths)
+    q = q_bits(90 + D, 0, B, 8 * G, D, "bf16")
+    scale = 1.0 / np.sqrt(D)
+    ref = packed_decode_attention(q, [recs[b][0] for b in range(B)], [recs[b][1] for b in range(B)],
+                                  signs, fmt, D, scale)
+    qd = to_device_bits(q, "bf16")
+    out = torch.empty_like(qd)
+    ws = pool.workspace(B, 8 * G, max(lengths))
+    pool.paged_decode(0, qd, i32(table), i32(lengths), max(lengths), scale, out, ws)
+    got = from_device_bits(out)
+    err = assert_decode_close(got, ref, "bf16", allow_output_rounding=True)
+    assert_decode_close(got[:3], ref[:3], "bf16")
+    print(f"packed {fmt} D={D}, {R} one-row slabs: max-abs {err:.2e}")
     assert pool.check_error() == 0
     pool.close()
 

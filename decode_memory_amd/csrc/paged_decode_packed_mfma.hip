@@ -60,6 +60,11 @@ namespace {
 #ifndef PAGEDKV_PMFMA_TARGET_WG
 #define PAGEDKV_PMFMA_TARGET_WG 256
 #endif
+// Token quads of the value products are scheduled one at a time (a
+// scheduling barrier after each) from this many value accumulators up.
+#ifndef PAGEDKV_PMFMA_QUAD_BARRIER_NV
+#define PAGEDKV_PMFMA_QUAD_BARRIER_NV 1
+#endif
 
 constexpr int kPWaves = 8;  // one wave per kv head; packed pools have 8
 constexpr int kPThreads = kPWaves * kWave;
@@ -485,7 +490,7 @@ __global__ __launch_bounds__(kPThreads, kPMinWaves<D>) void paged_decode_packed_
         }
         // keep each token quad's loads next to their products (bounds the
         // registers the scheduler would otherwise spend hoisting them)
-        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (NV >= PAGEDKV_PMFMA_QUAD_BARRIER_NV) __builtin_amdgcn_sched_barrier(0);
       }
       __builtin_amdgcn_wave_barrier();
     }

@@ -5,7 +5,9 @@ workspace admission"), section "Summary" and the "After" flowchart:
 
 * formats K8/V8, K8/V4, K4/V4 (bits of the K codes / bits of the V codes);
 * token-local affine groups with FP32 scale/offset metadata -- here groups of
-  32 consecutive values along head_dim of one token-head vector;
+  32 consecutive values along head_dim of one token-head vector (the packed
+  workload), or of 64 (the reading under which K4/V4 costs the five effective
+  bits per value and the 3.2x reduction the Summary states);
 * a fixed signed Hadamard basis for Q and K: K is rotated before it is
   quantised and the query gets the same rotation, so q'.k' = q.k; V is stored
   unrotated, so the attention output needs no inverse rotation;
@@ -78,14 +80,14 @@ def rotate_fp32(x: np.ndarray, signs: np.ndarray) -> np.ndarray:
     return (y * inv_sqrt_f32(d)).astype(np.float32)
 
 
-def quantise(x: np.ndarray, bits: int) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
-    """Affine group quantiser over groups of 32 along the last axis (fp32 ops).
+def quantise(x: np.ndarray, bits: int, group: int = GROUP) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """Affine group quantiser over groups of `group` along the last axis (fp32 ops).
 
-    Returns (codes uint8 [..., D], scale float32 [..., D/32], offset float32 [..., D/32])."""
+    Returns (codes uint8 [..., D], scale float32 [..., D/group], offset float32 [..., D/group])."""
     x = np.asarray(x, dtype=np.float32)
     d = x.shape[-1]
-    assert d % GROUP == 0
-    g = x.reshape(x.shape[:-1] + (d // GROUP, GROUP))
+    assert d % group == 0
+    g = x.reshape(x.shape[:-1] + (d // group, group))
     mn = g.min(axis=-1)
     mx = g.max(axis=-1)
     levels = np.float32((1 << bits) - 1)
@@ -98,9 +100,10 @@ def quantise(x: np.ndarray, bits: int) -> Tuple[np.ndarray, np.ndarray, np.ndarr
 
 
 def dequantise(codes: np.ndarray, scale: np.ndarray, offset: np.ndarray) -> np.ndarray:
-    """code * scale + offset, float64, per group of 32."""
+    """code * scale + offset, float64, per group (D / number of scales values)."""
     d = codes.shape[-1]
-    c = codes.astype(np.float64).reshape(codes.shape[:-1] + (d // GROUP, GROUP))
+    ng = scale.shape[-1]
+    c = codes.astype(np.float64).reshape(codes.shape[:-1] + (ng, d // ng))
     x = c * scale.astype(np.float64)[..., None] + offset.astype(np.float64)[..., None]
     return x.reshape(codes.shape)
 
@@ -124,7 +127,7 @@ def pack(codes: np.ndarray, scale: np.ndarray, offset: np.ndarray, bits: int) ->
     return np.concatenate([payload.astype(np.uint8), meta_bytes], axis=-1)
 
 
-def unpack(records: np.ndarray, head_dim: int, bits: int):
+def unpack(records: np.ndarray, head_dim: int, bits: int, group: int = GROUP):
     """uint8 records -> (codes uint8 [..., D], scale f32, offset f32)."""
     records = np.ascontiguousarray(records, dtype=np.uint8)
     nbytes = head_dim * bits // 8
@@ -136,32 +139,32 @@ def unpack(records: np.ndarray, head_dim: int, bits: int):
         codes[..., 0::2] = payload & 0x0F
         codes[..., 1::2] = payload >> 4
     meta = np.ascontiguousarray(records[..., nbytes:]).view("<f4")
-    meta = meta.reshape(records.shape[:-1] + (head_dim // GROUP, 2))
+    meta = meta.reshape(records.shape[:-1] + (head_dim // group, 2))
     return codes, meta[..., 0].astype(np.float32), meta[..., 1].astype(np.float32)
 
 
-def k_records(k_bits: np.ndarray, signs: np.ndarray, bits: int) -> np.ndarray:
+def k_records(k_bits: np.ndarray, signs: np.ndarray, bits: int, group: int = GROUP) -> np.ndarray:
     """bf16 K [..., D] -> packed records of the rotated K (quantised once, at write)."""
     k = widen(k_bits, "bf16").astype(np.float32)  # exact
-    codes, scale, offset = quantise(rotate_fp32(k, signs), bits)
+    codes, scale, offset = quantise(rotate_fp32(k, signs), bits, group)
     return pack(codes, scale, offset, bits)
 
 
-def v_records(v_bits: np.ndarray, bits: int) -> np.ndarray:
+def v_records(v_bits: np.ndarray, bits: int, group: int = GROUP) -> np.ndarray:
     """bf16 V [..., D] -> packed records of V (unrotated)."""
     v = widen(v_bits, "bf16").astype(np.float32)
-    codes, scale, offset = quantise(v, bits)
+    codes, scale, offset = quantise(v, bits, group)
     return pack(codes, scale, offset, bits)
 
 
-def dequantise_records(records: np.ndarray, head_dim: int, bits: int) -> np.ndarray:
-    codes, scale, offset = unpack(records, head_dim, bits)
+def dequantise_records(records: np.ndarray, head_dim: int, bits: int, group: int = GROUP) -> np.ndarray:
+    codes, scale, offset = unpack(records, head_dim, bits, group)
     return dequantise(codes, scale, offset)
 
 
 def packed_decode_attention(q_bits: np.ndarray, k_recs: Sequence[np.ndarray],
                             v_recs: Sequence[np.ndarray], signs: np.ndarray, fmt: str,
-                            head_dim: int, scale: float) -> np.ndarray:
+                            head_dim: int, scale: float, group: int = GROUP) -> np.ndarray:
     """Decode attention reading packed pages.
 
     q_bits: bf16 [B, n_q, D]; k_recs[b], v_recs[b]: uint8 [len_b, n_kv, rec].
@@ -169,6 +172,6 @@ def packed_decode_attention(q_bits: np.ndarray, k_recs: Sequence[np.ndarray],
     values are the dequantised records; the rest is the fp64 definition."""
     kbits, vbits = FORMATS[fmt]
     q_rot = rotate_exact(widen(q_bits, "bf16"), signs)
-    ks = [dequantise_records(k, head_dim, kbits) for k in k_recs]
-    vs = [dequantise_records(v, head_dim, vbits) for v in v_recs]
+    ks = [dequantise_records(k, head_dim, kbits, group) for k in k_recs]
+    vs = [dequantise_records(v, head_dim, vbits, group) for v in v_recs]
     return decode_attention(q_rot, ks, vs, scale)

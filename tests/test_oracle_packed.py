@@ -77,33 +77,51 @@ def test_inv_sqrt_exact_for_powers_of_four():
 
 
 @pytest.mark.parametrize("bits", [4, 8])
-def test_quantiser_error_bound_and_end_codes(bits):
+@pytest.mark.parametrize("group", [32, 64])
+def test_quantiser_error_bound_and_end_codes(bits, group):
     rng = np.random.default_rng(bits)
-    x = rng.standard_normal((200, 64)).astype(np.float32)
-    codes, scale, offset = quantise(x, bits)
+    x = rng.standard_normal((200, 128)).astype(np.float32)
+    ng = 128 // group
+    codes, scale, offset = quantise(x, bits, group)
+    assert scale.shape == (200, ng) and offset.shape == (200, ng)
     assert codes.max() <= (1 << bits) - 1
     xh = dequantise(codes, scale, offset)
-    step = np.repeat(scale.astype(np.float64), GROUP, axis=-1)
+    step = np.repeat(scale.astype(np.float64), group, axis=-1)
     assert (np.abs(xh - x) <= step / 2 * (1 + 1e-5) + 1e-6).all()
-    g = x.reshape(200, 2, GROUP)
-    c = codes.reshape(200, 2, GROUP)
-    assert (c[np.arange(200)[:, None], np.arange(2)[None], g.argmin(-1)] == 0).all()
-    assert (c[np.arange(200)[:, None], np.arange(2)[None], g.argmax(-1)] == (1 << bits) - 1).all()
+    g = x.reshape(200, ng, group)
+    c = codes.reshape(200, ng, group)
+    assert (c[np.arange(200)[:, None], np.arange(ng)[None], g.argmin(-1)] == 0).all()
+    assert (c[np.arange(200)[:, None], np.arange(ng)[None], g.argmax(-1)] == (1 << bits) - 1).all()
     assert np.array_equal(offset, g.min(-1))
 
 
+def test_group_of_64_shares_one_scale_over_a_ramp():
+    """x_i = i over one group of 64 at 4 bits: one (scale, offset) = (63/15, 0)
+    for the whole group, and code i = rint(i / scale); groups of 32 would give
+    two ranges (0..31, 32..63) instead."""
+    x = np.arange(64, dtype=np.float32)[None]
+    codes, scale, offset = quantise(x, 4, 64)
+    assert scale.shape == (1, 1) and scale[0, 0] == np.float32(63) / np.float32(15)
+    assert offset[0, 0] == 0
+    expect = np.rint(x[0].astype(np.float32) / scale[0, 0]).astype(np.uint8)
+    assert np.array_equal(codes[0], expect) and codes[0, -1] == 15 and codes[0, 0] == 0
+    c32, s32, o32 = quantise(x, 4, 32)
+    assert np.array_equal(o32[0], [0, 32]) and (s32[0] == np.float32(31) / np.float32(15)).all()
+
+
 @settings(max_examples=200, deadline=None)
-@given(st.lists(st.floats(-4, 4, width=32), min_size=GROUP, max_size=GROUP), st.sampled_from([4, 8]))
-def test_quantiser_picks_nearest_level_brute_force(vals, bits):
-    x = np.array(vals, dtype=np.float32)[None]
-    codes, scale, offset = quantise(x, bits)
+@given(st.lists(st.floats(-4, 4, width=32), min_size=64, max_size=64), st.sampled_from([4, 8]),
+       st.sampled_from([32, 64]))
+def test_quantiser_picks_nearest_level_brute_force(vals, bits, group):
+    x = np.array(vals[:group], dtype=np.float32)[None]
+    codes, scale, offset = quantise(x, bits, group)
     if scale[0, 0] == 0:
         assert not codes.any()
         return
     levels = np.arange(1 << bits) * np.float64(scale[0, 0]) + np.float64(offset[0, 0])
     dist = np.abs(x[0][:, None].astype(np.float64) - levels[None, :])
     best = dist.min(axis=1)
-    chosen = dist[np.arange(GROUP), codes[0]]
+    chosen = dist[np.arange(group), codes[0]]
     # the chosen level is the nearest one, up to fp32 rounding of (x - mn)/scale
     assert (chosen <= best + 1e-6 * (1 + np.abs(x[0]))).all()
 
@@ -117,14 +135,16 @@ def test_constant_group_is_exact():
 
 
 @pytest.mark.parametrize("bits", [4, 8])
-def test_pack_unpack_round_trip_and_nibble_order(bits):
+@pytest.mark.parametrize("group", [32, 64])
+def test_pack_unpack_round_trip_and_nibble_order(bits, group):
     rng = np.random.default_rng(10)
+    ng = 64 // group
     codes = rng.integers(0, 1 << bits, size=(4, 3, 64)).astype(np.uint8)
-    scale = rng.standard_normal((4, 3, 2)).astype(np.float32)
-    offset = rng.standard_normal((4, 3, 2)).astype(np.float32)
+    scale = rng.standard_normal((4, 3, ng)).astype(np.float32)
+    offset = rng.standard_normal((4, 3, ng)).astype(np.float32)
     rec = pack(codes, scale, offset, bits)
-    assert rec.shape[-1] == record_bytes(64, bits)
-    c2, s2, o2 = unpack(rec, 64, bits)
+    assert rec.shape[-1] == record_bytes(64, bits, group) == 64 * bits // 8 + 8 * ng
+    c2, s2, o2 = unpack(rec, 64, bits, group)
     assert np.array_equal(c2, codes) and np.array_equal(s2, scale) and np.array_equal(o2, offset)
     one = pack((np.arange(64)[None] % (1 << bits)).astype(np.uint8), np.ones((1, 2), np.float32),
                np.zeros((1, 2), np.float32), bits)
@@ -146,14 +166,15 @@ def test_golden_effective_bits():
 
 
 @pytest.mark.parametrize("fmt,tol", [("k8v8", 0.01), ("k8v4", 0.06), ("k4v4", 0.08)])
-@pytest.mark.parametrize("d", [64, 256])
-def test_packed_decode_approximates_bf16_attention(fmt, tol, d):
+@pytest.mark.parametrize("d,group", [(64, 32), (256, 32), (128, 64), (256, 64)])
+def test_packed_decode_approximates_bf16_attention(fmt, tol, d, group):
     """The packed route reproduces bf16 attention up to quantisation error.
 
     A wrong rotation of q (missing, other signs), a wrong nibble order or a
     wrong metadata order makes the error O(0.1 .. 1); quantisation alone keeps
     it below the per-format bound (the bound is looser at 4 bits: 15 levels
-    over the range of a group of 32 N(0,1) values is a step of about 0.3)."""
+    over the range of a group of 32 or 64 N(0,1) values is a step of about
+    0.3)."""
     B, n_kv, G, n = 2, 2, 4, 300
     signs = hadamard_signs(5, d)
     kb, vb = FORMATS[fmt]
@@ -163,34 +184,36 @@ def test_packed_decode_approximates_bf16_attention(fmt, tol, d):
         k, v = kv_bits_for_sequence(5, 0, b, n, n_kv, d, "bf16")
         ks.append(k)
         vs.append(v)
-        krs.append(k_records(k, signs, kb))
-        vrs.append(v_records(v, vb))
+        krs.append(k_records(k, signs, kb, group))
+        vrs.append(v_records(v, vb, group))
     ref = decode_attention_bits(q, ks, vs, "bf16", 1 / np.sqrt(d))
-    got = packed_decode_attention(q, krs, vrs, signs, fmt, d, 1 / np.sqrt(d))
+    got = packed_decode_attention(q, krs, vrs, signs, fmt, d, 1 / np.sqrt(d), group)
     err = np.abs(got - ref).max()
     assert err < tol, err
 
 
-def test_packed_decode_is_exact_when_quantisation_is_exact():
+@pytest.mark.parametrize("d,group", [(64, 32), (128, 64)])
+def test_packed_decode_is_exact_when_quantisation_is_exact(d, group):
     """Keys and values whose rotated / plain groups sit on an exact 8-bit grid
     reconstruct exactly, so packed attention equals the plain definition."""
-    d, n = 64, 40
+    n = 40
     signs = hadamard_signs(6, d)
     rng = np.random.default_rng(11)
     # V: integers 0..255 with both ends present in every group -> scale 1, offset 0
     v_int = rng.integers(0, 256, size=(n, 1, d)).astype(np.float32)
-    v_int[:, :, 0::GROUP] = 0
-    v_int[:, :, 1::GROUP] = 255
+    v_int[:, :, 0::group] = 0
+    v_int[:, :, 1::group] = 255
     vbits = bf16_bits_from_f32(v_int)  # integers < 256 are exact in bf16
-    v_rec = v_records(vbits, 8)
-    assert np.array_equal(dequantise_records(v_rec, d, 8), v_int.astype(np.float64))
+    v_rec = v_records(vbits, 8, group)
+    assert np.array_equal(dequantise_records(v_rec, d, 8, group), v_int.astype(np.float64))
     kbits = bf16_bits_from_f32(rng.standard_normal((n, 1, d)).astype(np.float32))
     qb = bf16_bits_from_f32(rng.standard_normal((1, 1, d)).astype(np.float32))
-    k_rec = k_records(kbits, signs, 8)
-    got = packed_decode_attention(qb, [k_rec], [v_rec], signs, "k8v8", d, 0.125)
+    k_rec = k_records(kbits, signs, 8, group)
+    scale = 1 / np.sqrt(d)
+    got = packed_decode_attention(qb, [k_rec], [v_rec], signs, "k8v8", d, scale, group)
     # the same keys, dequantised and rotated back (H is symmetric and
     # H H = d I, so x = sigma * (H x') / sqrt(d)), through the plain definition
-    khat = dequantise_records(k_rec, d, 8)
+    khat = dequantise_records(k_rec, d, 8, group)
     k_back = (khat @ sylvester_hadamard(d)) / np.sqrt(d) * signs
-    ref = decode_attention(widen(qb, "bf16"), [k_back], [v_int.astype(np.float64)], 0.125)
+    ref = decode_attention(widen(qb, "bf16"), [k_back], [v_int.astype(np.float64)], scale)
     np.testing.assert_allclose(got, ref, rtol=0, atol=1e-9)

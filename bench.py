@@ -662,66 +662,77 @@ def run_packed(args, torch, pd):
     all_rows = torch.as_tensor(np.concatenate([r[t_tok // bs] for r in rows]).astype(np.int32), device=dev)
     all_slots = torch.as_tensor(np.tile((t_tok % bs).astype(np.int32), B), device=dev)
     timer = Timer(torch)
+
+    def measure(D, fmt, group):
+        """One pool of one format and group size: fill, time write_block, the
+        whole decode call and its two stages."""
+        scale = 1.0 / float(np.sqrt(D))
+        signs = hadamard_signs(w.seed, D) if fmt != "bf16" else None
+        k_rec, v_rec = pd.record_bytes(pd.FORMAT_NAMES[fmt], D, group)
+        kv_bytes = B * n * n_kv * (k_rec + v_rec)
+        copies = max(2, -(-3 * MALL_BYTES // kv_bytes))  # rotate past the last-level cache
+        pool = pd.SlabPool(copies, bs, n_kv, D, S, -(-cap // S) + 1, fmt, hadamard_signs=signs,
+                           device=dev, group_size=group)
+        pool.reserve_rows(cap)
+        for layer in range(copies):
+            k = normal_device((w.seed, D, layer, 0), (B * n, n_kv, D), "bf16", dev)
+            v = normal_device((w.seed, D, layer, 1), (B * n, n_kv, D), "bf16", dev)
+            pool.write_block(layer, all_rows, all_slots, k, v)
+            if layer < copies - 1:
+                del k, v
+        # the write of a whole layer (16 x 16384 tokens; packed formats
+        # rotate K and quantise K and V here), rewriting the same values
+        wb_us = timer(lambda: pool.write_block(copies - 1, all_rows, all_slots, k, v), 3)
+        wb_bytes = 2 * B * n * n_kv * D * 2 + kv_bytes + B * n * 8
+        del k, v
+        q = normal_device((w.seed, D, 2), (B, n_q, D), "bf16", dev)
+        out = torch.empty_like(q)
+        ws = pool.workspace(B, n_q, n)
+        torch.cuda.synchronize()
+        if pool.check_error():
+            raise RuntimeError(f"device error while filling the {fmt} D={D} group {group} pool")
+        it = iter(range(1 << 30))
+
+        def call():
+            pool.paged_decode(next(it) % copies, q, table, lens, n, scale, out, ws)
+
+        for _ in range(args.warmup):
+            call()
+        us = timer(call, max(args.steps, copies))
+
+        def decode_call(layer, stage):
+            pool.paged_decode(layer, q, table, lens, n, scale, out, ws, stage=stage)
+
+        split_us, combine_us = stage_times(timer, decode_call, range(copies),
+                                           max(2, args.steps // copies), torch)
+        if pool.check_error():
+            raise RuntimeError(f"device error during the {fmt} D={D} group {group} timing")
+        pool.close()
+        d_bytes = decode_bytes(lengths, n_kv, n_q, D, bs, k_rec + v_rec)
+        return {
+            "us_per_call": round(us, 2), "split_us": round(split_us, 2),
+            "combine_us": round(combine_us, 2), "kv_bytes": kv_bytes,
+            "algorithmic_bytes": d_bytes,
+            "bits_per_value": round(8 * (k_rec + v_rec) / (2 * D), 3),
+            "split_gbs": round(d_bytes / (split_us * 1e-6) / 1e9, 1),
+            "split_pct_of_peak": round(100.0 * d_bytes / (split_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 2),
+            "call_gbs": round(d_bytes / (us * 1e-6) / 1e9, 1),
+            "kv_tokens_attended_per_s": round(B * n / (us * 1e-6), 1),
+            "pool_copies": copies,
+            "write_block_us": round(wb_us, 2), "write_block_bytes": wb_bytes,
+            "write_block_gbs": round(wb_bytes / (wb_us * 1e-6) / 1e9, 1),
+        }
+
+    # the workload: every head_dim, bf16 and the packed formats with groups of 32
     per, tot_bytes, tot_us = {}, 0, 0.0
     for D in w.head_dims:
-        scale = 1.0 / float(np.sqrt(D))
         for fmt in ("bf16",) + tuple(w.formats):
-            signs = hadamard_signs(w.seed, D) if fmt != "bf16" else None
-            k_rec, v_rec = pd.record_bytes(pd.FORMAT_NAMES[fmt], D)
-            kv_bytes = B * n * n_kv * (k_rec + v_rec)
-            copies = max(2, -(-3 * MALL_BYTES // kv_bytes))  # rotate past the last-level cache
-            pool = pd.SlabPool(copies, bs, n_kv, D, S, -(-cap // S) + 1, fmt, hadamard_signs=signs,
-                               device=dev)
-            pool.reserve_rows(cap)
-            for layer in range(copies):
-                k = normal_device((w.seed, D, layer, 0), (B * n, n_kv, D), "bf16", dev)
-                v = normal_device((w.seed, D, layer, 1), (B * n, n_kv, D), "bf16", dev)
-                pool.write_block(layer, all_rows, all_slots, k, v)
-                if layer < copies - 1:
-                    del k, v
-            # the write of a whole layer (16 x 16384 tokens; packed formats
-            # rotate K and quantise K and V here), rewriting the same values
-            wb_us = timer(lambda: pool.write_block(copies - 1, all_rows, all_slots, k, v), 3)
-            wb_bytes = 2 * B * n * n_kv * D * 2 + kv_bytes + B * n * 8
-            del k, v
-            q = normal_device((w.seed, D, 2), (B, n_q, D), "bf16", dev)
-            out = torch.empty_like(q)
-            ws = pool.workspace(B, n_q, n)
-            torch.cuda.synchronize()
-            if pool.check_error():
-                raise RuntimeError(f"device error while filling the {fmt} D={D} pool")
-            it = iter(range(1 << 30))
-
-            def call():
-                pool.paged_decode(next(it) % copies, q, table, lens, n, scale, out, ws)
-
-            for _ in range(args.warmup):
-                call()
-            us = timer(call, max(args.steps, copies))
-
-            def decode_call(layer, stage):
-                pool.paged_decode(layer, q, table, lens, n, scale, out, ws, stage=stage)
-
-            split_us, combine_us = stage_times(timer, decode_call, range(copies),
-                                               max(2, args.steps // copies), torch)
-            if pool.check_error():
-                raise RuntimeError(f"device error during the {fmt} D={D} timing")
-            pool.close()
-            d_bytes = decode_bytes(lengths, n_kv, n_q, D, bs, k_rec + v_rec)
-            tot_bytes += d_bytes
-            tot_us += us
-            per[f"{fmt}_d{D}"] = {
-                "us_per_call": round(us, 2), "split_us": round(split_us, 2),
-                "combine_us": round(combine_us, 2), "kv_bytes": kv_bytes,
-                "algorithmic_bytes": d_bytes,
-                "split_gbs": round(d_bytes / (split_us * 1e-6) / 1e9, 1),
-                "split_pct_of_peak": round(100.0 * d_bytes / (split_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 2),
-                "call_gbs": round(d_bytes / (us * 1e-6) / 1e9, 1),
-                "kv_tokens_attended_per_s": round(B * n / (us * 1e-6), 1),
-                "pool_copies": copies,
-                "write_block_us": round(wb_us, 2), "write_block_bytes": wb_bytes,
-                "write_block_gbs": round(wb_bytes / (wb_us * 1e-6) / 1e9, 1),
-            }
+            r = measure(D, fmt, 0 if fmt == "bf16" else 32)
+            per[f"{fmt}_d{D}"] = r
+            tot_bytes += r["algorithmic_bytes"]
+            tot_us += r["us_per_call"]
+    # beside it: groups of 64 at head_dim 256 (K4/V4 at five bits per value)
+    group64 = {f"{fmt}_d256": measure(256, fmt, 64) for fmt in w.formats} if 256 in w.head_dims else {}
     value = tot_bytes / (tot_us * 1e-6) / 1e9
     worst = min((k for k in per if not k.startswith("bf16")), key=lambda k: per[k]["split_gbs"])
     result = base_result(args, value, tot_us / 1e3, "bf16 q, packed K/V, fp32 accumulate", {
@@ -739,6 +750,7 @@ def run_packed(args, torch, pd):
                      "algorithmic_bytes_per_launch": p["algorithmic_bytes"],
                      "avg_launch_us": p["split_us"]},
         "formats": per,
+        "group64_formats": group64,
     })
     result["cpu_baseline"] = cpu_baseline_packed(w, args.cpu_seconds) if args.cpu_seconds > 0 else None
     return result

@@ -45,7 +45,8 @@ class PoolDesc(ctypes.Structure):
     _fields_ = [("n_layers", ctypes.c_int32), ("block_size", ctypes.c_int32),
                 ("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
                 ("slab_blocks", ctypes.c_int32), ("max_slabs", ctypes.c_int32),
-                ("format", ctypes.c_int32), ("hadamard_signs", ctypes.POINTER(ctypes.c_int8))]
+                ("format", ctypes.c_int32), ("hadamard_signs", ctypes.POINTER(ctypes.c_int8)),
+                ("group_size", ctypes.c_int32)]
 
 
 class PoolStats(ctypes.Structure):
@@ -105,7 +106,7 @@ def _declare(lib):
     sig = {
         "pd_version": (_i32, []),
         "pd_last_error": (ctypes.c_char_p, []),
-        "pd_record_bytes": (_i32, [_i32, _i32, _p_i32, _p_i32]),
+        "pd_record_bytes": (_i32, [_i32, _i32, _i32, _p_i32, _p_i32]),
         "pd_pool_create": (_i32, [ctypes.POINTER(PoolDesc), ctypes.POINTER(_vp)]),
         "pd_pool_destroy": (_i32, [_vp]),
         "pd_slab_bytes": (_i32, [_vp, ctypes.POINTER(_sz), ctypes.POINTER(_sz)]),
@@ -192,20 +193,22 @@ def version() -> int:
     return lib().pd_version()
 
 
-def record_bytes(fmt: int, head_dim: int):
+def record_bytes(fmt: int, head_dim: int, group_size: int = 0):
+    """Bytes of one K and one V token-head record (group_size 0: 32)."""
     k, v = ctypes.c_int32(), ctypes.c_int32()
-    _check(lib().pd_record_bytes(fmt, head_dim, ctypes.byref(k), ctypes.byref(v)))
+    _check(lib().pd_record_bytes(fmt, head_dim, group_size, ctypes.byref(k), ctypes.byref(v)))
     return k.value, v.value
 
 
 def pool_create(n_layers, block_size, n_kv_heads, head_dim, slab_blocks, max_slabs, fmt,
-                hadamard_signs=None) -> int:
+                hadamard_signs=None, group_size=0) -> int:
     signs_buf = None
     if hadamard_signs is not None:
         vals = [int(x) for x in hadamard_signs]
         signs_buf = (ctypes.c_int8 * len(vals))(*vals)
     desc = PoolDesc(n_layers, block_size, n_kv_heads, head_dim, slab_blocks, max_slabs, fmt,
-                    ctypes.cast(signs_buf, ctypes.POINTER(ctypes.c_int8)) if signs_buf else None)
+                    ctypes.cast(signs_buf, ctypes.POINTER(ctypes.c_int8)) if signs_buf else None,
+                    group_size)
     out = ctypes.c_void_p()
     _check(lib().pd_pool_create(ctypes.byref(desc), ctypes.byref(out)))
     return out.value
@@ -439,16 +442,17 @@ class SlabPool:
 
     def __init__(self, n_layers: int, block_size: int, n_kv_heads: int, head_dim: int,
                  slab_blocks: int, max_slabs: int, fmt="bf16", hadamard_signs=None,
-                 device="cuda"):
+                 device="cuda", group_size=0):
         self.fmt = FORMAT_NAMES[fmt] if isinstance(fmt, str) else int(fmt)
         self.n_layers, self.block_size, self.n_kv_heads = n_layers, block_size, n_kv_heads
         self.head_dim, self.slab_blocks, self.max_slabs = head_dim, slab_blocks, max_slabs
         self.device = torch.device(device)
         with torch.cuda.device(self.device):
             self.handle = pool_create(n_layers, block_size, n_kv_heads, head_dim, slab_blocks,
-                                      max_slabs, self.fmt, hadamard_signs)
+                                      max_slabs, self.fmt, hadamard_signs, group_size)
         self.k_slab_bytes, self.v_slab_bytes = slab_bytes(self.handle)
-        self.k_record_bytes, self.v_record_bytes = record_bytes(self.fmt, head_dim)
+        self.group_size = self.storage_identity().group_size
+        self.k_record_bytes, self.v_record_bytes = record_bytes(self.fmt, head_dim, self.group_size)
         self.k_slabs: List[List[torch.Tensor]] = [[] for _ in range(n_layers)]
         self.v_slabs: List[List[torch.Tensor]] = [[] for _ in range(n_layers)]
 

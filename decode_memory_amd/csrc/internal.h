@@ -34,6 +34,7 @@ struct WriteArgs {
   // packed formats
   int32_t head_dim;
   int32_t k_bits, v_bits;
+  int32_t qgroup;      // values per (scale, offset) pair: 32 or 64
   const float* signs;  // device [head_dim] of +-1 (packed only)
   float inv_sqrt_d;
 };
@@ -87,6 +88,7 @@ struct DecodeArgs {
   int32_t blocks_per_split;  // most blocks any split takes (<= 64)
   // packed formats
   int32_t k_bits, v_bits;
+  int32_t qgroup;  // values per (scale, offset) pair: 32 or 64
   const float* signs;
   float inv_sqrt_d;
 };
@@ -104,7 +106,8 @@ hipError_t launch_paged_decode_row(const DecodeArgs& a, bool bf16, int32_t head_
 hipError_t launch_decode_combine(const DecodeArgs& a, bool bf16, int32_t head_dim, hipStream_t s);
 hipError_t launch_paged_decode_packed_mfma(const DecodeArgs& a, int32_t head_dim, int32_t group,
                                            hipStream_t s);
-bool packed_mfma_supported(int32_t n_kv, int32_t head_dim, int32_t group, int32_t block_size);
+bool packed_mfma_supported(int32_t n_kv, int32_t head_dim, int32_t group, int32_t block_size,
+                           int32_t qgroup);
 int packed_mfma_target_workgroups(int32_t head_dim);
 // Row kernel: head groups per workgroup (0 = shape not supported) and kv
 // heads per workgroup.

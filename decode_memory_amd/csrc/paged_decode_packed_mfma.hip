@@ -7,8 +7,8 @@
 // Hadamard basis before they were quantised, so the query gets the same
 // rotation (q'.k' = q.k); values are stored unrotated.  A token-head record is
 // its codes (8-bit bytes, or 4-bit nibbles with value 2i in the low nibble of
-// byte i) followed by one (fp32 scale, fp32 offset) per group of 32 values; a
-// value is code * scale + offset.  Per group g of a key,
+// byte i) followed by one (fp32 scale, fp32 offset) per group of GS = 32 or
+// 64 values; a value is code * scale + offset.  Per group g of a key,
 //   q'.k = scale_g * sum_{i in g} q'_i c_i + offset_g * sum_{i in g} q'_i,
 // and per group of a value
 //   sum_t p_t v_t = sum_t (p_t scale_t) c_t + sum_t p_t offset_t.
@@ -22,8 +22,9 @@
 // in LDS with 16-byte coalesced loads, the next stage's loads in flight in
 // registers while the current one is computed.  A wave works through its
 // head's tokens 16 at a time:
-//   scores: one 16x16x32 product per group of 32 values, A = q' (query head
-//     j in row 4j, other rows zero), B = the 16 tokens' codes of the group;
+//   scores: one 16x16x32 product per 32-value k-block (the k-blocks of one
+//     group chain their products), A = q' (query head j in row 4j, other
+//     rows zero), B = the 16 tokens' codes of the k-block;
 //     the score of (query head j, token n) lands in lane n + 16 j, so the
 //     online softmax runs on every lane and its reductions over tokens are
 //     16-lane DPP row operations;
@@ -81,11 +82,13 @@ typedef float f4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(1))) u32x4 gu32x4;
 
-template <int D, int KB, int VB>
+template <int D, int KB, int VB, int GS>
 struct PShape {
-  static constexpr int NG = D / 32;                    // groups of 32 values
+  static constexpr int NKB = D / 32;   // 32-value k-blocks of the score products
+  static constexpr int NMG = D / GS;   // (scale, offset) groups of a record
+  static constexpr int KPG = GS / 32;  // k-blocks per group
   static constexpr int KCODE = D * KB / 8, VCODE = D * VB / 8;
-  static constexpr int KREC = KCODE + NG * 8, VREC = VCODE + NG * 8;
+  static constexpr int KREC = KCODE + NMG * 8, VREC = VCODE + NMG * 8;
   static constexpr int KROW = 8 * KREC, VROW = 8 * VREC;  // one token, every head
   // LDS pitch of a staged token row: 16 bytes of padding spread the rows of
   // consecutive tokens over the banks
@@ -217,19 +220,19 @@ __device__ __forceinline__ float row_max16(float v) {
   return v;
 }
 
-template <int D, int KB, int VB, int G>
+template <int D, int KB, int VB, int G, int GS>
 __global__ __launch_bounds__(kPThreads, kPMinWaves<D>) void paged_decode_packed_mfma_kernel(DecodeArgs a) {
-  using S = PShape<D, KB, VB>;
-  constexpr int NG = S::NG, T = S::T, PK = S::PK, PV = S::PV;
+  using S = PShape<D, KB, VB, GS>;
+  constexpr int NKB = S::NKB, NMG = S::NMG, KPG = S::KPG, T = S::T, PK = S::PK, PV = S::PV;
   constexpr int KREC = S::KREC, VREC = S::VREC, KROW = S::KROW, VROW = S::VROW;
   constexpr int NV = D / 64;  // value accumulators (64 dimensions each, one per lane)
-  constexpr int AUX = (G * D > NG * 4 * kSub) ? G * D : NG * 4 * kSub;  // floats per wave
+  constexpr int AUX = (G * D > NMG * 4 * kSub) ? G * D : NMG * 4 * kSub;  // floats per wave
   static_assert(G <= 4, "query heads of a kv head take rows 0, 4, 8, 12");
 
   __shared__ __attribute__((aligned(16))) unsigned char s_stage[S::STAGE];
   __shared__ __attribute__((aligned(16))) float s_aux[kPWaves][AUX];  // q' transform, then p^T
-  __shared__ float s_qs[kPWaves][G * NG];  // sum of q' per (query head, group)
-  __shared__ float s_kb[kPWaves][G * NG];  // 1024 * sum of the f16 A operand, likewise
+  __shared__ float s_qs[kPWaves][G * NMG];  // sum of q' per (query head, group)
+  __shared__ float s_kb[kPWaves][G * NMG];  // 1024 * sum of the f16 A operand, likewise
   __shared__ uint64_t s_kt[kPLdsSlabs];    // slab base pointers of the layer
   __shared__ uint64_t s_vt[kPLdsSlabs];
 
@@ -339,14 +342,13 @@ __global__ __launch_bounds__(kPThreads, kPMinWaves<D>) void paged_decode_packed_
   const float qs = a.inv_sqrt_d * a.scale_log2;  // scores live in the exp2 domain
   // A operands of the score products: row m = n holds query head m / 4 when
   // m % 4 == 0 (rows of absent query heads and the rest are zero), k-block J
-  h8 aq[NG];
+  h8 aq[NKB];
   {
     const bool live = (n % 4) == 0 && n / 4 < G;
     const int jq = live ? n / 4 : 0;
 #pragma unroll
-    for (int g = 0; g < NG; ++g)
+    for (int g = 0; g < NKB; ++g)
 #pragma unroll
-      for (int e = 0; e < 8; ++e)
       for (int e = 0; e < 8; ++e) {
         const int v = J * 8 + key_value_index<KB>(e);
         aq[g][e] = static_cast<_Float16>(live ? sq[jq * D + g * 32 + v] * qs * key_q_factor<KB>(v) : 0.f);
@@ -356,11 +358,11 @@ __global__ __launch_bounds__(kPThreads, kPMinWaves<D>) void paged_decode_packed_
   // term) and 1024 times the sum of the A operand's f16 values (the bias the
   // biased key codes add); each lane then takes those of query head J of the
   // score layout
-  for (int i = lane; i < G * NG; i += kWave) {
-    const float* src = sq + (i / NG) * D + (i % NG) * 32;
+  for (int i = lane; i < G * NMG; i += kWave) {
+    const float* src = sq + (i / NMG) * D + (i % NMG) * GS;
     float acc = 0.f, ab = 0.f;
 #pragma unroll 8
-    for (int k = 0; k < 32; ++k) {
+    for (int k = 0; k < GS; ++k) {
       acc += src[k];
       ab += static_cast<float>(static_cast<_Float16>(src[k] * qs * key_q_factor<KB>(k)));
     }
@@ -368,17 +370,17 @@ __global__ __launch_bounds__(kPThreads, kPMinWaves<D>) void paged_decode_packed_
     s_kb[h][i] = ab * 1024.f;
   }
   __syncthreads();  // the per-wave area is reused for p^T below
-  float qsum[NG], kbias[NG];
+  float qsum[NMG], kbias[NMG];
 #pragma unroll
-  for (int g = 0; g < NG; ++g) {
-    qsum[g] = J < G ? s_qs[h][J * NG + g] : 0.f;
-    kbias[g] = J < G ? s_kb[h][J * NG + g] : 0.f;
+  for (int g = 0; g < NMG; ++g) {
+    qsum[g] = J < G ? s_qs[h][J * NMG + g] : 0.f;
+    kbias[g] = J < G ? s_kb[h][J * NMG + g] : 0.f;
   }
 
-  float m_run = -INFINITY, l_run = 0.f, bias[NG];
+  float m_run = -INFINITY, l_run = 0.f, bias[NMG];
   f4 acc[NV];  // lane l: dimension 64 i + l, register r: query head r
 #pragma unroll
-  for (int g = 0; g < NG; ++g) bias[g] = 0.f;
+  for (int g = 0; g < NMG; ++g) bias[g] = 0.f;
 #pragma unroll
   for (int i = 0; i < NV; ++i) acc[i] = f4{0.f, 0.f, 0.f, 0.f};
   // p * scale * 1024 as f16: [group][query head][token of the sub-tile]
@@ -412,11 +414,17 @@ __global__ __launch_bounds__(kPThreads, kPMinWaves<D>) void paged_decode_packed_
       const unsigned char* krow = s_stage + (lt0 + n) * PK + h * KREC;
       float sv = 0.f;
 #pragma unroll
-      for (int g = 0; g < NG; ++g) {
-        const h8 bk = key_codes<KB>(krow + g * (32 * KB / 8) + J * KB);
-        const f4 c = __builtin_amdgcn_mfma_f32_16x16x32_f16(aq[g], bk, f4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-        const float2 km = *reinterpret_cast<const float2*>(krow + S::KCODE + 8 * g);
-        sv = fmaf(c[0] - kbias[g], km.x, fmaf(km.y, qsum[g], sv));
+      for (int mg = 0; mg < NMG; ++mg) {
+        // the k-blocks of one group accumulate in one product chain
+        f4 c = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < KPG; ++kk) {
+          const int g = mg * KPG + kk;
+          const h8 bk = key_codes<KB>(krow + g * (32 * KB / 8) + J * KB);
+          c = __builtin_amdgcn_mfma_f32_16x16x32_f16(aq[g], bk, c, 0, 0, 0);
+        }
+        const float2 km = *reinterpret_cast<const float2*>(krow + S::KCODE + 8 * mg);
+        sv = fmaf(c[0] - kbias[mg], km.x, fmaf(km.y, qsum[mg], sv));
       }
       const bool tv = J < G && t0 + lt0 + n < nt;
       const float sc = tv ? sv : -INFINITY;
@@ -429,7 +437,7 @@ __global__ __launch_bounds__(kPThreads, kPMinWaves<D>) void paged_decode_packed_
       // value metadata of token n; invisible tokens add nothing even if it is garbage
       const unsigned char* vrow = s_stage + T * PK + (lt0 + n) * PV + h * VREC;
 #pragma unroll
-      for (int g = 0; g < NG; ++g) {
+      for (int g = 0; g < NMG; ++g) {
         const float2 vm = *reinterpret_cast<const float2*>(vrow + S::VCODE + 8 * g);
         bias[g] = fmaf(bias[g], alpha, tv ? p * vm.y : 0.f);
         sp[(g * 4 + J) * kSub + n] = static_cast<_Float16>(tv ? pk * vm.x : 0.f);
@@ -457,7 +465,7 @@ __global__ __launch_bounds__(kPThreads, kPMinWaves<D>) void paged_decode_packed_
 #pragma unroll
           for (int i = 0; i < NV; ++i) {
             const int d = 64 * i + lane;
-            const h4 ap = *reinterpret_cast<const h4*>(sp + (d / 32 * 4 + qa) * kSub + 4 * tq);
+            const h4 ap = *reinterpret_cast<const h4*>(sp + (d / GS * 4 + qa) * kSub + 4 * tq);
             uint32_t x01, x23;
             byte_column<PV>(vtok + d, x01, x23);
             const uint32_t u2[2] = {unbias(x01 | kBias2), unbias(x23 | kBias2)};
@@ -467,7 +475,7 @@ __global__ __launch_bounds__(kPThreads, kPMinWaves<D>) void paged_decode_packed_
           // 4-bit codes, 64 dimensions: lane l takes code byte l % 32 of the 4
           // tokens and its low (l < 32) or high nibble: dimension vdim(0, l)
           const int bi = lane % 32;
-          const h4 ap = *reinterpret_cast<const h4*>(sp + (bi / 16 * 4 + qa) * kSub + 4 * tq);
+          const h4 ap = *reinterpret_cast<const h4*>(sp + (bi / (GS / 2) * 4 + qa) * kSub + 4 * tq);
           uint32_t x01, x23;
           byte_column<PV>(vtok + bi, x01, x23);
           const uint32_t u2[2] = {unbias((x01 & nib_mask) | kBias2), unbias((x23 & nib_mask) | kBias2)};
@@ -479,7 +487,7 @@ __global__ __launch_bounds__(kPThreads, kPMinWaves<D>) void paged_decode_packed_
 #pragma unroll
           for (int k = 0; k < NV / 2; ++k) {
             const int bi = lane + 64 * k;
-            const h4 ap = *reinterpret_cast<const h4*>(sp + (bi / 16 * 4 + qa) * kSub + 4 * tq);
+            const h4 ap = *reinterpret_cast<const h4*>(sp + (bi / (GS / 2) * 4 + qa) * kSub + 4 * tq);
             uint32_t x01, x23;
             byte_column<PV>(vtok + bi, x01, x23);
             const uint32_t ul[2] = {unbias((x01 & 0x000f000fu) | kBias2), unbias((x23 & 0x000f000fu) | kBias2)};
@@ -499,23 +507,23 @@ __global__ __launch_bounds__(kPThreads, kPMinWaves<D>) void paged_decode_packed_
   // partials: (max, sum) and the group offsets' sums are uniform over score
   // row r; lane l holds dimension 64 i + l of query head r in register r
   const float l_tot = group_sum<kSub>(l_run);
-  float btot[NG];
+  float btot[NMG];
 #pragma unroll
-  for (int g = 0; g < NG; ++g) btot[g] = group_sum<kSub>(bias[g]);
+  for (int g = 0; g < NMG; ++g) btot[g] = group_sum<kSub>(bias[g]);
 #pragma unroll
   for (int r = 0; r < G; ++r) {
     const size_t hs = (static_cast<size_t>(b) * a.n_q + h * G + r) * n_split + s;
     float* part_acc = a.partials + hs * D;
-    float bq[NG];  // the group offsets' sums of query head r
+    float bq[NMG];  // the group offsets' sums of query head r
 #pragma unroll
-    for (int g = 0; g < NG; ++g)
+    for (int g = 0; g < NMG; ++g)
       bq[g] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, btot[g]), kSub * r));
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
       const int d = vdim<VB, NV>(i, lane);
       float bsel = 0.f;
 #pragma unroll
-      for (int g = 0; g < NG; ++g) bsel = d / 32 == g ? bq[g] : bsel;
+      for (int g = 0; g < NMG; ++g) bsel = d / GS == g ? bq[g] : bsel;
       part_acc[d] = fmaf(acc[i][r], vacc_scale<VB, NV>(i, lane), bsel);
     }
     if (lane == kSub * r) {
@@ -525,38 +533,41 @@ __global__ __launch_bounds__(kPThreads, kPMinWaves<D>) void paged_decode_packed_
   }
 }
 
-template <int D, int KB, int VB, int G>
+template <int D, int KB, int VB, int G, int GS>
 hipError_t launch_mfma(const DecodeArgs& a, hipStream_t s) {
   const int grid = round_up(a.B * a.n_split, kXcds);
-  hipLaunchKernelGGL((paged_decode_packed_mfma_kernel<D, KB, VB, G>), dim3(grid), dim3(kPThreads), 0, s, a);
+  hipLaunchKernelGGL((paged_decode_packed_mfma_kernel<D, KB, VB, G, GS>), dim3(grid), dim3(kPThreads), 0, s, a);
   return hipGetLastError();
 }
 
-template <int D, int KB, int VB>
+template <int D, int KB, int VB, int GS>
 hipError_t mfma_by_group(const DecodeArgs& a, int group, hipStream_t s) {
   switch (group) {
-    case 1: return launch_mfma<D, KB, VB, 1>(a, s);
-    case 2: return launch_mfma<D, KB, VB, 2>(a, s);
-    case 4: return launch_mfma<D, KB, VB, 4>(a, s);
+    case 1: return launch_mfma<D, KB, VB, 1, GS>(a, s);
+    case 2: return launch_mfma<D, KB, VB, 2, GS>(a, s);
+    case 4: return launch_mfma<D, KB, VB, 4, GS>(a, s);
     default: return hipErrorInvalidValue;
   }
 }
 
 template <int KB, int VB>
 hipError_t mfma_by_dim(const DecodeArgs& a, int head_dim, int group, hipStream_t s) {
-  switch (head_dim) {
-    case 64: return mfma_by_group<64, KB, VB>(a, group, s);
-    case 128: return mfma_by_group<128, KB, VB>(a, group, s);
-    case 256: return mfma_by_group<256, KB, VB>(a, group, s);
+  switch (head_dim * 100 + a.qgroup) {
+    case 6432: return mfma_by_group<64, KB, VB, 32>(a, group, s);
+    case 12832: return mfma_by_group<128, KB, VB, 32>(a, group, s);
+    case 25632: return mfma_by_group<256, KB, VB, 32>(a, group, s);
+    case 12864: return mfma_by_group<128, KB, VB, 64>(a, group, s);
+    case 25664: return mfma_by_group<256, KB, VB, 64>(a, group, s);
     default: return hipErrorInvalidValue;
   }
 }
 
 }  // namespace
 
-bool packed_mfma_supported(int32_t n_kv, int32_t head_dim, int32_t group, int32_t block_size) {
+bool packed_mfma_supported(int32_t n_kv, int32_t head_dim, int32_t group, int32_t block_size,
+                           int32_t qgroup) {
   return n_kv == kPWaves && block_size == kPBS && (head_dim == 64 || head_dim == 128 || head_dim == 256) &&
-         (group == 1 || group == 2 || group == 4);
+         (group == 1 || group == 2 || group == 4) && (qgroup == 32 || (qgroup == 64 && head_dim >= 128));
 }
 
 // Workgroups a launch aims for: two per CU where a workgroup's registers allow it.

@@ -37,6 +37,7 @@ struct pd_pool {
   int device = 0;
   int32_t k_rec = 0, v_rec = 0;
   int32_t k_bits = 16, v_bits = 16;
+  int32_t qgroup = 0;  // packed: values per (scale, offset) pair
   size_t k_slab_bytes = 0, v_slab_bytes = 0;
   int64_t n_slabs = 0;
   int64_t append_events = 0;
@@ -82,9 +83,18 @@ void format_bits(int32_t f, int32_t* kb, int32_t* vb) {
   }
 }
 
-int32_t record_bytes_for(int32_t bits, int32_t d) {
+int32_t record_bytes_for(int32_t bits, int32_t d, int32_t qgroup) {
   if (bits == 16) return 2 * d;
-  return d * bits / 8 + (d / 32) * 8;  // codes + (scale, offset) per 32 values
+  return d * bits / 8 + (d / qgroup) * 8;  // codes + (scale, offset) per group
+}
+
+// The packed group size a pool or query asks for (0 means 32); 0 if it is
+// not one the kernels take for this head_dim.
+int32_t packed_group_or_zero(int32_t group_size, int32_t head_dim) {
+  const int32_t g = group_size == 0 ? 32 : group_size;
+  if (g == 32) return 32;
+  if (g == 64 && head_dim >= 128) return 64;
+  return 0;
 }
 
 LayerView layer_view(const pd_pool* p, int32_t layer) {
@@ -216,7 +226,7 @@ struct DecodePlan {
 // storage shape and (B, group, max_len), so a dense call and a paged call of
 // the same shape run the same arithmetic in the same order.
 bool make_decode_plan_for(int32_t format, int32_t n_kv, int32_t D, int32_t bs, int32_t B,
-                          int32_t group, int32_t max_len, DecodePlan* out) {
+                          int32_t group, int32_t max_len, int32_t qgroup, DecodePlan* out) {
   const bool d_ok = D == 64 || D == 128 || D == 256;
   const bool g_ok = group == 1 || group == 2 || group == 4 || group == 8;
   if (!d_ok || !g_ok) return false;
@@ -233,7 +243,7 @@ bool make_decode_plan_for(int32_t format, int32_t n_kv, int32_t D, int32_t bs, i
       max_bps = PAGEDKV_ROW_MAX_BLOCKS_PER_SPLIT;
     }
   } else {
-    if (!packed_mfma_supported(n_kv, D, group, bs)) return false;
+    if (!packed_mfma_supported(n_kv, D, group, bs, qgroup)) return false;
     plan.kind = 2;
     units = B;  // a packed workgroup covers every kv head of its sequence
     target = packed_mfma_target_workgroups(D);
@@ -245,7 +255,7 @@ bool make_decode_plan_for(int32_t format, int32_t n_kv, int32_t D, int32_t bs, i
 
 bool make_decode_plan(const pd_pool* p, int32_t B, int32_t group, int32_t max_len, DecodePlan* out) {
   return make_decode_plan_for(p->desc.format, p->desc.n_kv_heads, p->desc.head_dim, p->desc.block_size,
-                              B, group, max_len, out);
+                              B, group, max_len, p->qgroup, out);
 }
 
 }  // namespace
@@ -256,13 +266,17 @@ int32_t pd_version(void) { return PD_VERSION; }
 
 const char* pd_last_error(void) { return g_last_error.c_str(); }
 
-pd_status pd_record_bytes(int32_t format, int32_t head_dim, int32_t* k_bytes, int32_t* v_bytes) {
+pd_status pd_record_bytes(int32_t format, int32_t head_dim, int32_t group_size, int32_t* k_bytes,
+                          int32_t* v_bytes) {
   if (!is_native(format) && !is_packed(format)) return fail(PD_ERR_ARG, "unknown format %d", format);
   if (head_dim <= 0) return fail(PD_ERR_ARG, "head_dim must be positive");
+  const int32_t g = group_size == 0 ? 32 : group_size;
+  if (is_packed(format) && (g <= 0 || head_dim % g != 0))
+    return fail(PD_ERR_ARG, "group_size %d does not divide head_dim %d", group_size, head_dim);
   int32_t kb, vb;
   format_bits(format, &kb, &vb);
-  if (k_bytes) *k_bytes = record_bytes_for(kb, head_dim);
-  if (v_bytes) *v_bytes = record_bytes_for(vb, head_dim);
+  if (k_bytes) *k_bytes = record_bytes_for(kb, head_dim, g);
+  if (v_bytes) *v_bytes = record_bytes_for(vb, head_dim, g);
   return PD_OK;
 }
 
@@ -280,6 +294,11 @@ pd_status pd_pool_create(const pd_pool_desc* d, pd_pool** out) {
     return fail(PD_ERR_UNSUPPORTED, "block_size %d (supported: 16, 32, 64)", d->block_size);
   if (is_packed(d->format) && d->block_size != 32)
     return fail(PD_ERR_UNSUPPORTED, "packed formats use block_size 32");
+  if (is_native(d->format) && d->group_size != 0)
+    return fail(PD_ERR_ARG, "group_size %d: 16-bit formats have no groups (pass 0)", d->group_size);
+  if (is_packed(d->format) && packed_group_or_zero(d->group_size, d->head_dim) == 0)
+    return fail(PD_ERR_UNSUPPORTED, "group_size %d with head_dim %d (supported: 32; 64 with head_dim 128, 256)",
+                d->group_size, d->head_dim);
   if (is_packed(d->format)) {
     if (!d->hadamard_signs) return fail(PD_ERR_ARG, "packed formats need hadamard_signs");
     for (int i = 0; i < d->head_dim; ++i)
@@ -293,8 +312,10 @@ pd_status pd_pool_create(const pd_pool_desc* d, pd_pool** out) {
   p->desc = *d;
   p->desc.hadamard_signs = nullptr;
   format_bits(d->format, &p->k_bits, &p->v_bits);
-  p->k_rec = record_bytes_for(p->k_bits, d->head_dim);
-  p->v_rec = record_bytes_for(p->v_bits, d->head_dim);
+  p->qgroup = is_packed(d->format) ? packed_group_or_zero(d->group_size, d->head_dim) : 0;
+  p->desc.group_size = p->qgroup;
+  p->k_rec = record_bytes_for(p->k_bits, d->head_dim, p->qgroup);
+  p->v_rec = record_bytes_for(p->v_bits, d->head_dim, p->qgroup);
   const size_t per = static_cast<size_t>(d->slab_blocks) * d->block_size * d->n_kv_heads;
   p->k_slab_bytes = per * p->k_rec;
   p->v_slab_bytes = per * p->v_rec;
@@ -415,6 +436,7 @@ pd_status pd_write_block(pd_pool* p, int32_t layer, int32_t n, const int32_t* ro
   a.head_dim = p->desc.head_dim;
   a.k_bits = p->k_bits;
   a.v_bits = p->v_bits;
+  a.qgroup = p->qgroup;
   a.signs = p->d_signs;
   a.inv_sqrt_d = p->inv_sqrt_d;
   hipError_t e = launch_write_block(a, p->desc.format, stream);
@@ -457,7 +479,7 @@ void identity_of(const pd_pool* p, pd_storage_identity* id) {
   id->head_dim = p->desc.head_dim;
   id->k_record_bytes = p->k_rec;
   id->v_record_bytes = p->v_rec;
-  id->group_size = is_packed(p->desc.format) ? 32 : 0;
+  id->group_size = p->qgroup;
   id->signs_hash = p->signs_hash;
 }
 
@@ -657,6 +679,7 @@ static pd_status decode_call(pd_pool* p, int32_t layer, int32_t B, int32_t n_q_h
   a.blocks_per_split = plan.split.blocks_per_split;
   a.k_bits = p->k_bits;
   a.v_bits = p->v_bits;
+  a.qgroup = p->qgroup;
   a.signs = p->d_signs;
   a.inv_sqrt_d = p->inv_sqrt_d;
   const bool bf16 = p->desc.format == PD_FMT_BF16;
@@ -717,7 +740,7 @@ pd_status dense_plan(const pd_dense_desc* d, int32_t B, int32_t n_q_heads, int32
     return fail(PD_ERR_UNSUPPORTED, "max_len %d beyond %lld", max_len,
                 static_cast<long long>(max_decode_len(kDenseBlock)));
   const int32_t group = n_q_heads / d->n_kv_heads;
-  if (!make_decode_plan_for(d->format, d->n_kv_heads, d->head_dim, kDenseBlock, B, group, max_len, plan) ||
+  if (!make_decode_plan_for(d->format, d->n_kv_heads, d->head_dim, kDenseBlock, B, group, max_len, 0, plan) ||
       plan->kind != 1)
     return fail(PD_ERR_UNSUPPORTED,
                 "dense decode needs the row kernel's shapes (n_kv_heads * head_dim * 2 a multiple of "

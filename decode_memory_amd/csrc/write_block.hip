@@ -179,8 +179,10 @@ __device__ __forceinline__ void fwht_rotate8(float (&x)[8], const float* signs, 
   for (int e = 0; e < 8; ++e) x[e] = __fmul_rn(x[e], inv_sqrt_d);
 }
 
-template <int D>
+template <int D, int GS>
 __global__ __launch_bounds__(kThreads) void write_block_packed_kernel(WriteArgs a) {
+  static_assert(GS == 32 || GS == 64, "groups of 32 or 64 values");
+  constexpr int LPG = GS / 8;       // lanes per group
   constexpr int LPT = D / 8;        // lanes per vector
   constexpr int VPW = kWave / LPT;  // vectors per wave
   const int lane = threadIdx.x % kWave;
@@ -223,7 +225,9 @@ __global__ __launch_bounds__(kThreads) void write_block_packed_kernel(WriteArgs 
         for (int e = 0; e < 8; ++e) x[e] = y[e];
       }
     }
-    // group of 32 values = 4 lanes: min and max in the lane, then across them
+    // a group is LPG aligned lanes (4 or 8): min and max in the lane, then
+    // across the lane quad, then (groups of 64) across the two quads of the
+    // 8-lane half row
     float mn = x[0], mx = x[0];
 #pragma unroll
     for (int e = 1; e < 8; ++e) {
@@ -234,6 +238,10 @@ __global__ __launch_bounds__(kThreads) void write_block_packed_kernel(WriteArgs 
     mx = fmaxf(mx, dpp<kDppXor1>(mx));
     mn = fminf(mn, dpp<kDppXor2>(mn));
     mx = fmaxf(mx, dpp<kDppXor2>(mx));
+    if constexpr (LPG == 8) {
+      mn = fminf(mn, dpp<kDppHalfMirror>(mn));
+      mx = fmaxf(mx, dpp<kDppHalfMirror>(mx));
+    }
     const int bits = is_v ? a.v_bits : a.k_bits;
     const float levels = static_cast<float>((1 << bits) - 1);
     const float scale = __fdiv_rn(__fsub_rn(mx, mn), levels);
@@ -257,8 +265,8 @@ __global__ __launch_bounds__(kThreads) void write_block_packed_kernel(WriteArgs 
           (code[0] | (code[1] << 4)) | ((code[2] | (code[3] << 4)) << 8) |
           ((code[4] | (code[5] << 4)) << 16) | ((code[6] | (code[7] << 4)) << 24);
     }
-    if ((c & 3) == 0) {
-      float* meta = reinterpret_cast<float*>(rec + D * bits / 8) + 2 * (c / 4);
+    if (c % LPG == 0) {
+      float* meta = reinterpret_cast<float*>(rec + D * bits / 8) + 2 * (c / LPG);
       *reinterpret_cast<float2*>(meta) = make_float2(scale, mn);
     }
   }
@@ -301,15 +309,22 @@ hipError_t launch_write_block(const WriteArgs& a, int32_t format, hipStream_t s)
   const long long waves = (2LL * a.n * a.lv.n_kv * (a.head_dim / 8) + kWave - 1) / kWave;
   long long grid = (waves + kThreads / kWave - 1) / (kThreads / kWave);
   if (grid > 65536) grid = 65536;
-  switch (a.head_dim) {
-    case 64:
-      hipLaunchKernelGGL(write_block_packed_kernel<64>, dim3(grid), dim3(kThreads), 0, s, a);
+  const int key = a.head_dim * 100 + a.qgroup;
+  switch (key) {
+    case 6432:
+      hipLaunchKernelGGL((write_block_packed_kernel<64, 32>), dim3(grid), dim3(kThreads), 0, s, a);
       break;
-    case 128:
-      hipLaunchKernelGGL(write_block_packed_kernel<128>, dim3(grid), dim3(kThreads), 0, s, a);
+    case 12832:
+      hipLaunchKernelGGL((write_block_packed_kernel<128, 32>), dim3(grid), dim3(kThreads), 0, s, a);
       break;
-    case 256:
-      hipLaunchKernelGGL(write_block_packed_kernel<256>, dim3(grid), dim3(kThreads), 0, s, a);
+    case 25632:
+      hipLaunchKernelGGL((write_block_packed_kernel<256, 32>), dim3(grid), dim3(kThreads), 0, s, a);
+      break;
+    case 12864:
+      hipLaunchKernelGGL((write_block_packed_kernel<128, 64>), dim3(grid), dim3(kThreads), 0, s, a);
+      break;
+    case 25664:
+      hipLaunchKernelGGL((write_block_packed_kernel<256, 64>), dim3(grid), dim3(kThreads), 0, s, a);
       break;
     default:
       return hipErrorInvalidValue;

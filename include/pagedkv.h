@@ -93,6 +93,10 @@ typedef struct pd_pool_desc {
   int32_t format;        /* pd_format                                           */
   const int8_t* hadamard_signs; /* host, [head_dim] of +1/-1; packed formats
                                    only (copied at create), else NULL           */
+  int32_t group_size;    /* packed formats: values per (fp32 scale, offset)
+                            pair, 32 or 64 (64 needs head_dim 128 or 256, so
+                            that a record is whole 16-byte units); 0 means 32.
+                            16-bit formats: 0                                  */
 } pd_pool_desc;
 
 typedef struct pd_stats {
@@ -129,7 +133,8 @@ typedef struct pd_storage_identity {
   int32_t head_dim;
   int32_t k_record_bytes;
   int32_t v_record_bytes;
-  int32_t group_size;       /* values per (scale, offset) pair: 32 packed, 0     */
+  int32_t group_size;       /* values per (scale, offset) pair: 32 or 64 packed,
+                               0 for 16-bit formats                            */
   uint64_t signs_hash;      /* packed: pd_signs_hash of the Hadamard signs; 0   */
 } pd_storage_identity;
 
@@ -141,8 +146,12 @@ int32_t pd_version(void);
 /* Description of the last error on this thread ("" if none). */
 const char* pd_last_error(void);
 
-/* Bytes of one K and one V token-head record for a format and head_dim. */
-pd_status pd_record_bytes(int32_t format, int32_t head_dim, int32_t* k_bytes, int32_t* v_bytes);
+/* Bytes of one K and one V token-head record for a format, head_dim and
+ * group size (packed: codes + 8 bytes per group; group_size 0 means 32;
+ * 16-bit formats ignore it).  mlx-swift-lm PR #142, section "Summary": with
+ * 4-bit codes and groups of 64 a value costs five bits. */
+pd_status pd_record_bytes(int32_t format, int32_t head_dim, int32_t group_size, int32_t* k_bytes,
+                          int32_t* v_bytes);
 
 /*
  * Create an empty pool (no slabs) on the current HIP device.

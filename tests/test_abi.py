@@ -35,8 +35,16 @@ def test_version_and_record_bytes():
     for fmt, (kb, vb) in {pd.FMT_K8V8: (8, 8), pd.FMT_K8V4: (8, 4), pd.FMT_K4V4: (4, 4)}.items():
         for d in (64, 128, 256):
             assert pd.record_bytes(fmt, d) == (oracle_record_bytes(d, kb), oracle_record_bytes(d, vb))
+            assert pd.record_bytes(fmt, d, 64) == (oracle_record_bytes(d, kb, 64),
+                                                   oracle_record_bytes(d, vb, 64))
+    # K4 records with groups of 64 cost five bits per value (the PR #142 Summary figure)
+    k4, _ = pd.record_bytes(pd.FMT_K4V4, 256, 64)
+    assert k4 * 8 / 256 == 5 and 16 / (k4 * 8 / 256) == 3.2
     with pytest.raises(pd.PagedKVError) as e:
         pd.record_bytes(9, 64)
+    assert e.value.status == -1
+    with pytest.raises(pd.PagedKVError) as e:
+        pd.record_bytes(pd.FMT_K8V8, 64, 48)           # a group must divide head_dim
     assert e.value.status == -1
 
 
@@ -48,6 +56,9 @@ def test_version_and_record_bytes():
     (dict(slab_blocks=0), -1),
     (dict(fmt=pd.FMT_K4V4, hadamard_signs=None), -1),   # packed needs signs
     (dict(fmt=pd.FMT_K4V4, head_dim=64, hadamard_signs=[1, 0] * 32), -1),  # not +-1
+    (dict(fmt=pd.FMT_K4V4, head_dim=64, hadamard_signs=[1] * 64, group_size=64), -4),  # 40-byte records
+    (dict(fmt=pd.FMT_K8V8, head_dim=128, hadamard_signs=[1] * 128, group_size=16), -4),
+    (dict(fmt=pd.FMT_BF16, group_size=32), -1),  # 16-bit formats have no groups
 ])
 def test_pool_create_validates_on_host(kwargs, status):
     args = dict(n_layers=2, block_size=32, n_kv_heads=8, head_dim=128, slab_blocks=4,

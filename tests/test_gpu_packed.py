@@ -23,13 +23,13 @@ pytestmark = pytest.mark.gpu
 BS = 32
 
 
-def _packed_pool(fmt, D, lengths, rows, seed, cap, n_kv=8, keep=None, slab_blocks=32):
+def _packed_pool(fmt, D, lengths, rows, seed, cap, n_kv=8, keep=None, slab_blocks=32, group=32):
     """Write every sequence through the quantising write_block; return the pool,
     the oracle's records of the sequences in `keep` and the sign vector."""
     kb, vb = FORMATS[fmt]
     signs = hadamard_signs(seed, D)
     pool = pd.SlabPool(1, BS, n_kv, D, slab_blocks, -(-cap // slab_blocks) + 2, fmt,
-                       hadamard_signs=signs)
+                       hadamard_signs=signs, group_size=group)
     pool.reserve_rows(cap)
     recs = {}
     for b, n in enumerate(lengths):
@@ -39,20 +39,22 @@ def _packed_pool(fmt, D, lengths, rows, seed, cap, n_kv=8, keep=None, slab_block
         r, s = token_targets(rows[b], int(n), BS)
         pool.write_block(0, i32(r), i32(s), to_device_bits(k, "bf16"), to_device_bits(v, "bf16"))
         if keep is None or b in keep:
-            recs[b] = (k_records(k, signs, kb), v_records(v, vb))
+            recs[b] = (k_records(k, signs, kb, group), v_records(v, vb, group))
     torch.cuda.synchronize()
     return pool, recs, signs
 
 
 @pytest.mark.parametrize("fmt", ["k8v8", "k8v4", "k4v4"])
-@pytest.mark.parametrize("D", [64, 128, 256])
-def test_quantising_write_and_gather_are_bit_exact(fmt, D):
+@pytest.mark.parametrize("D,group", [(64, 32), (128, 32), (256, 32), (128, 64), (256, 64)])
+def test_quantising_write_and_gather_are_bit_exact(fmt, D, group):
     kb, vb = FORMATS[fmt]
     lengths = [70, 1, 33, 0, 256]
     rows, _, R = shuffled_rows(np.random.default_rng(D), lengths, BS, 32, spare_rows=2)
-    pool, recs, _ = _packed_pool(fmt, D, lengths, rows, 50 + D, R)
-    assert pool.k_record_bytes == record_bytes(D, kb) and pool.v_record_bytes == record_bytes(D, vb)
-    model = SlabPoolModel(1, BS, 8, record_bytes(D, kb), record_bytes(D, vb), 32)
+    pool, recs, _ = _packed_pool(fmt, D, lengths, rows, 50 + D, R, group=group)
+    krec, vrec = record_bytes(D, kb, group), record_bytes(D, vb, group)
+    assert pool.group_size == group
+    assert pool.k_record_bytes == krec and pool.v_record_bytes == vrec
+    model = SlabPoolModel(1, BS, 8, krec, vrec, 32)
     model.reserve_rows(R)
     for b, (kr, vr) in recs.items():
         r, s = token_targets(rows[b], lengths[b], BS)
@@ -60,8 +62,8 @@ def test_quantising_write_and_gather_are_bit_exact(fmt, D):
     for slab in range(model.n_slabs):
         got_k = pool.slab_view(0, slab, "k").cpu().numpy()
         got_v = pool.slab_view(0, slab, "v").cpu().numpy()
-        assert np.array_equal(got_k, model.k_slabs[0][slab]), (fmt, D, "K", slab)
-        assert np.array_equal(got_v, model.v_slabs[0][slab]), (fmt, D, "V", slab)
+        assert np.array_equal(got_k, model.k_slabs[0][slab]), (fmt, D, group, "K", slab)
+        assert np.array_equal(got_v, model.v_slabs[0][slab]), (fmt, D, group, "V", slab)
     table = make_block_table(rows)
     t_out = max(lengths)
     gk = torch.empty((len(lengths), 8, t_out, pool.k_record_bytes), dtype=torch.uint8, device="cuda")
@@ -74,17 +76,18 @@ def test_quantising_write_and_gather_are_bit_exact(fmt, D):
 
 
 @pytest.mark.parametrize("fmt", ["k8v8", "k8v4", "k4v4"])
-@pytest.mark.parametrize("D,G", [(64, 4), (256, 4), (128, 2), (64, 1)])
-def test_packed_decode_matches_oracle(fmt, D, G):
+@pytest.mark.parametrize("D,G,group", [(64, 4, 32), (256, 4, 32), (128, 2, 32), (64, 1, 32),
+                                       (128, 4, 64), (256, 2, 64), (256, 1, 64)])
+def test_packed_decode_matches_oracle(fmt, D, G, group):
     lengths = [300, 1, 45, 0, 1024, 64]
     rows, _, R = shuffled_rows(np.random.default_rng(D + G), lengths, BS, 32, spare_rows=2)
-    pool, recs, signs = _packed_pool(fmt, D, lengths, rows, 60 + D + G, R)
+    pool, recs, signs = _packed_pool(fmt, D, lengths, rows, 60 + D + G, R, group=group)
     B = len(lengths)
     q = q_bits(60 + D + G, 0, B, 8 * G, D, "bf16")
     scale = 1.0 / np.sqrt(D)
     kr = [recs[b][0] if b in recs else np.zeros((0, 8, pool.k_record_bytes), np.uint8) for b in range(B)]
     vr = [recs[b][1] if b in recs else np.zeros((0, 8, pool.v_record_bytes), np.uint8) for b in range(B)]
-    ref = packed_decode_attention(q, kr, vr, signs, fmt, D, scale)
+    ref = packed_decode_attention(q, kr, vr, signs, fmt, D, scale, group)
     qd = to_device_bits(q, "bf16")
     out = torch.empty_like(qd)
     ws = pool.workspace(B, 8 * G, max(lengths))
@@ -125,18 +128,19 @@ def test_packed_decode_with_more_slabs_than_its_lds_table(fmt, D, G):
     pool.close()
 
 
-@pytest.mark.parametrize("D", [64, 256])
-@pytest.mark.parametrize("fmt", ["k8v8", "k8v4", "k4v4"])
-def test_packed_workload_full_size_sampled(fmt, D):
+@pytest.mark.parametrize("fmt,D,group", [(f, d, 32) for f in ("k8v8", "k8v4", "k4v4") for d in (64, 256)]
+                         + [("k4v4", 256, 64)])
+def test_packed_workload_full_size_sampled(fmt, D, group):
     """The packed workload at full size (16 x 16384 tokens, 8 kv heads, GQA 4):
     every sequence is written and decoded on the device; the oracle checks the
-    records and outputs of sequences 0 and 15."""
+    records and outputs of sequences 0 and 15.  Groups of 64 (K4/V4 at five
+    bits per value) run at the same size."""
     w = WORKLOADS["packed_16x16k"]
     lengths = [w.length] * w.batch
     rows = monotone_rows(lengths, BS)
     cap = int(rows[-1].max()) + 1
     sample = (0, w.batch - 1)
-    pool, recs, signs = _packed_pool(fmt, D, lengths, rows, w.seed, cap, keep=sample)
+    pool, recs, signs = _packed_pool(fmt, D, lengths, rows, w.seed, cap, keep=sample, group=group)
     q = q_bits(w.seed, 0, w.batch, w.n_q_heads, D, "bf16")
     scale = 1.0 / np.sqrt(D)
     qd = to_device_bits(q, "bf16")
@@ -155,8 +159,8 @@ def test_packed_workload_full_size_sampled(fmt, D):
         assert np.array_equal(gk[i], recs[b][0].transpose(1, 0, 2)), (fmt, D, b)
         assert np.array_equal(gv[i], recs[b][1].transpose(1, 0, 2)), (fmt, D, b)
     ref = packed_decode_attention(q[list(sample)], [recs[b][0] for b in sample],
-                                  [recs[b][1] for b in sample], signs, fmt, D, scale)
+                                  [recs[b][1] for b in sample], signs, fmt, D, scale, group)
     err = assert_decode_close(got[list(sample)], ref, "bf16")
-    print(f"packed {fmt} D={D}: max-abs {err:.2e}")
+    print(f"packed {fmt} D={D} group {group}: max-abs {err:.2e}")
     assert pool.check_error() == 0
     pool.close()

@@ -18,15 +18,16 @@ from tests.gpu_util import i32, to_device_bits, token_targets
 pytestmark = pytest.mark.gpu
 
 
-def _pools(fmt, D, lengths, S, seed, n_layers=2, n_kv=8, bs=32, spare=6):
+def _pools(fmt, D, lengths, S, seed, n_layers=2, n_kv=8, bs=32, spare=6, group=32):
     """A device pool and the oracle's model holding the same blocks."""
     rows, _, R = shuffled_rows(np.random.default_rng(seed), lengths, bs, S, spare_rows=spare)
     packed = fmt in FORMATS
     signs = hadamard_signs(seed, D) if packed else None
     kb, vb = FORMATS[fmt] if packed else (16, 16)
-    krec = record_bytes(D, kb) if packed else 2 * D
-    vrec = record_bytes(D, vb) if packed else 2 * D
-    pool = pd.SlabPool(n_layers, bs, n_kv, D, S, -(-R // S) + 4, fmt, hadamard_signs=signs)
+    krec = record_bytes(D, kb, group) if packed else 2 * D
+    vrec = record_bytes(D, vb, group) if packed else 2 * D
+    pool = pd.SlabPool(n_layers, bs, n_kv, D, S, -(-R // S) + 4, fmt, hadamard_signs=signs,
+                       group_size=group if packed else 0)
     pool.reserve_rows(R)
     model = SlabPoolModel(n_layers, bs, n_kv, krec, vrec, S)
     model.reserve_rows(R)
@@ -36,16 +37,17 @@ def _pools(fmt, D, lengths, S, seed, n_layers=2, n_kv=8, bs=32, spare=6):
             r, s = token_targets(rows[b], n, bs)
             pool.write_block(layer, i32(r), i32(s), to_device_bits(k, "bf16"), to_device_bits(v, "bf16"))
             if packed:
-                model.write(layer, r, s, k_records(k, signs, kb), v_records(v, vb))
+                model.write(layer, r, s, k_records(k, signs, kb, group), v_records(v, vb, group))
             else:
                 model.write(layer, r, s, records_from_u16(k), records_from_u16(v))
     return pool, model, rows, R, signs
 
 
-@pytest.mark.parametrize("fmt,D", [("bf16", 128), ("k4v4", 64), ("k8v4", 256), ("k8v8", 64)])
-def test_export_is_bit_exact_and_round_trips_into_another_pool(fmt, D):
+@pytest.mark.parametrize("fmt,D,group", [("bf16", 128, 0), ("k4v4", 64, 32), ("k8v4", 256, 32),
+                                         ("k8v8", 64, 32), ("k4v4", 256, 64)])
+def test_export_is_bit_exact_and_round_trips_into_another_pool(fmt, D, group):
     lengths = [100, 33, 64]
-    pool, model, rows, R, signs = _pools(fmt, D, lengths, 4, 300 + D)
+    pool, model, rows, R, signs = _pools(fmt, D, lengths, 4, 300 + D, group=group)
     blocks = np.concatenate(rows).astype(np.int32)
     got = pool.export_blocks(i32(blocks)).cpu().numpy()
     assert got.shape[1] == pd.block_bytes(pool.handle)
@@ -53,9 +55,9 @@ def test_export_is_bit_exact_and_round_trips_into_another_pool(fmt, D):
     ident = pool.storage_identity()
     assert ident.format == pd.FORMAT_NAMES[fmt] and ident.n_layers == 2
     if fmt in FORMATS:
-        assert ident.signs_hash == signs_fingerprint(signs) and ident.group_size == 32
+        assert ident.signs_hash == signs_fingerprint(signs) and ident.group_size == group
     # another pool of the same identity, other slab size, other rows
-    other = pd.SlabPool(2, 32, 8, D, 3, 16, fmt, hadamard_signs=signs)
+    other = pd.SlabPool(2, 32, 8, D, 3, 16, fmt, hadamard_signs=signs, group_size=group)
     new_rows = np.arange(len(blocks), dtype=np.int32)[::-1] * 2 + 1
     other.reserve_rows(int(new_rows.max()) + 1)
     other.import_blocks(ident, i32(new_rows), pool.export_blocks(i32(blocks)))
@@ -107,15 +109,18 @@ def test_decode_after_restore_is_bit_identical():
     fresh.close()
 
 
-@pytest.mark.parametrize("change", ["format", "head_dim", "signs", "n_layers", "n_kv_heads"])
+@pytest.mark.parametrize("change", ["format", "head_dim", "signs", "n_layers", "n_kv_heads", "group_size"])
 def test_incompatible_identity_is_rejected_before_anything_happens(change):
     lengths = [64, 40]
-    pool, model, rows, R, signs = _pools("k4v4", 64, lengths, 4, 77)
+    D = 128 if change == "group_size" else 64  # groups of 64 need head_dim >= 128
+    pool, model, rows, R, signs = _pools("k4v4", D, lengths, 4, 77)
     blocks = np.concatenate(rows).astype(np.int32)
     payload = pool.export_blocks(i32(blocks))
     ident = pool.storage_identity()
-    kw = dict(n_layers=2, block_size=32, n_kv=8, D=64, fmt="k4v4", signs=signs)
-    if change == "format":
+    kw = dict(n_layers=2, block_size=32, n_kv=8, D=D, fmt="k4v4", signs=signs, group=32)
+    if change == "group_size":
+        kw["group"] = 64
+    elif change == "format":
         kw["fmt"] = "k8v4"
     elif change == "head_dim":
         kw["D"] = 128
@@ -129,7 +134,7 @@ def test_incompatible_identity_is_rejected_before_anything_happens(change):
     else:
         kw["n_kv"] = 4
     target = pd.SlabPool(kw["n_layers"], kw["block_size"], kw["n_kv"], kw["D"], 4, 16, kw["fmt"],
-                         hadamard_signs=kw["signs"])
+                         hadamard_signs=kw["signs"], group_size=kw["group"])
     target.reserve_rows(8)
     before = [s.clone() for s in target.k_slabs[0]]
     with pytest.raises(pd.PagedKVError) as e:

@@ -11,14 +11,17 @@
 // store addresses, so every byte is read once and written once.
 //
 // Decomposition: one workgroup per (sequence, chunk of kChunk logical
-// blocks).  Lane i of the first wave resolves block i of the chunk: its row,
+// blocks; one block measured fastest: more, shorter workgroups keep the
+// memory system busier than fewer, longer ones).  Lane i of the first wave resolves block i of the chunk: its row,
 // the row's slab and that slab's base pointer (blocks of one same-slab run
 // resolve to the same base).  The workgroup then copies the chunk's blocks in
 // logical order as 16-byte vectors: each block's source is one contiguous
 // row [block_size, n_kv, record]; the destination is n_kv contiguous pieces
-// of block_size records.  Every thread issues kUnroll loads before it
-// stores, so a CU keeps enough reads in flight to stream at the HBM rate;
-// both sides are non-temporal, since each byte is touched once.  The first
+// of block_size records.  A block's K row and V row form one range of
+// 16-byte units; every thread issues kUnroll loads of it before it stores, so
+// a CU keeps enough reads in flight to stream at the HBM rate, and both sides
+// are non-temporal, since each byte is touched once.  A unit's (slot, head,
+// piece) comes from reciprocal multiplies rather than divisions.  The first
 // chunk's workgroup also counts the sequence's runs over the whole row list
 // for n_runs_out.
 #include "device_common.h"
@@ -28,9 +31,20 @@ namespace pagedkv {
 
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kChunk = 2;   // logical blocks per workgroup
-constexpr int kUnroll = 16; // 16-byte loads in flight per thread
+#ifndef PAGEDKV_GATHER_CHUNK
+#define PAGEDKV_GATHER_CHUNK 1
+#endif
+#ifndef PAGEDKV_GATHER_UNROLL
+#define PAGEDKV_GATHER_UNROLL 32
+#endif
+
+#ifndef PAGEDKV_GATHER_THREADS
+#define PAGEDKV_GATHER_THREADS 256
+#endif
+
+constexpr int kThreads = PAGEDKV_GATHER_THREADS;
+constexpr int kChunk = PAGEDKV_GATHER_CHUNK;    // logical blocks per workgroup
+constexpr int kUnroll = PAGEDKV_GATHER_UNROLL;  // 16-byte loads in flight per thread
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(1))) u32x4 gu32x4;
@@ -39,7 +53,17 @@ __device__ __forceinline__ int slab_of(int32_t row, const LayerView& lv) {
   return (row < 0 || row >= lv.capacity_rows) ? -1 : row / lv.slab_blocks;
 }
 
-__global__ __launch_bounds__(kThreads) void gather_kernel(GatherArgs a) {
+// n / d for the divisor behind m = ceil(2^32 / d) (m = 0: d = 1): one high
+// multiply, exact while n < 2^32 / d, which the launch checks.
+__device__ __forceinline__ uint32_t div_by(uint32_t n, uint32_t m) {
+  return m ? __umulhi(n, m) : n;
+}
+
+struct GatherDiv {
+  uint32_t m_kunits, m_vunits, m_nkv;  // reciprocals of the units per K / V record and of n_kv
+};
+
+__global__ __launch_bounds__(kThreads) void gather_kernel(GatherArgs a, GatherDiv dv) {
   __shared__ const char* s_ksrc[kChunk];  // source row of each block, null = zeros
   __shared__ const char* s_vsrc[kChunk];
   __shared__ int s_runs[kThreads / kWave];
@@ -104,44 +128,57 @@ __global__ __launch_bounds__(kThreads) void gather_kernel(GatherArgs a) {
 
   char* kout = static_cast<char*>(a.k_out);
   char* vout = static_cast<char*>(a.v_out);
+  const int ku = lv.k_rec / 16, vu = lv.v_rec / 16;  // 16-byte units per record
+  const int KU = bs * n_kv * ku;                       // units of a K block row
+  const int TU = KU + bs * n_kv * vu;                  // then those of the V row
   for (int i = 0; i < kChunk; ++i) {
     const int blk = blk0 + i;
     if (blk * bs >= a.t_out) break;
-    // K then V: unit u of the row covers (slot, head, 16-byte piece)
-    for (int pass = 0; pass < 2; ++pass) {
-      const int rec = pass ? lv.v_rec : lv.k_rec;
-      const int units = rec / 16;
-      const char* src = pass ? s_vsrc[i] : s_ksrc[i];
-      char* dst = pass ? vout : kout;
-      const int total_units = bs * n_kv * units;
-      // tokens of this block that exist in the output / are visible
-      const int t_end = min(bs, a.t_out - blk * bs);
-      const int t_vis = src ? max(0, min(bs, len - blk * bs)) : 0;
-      for (int u0 = threadIdx.x; u0 < total_units; u0 += kThreads * kUnroll) {
-        u32x4 v[kUnroll];
+    const char* ksrc = s_ksrc[i];
+    const char* vsrc = s_vsrc[i];
+    // tokens of this block that exist in the output / are visible
+    const int t_end = min(bs, a.t_out - blk * bs);
+    const int t_vis = ksrc ? max(0, min(bs, len - blk * bs)) : 0;
+    // unit u < KU is (slot, head, 16-byte piece) of the K row, the rest of
+    // the V row; K and V loads are in flight together
+    for (int u0 = threadIdx.x; u0 < TU; u0 += kThreads * kUnroll) {
+      u32x4 v[kUnroll];
+      int slot_of[kUnroll];
 #pragma unroll
-        for (int j = 0; j < kUnroll; ++j) {
-          const int u = u0 + j * kThreads;
-          const int slot = u / (units * n_kv);
-          v[j] = (u32x4){0u, 0u, 0u, 0u};
-          if (u < total_units && slot < t_vis)
-            v[j] = __builtin_nontemporal_load((const gu32x4*)src + u);
-        }
+      for (int j = 0; j < kUnroll; ++j) {
+        const int u = u0 + j * kThreads;
+        const bool is_v = u >= KU;
+        const int uu = is_v ? u - KU : u;
+        const uint32_t rr = div_by(uu, is_v ? dv.m_vunits : dv.m_kunits);  // record in the row
+        const int slot = static_cast<int>(div_by(rr, dv.m_nkv));
+        slot_of[j] = slot;
+        v[j] = (u32x4){0u, 0u, 0u, 0u};
+        if (u < TU && slot < t_vis)
+          v[j] = __builtin_nontemporal_load((const gu32x4*)(is_v ? vsrc : ksrc) + uu);
+      }
 #pragma unroll
-        for (int j = 0; j < kUnroll; ++j) {
-          const int u = u0 + j * kThreads;
-          const int piece = u % units;
-          const int head = (u / units) % n_kv;
-          const int slot = u / (units * n_kv);
-          if (u < total_units && slot < t_end) {
-            const size_t o = ((static_cast<size_t>(b) * n_kv + head) * a.t_out + blk * bs + slot) * rec +
-                             piece * 16;
-            __builtin_nontemporal_store(v[j], (gu32x4*)(dst + o));
-          }
+      for (int j = 0; j < kUnroll; ++j) {
+        const int u = u0 + j * kThreads;
+        const bool is_v = u >= KU;
+        const int uu = is_v ? u - KU : u;
+        const int units = is_v ? vu : ku;
+        const int rr = static_cast<int>(div_by(uu, is_v ? dv.m_vunits : dv.m_kunits));
+        const int piece = uu - rr * units;
+        const int slot = slot_of[j];
+        const int head = rr - slot * n_kv;
+        if (u < TU && slot < t_end) {
+          const int rec = is_v ? lv.v_rec : lv.k_rec;
+          const size_t o = ((static_cast<size_t>(b) * n_kv + head) * a.t_out + blk * bs + slot) * rec +
+                           piece * 16;
+          __builtin_nontemporal_store(v[j], (gu32x4*)((is_v ? vout : kout) + o));
         }
       }
     }
   }
+}
+
+uint32_t reciprocal(uint32_t d) {  // ceil(2^32 / d); 0 for d = 1
+  return d <= 1 ? 0u : static_cast<uint32_t>(((uint64_t{1} << 32) + d - 1) / d);
 }
 
 }  // namespace
@@ -153,7 +190,14 @@ hipError_t launch_gather(const GatherArgs& a, hipStream_t s) {
   if (total == 0) return hipSuccess;
   if (total > (1LL << 30)) return hipErrorInvalidValue;
   const int grid = round_up(static_cast<int>(total), kXcds);
-  hipLaunchKernelGGL(gather_kernel, dim3(grid), dim3(kThreads), 0, s, a);
+  const uint32_t ku = a.lv.k_rec / 16, vu = a.lv.v_rec / 16, n_kv = a.lv.n_kv;
+  // the reciprocal divisions are exact while n < 2^32 / d for every index n
+  const uint64_t recs = static_cast<uint64_t>(bs) * n_kv;
+  const uint64_t max_units = recs * (ku > vu ? ku : vu);
+  const uint64_t max_div = ku > vu ? (ku > n_kv ? ku : n_kv) : (vu > n_kv ? vu : n_kv);
+  if (ku == 0 || vu == 0 || max_units * max_div >= (uint64_t{1} << 32)) return hipErrorInvalidValue;
+  const GatherDiv dv{reciprocal(ku), reciprocal(vu), reciprocal(n_kv)};
+  hipLaunchKernelGGL(gather_kernel, dim3(grid), dim3(kThreads), 0, s, a, dv);
   return hipGetLastError();
 }
 

@@ -25,6 +25,7 @@
 // chunk's workgroup also counts the sequence's runs over the whole row list
 // for n_runs_out.
 #include "device_common.h"
+#include "index_math.h"
 #include "internal.h"
 
 namespace pagedkv {
@@ -51,12 +52,6 @@ typedef __attribute__((address_space(1))) u32x4 gu32x4;
 
 __device__ __forceinline__ int slab_of(int32_t row, const LayerView& lv) {
   return (row < 0 || row >= lv.capacity_rows) ? -1 : row / lv.slab_blocks;
-}
-
-// n / d for the divisor behind m = ceil(2^32 / d) (m = 0: d = 1): one high
-// multiply, exact while n < 2^32 / d, which the launch checks.
-__device__ __forceinline__ uint32_t div_by(uint32_t n, uint32_t m) {
-  return m ? __umulhi(n, m) : n;
 }
 
 struct GatherDiv {
@@ -177,9 +172,7 @@ __global__ __launch_bounds__(kThreads) void gather_kernel(GatherArgs a, GatherDi
   }
 }
 
-uint32_t reciprocal(uint32_t d) {  // ceil(2^32 / d); 0 for d = 1
-  return d <= 1 ? 0u : static_cast<uint32_t>(((uint64_t{1} << 32) + d - 1) / d);
-}
+
 
 }  // namespace
 
@@ -196,7 +189,7 @@ hipError_t launch_gather(const GatherArgs& a, hipStream_t s) {
   const uint64_t max_units = recs * (ku > vu ? ku : vu);
   const uint64_t max_div = ku > vu ? (ku > n_kv ? ku : n_kv) : (vu > n_kv ? vu : n_kv);
   if (ku == 0 || vu == 0 || max_units * max_div >= (uint64_t{1} << 32)) return hipErrorInvalidValue;
-  const GatherDiv dv{reciprocal(ku), reciprocal(vu), reciprocal(n_kv)};
+  const GatherDiv dv{reciprocal_u32(ku), reciprocal_u32(vu), reciprocal_u32(n_kv)};
   hipLaunchKernelGGL(gather_kernel, dim3(grid), dim3(kThreads), 0, s, a, dv);
   return hipGetLastError();
 }

@@ -440,6 +440,7 @@ pd_status pd_write_block(pd_pool* p, int32_t layer, int32_t n, const int32_t* ro
   a.signs = p->d_signs;
   a.inv_sqrt_d = p->inv_sqrt_d;
   hipError_t e = launch_write_block(a, p->desc.format, stream);
+  if (e == hipErrorInvalidValue) return fail(PD_ERR_UNSUPPORTED, "no write_block kernel for this shape");
   if (e != hipSuccess) return hip_fail(e, "write_block launch");
   return PD_OK;
 }

@@ -10,9 +10,10 @@
 // (mlx-swift-lm PR #142, "Add packed paged KV formats with bounded workspace
 // admission", section "Summary" and the "After" flowchart: "quantize fresh
 // K/V once"): K is rotated by H diag(sigma) / sqrt(D) with a fast
-// Walsh-Hadamard butterfly network, then each group of 32 values is mapped to
-// unsigned codes with an fp32 (scale, offset) pair.
+// Walsh-Hadamard butterfly network, then each group of 32 or 64 values is
+// mapped to unsigned codes with an fp32 (scale, offset) pair.
 #include "device_common.h"
+#include "index_math.h"
 #include "internal.h"
 
 namespace pagedkv {
@@ -50,7 +51,10 @@ __device__ __forceinline__ size_t token_in_slab(const LayerView& lv, int32_t row
 }
 
 // 16-bit pools: one workgroup per token copies its n_kv records of K and V
-// (contiguous in the source and in the slab) as 16-byte vectors.
+// (contiguous in the source and in the slab) as 16-byte vectors.  Every lane
+// resolves the target itself, so no barrier stands between the row lookup
+// and the stores; measured fastest when a token fills the workgroup's lanes
+// (2 KiB or more of K).
 __global__ __launch_bounds__(kThreads) void write_block_native_kernel(WriteArgs a) {
   const size_t tok_bytes = static_cast<size_t>(a.lv.n_kv) * a.lv.k_rec;  // == V bytes
   const int n16 = static_cast<int>(tok_bytes / 16);
@@ -69,6 +73,86 @@ __global__ __launch_bounds__(kThreads) void write_block_native_kernel(WriteArgs 
       kd[j] = ks[j];
       vd[j] = vs[j];
     }
+  }
+}
+
+
+// 16-bit pools whose tokens are small (fewer than kWbMultiBelow 16-byte units
+// of K per token): a workgroup copies a chunk of consecutive tokens, each token's
+// n_kv records of K and of V (contiguous in the source and in the slab) as
+// 16-byte vectors.  Unit f of the chunk is 16-byte piece f % (2 n16) of token
+// f / (2 n16) (K pieces, then V pieces); every thread issues kWbLoads source
+// loads first, and the first lanes resolve the chunk's (row, slot) targets
+// into LDS while those loads are in flight.  Several tokens per workgroup keep every lane busy when a
+// token's records are small (1 KiB of K at head_dim 64 with 8 kv heads).
+#ifndef PAGEDKV_WB_LOADS
+#define PAGEDKV_WB_LOADS 4
+#endif
+// Tokens with at least this many 16-byte units of K (2 KiB) take one
+// workgroup each; smaller ones are packed several to a workgroup.
+constexpr int kWbMultiBelow = 128;
+constexpr int kWbLoads = PAGEDKV_WB_LOADS;
+static_assert(2 * kWbMultiBelow <= kThreads * kWbLoads, "a token of the multi-token kernel fits one batch");
+constexpr int kWbMaxTokens = kThreads * kWbLoads / 16 > 0 ? kThreads * kWbLoads / 16 : 1;
+
+__global__ __launch_bounds__(kThreads) void write_block_native_multi_kernel(WriteArgs a, int tpw, uint32_t m_upt) {
+  __shared__ char* s_kd[kWbMaxTokens];  // slab address of each token of the chunk, null = skip
+  __shared__ char* s_vd[kWbMaxTokens];
+  const size_t tok_bytes = static_cast<size_t>(a.lv.n_kv) * a.lv.k_rec;  // == V bytes
+  const int n16 = static_cast<int>(tok_bytes / 16);
+  const int upt = 2 * n16;  // units per token
+  const char* ksrc = static_cast<const char*>(a.k_src);
+  const char* vsrc = static_cast<const char*>(a.v_src);
+  uint4 v[kWbLoads];
+  // unit f of the chunk starting at token i0: source loads (they do not
+  // depend on the targets) and stores to the resolved targets
+  auto load = [&](int i0, int f0, int total) {
+#pragma unroll
+    for (int j = 0; j < kWbLoads; ++j) {
+      const int f = f0 + j * kThreads;
+      if (f < total) {
+        const int t = static_cast<int>(div_by(f, m_upt));
+        const int r = f - t * upt;
+        const bool is_v = r >= n16;
+        const size_t off = static_cast<size_t>(i0 + t) * tok_bytes + static_cast<size_t>(is_v ? r - n16 : r) * 16;
+        v[j] = *reinterpret_cast<const uint4*>((is_v ? vsrc : ksrc) + off);
+      }
+    }
+  };
+  auto store = [&](int f0, int total) {
+#pragma unroll
+    for (int j = 0; j < kWbLoads; ++j) {
+      const int f = f0 + j * kThreads;
+      if (f < total) {
+        const int t = static_cast<int>(div_by(f, m_upt));
+        const int r = f - t * upt;
+        const bool is_v = r >= n16;
+        char* d = is_v ? s_vd[t] : s_kd[t];
+        if (d) *reinterpret_cast<uint4*>(d + static_cast<size_t>(is_v ? r - n16 : r) * 16) = v[j];
+      }
+    }
+  };
+  for (int i0 = blockIdx.x * tpw; i0 < a.n; i0 += gridDim.x * tpw) {
+    const int nt = min(tpw, a.n - i0);
+    const int total = nt * upt;
+    __syncthreads();  // the previous chunk's targets are no longer read
+    load(i0, threadIdx.x, total);
+    if (threadIdx.x < nt) {
+      const int i = i0 + threadIdx.x;
+      const int32_t row = a.rows[i], slot = a.slots[i];
+      char* kd = nullptr;
+      char* vd = nullptr;
+      if (valid_target(a.lv, row, slot, true)) {
+        int slab;
+        const size_t tok = token_in_slab(a.lv, row, slot, &slab);
+        kd = static_cast<char*>(const_cast<void*>(a.lv.k_tab[slab])) + tok * tok_bytes;
+        vd = static_cast<char*>(const_cast<void*>(a.lv.v_tab[slab])) + tok * tok_bytes;
+      }
+      s_kd[threadIdx.x] = kd;
+      s_vd[threadIdx.x] = vd;
+    }
+    __syncthreads();
+    store(threadIdx.x, total);  // one batch covers the chunk: tpw * upt <= kThreads * kWbLoads
   }
 }
 
@@ -302,8 +386,21 @@ hipError_t launch_row_move(const RowMoveArgs& a, int mode, hipStream_t s) {
 hipError_t launch_write_block(const WriteArgs& a, int32_t format, hipStream_t s) {
   if (a.n == 0) return hipSuccess;
   if (format == PD_FMT_FP16 || format == PD_FMT_BF16) {
-    const int grid = a.n < 65536 ? a.n : 65536;
-    hipLaunchKernelGGL(write_block_native_kernel, dim3(grid), dim3(kThreads), 0, s, a);
+    const long long upt = 2LL * a.lv.n_kv * a.lv.k_rec / 16;  // 16-byte units per token
+    if (upt / 2 >= kWbMultiBelow) {
+      const int grid = a.n < 65536 ? a.n : 65536;
+      hipLaunchKernelGGL(write_block_native_kernel, dim3(grid), dim3(kThreads), 0, s, a);
+      return hipGetLastError();
+    }
+    int tpw = static_cast<int>(kThreads * kWbLoads / upt);
+    tpw = tpw < 1 ? 1 : (tpw > kWbMaxTokens ? kWbMaxTokens : tpw);
+    // the reciprocal division is exact while every unit index f < tpw * upt
+    // stays below 2^32 / upt
+    if (upt < 2 || static_cast<uint64_t>(tpw) * upt * upt >= (uint64_t{1} << 32)) return hipErrorInvalidValue;
+    const long long chunks = (a.n + tpw - 1) / tpw;
+    const int grid = static_cast<int>(chunks < 65536 ? chunks : 65536);
+    hipLaunchKernelGGL(write_block_native_multi_kernel, dim3(grid), dim3(kThreads), 0, s, a, tpw,
+                       reciprocal_u32(static_cast<uint32_t>(upt)));
     return hipGetLastError();
   }
   const long long waves = (2LL * a.n * a.lv.n_kv * (a.head_dim / 8) + kWave - 1) / kWave;

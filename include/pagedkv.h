@@ -219,6 +219,8 @@ pd_status pd_slab_for_row(const pd_pool* pool, int32_t layer, int64_t row, void*
  * A row outside [0, capacity_rows) or a slot outside [0, block_size) sets a
  * device error bit and that token is skipped.  Two tokens with the same
  * (row, slot) in one call give an unspecified winner.  n == 0 is a no-op.
+ * Errors: PD_ERR_ARG (null or misaligned pointers, n < 0), PD_ERR_RANGE
+ * (layer), PD_ERR_HIP.
  */
 pd_status pd_write_block(pd_pool* pool, int32_t layer, int32_t n, const int32_t* rows,
                          const int32_t* slots, const void* k_src, const void* v_src,

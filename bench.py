@@ -349,7 +349,17 @@ def run_qwen3_0p6b(args, torch, pd):
 
     timer = Timer(torch)
 
+    # A decode step: every layer appends the sequences' newest token (position
+    # n - 1) and attends over all n tokens, in one launch of the split kernel
+    # plus the combine (pd_paged_decode_append).  The unfused step (write_block,
+    # then paged_decode) does the same work in three launches per layer; it
+    # is timed beside and must give the same bits.
     def step():
+        for layer in range(L):
+            pool.paged_decode_append(layer, qs[layer], k_new[layer], v_new[layer], table, lens, n,
+                                     w.scale, outs[layer], ws)
+
+    def step_unfused():
         for layer in range(L):
             pool.write_block(layer, new_rows, new_slots, k_new[layer], v_new[layer])
             pool.paged_decode(layer, qs[layer], table, lens, n, w.scale, outs[layer], ws)
@@ -363,8 +373,17 @@ def run_qwen3_0p6b(args, torch, pd):
     # per-stage launch durations first, right after the warm-up steps
     split_us, combine_us = stage_times(timer, decode_call, range(L), args.steps, torch)
 
+    step_unfused()
+    torch.cuda.synchronize()
+    unfused_out = [o.clone() for o in outs]
+    step()
+    torch.cuda.synchronize()
+    if not all(torch.equal(a, b) for a, b in zip(unfused_out, outs)):
+        raise RuntimeError("the fused append step differs from write_block + paged_decode")
+    del unfused_out
+
     # The step as a serving loop runs it: captured once into a HIP graph and
-    # replayed (28 x write_block + split + combine, no host work per launch).
+    # replayed (28 x append-and-split + combine, no host work per launch).
     graph = Graph(torch, step)
     check_graph_replays(torch, step, graph, outs)
     for _ in range(args.warmup):
@@ -374,6 +393,12 @@ def run_qwen3_0p6b(args, torch, pd):
     if pool.check_error():
         raise RuntimeError("device error during the timed steps")
     eager_ms = timer(step, args.steps) / 1e3
+    graph_unfused = Graph(torch, step_unfused)
+    check_graph_replays(torch, step_unfused, graph_unfused, outs)
+    for _ in range(args.warmup):
+        graph_unfused()
+    unfused_ms = timer(graph_unfused, args.steps) / 1e3
+    del graph_unfused
 
     d_bytes = decode_bytes(lengths, n_kv, n_q, D, bs)
     w_bytes = write_bytes(B, n_kv, D)
@@ -417,8 +442,11 @@ def run_qwen3_0p6b(args, torch, pd):
         "pct_of_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
         "kv_tokens_attended_per_s": round(sum(lengths) * L / (step_ms * 1e-3), 1),
         "roofline": rl,
-        "step_timing": "HIP graph of the 28-layer step, replayed; every replay checked bit-equal to the eager step",
+        "step_timing": ("HIP graph of the 28-layer step (per layer: append the newest token and attend, "
+                        "then combine), replayed; every replay checked bit-equal to the eager step, and "
+                        "the step bit-equal to write_block + paged_decode"),
         "eager_ms_per_step": round(eager_ms, 4),
+        "unfused_ms_per_step": round(unfused_ms, 4),
         "paged_decode": {"split_us": round(split_us, 3), "combine_us": round(combine_us, 3),
                          "achieved_gbs_both_stages": round(d_bytes / ((split_us + combine_us) * 1e-6) / 1e9, 1)},
         "write_block": {"decode_step_bytes_per_launch": w_bytes,

@@ -90,7 +90,7 @@ EXPORTS = [
     "pd_version", "pd_last_error", "pd_record_bytes", "pd_pool_create", "pd_pool_destroy",
     "pd_slab_bytes", "pd_append_slab", "pd_slabs_needed", "pd_reserve_rows", "pd_slab_for_row",
     "pd_write_block", "pd_copy_on_write_block", "pd_gather_visible", "pd_decode_workspace_bytes",
-    "pd_paged_decode",
+    "pd_paged_decode", "pd_paged_decode_append",
     "pd_paged_decode_split", "pd_paged_decode_combine", "pd_pool_stats", "pd_pool_check_error",
     "pd_signs_hash", "pd_storage_identity_of", "pd_identity_check", "pd_block_bytes",
     "pd_export_blocks", "pd_import_blocks", "pd_dense_workspace_bytes", "pd_dense_decode",
@@ -119,6 +119,8 @@ def _declare(lib):
         "pd_gather_visible": (_i32, [_vp, _i32, _i32, _vp, _i32, _vp, _i32, _vp, _vp, _vp, _vp]),
         "pd_decode_workspace_bytes": (_i32, [_vp, _i32, _i32, _i32, ctypes.POINTER(_sz)]),
         "pd_paged_decode": (_i32, [_vp, _i32, _i32, _i32, _vp, _vp, _i32, _vp, _i32,
+                                   ctypes.c_float, _vp, _vp, _sz, _vp]),
+        "pd_paged_decode_append": (_i32, [_vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _i32, _vp, _i32,
                                    ctypes.c_float, _vp, _vp, _sz, _vp]),
         "pd_paged_decode_split": (_i32, [_vp, _i32, _i32, _i32, _vp, _vp, _i32, _vp, _i32,
                                          ctypes.c_float, _vp, _vp, _sz, _vp]),
@@ -415,6 +417,28 @@ def paged_decode(pool: int, layer: int, q: torch.Tensor, block_table: torch.Tens
                                  _stream(stream)))
 
 
+def paged_decode_append(pool: int, layer: int, q: torch.Tensor, k_new: torch.Tensor,
+                        v_new: torch.Tensor, block_table: torch.Tensor, lens: torch.Tensor,
+                        max_len: int, scale: float, out: torch.Tensor, workspace: torch.Tensor,
+                        stream=None) -> None:
+    """pd_paged_decode_append: write token lens[b] - 1 of every sequence from
+    k_new/v_new [B, n_kv, D], then attend (one launch of the split kernel)."""
+    B, n_q, D = q.shape
+    _require(q, "q")
+    _require(k_new, "k_new", q.dtype)
+    _require(v_new, "v_new", q.dtype, k_new.numel())
+    _require(block_table, "block_table", torch.int32)
+    _require(lens, "lens", torch.int32, B)
+    _require(out, "out", q.dtype, q.numel())
+    _require(workspace, "workspace")
+    if block_table.shape[0] != B or k_new.shape[0] != B:
+        raise ValueError("block_table rows and k_new's first dimension must equal the batch size")
+    _check(lib().pd_paged_decode_append(pool, layer, B, n_q, _ptr(q), _ptr(k_new), _ptr(v_new),
+                                        _ptr(block_table), block_table.shape[1], _ptr(lens), max_len,
+                                        float(scale), _ptr(out), _ptr(workspace),
+                                        workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
 def pool_stats(pool: int) -> dict:
     s = PoolStats()
     _check(lib().pd_pool_stats(pool, ctypes.byref(s)))
@@ -555,6 +579,13 @@ class SlabPool:
                      stream=None, stage="all"):
         paged_decode(self.handle, layer, q, block_table, lens, max_len, scale, out, workspace,
                      stream, stage)
+
+    def paged_decode_append(self, layer, q, k_new, v_new, block_table, lens, max_len, scale, out,
+                            workspace, stream=None):
+        if k_new.numel() != q.shape[0] * self.n_kv_heads * self.head_dim:
+            raise ValueError("k_new must be [B, n_kv_heads, head_dim]")
+        paged_decode_append(self.handle, layer, q, k_new, v_new, block_table, lens, max_len, scale,
+                            out, workspace, stream)
 
     def stats(self) -> dict:
         return pool_stats(self.handle)

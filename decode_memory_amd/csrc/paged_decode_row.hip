@@ -186,7 +186,8 @@ __global__ __launch_bounds__(kRowThreads, PAGEDKV_ROW_WAVES_PER_SIMD) void paged
   }
 
   const int cap_len = min(a.max_blocks, n_split * a.blocks_per_split) * kBS;
-  if (len < 0 || len > cap_len) {
+  const bool len_ok = len >= 0 && len <= cap_len;
+  if (!len_ok) {
     if (threadIdx.x == 0 && s == 0 && hset == 0) set_error(lv.err, PD_DEVERR_LENGTH);
     len = len < 0 ? 0 : cap_len;
   }
@@ -207,6 +208,31 @@ __global__ __launch_bounds__(kRowThreads, PAGEDKV_ROW_WAVES_PER_SIMD) void paged
     for (int e = 0; e < 8; ++e) acc[i][e] = 0.f;
   }
   const uint32_t lane_off = static_cast<uint32_t>(kvh * D * 2 + c * 16);
+
+  // Fused append (pd_paged_decode_append): token len - 1 of the sequence is
+  // new.  The workgroup whose split owns its block -- the only one that reads
+  // those bytes -- stores this workgroup's kv heads of it (each head group's
+  // slice-0 wave, 16 bytes per lane of K and of V, laid out [n_kv, D] as in
+  // a token row) before any tile is requested; the stores are waited for
+  // and a barrier orders them before every wave's loads.  A rejected length
+  // or row appends nothing.
+  if (a.k_new && len_ok && len > 0) {
+    const int p = len - 1;
+    const int jb = p / kBS;
+    if (jb % n_split == s) {  // uniform over the workgroup
+      const int jj = jb / n_split;  // this split's jj-th block
+      if (slice == 0 && ((ok_mask >> jj) & 1)) {
+        const size_t src = static_cast<size_t>(b) * tok_bytes + lane_off;
+        const uint32_t off = lane_off + static_cast<uint32_t>(p % kBS) * tok_bytes;
+        const uint4 kn = *reinterpret_cast<const uint4*>(static_cast<const char*>(a.k_new) + src);
+        const uint4 vn = *reinterpret_cast<const uint4*>(static_cast<const char*>(a.v_new) + src);
+        *reinterpret_cast<uint4*>(const_cast<char*>(lane_ptr(kaddr, jj)) + off) = kn;
+        *reinterpret_cast<uint4*>(const_cast<char*>(lane_ptr(vaddr, jj)) + off) = vn;
+      }
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the stores have reached L2
+      __syncthreads();
+    }
+  }
 
   // Tile i: block j = i / NT of the split, tokens (k*SLICES + slice)*kTile +
   // [0, kTile) with k = i % NT -- at any moment the slices of a head group

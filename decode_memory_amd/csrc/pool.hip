@@ -637,7 +637,8 @@ static const int kStageSplit = 1, kStageCombine = 2;
 static pd_status decode_call(pd_pool* p, int32_t layer, int32_t B, int32_t n_q_heads, const void* q,
                       const int32_t* block_table, int32_t max_blocks, const int32_t* lens,
                       int32_t max_len, float scale, void* out, void* workspace,
-                      size_t workspace_bytes, hipStream_t stream, int stages) {
+                      size_t workspace_bytes, hipStream_t stream, int stages,
+                      const void* k_new = nullptr, const void* v_new = nullptr) {
   if (pd_status st = check_pool(p)) return st;
   if (pd_status st = check_layer(p, layer)) return st;
   if (B < 0 || max_blocks < 1 || max_len < 0) return fail(PD_ERR_ARG, "B < 0, max_blocks < 1 or max_len < 0");
@@ -664,6 +665,16 @@ static pd_status decode_call(pd_pool* p, int32_t layer, int32_t B, int32_t n_q_h
   const size_t need = decode_workspace_bytes(B, n_q_heads, p->desc.head_dim, plan.split);
   if (workspace_bytes < need)
     return fail(PD_ERR_CAPACITY, "workspace %zu bytes, %zu needed", workspace_bytes, need);
+  if (k_new || v_new) {
+    if (!k_new || !v_new) return fail(PD_ERR_ARG, "k_new and v_new go together");
+    if ((reinterpret_cast<uintptr_t>(k_new) | reinterpret_cast<uintptr_t>(v_new)) & 15)
+      return fail(PD_ERR_ARG, "k_new and v_new must be 16-byte aligned");
+    if (plan.kind != 1)
+      return fail(PD_ERR_UNSUPPORTED,
+                  "the fused append runs in the 16-bit row kernel only (format %d, head_dim %d, group %d): "
+                  "use pd_write_block, then pd_paged_decode",
+                  p->desc.format, p->desc.head_dim, group);
+  }
   DecodeArgs a{};
   a.lv = layer_view(p, layer);
   a.B = B;
@@ -678,6 +689,8 @@ static pd_status decode_call(pd_pool* p, int32_t layer, int32_t B, int32_t n_q_h
   a.ml_offset = decode_ml_offset(B, n_q_heads, p->desc.head_dim, plan.split);
   a.n_split = plan.split.n_split;
   a.blocks_per_split = plan.split.blocks_per_split;
+  a.k_new = k_new;
+  a.v_new = v_new;
   a.k_bits = p->k_bits;
   a.v_bits = p->v_bits;
   a.qgroup = p->qgroup;
@@ -707,6 +720,16 @@ pd_status pd_paged_decode(pd_pool* p, int32_t layer, int32_t B, int32_t n_q_head
                           size_t workspace_bytes, hipStream_t stream) {
   return decode_call(p, layer, B, n_q_heads, q, block_table, max_blocks, lens, max_len, scale, out,
                      workspace, workspace_bytes, stream, kStageSplit | kStageCombine);
+}
+
+pd_status pd_paged_decode_append(pd_pool* p, int32_t layer, int32_t B, int32_t n_q_heads,
+                                 const void* q, const void* k_new, const void* v_new,
+                                 const int32_t* block_table, int32_t max_blocks, const int32_t* lens,
+                                 int32_t max_len, float scale, void* out, void* workspace,
+                                 size_t workspace_bytes, hipStream_t stream) {
+  if (!k_new || !v_new) return fail(PD_ERR_ARG, "NULL k_new or v_new");
+  return decode_call(p, layer, B, n_q_heads, q, block_table, max_blocks, lens, max_len, scale, out,
+                     workspace, workspace_bytes, stream, kStageSplit | kStageCombine, k_new, v_new);
 }
 
 pd_status pd_paged_decode_split(pd_pool* p, int32_t layer, int32_t B, int32_t n_q_heads,

@@ -302,6 +302,30 @@ pd_status pd_paged_decode(pd_pool* pool, int32_t layer, int32_t B, int32_t n_q_h
                           void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * Append then attend, in one launch of the split kernel: mlxcel #2171
+ * ("refactor: one KV storage abstraction with dense and paged backends",
+ * section "Proposed Solution"): attend(q, k, v, scale, mask) takes the new
+ * token's K and V with its query; mlxcel #235, "Proposed solution", touch
+ * point 1: the write lands in the slab of its row.  Token lens[b] - 1 of each
+ * sequence is the new one: k_new[b], v_new[b] (device [B, n_kv_heads,
+ * head_dim], the pool's 16-bit dtype, 16-byte aligned) are written to row
+ * block_table[b][(lens[b] - 1) / block_size], slot (lens[b] - 1) %
+ * block_size, of `layer`, and the attention reads them there.  Pool bytes
+ * and outputs are bit for bit those of pd_write_block of the same tokens
+ * followed by pd_paged_decode.  Sequences with lens[b] == 0 append nothing;
+ * a length or row the kernel rejects (device error word, as pd_paged_decode)
+ * appends nothing for that sequence.  Other arguments as pd_paged_decode.
+ * Only where the 16-bit row kernel runs (n_kv_heads * head_dim * 2 a multiple
+ * of 1024 bytes, block_size 32, head_dim 64/128/256, group 1/2/4/8); else
+ * PD_ERR_UNSUPPORTED (use pd_write_block, then pd_paged_decode).
+ */
+pd_status pd_paged_decode_append(pd_pool* pool, int32_t layer, int32_t B, int32_t n_q_heads,
+                                 const void* q, const void* k_new, const void* v_new,
+                                 const int32_t* block_table, int32_t max_blocks, const int32_t* lens,
+                                 int32_t max_len, float scale, void* out, void* workspace,
+                                 size_t workspace_bytes, hipStream_t stream);
+
+/*
  * Dense decode: the same attention as pd_paged_decode over per-sequence
  * contiguous K/V, with no pool.  mlxcel #2171 ("refactor: one KV storage
  * abstraction with dense and paged backends", section "Proposed Solution":

@@ -7,9 +7,11 @@ kv heads, head_dim 128, bf16, N(0,1) K/V/Q from fixed seeds, rows allocated
 monotonically per sequence (4 same-slab runs each).
 
 A step is one decode step of the whole batch: for each of the 28 layers,
-write_block stores each sequence's newest token (position len-1) into its
-row's slab, then paged_decode attends over all len tokens.  Inputs are
-resident in HBM before timing starts.  The 28-layer step touches 3.5 GiB of
+paged_decode_append stores each sequence's newest token (position len-1) into
+its row's slab and attends over all len tokens, in the split kernel's launch
+(then the combine).  The unfused form -- write_block, then paged_decode --
+does the same work in three launches per layer; it is checked bit-equal and
+timed beside.  Inputs are resident in HBM before timing starts.  The 28-layer step touches 3.5 GiB of
 KV, far more than the last-level cache, so every layer is read from HBM.
 
 The timed step is captured once into a HIP graph and replayed, as a serving
@@ -28,9 +30,9 @@ own JSON line of the same form:
   fragmented_64      64 sequences of U{512..16384} tokens on rows popped from a
                      shuffled free list; a step writes one new token per
                      sequence (a fresh row at each block boundary) and decodes.
-  qwen3_1p7b_32x16k  28 layers x 32 sequences x 16384 tokens (56 GiB of KV); the
-                     same step as the default, plus gather_visible of a layer
-                     to [32, 8, 16384, 128] per tensor.
+  qwen3_1p7b_32x16k  28 layers x 32 sequences x 16384 tokens (56 GiB of KV); a
+                     write_block + paged_decode step, plus gather_visible of a
+                     layer to [32, 8, 16384, 128] per tensor.
   footprint_8x4k     8 distinct ~4.2k-token prompts prefilled one after another
                      (qwen3-0.6b KV shape): peak HBM of the slab pool over the
                      dense backend's (its own metric; lower is better).

@@ -19,7 +19,8 @@
  *   paged KV formats with bounded workspace admission", section "Summary"):
  *   unsigned codes of the given bit width (8-bit: one byte per value; 4-bit:
  *   value 2i in the low nibble of byte i), then one (fp32 scale, fp32 offset)
- *   pair per group of 32 values, little endian; a value is code*scale+offset.
+ *   pair per group of 32 or 64 values (pd_pool_desc.group_size), little
+ *   endian; a value is code*scale+offset.
  *   K is rotated by the fixed signed Hadamard basis H*diag(sigma)/sqrt(D)
  *   before it is quantised; V is not rotated.  Packed pools take bf16 keys,
  *   values and queries and produce bf16 outputs.

@@ -21,7 +21,8 @@
 // n_split, ...  Whole token rows of a block (every head, K and V) are staged
 // in LDS with 16-byte coalesced loads, the next stage's loads in flight in
 // registers while the current one is computed.  A wave works through its
-// head's tokens 16 at a time:
+// head's tokens in steps of up to 32 (two 16-token sub-tiles whose score
+// products are issued together, then one online-softmax update):
 //   scores: one 16x16x32 product per 32-value k-block (the k-blocks of one
 //     group chain their products), A = q' (query head j in row 4j, other
 //     rows zero), B = the 16 tokens' codes of the k-block;
@@ -61,6 +62,12 @@ namespace {
 #ifndef PAGEDKV_PMFMA_TARGET_WG
 #define PAGEDKV_PMFMA_TARGET_WG 256
 #endif
+// Tokens per online-softmax step: 16-token sub-tiles of one stage whose score
+// products are issued together and whose softmax update is one step (capped
+// by the tokens of a stage).
+#ifndef PAGEDKV_PMFMA_STEP_TOKENS
+#define PAGEDKV_PMFMA_STEP_TOKENS 32
+#endif
 // Token quads of the value products are scheduled one at a time (a
 // scheduling barrier after each) from this many value accumulators up.
 #ifndef PAGEDKV_PMFMA_QUAD_BARRIER_NV
@@ -99,6 +106,9 @@ struct PShape {
   static constexpr int KU = T * KROW / 16, VU = T * VROW / 16;  // 16-byte units
   static constexpr int UPT = (KU + VU + kPThreads - 1) / kPThreads;
   static constexpr int STAGE = T * (PK + PV);
+  // 16-token sub-tiles per softmax step, and the step's tokens
+  static constexpr int NSUB = (PAGEDKV_PMFMA_STEP_TOKENS < T ? PAGEDKV_PMFMA_STEP_TOKENS : T) / 16;
+  static constexpr int STEP = NSUB * 16;
   static_assert(KREC % 16 == 0 && VREC % 16 == 0, "records are whole 16-byte units");
 };
 
@@ -224,9 +234,11 @@ template <int D, int KB, int VB, int G, int GS>
 __global__ __launch_bounds__(kPThreads, kPMinWaves<D>) void paged_decode_packed_mfma_kernel(DecodeArgs a) {
   using S = PShape<D, KB, VB, GS>;
   constexpr int NKB = S::NKB, NMG = S::NMG, KPG = S::KPG, T = S::T, PK = S::PK, PV = S::PV;
+  constexpr int NSUB = S::NSUB, STEP = S::STEP;
   constexpr int KREC = S::KREC, VREC = S::VREC, KROW = S::KROW, VROW = S::VROW;
   constexpr int NV = D / 64;  // value accumulators (64 dimensions each, one per lane)
-  constexpr int AUX = (G * D > NMG * 4 * kSub) ? G * D : NMG * 4 * kSub;  // floats per wave
+  // floats per wave: the q' transform, then p^T as f16 [group][4][STEP]
+  constexpr int AUX = (G * D > NMG * 2 * STEP) ? G * D : NMG * 2 * STEP;
   static_assert(G <= 4, "query heads of a kv head take rows 0, 4, 8, 12");
 
   __shared__ __attribute__((aligned(16))) unsigned char s_stage[S::STAGE];
@@ -383,7 +395,7 @@ __global__ __launch_bounds__(kPThreads, kPMinWaves<D>) void paged_decode_packed_
   for (int g = 0; g < NMG; ++g) bias[g] = 0.f;
 #pragma unroll
   for (int i = 0; i < NV; ++i) acc[i] = f4{0.f, 0.f, 0.f, 0.f};
-  // p * scale * 1024 as f16: [group][query head][token of the sub-tile]
+  // p * scale * 1024 as f16: [group][query head][token of the step]
   _Float16* sp = reinterpret_cast<_Float16*>(s_aux[h]);
 
   for (int i = 0; i < n_stages; ++i) {
@@ -406,41 +418,60 @@ __global__ __launch_bounds__(kPThreads, kPMinWaves<D>) void paged_decode_packed_
     const int jb = i / SPB, t0 = (i % SPB) * T;
     const int nt = ((ok_mask >> jb) & 1) ? min(kPBS, len - (s + jb * n_split) * kPBS) : 0;
 #pragma unroll
-    for (int sub = 0; sub < T / kSub; ++sub) {
-      const int lt0 = sub * kSub;  // first token of the sub-tile in the stage
-      if (t0 + lt0 >= nt) break;   // uniform: the rest of the stage is past the length
+    for (int st = 0; st < T / STEP; ++st) {
+      const int lt0 = st * STEP;  // first token of the step in the stage
+      if (t0 + lt0 >= nt) break;  // uniform: the rest of the stage is past the length
 
-      // scores: lane (n, J) = (token n, query head J)
-      const unsigned char* krow = s_stage + (lt0 + n) * PK + h * KREC;
-      float sv = 0.f;
+      // scores of each sub-tile: lane (n, J) = (token n, query head J);
+      // sub-tiles past the length are computed and masked
+      float sc[NSUB];
+      bool tv[NSUB];
 #pragma unroll
-      for (int mg = 0; mg < NMG; ++mg) {
-        // the k-blocks of one group accumulate in one product chain
-        f4 c = f4{0.f, 0.f, 0.f, 0.f};
+      for (int u = 0; u < NSUB; ++u) {
+        const unsigned char* krow = s_stage + (lt0 + u * kSub + n) * PK + h * KREC;
+        float sv = 0.f;
 #pragma unroll
-        for (int kk = 0; kk < KPG; ++kk) {
-          const int g = mg * KPG + kk;
-          const h8 bk = key_codes<KB>(krow + g * (32 * KB / 8) + J * KB);
-          c = __builtin_amdgcn_mfma_f32_16x16x32_f16(aq[g], bk, c, 0, 0, 0);
+        for (int mg = 0; mg < NMG; ++mg) {
+          // the k-blocks of one group accumulate in one product chain
+          f4 c = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int kk = 0; kk < KPG; ++kk) {
+            const int g = mg * KPG + kk;
+            const h8 bk = key_codes<KB>(krow + g * (32 * KB / 8) + J * KB);
+            c = __builtin_amdgcn_mfma_f32_16x16x32_f16(aq[g], bk, c, 0, 0, 0);
+          }
+          const float2 km = *reinterpret_cast<const float2*>(krow + S::KCODE + 8 * mg);
+          sv = fmaf(c[0] - kbias[mg], km.x, fmaf(km.y, qsum[mg], sv));
         }
-        const float2 km = *reinterpret_cast<const float2*>(krow + S::KCODE + 8 * mg);
-        sv = fmaf(c[0] - kbias[mg], km.x, fmaf(km.y, qsum[mg], sv));
+        tv[u] = J < G && t0 + lt0 + u * kSub + n < nt;
+        sc[u] = tv[u] ? sv : -INFINITY;
       }
-      const bool tv = J < G && t0 + lt0 + n < nt;
-      const float sc = tv ? sv : -INFINITY;
-      const float m_new = fmaxf(m_run, row_max16(sc));  // -inf while nothing is visible
+      float mx = sc[0];
+#pragma unroll
+      for (int u = 1; u < NSUB; ++u) mx = fmaxf(mx, sc[u]);
+      const float m_new = fmaxf(m_run, row_max16(mx));  // -inf while nothing is visible
       const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
-      const float p = (sc == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(sc - m_new);
+      float p[NSUB];
+#pragma unroll
+      for (int u = 0; u < NSUB; ++u) p[u] = (sc[u] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(sc[u] - m_new);
       m_run = m_new;
-      l_run = fmaf(l_run, alpha, p);
-      const float pk = p * kPScale;
-      // value metadata of token n; invisible tokens add nothing even if it is garbage
-      const unsigned char* vrow = s_stage + T * PK + (lt0 + n) * PV + h * VREC;
+      l_run = fmaf(l_run, alpha, p[0]);
+#pragma unroll
+      for (int u = 1; u < NSUB; ++u) l_run += p[u];
+      // value metadata of the step's tokens; invisible tokens add nothing even
+      // if it is garbage
 #pragma unroll
       for (int g = 0; g < NMG; ++g) {
-        const float2 vm = *reinterpret_cast<const float2*>(vrow + S::VCODE + 8 * g);
-        bias[g] = fmaf(bias[g], alpha, tv ? p * vm.y : 0.f);
-        sp[(g * 4 + J) * kSub + n] = static_cast<_Float16>(tv ? pk * vm.x : 0.f);
+        float bg = bias[g];
+#pragma unroll
+        for (int u = 0; u < NSUB; ++u) {
+          const unsigned char* vrow = s_stage + T * PK + (lt0 + u * kSub + n) * PV + h * VREC;
+          const float2 vm = *reinterpret_cast<const float2*>(vrow + S::VCODE + 8 * g);
+          const float term = tv[u] ? p[u] * vm.y : 0.f;
+          bg = u == 0 ? fmaf(bg, alpha, term) : bg + term;
+          sp[(g * 4 + J) * STEP + u * kSub + n] = static_cast<_Float16>(tv[u] ? (p[u] * kPScale) * vm.x : 0.f);
+        }
+        bias[g] = bg;
       }
       if (__ballot(alpha != 1.f)) {
         // alpha of query head r is uniform over score row r
@@ -459,13 +490,13 @@ __global__ __launch_bounds__(kPThreads, kPMinWaves<D>) void paged_decode_packed_
       // 4-bit codes, 64 dimensions: the nibble of this lane, in place
       const uint32_t nib_mask = lane < 32 ? 0x000f000fu : 0x00f000f0u;
 #pragma unroll
-      for (int tq = 0; tq < kSub / 4; ++tq) {
+      for (int tq = 0; tq < STEP / 4; ++tq) {
         const unsigned char* vtok = s_stage + T * PK + (lt0 + 4 * tq) * PV + h * VREC;
         if constexpr (VB == 8) {
 #pragma unroll
           for (int i = 0; i < NV; ++i) {
             const int d = 64 * i + lane;
-            const h4 ap = *reinterpret_cast<const h4*>(sp + (d / GS * 4 + qa) * kSub + 4 * tq);
+            const h4 ap = *reinterpret_cast<const h4*>(sp + (d / GS * 4 + qa) * STEP + 4 * tq);
             uint32_t x01, x23;
             byte_column<PV>(vtok + d, x01, x23);
             const uint32_t u2[2] = {unbias(x01 | kBias2), unbias(x23 | kBias2)};
@@ -475,7 +506,7 @@ __global__ __launch_bounds__(kPThreads, kPMinWaves<D>) void paged_decode_packed_
           // 4-bit codes, 64 dimensions: lane l takes code byte l % 32 of the 4
           // tokens and its low (l < 32) or high nibble: dimension vdim(0, l)
           const int bi = lane % 32;
-          const h4 ap = *reinterpret_cast<const h4*>(sp + (bi / (GS / 2) * 4 + qa) * kSub + 4 * tq);
+          const h4 ap = *reinterpret_cast<const h4*>(sp + (bi / (GS / 2) * 4 + qa) * STEP + 4 * tq);
           uint32_t x01, x23;
           byte_column<PV>(vtok + bi, x01, x23);
           const uint32_t u2[2] = {unbias((x01 & nib_mask) | kBias2), unbias((x23 & nib_mask) | kBias2)};
@@ -487,7 +518,7 @@ __global__ __launch_bounds__(kPThreads, kPMinWaves<D>) void paged_decode_packed_
 #pragma unroll
           for (int k = 0; k < NV / 2; ++k) {
             const int bi = lane + 64 * k;
-            const h4 ap = *reinterpret_cast<const h4*>(sp + (bi / (GS / 2) * 4 + qa) * kSub + 4 * tq);
+            const h4 ap = *reinterpret_cast<const h4*>(sp + (bi / (GS / 2) * 4 + qa) * STEP + 4 * tq);
             uint32_t x01, x23;
             byte_column<PV>(vtok + bi, x01, x23);
             const uint32_t ul[2] = {unbias((x01 & 0x000f000fu) | kBias2), unbias((x23 & 0x000f000fu) | kBias2)};

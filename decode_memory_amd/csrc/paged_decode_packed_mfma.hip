@@ -422,13 +422,10 @@ __global__ __launch_bounds__(kPThreads, kPMinWaves<D>) void paged_decode_packed_
       const int lt0 = st * STEP;  // first token of the step in the stage
       if (t0 + lt0 >= nt) break;  // uniform: the rest of the stage is past the length
 
-      // scores of each sub-tile: lane (n, J) = (token n, query head J);
-      // sub-tiles past the length are computed and masked
-      float sc[NSUB];
-      bool tv[NSUB];
-#pragma unroll
-      for (int u = 0; u < NSUB; ++u) {
-        const unsigned char* krow = s_stage + (lt0 + u * kSub + n) * PK + h * KREC;
+      float alpha;
+      if constexpr (NSUB == 1) {
+        // scores: lane (n, J) = (token n, query head J)
+        const unsigned char* krow = s_stage + (lt0 + n) * PK + h * KREC;
         float sv = 0.f;
 #pragma unroll
         for (int mg = 0; mg < NMG; ++mg) {
@@ -443,35 +440,87 @@ __global__ __launch_bounds__(kPThreads, kPMinWaves<D>) void paged_decode_packed_
           const float2 km = *reinterpret_cast<const float2*>(krow + S::KCODE + 8 * mg);
           sv = fmaf(c[0] - kbias[mg], km.x, fmaf(km.y, qsum[mg], sv));
         }
-        tv[u] = J < G && t0 + lt0 + u * kSub + n < nt;
-        sc[u] = tv[u] ? sv : -INFINITY;
-      }
-      float mx = sc[0];
+        const bool tv = J < G && t0 + lt0 + n < nt;
+        const float sc = tv ? sv : -INFINITY;
+        const float m_new = fmaxf(m_run, row_max16(sc));  // -inf while nothing is visible
+        alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+        const float p = (sc == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(sc - m_new);
+        m_run = m_new;
+        l_run = fmaf(l_run, alpha, p);
+        const float pk = p * kPScale;
+        // value metadata of token n; invisible tokens add nothing even if it is garbage
+        const unsigned char* vrow = s_stage + T * PK + (lt0 + n) * PV + h * VREC;
 #pragma unroll
-      for (int u = 1; u < NSUB; ++u) mx = fmaxf(mx, sc[u]);
-      const float m_new = fmaxf(m_run, row_max16(mx));  // -inf while nothing is visible
-      const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
-      float p[NSUB];
+        for (int g = 0; g < NMG; ++g) {
+          const float2 vm = *reinterpret_cast<const float2*>(vrow + S::VCODE + 8 * g);
+          bias[g] = fmaf(bias[g], alpha, tv ? p * vm.y : 0.f);
+          sp[(g * 4 + J) * STEP + n] = static_cast<_Float16>(tv ? pk * vm.x : 0.f);
+        }
+      } else {
+        // scores of each sub-tile: lane (n, J) = (token n, query head J);
+        // sub-tiles past the length are computed and masked
+        float sc[NSUB];
+        bool tv[NSUB];
 #pragma unroll
-      for (int u = 0; u < NSUB; ++u) p[u] = (sc[u] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(sc[u] - m_new);
-      m_run = m_new;
-      l_run = fmaf(l_run, alpha, p[0]);
+        for (int u = 0; u < NSUB; ++u) {
+          const unsigned char* krow = s_stage + (lt0 + u * kSub + n) * PK + h * KREC;
+          float sv = 0.f;
 #pragma unroll
-      for (int u = 1; u < NSUB; ++u) l_run += p[u];
-      // value metadata of the step's tokens; invisible tokens add nothing even
-      // if it is garbage
+          for (int mg = 0; mg < NMG; ++mg) {
+            f4 c = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int g = 0; g < NMG; ++g) {
-        float bg = bias[g];
+            for (int kk = 0; kk < KPG; ++kk) {
+              const int g = mg * KPG + kk;
+              const h8 bk = key_codes<KB>(krow + g * (32 * KB / 8) + J * KB);
+              c = __builtin_amdgcn_mfma_f32_16x16x32_f16(aq[g], bk, c, 0, 0, 0);
+            }
+            const float2 km = *reinterpret_cast<const float2*>(krow + S::KCODE + 8 * mg);
+            sv = fmaf(c[0] - kbias[mg], km.x, fmaf(km.y, qsum[mg], sv));
+          }
+          tv[u] = J < G && t0 + lt0 + u * kSub + n < nt;
+          sc[u] = tv[u] ? sv : -INFINITY;
+        }
+        float mx = sc[0];
+#pragma unroll
+        for (int u = 1; u < NSUB; ++u) mx = fmaxf(mx, sc[u]);
+        const float m_new = fmaxf(m_run, row_max16(mx));  // -inf while nothing is visible
+        alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+        float p[NSUB];
+#pragma unroll
+        for (int u = 0; u < NSUB; ++u) {
+          const float e = __builtin_amdgcn_exp2f(sc[u] - m_new);  // NaN when both are -inf: not used
+          p[u] = (sc[u] == -INFINITY) ? 0.f : e;
+        }
+        m_run = m_new;
+        l_run = fmaf(l_run, alpha, p[0]);
+#pragma unroll
+        for (int u = 1; u < NSUB; ++u) l_run += p[u];
+        // value metadata of the step's tokens, all read before any p^T store
+        // (so the reads go out together); invisible tokens add nothing even if
+        // it is garbage
+        float2 vm[NSUB][NMG];
 #pragma unroll
         for (int u = 0; u < NSUB; ++u) {
           const unsigned char* vrow = s_stage + T * PK + (lt0 + u * kSub + n) * PV + h * VREC;
-          const float2 vm = *reinterpret_cast<const float2*>(vrow + S::VCODE + 8 * g);
-          const float term = tv[u] ? p[u] * vm.y : 0.f;
-          bg = u == 0 ? fmaf(bg, alpha, term) : bg + term;
-          sp[(g * 4 + J) * STEP + u * kSub + n] = static_cast<_Float16>(tv[u] ? (p[u] * kPScale) * vm.x : 0.f);
+#pragma unroll
+          for (int g = 0; g < NMG; ++g) {
+            vm[u][g] = *reinterpret_cast<const float2*>(vrow + S::VCODE + 8 * g);
+            // every lane reads (the compiler would otherwise move reads used
+            // only for visible tokens behind a branch)
+            asm volatile("" : "+v"(vm[u][g]));
+          }
         }
-        bias[g] = bg;
+#pragma unroll
+        for (int g = 0; g < NMG; ++g) {
+          float bg = fmaf(bias[g], alpha, tv[0] ? p[0] * vm[0][g].y : 0.f);
+#pragma unroll
+          for (int u = 0; u < NSUB; ++u) {
+            if (u > 0) bg += tv[u] ? p[u] * vm[u][g].y : 0.f;
+            sp[(g * 4 + J) * STEP + u * kSub + n] =
+                static_cast<_Float16>(tv[u] ? (p[u] * kPScale) * vm[u][g].x : 0.f);
+          }
+          bias[g] = bg;
+        }
       }
       if (__ballot(alpha != 1.f)) {
         // alpha of query head r is uniform over score row r

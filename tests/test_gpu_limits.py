@@ -2,9 +2,9 @@
 lengths beyond what a call can read.
 
 At block_size 32 the plan holds 64 blocks per split and 256 splits, 524,288
-tokens: the only length at which the row kernel reads 64 blocks per split
-(its last lane's row and the top bit of the block mask) and the combine
-merges 256 splits.  Keys are all equal there, so the softmax is uniform and
+tokens: the only length at which the row kernel and the packed kernel read
+64 blocks per split (the last lane's row and the top bit of the block mask)
+and the combine merges 256 splits.  Keys are all equal there, so the softmax is uniform and
 the output is the plain mean of the values, a closed form over the periodic
 value pattern (mlxcel #2171, "Proposed Solution": attend(q, k, v, scale,
 mask) with one query token; with equal scores it reduces to the mean)."""
@@ -102,4 +102,45 @@ def test_lengths_beyond_the_call_are_clamped_and_flagged():
         pool.paged_decode(0, q, i32(np.zeros((2, MAX_LEN // BS + 1), np.int32)), i32([1, 1]),
                           MAX_LEN + 1, 0.1, out, pool.workspace(2, n_kv * G, 100))
     assert e.value.status == -4
+    pool.close()
+
+
+@pytest.mark.parametrize("fmt", ["k4v4", "k8v8"])
+def test_longest_packed_sequence_the_plan_holds(fmt):
+    """The packed kernel at the longest plan (256 splits of 64 blocks): equal
+    keys give equal scores, so the output is the mean of the dequantised
+    value records (mlx-swift-lm PR #142, "Add packed paged KV formats with
+    bounded workspace admission", section "Summary": attention reads the
+    packed pages directly), here a closed form over the periodic pattern."""
+    from oracle.packed import FORMATS, dequantise_records, v_records
+    from synth import hadamard_signs
+    n, n_kv, G, D, P = MAX_LEN, 8, 4, 64, 5
+    vb = FORMATS[fmt][1]
+    rng = np.random.default_rng(13)
+    kvec = _bf16(rng.standard_normal((n_kv, D)))
+    pattern = _bf16(rng.standard_normal((P, n_kv, D)))
+    t = np.arange(n)
+    sel = (2 * t[:, None] + np.arange(n_kv)[None, :]) % P
+    v_bits = pattern[sel, np.arange(n_kv)[None, :]]
+    k_bits = np.broadcast_to(kvec, (n, n_kv, D))
+    rows = monotone_rows([n], BS)
+    signs = hadamard_signs(13, D)
+    S = 512
+    pool = pd.SlabPool(1, BS, n_kv, D, S, n // BS // S + 1, fmt, hadamard_signs=signs)
+    pool.reserve_rows(n // BS)
+    pool.write_block(0, i32(rows[0][t // BS]), i32(t % BS),
+                     to_device_bits(np.ascontiguousarray(k_bits), "bf16"),
+                     to_device_bits(np.ascontiguousarray(v_bits), "bf16"))
+    q = to_device_bits(q_bits(13, 0, 1, n_kv * G, D, "bf16"), "bf16")
+    out = torch.empty_like(q)
+    pool.paged_decode(0, q, i32(make_block_table(rows)), i32([n]), n, 1 / 8, out,
+                      pool.workspace(1, n_kv * G, n))
+    torch.cuda.synchronize()
+    assert pool.check_error() == 0
+    deq = dequantise_records(v_records(pattern, vb), D, vb)  # [P, n_kv, D]
+    ref = np.empty((1, n_kv * G, D))
+    for h in range(n_kv):
+        counts = np.bincount(sel[:, h], minlength=P).astype(np.float64)
+        ref[0, h * G:(h + 1) * G] = counts @ deq[:, h] / n
+    assert_decode_close(from_device_bits(out), ref, "bf16", allow_output_rounding=True)
     pool.close()

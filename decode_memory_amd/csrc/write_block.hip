@@ -76,15 +76,15 @@ __global__ __launch_bounds__(kThreads) void write_block_native_kernel(WriteArgs 
   }
 }
 
-
 // 16-bit pools whose tokens are small (fewer than kWbMultiBelow 16-byte units
-// of K per token): a workgroup copies a chunk of consecutive tokens, each token's
-// n_kv records of K and of V (contiguous in the source and in the slab) as
-// 16-byte vectors.  Unit f of the chunk is 16-byte piece f % (2 n16) of token
-// f / (2 n16) (K pieces, then V pieces); every thread issues kWbLoads source
-// loads first, and the first lanes resolve the chunk's (row, slot) targets
-// into LDS while those loads are in flight.  Several tokens per workgroup keep every lane busy when a
-// token's records are small (1 KiB of K at head_dim 64 with 8 kv heads).
+// of K per token): a workgroup copies a chunk of consecutive tokens, each
+// token's n_kv records of K and of V (contiguous in the source and in the
+// slab) as 16-byte vectors.  Unit f of the chunk is 16-byte piece f % (2 n16)
+// of token f / (2 n16) (K pieces, then V pieces); every thread issues
+// kWbLoads source loads first, and the first lanes resolve the chunk's (row,
+// slot) targets into LDS while those loads are in flight.  Several tokens per
+// workgroup keep every lane busy when a token's records are small (1 KiB of K
+// at head_dim 64 with 8 kv heads).
 #ifndef PAGEDKV_WB_LOADS
 #define PAGEDKV_WB_LOADS 4
 #endif

@@ -123,7 +123,8 @@ def pack(codes: np.ndarray, scale: np.ndarray, offset: np.ndarray, bits: int) ->
     else:
         raise ValueError(bits)
     meta = np.stack([scale.astype("<f4"), offset.astype("<f4")], axis=-1)  # [..., ng, 2]
-    meta_bytes = np.ascontiguousarray(meta).view(np.uint8).reshape(codes.shape[:-1] + (-1,))
+    # the width is given, not inferred: numpy cannot infer an axis of an empty array
+    meta_bytes = np.ascontiguousarray(meta).view(np.uint8).reshape(codes.shape[:-1] + (meta.shape[-2] * 8,))
     return np.concatenate([payload.astype(np.uint8), meta_bytes], axis=-1)
 
 

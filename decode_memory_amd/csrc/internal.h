@@ -86,8 +86,8 @@ struct DecodeArgs {
   size_t ml_offset;      // floats
   int32_t n_split;       // split s of a sequence takes logical blocks s, s + n_split, ...
   int32_t blocks_per_split;  // most blocks any split takes (<= 64)
-  // fused append (16-bit pools, row kernel): [B, n_kv, D] of the new token
-  // len_b - 1 of each sequence, or null
+  // fused append (row kernel, packed kernel): [B, n_kv, D] 16-bit values of
+  // the new token len_b - 1 of each sequence (bf16 for packed pools), or null
   const void* k_new;
   const void* v_new;
   // packed formats

@@ -1,0 +1,100 @@
+// Packing one token-head vector of a packed pool: the signed Hadamard
+// rotation of K and the affine group quantisation (mlx-swift-lm PR #142, "Add
+// packed paged KV formats with bounded workspace admission", section
+// "Summary": K is rotated by a fixed signed Hadamard basis, then each group of
+// 32 or 64 values gets unsigned codes with an fp32 (scale, offset) pair).
+// A lane holds 8 consecutive values of the vector and D/8 lanes, aligned to a
+// multiple of D/8, hold the vector.  Every lane of the wave must call these
+// functions (they exchange values across lanes); lanes whose vector is not
+// stored still compute.
+#pragma once
+
+#include "device_common.h"
+
+namespace pagedkv {
+
+// x' = H diag(sigma) x / sqrt(D), with H the Sylvester Hadamard matrix
+// applied as the butterfly network h = 1, 2, ..., D/2, each pair (a, b) ->
+// (a + b, a - b) in fp32 (the lower index gets a + b), then one multiply by
+// 1/sqrt(D).  Stages h < 8 pair values inside a lane, the others pair lanes c
+// and c ^ (h / 8) of the vector's lane group.
+template <int D>
+__device__ __forceinline__ void fwht_rotate8(float (&x)[8], const float* signs, int c,
+                                             float inv_sqrt_d) {
+  constexpr int LPT = D / 8;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) x[e] *= signs[8 * c + e];  // exact sign flips
+#pragma unroll
+  for (int h = 1; h < 8; h <<= 1) {
+    float y[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) y[e] = (e & h) ? __fsub_rn(x[e ^ h], x[e]) : __fadd_rn(x[e], x[e ^ h]);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = y[e];
+  }
+#pragma unroll
+  for (int hl = 1; hl < LPT; hl <<= 1) {
+    const bool upper = (c & hl) != 0;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float other = __shfl_xor(x[e], hl, kWave);
+      x[e] = upper ? __fsub_rn(other, x[e]) : __fadd_rn(x[e], other);
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) x[e] = __fmul_rn(x[e], inv_sqrt_d);
+}
+
+// Quantise the lane's 8 values (values 8c .. 8c+7 of the vector) with the
+// (scale, offset) of their group of GS values, all in fp32: mn = min, mx =
+// max, scale = (mx - mn) / (2^bits - 1), offset = mn, code = clamp(rint((x -
+// mn) / scale)) with round-half-even, and a constant group gets code 0.  When
+// rec is not null the codes (8-bit: one byte per value; 4-bit: value 2i in
+// the low nibble of byte i) and, from the group's first lane, the (scale,
+// offset) pair are stored into the record rec of a D-value vector.
+template <int D, int GS>
+__device__ __forceinline__ void quantise_store8(const float (&x)[8], int c, int bits, char* rec) {
+  static_assert(GS == 32 || GS == 64, "groups of 32 or 64 values");
+  constexpr int LPG = GS / 8;  // lanes per group
+  // min and max in the lane, then across the lane quad, then (groups of 64)
+  // across the two quads of the 8-lane half row
+  float mn = x[0], mx = x[0];
+#pragma unroll
+  for (int e = 1; e < 8; ++e) {
+    mn = fminf(mn, x[e]);
+    mx = fmaxf(mx, x[e]);
+  }
+  mn = fminf(mn, dpp<kDppXor1>(mn));
+  mx = fmaxf(mx, dpp<kDppXor1>(mx));
+  mn = fminf(mn, dpp<kDppXor2>(mn));
+  mx = fmaxf(mx, dpp<kDppXor2>(mx));
+  if constexpr (LPG == 8) {
+    mn = fminf(mn, dpp<kDppHalfMirror>(mn));
+    mx = fmaxf(mx, dpp<kDppHalfMirror>(mx));
+  }
+  const float levels = static_cast<float>((1 << bits) - 1);
+  const float scale = __fdiv_rn(__fsub_rn(mx, mn), levels);
+  uint32_t code[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    float t = 0.f;
+    if (scale != 0.f) t = fminf(fmaxf(rintf(__fdiv_rn(__fsub_rn(x[e], mn), scale)), 0.f), levels);
+    code[e] = static_cast<uint32_t>(t);
+  }
+  if (!rec) return;
+  if (bits == 8) {
+    *reinterpret_cast<uint2*>(rec + 8 * c) =
+        make_uint2(code[0] | (code[1] << 8) | (code[2] << 16) | (code[3] << 24),
+                   code[4] | (code[5] << 8) | (code[6] << 16) | (code[7] << 24));
+  } else {
+    *reinterpret_cast<uint32_t*>(rec + 4 * c) =
+        (code[0] | (code[1] << 4)) | ((code[2] | (code[3] << 4)) << 8) |
+        ((code[4] | (code[5] << 4)) << 16) | ((code[6] | (code[7] << 4)) << 24);
+  }
+  if (c % LPG == 0) {
+    float* meta = reinterpret_cast<float*>(rec + D * bits / 8) + 2 * (c / LPG);
+    *reinterpret_cast<float2*>(meta) = make_float2(scale, mn);
+  }
+}
+
+}  // namespace pagedkv

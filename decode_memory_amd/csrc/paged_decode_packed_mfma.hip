@@ -48,6 +48,7 @@
 // combine kernel merges them.
 #include "device_common.h"
 #include "internal.h"
+#include "pack_vector.h"
 
 namespace pagedkv {
 
@@ -279,7 +280,8 @@ __global__ __launch_bounds__(kPThreads, kPMinWaves<D>) void paged_decode_packed_
     load_words<EPL>(a.signs + (lane * EPL) % D, sgw);
   }
   const int cap_len = min(a.max_blocks, n_split * a.blocks_per_split) * kPBS;
-  if (len < 0 || len > cap_len) {
+  const bool len_ok = len >= 0 && len <= cap_len;
+  if (!len_ok) {
     if (threadIdx.x == 0 && s == 0) set_error(lv.err, PD_DEVERR_LENGTH);
     len = len < 0 ? 0 : cap_len;
   }
@@ -316,6 +318,51 @@ __global__ __launch_bounds__(kPThreads, kPMinWaves<D>) void paged_decode_packed_
   }
   constexpr int SPB = kPBS / T;  // stages per block
   const int n_stages = lv.capacity_rows > 0 ? nblk * SPB : 0;
+
+  // Fused append (pd_paged_decode_append): token len - 1 of the sequence is
+  // new.  The workgroup whose split owns its block -- the only one that reads
+  // those bytes -- packs it before the first stage is requested: wave h takes
+  // kv head h, its first D/8 lanes the K vector (rotated) and the next D/8
+  // the V vector, and stores both records into the token's slot; the stores
+  // are waited for and a barrier orders them before the stage loads.  A
+  // rejected length or row appends nothing.
+  if (a.k_new && len_ok && len > 0) {
+    const int p = len - 1;
+    const int jb = p / kPBS;
+    if (jb % n_split == s) {  // uniform over the workgroup
+      constexpr int LPT = D / 8;
+      const int jj = jb / n_split;  // this split's jj-th block
+      const bool row_live = (ok_mask >> jj) & 1;
+      const int c = lane % LPT, part = lane / LPT;  // part 0: K, 1: V, others idle
+      char* kb = const_cast<char*>(lane_ptr(kaddr, jj));
+      char* vb = const_cast<char*>(lane_ptr(vaddr, jj));
+      float x[8];
+      {
+        uint4 u = make_uint4(0, 0, 0, 0);
+        if (part < 2)
+          u = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(part ? a.v_new : a.k_new) +
+                                              (static_cast<size_t>(b) * kPWaves + h) * D + 8 * c);
+        widen8<true>(u, x);
+      }
+      float y[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) y[e] = x[e];
+      fwht_rotate8<D>(y, a.signs, c, a.inv_sqrt_d);  // every lane takes part
+      if (part == 0) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = y[e];
+      }
+      char* rec = nullptr;
+      if (row_live && part < 2) {
+        const int slot = p % kPBS;
+        rec = part == 0 ? kb + static_cast<size_t>(slot) * KROW + h * KREC
+                        : vb + static_cast<size_t>(slot) * VROW + h * VREC;
+      }
+      quantise_store8<D, GS>(x, c, part == 0 ? KB : VB, rec);
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the stores have reached L2
+      __syncthreads();
+    }
+  }
 
   // Stage loads: unit u < KU is 16 bytes of the K rows, the rest of the V rows.
   u32x4 rg[S::UPT];

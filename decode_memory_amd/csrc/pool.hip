@@ -669,10 +669,10 @@ static pd_status decode_call(pd_pool* p, int32_t layer, int32_t B, int32_t n_q_h
     if (!k_new || !v_new) return fail(PD_ERR_ARG, "k_new and v_new go together");
     if ((reinterpret_cast<uintptr_t>(k_new) | reinterpret_cast<uintptr_t>(v_new)) & 15)
       return fail(PD_ERR_ARG, "k_new and v_new must be 16-byte aligned");
-    if (plan.kind != 1)
+    if (plan.kind != 1 && plan.kind != 2)
       return fail(PD_ERR_UNSUPPORTED,
-                  "the fused append runs in the 16-bit row kernel only (format %d, head_dim %d, group %d): "
-                  "use pd_write_block, then pd_paged_decode",
+                  "the fused append runs in the 16-bit row kernel and the packed kernel only (format %d, "
+                  "head_dim %d, group %d): use pd_write_block, then pd_paged_decode",
                   p->desc.format, p->desc.head_dim, group);
   }
   DecodeArgs a{};

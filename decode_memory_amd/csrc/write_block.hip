@@ -15,6 +15,7 @@
 #include "device_common.h"
 #include "index_math.h"
 #include "internal.h"
+#include "pack_vector.h"
 
 namespace pagedkv {
 
@@ -231,42 +232,8 @@ __global__ __launch_bounds__(kThreads) void row_move_kernel(RowMoveArgs a) {
 // Jobs are ordered all K vectors first, then all V vectors, so a wave rarely
 // mixes the two.
 
-// Rotate a K vector: x' = H diag(sigma) x / sqrt(D), with H the Sylvester
-// Hadamard matrix applied as the butterfly network h = 1, 2, ..., D/2, each
-// pair (a, b) -> (a + b, a - b) in fp32 (the lower index gets a + b), then
-// one multiply by 1/sqrt(D).  Stages h < 8 pair values inside a lane, the
-// others pair lanes c and c ^ (h / 8) of the vector's lane group.
-template <int D>
-__device__ __forceinline__ void fwht_rotate8(float (&x)[8], const float* signs, int c,
-                                             float inv_sqrt_d) {
-  constexpr int LPT = D / 8;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) x[e] *= signs[8 * c + e];  // exact sign flips
-#pragma unroll
-  for (int h = 1; h < 8; h <<= 1) {
-    float y[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) y[e] = (e & h) ? __fsub_rn(x[e ^ h], x[e]) : __fadd_rn(x[e], x[e ^ h]);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) x[e] = y[e];
-  }
-#pragma unroll
-  for (int hl = 1; hl < LPT; hl <<= 1) {
-    const bool upper = (c & hl) != 0;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float other = __shfl_xor(x[e], hl, kWave);
-      x[e] = upper ? __fsub_rn(other, x[e]) : __fadd_rn(x[e], other);
-    }
-  }
-#pragma unroll
-  for (int e = 0; e < 8; ++e) x[e] = __fmul_rn(x[e], inv_sqrt_d);
-}
-
 template <int D, int GS>
 __global__ __launch_bounds__(kThreads) void write_block_packed_kernel(WriteArgs a) {
-  static_assert(GS == 32 || GS == 64, "groups of 32 or 64 values");
-  constexpr int LPG = GS / 8;       // lanes per group
   constexpr int LPT = D / 8;        // lanes per vector
   constexpr int VPW = kWave / LPT;  // vectors per wave
   const int lane = threadIdx.x % kWave;
@@ -309,50 +276,13 @@ __global__ __launch_bounds__(kThreads) void write_block_packed_kernel(WriteArgs 
         for (int e = 0; e < 8; ++e) x[e] = y[e];
       }
     }
-    // a group is LPG aligned lanes (4 or 8): min and max in the lane, then
-    // across the lane quad, then (groups of 64) across the two quads of the
-    // 8-lane half row
-    float mn = x[0], mx = x[0];
-#pragma unroll
-    for (int e = 1; e < 8; ++e) {
-      mn = fminf(mn, x[e]);
-      mx = fmaxf(mx, x[e]);
+    char* rec = nullptr;
+    if (ok) {
+      const int rec_bytes = is_v ? a.lv.v_rec : a.lv.k_rec;
+      rec = static_cast<char*>(const_cast<void*>(is_v ? a.lv.v_tab[slab] : a.lv.k_tab[slab])) +
+            (tok * a.lv.n_kv + head) * rec_bytes;
     }
-    mn = fminf(mn, dpp<kDppXor1>(mn));
-    mx = fmaxf(mx, dpp<kDppXor1>(mx));
-    mn = fminf(mn, dpp<kDppXor2>(mn));
-    mx = fmaxf(mx, dpp<kDppXor2>(mx));
-    if constexpr (LPG == 8) {
-      mn = fminf(mn, dpp<kDppHalfMirror>(mn));
-      mx = fmaxf(mx, dpp<kDppHalfMirror>(mx));
-    }
-    const int bits = is_v ? a.v_bits : a.k_bits;
-    const float levels = static_cast<float>((1 << bits) - 1);
-    const float scale = __fdiv_rn(__fsub_rn(mx, mn), levels);
-    uint32_t code[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      float t = 0.f;
-      if (scale != 0.f) t = fminf(fmaxf(rintf(__fdiv_rn(__fsub_rn(x[e], mn), scale)), 0.f), levels);
-      code[e] = static_cast<uint32_t>(t);
-    }
-    if (!ok) continue;
-    const int rec_bytes = is_v ? a.lv.v_rec : a.lv.k_rec;
-    char* rec = static_cast<char*>(const_cast<void*>(is_v ? a.lv.v_tab[slab] : a.lv.k_tab[slab])) +
-                (tok * a.lv.n_kv + head) * rec_bytes;
-    if (bits == 8) {
-      *reinterpret_cast<uint2*>(rec + 8 * c) =
-          make_uint2(code[0] | (code[1] << 8) | (code[2] << 16) | (code[3] << 24),
-                     code[4] | (code[5] << 8) | (code[6] << 16) | (code[7] << 24));
-    } else {
-      *reinterpret_cast<uint32_t*>(rec + 4 * c) =
-          (code[0] | (code[1] << 4)) | ((code[2] | (code[3] << 4)) << 8) |
-          ((code[4] | (code[5] << 4)) << 16) | ((code[6] | (code[7] << 4)) << 24);
-    }
-    if (c % LPG == 0) {
-      float* meta = reinterpret_cast<float*>(rec + D * bits / 8) + 2 * (c / LPG);
-      *reinterpret_cast<float2*>(meta) = make_float2(scale, mn);
-    }
+    quantise_store8<D, GS>(x, c, is_v ? a.v_bits : a.k_bits, rec);
   }
 }
 

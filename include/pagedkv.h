@@ -309,16 +309,23 @@ pd_status pd_paged_decode(pd_pool* pool, int32_t layer, int32_t B, int32_t n_q_h
  * token's K and V with its query; mlxcel #235, "Proposed solution", touch
  * point 1: the write lands in the slab of its row.  Token lens[b] - 1 of each
  * sequence is the new one: k_new[b], v_new[b] (device [B, n_kv_heads,
- * head_dim], the pool's 16-bit dtype, 16-byte aligned) are written to row
+ * head_dim], the pool's 16-bit dtype, bf16 for packed pools, 16-byte
+ * aligned) are written to row
  * block_table[b][(lens[b] - 1) / block_size], slot (lens[b] - 1) %
  * block_size, of `layer`, and the attention reads them there.  Pool bytes
  * and outputs are bit for bit those of pd_write_block of the same tokens
  * followed by pd_paged_decode.  Sequences with lens[b] == 0 append nothing;
  * a length or row the kernel rejects (device error word, as pd_paged_decode)
  * appends nothing for that sequence.  Other arguments as pd_paged_decode.
+ * In a packed pool the new token is rotated (keys) and quantised in the
+ * launch to the records pd_write_block stores (mlx-swift-lm PR #142, "Add
+ * packed paged KV formats with bounded workspace admission", section
+ * "Summary": fresh K/V are quantised once, attention reads the packed pages).
  * Only where the 16-bit row kernel runs (n_kv_heads * head_dim * 2 a multiple
- * of 1024 bytes, block_size 32, head_dim 64/128/256, group 1/2/4/8); else
- * PD_ERR_UNSUPPORTED (use pd_write_block, then pd_paged_decode).
+ * of 1024 bytes, block_size 32, head_dim 64/128/256, group 1/2/4/8) or the
+ * packed kernel runs (n_kv_heads 8, block_size 32, head_dim 64/128/256, group
+ * 1/2/4; group_size 64 needs head_dim >= 128); else PD_ERR_UNSUPPORTED (use
+ * pd_write_block, then pd_paged_decode).
  */
 pd_status pd_paged_decode_append(pd_pool* pool, int32_t layer, int32_t B, int32_t n_q_heads,
                                  const void* q, const void* k_new, const void* v_new,

@@ -22,11 +22,12 @@ pytestmark = pytest.mark.gpu
 BS = 32
 
 
-def _fill(lengths, rows, R, S, n_kv, D, dtype, seed, n_layers=1):
+def _fill(lengths, rows, R, S, n_kv, D, dtype, seed, n_layers=1, fmt=None, signs=None, group=0):
     """A pool holding tokens 0 .. len-2 of every sequence and, in the slot of
     token len-1, the bytes of another token (the append must replace them).
     Returns the pool and the full K/V bit patterns per layer and sequence."""
-    pool = pd.SlabPool(n_layers, BS, n_kv, D, S, -(-R // S) + 2, dtype)
+    pool = pd.SlabPool(n_layers, BS, n_kv, D, S, -(-R // S) + 2, fmt or dtype, hadamard_signs=signs,
+                       group_size=group)
     pool.reserve_rows(R)
     kv = []
     for layer in range(n_layers):
@@ -129,15 +130,59 @@ def test_append_with_a_rejected_row_appends_nothing():
     pool.close()
 
 
-@pytest.mark.parametrize("case", ["packed", "column_kernel", "misaligned"])
-def test_append_rejects_what_it_cannot_fuse(case):
+@pytest.mark.parametrize("fmt,D,G,group", [("k8v8", 64, 4, 32), ("k4v4", 256, 2, 32), ("k8v4", 128, 1, 64),
+                                            ("k4v4", 64, 1, 32)])
+def test_packed_append_equals_write_then_decode(fmt, D, G, group):
+    """Packed pools: the decode kernel's owner workgroup rotates and
+    quantises the new token itself (mlx-swift-lm PR #142, "Add packed paged
+    KV formats with bounded workspace admission", section "Summary": fresh
+    K/V are quantised once); the records it stores are those the quantising
+    write_block stores, byte for byte, and so are the outputs."""
+    from oracle.packed import FORMATS, k_records, packed_decode_attention, v_records
     from synth import hadamard_signs
+    lengths = [0, 1, 31, 32, 33, 700, 2500]
+    n_kv, seed = 8, 800 + D + G
+    signs = hadamard_signs(seed, D)
+    rows, _, R = shuffled_rows(np.random.default_rng(seed), lengths, BS, 4, spare_rows=3)
+    table = i32(make_block_table(rows))
+    lens = i32(lengths)
+    B, n_q, ml = len(lengths), n_kv * G, max(lengths)
+    qb = q_bits(seed, 0, B, n_q, D, "bf16")
+    q = to_device_bits(qb, "bf16")
+    scale = 1 / np.sqrt(D)
+    outs, slabs = [], []
+    for fused in (False, True):
+        pool, kv = _fill(lengths, rows, R, 4, n_kv, D, "bf16", seed, fmt=fmt, signs=signs, group=group)
+        kn, vn = _new_tokens(kv, 0, lengths, n_kv, D, "bf16")
+        out = torch.empty_like(q)
+        ws = pool.workspace(B, n_q, ml)
+        if fused:
+            pool.paged_decode_append(0, q, kn, vn, table, lens, ml, scale, out, ws)
+        else:
+            live = [b for b, n in enumerate(lengths) if n]
+            r = i32([int(rows[b][(lengths[b] - 1) // BS]) for b in live])
+            s = i32([(lengths[b] - 1) % BS for b in live])
+            pool.write_block(0, r, s, kn[live].contiguous(), vn[live].contiguous())
+            pool.paged_decode(0, q, table, lens, ml, scale, out, ws)
+        torch.cuda.synchronize()
+        assert pool.check_error() == 0
+        outs.append(from_device_bits(out))
+        slabs.append(_slabs(pool))
+        pool.close()
+    assert np.array_equal(outs[0], outs[1])
+    assert all(torch.equal(a, b) for a, b in zip(slabs[0], slabs[1]))
+    kb, vb = FORMATS[fmt]
+    kr = [k_records(k, signs, kb, group) for k, _ in kv[0]]
+    vr = [v_records(v, vb, group) for _, v in kv[0]]
+    ref = packed_decode_attention(qb, kr, vr, signs, fmt, D, scale, group)
+    assert_decode_close(outs[1], ref, "bf16", allow_output_rounding=True)
+
+
+@pytest.mark.parametrize("case", ["column_kernel", "misaligned"])
+def test_append_rejects_what_it_cannot_fuse(case):
     lengths = [40]
     rows = monotone_rows(lengths, BS)
-    if case == "packed":
-        pool = pd.SlabPool(1, BS, 8, 64, 4, 4, "k4v4", hadamard_signs=hadamard_signs(3, 64))
-        n_kv, D, status = 8, 64, -4
-    elif case == "column_kernel":                           # 2 x 64 x 2 = 256-byte token rows
+    if case == "column_kernel":                           # 2 x 64 x 2 = 256-byte token rows
         pool = pd.SlabPool(1, BS, 2, 64, 4, 4, "bf16")
         n_kv, D, status = 2, 64, -4
     else:

@@ -96,7 +96,7 @@ def measured_traffic():
 
 
 PACKED_TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "paged_decode_packed_16x16k_traffic.md")
-PACKED_SOURCES = ("paged_decode_packed_mfma.hip", "device_common.h")
+PACKED_SOURCES = ("paged_decode_packed_mfma.hip", "pack_vector.h", "device_common.h")
 
 
 def measured_packed_traffic(case: str):

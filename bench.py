@@ -145,6 +145,21 @@ def blas_threads():
         return os.cpu_count()
 
 
+def host_cpu():
+    """The host's CPU model (from /proc/cpuinfo) and logical CPU count, for
+    the record beside a CPU timing."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:  # pragma: no cover
+        pass
+    return {"cpu_model": model, "nproc": os.cpu_count()}
+
+
 def cpu_baseline(w, target_s: float):
     """The oracle's fp64 decode over whole layers of the workload, until about
     target_s seconds of CPU work have been timed."""
@@ -167,6 +182,7 @@ def cpu_baseline(w, target_s: float):
         "unit": "GB/s",
         "tokens_attended_per_s": round(sum(lengths) * layers / elapsed, 1),
         "cores": int(blas_threads()),
+        **host_cpu(),
         "kind": "oracle",
         "sample": f"{layers} of {w.n_layers} layers of the same batch ({w.batch} x {w.length} "
                   f"tokens), numpy fp64 decode_attention, {elapsed:.1f} s",
@@ -195,6 +211,7 @@ def cpu_baseline_sequences(w, lengths, target_s: float):
         "unit": "GB/s",
         "tokens_attended_per_s": round(sum(done) / elapsed, 1),
         "cores": int(blas_threads()),
+        **host_cpu(),
         "kind": "oracle",
         "sample": f"{len(done)} of {len(lengths)} sequences of layer 0 ({sum(done)} tokens), "
                   f"numpy fp64 decode_attention, {elapsed:.1f} s",
@@ -904,7 +921,7 @@ def cpu_baseline_packed(w, target_s):
     nbytes = decode_bytes([w.length] * done, w.n_kv_heads, w.n_q_heads, D, w.block_size, rec)
     return {"value": round(nbytes / elapsed / 1e9, 3), "unit": "GB/s",
             "tokens_attended_per_s": round(done * w.length / elapsed, 1),
-            "cores": int(blas_threads()), "kind": "oracle",
+            "cores": int(blas_threads()), **host_cpu(), "kind": "oracle",
             "sample": f"{done} of {w.batch} sequences, K4V4 head_dim 64, numpy fp64 "
                       f"packed_decode_attention, {elapsed:.1f} s"}
 

@@ -295,7 +295,11 @@ __global__ __launch_bounds__(kCWaves * kWave) void combine_kernel(DecodeArgs a) 
   constexpr int CH = D / kWave;  // 64-column chunks per query head
   constexpr int KM = kMaxSplits / kWave;
   const int lane = threadIdx.x % kWave;
-  const int item = blockIdx.x * kCWaves + __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  // the split kernel's work ids are (sequence, head set, split) in order and
+  // XCD x runs a contiguous range of them; the same mapping here gives XCD x
+  // the combine of those sequences, whose partials are still in its L2
+  const int wg = xcd_work_id(blockIdx.x, gridDim.x);
+  const int item = wg * kCWaves + __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int total = a.B * a.n_q;
   if (item >= total * CH) return;
   const int hq = item / CH;                 // (sequence, query head) index
@@ -368,7 +372,7 @@ hipError_t launch_typed(const DecodeArgs& a, hipStream_t s) {
 template <int D, bool BF16>
 hipError_t launch_combine_typed(const DecodeArgs& a, hipStream_t s) {
   const long long waves = static_cast<long long>(a.B) * a.n_q * (D / kWave);
-  const int grid = static_cast<int>((waves + kCWaves - 1) / kCWaves);
+  const int grid = round_up(static_cast<int>((waves + kCWaves - 1) / kCWaves), kXcds);
   hipLaunchKernelGGL((combine_kernel<D, BF16>), dim3(grid), dim3(kCWaves * kWave), 0, s, a);
   return hipGetLastError();
 }

@@ -105,13 +105,15 @@ def test_lengths_beyond_the_call_are_clamped_and_flagged():
     pool.close()
 
 
-@pytest.mark.parametrize("fmt", ["k4v4", "k8v8"])
-def test_longest_packed_sequence_the_plan_holds(fmt):
+@pytest.mark.parametrize("fmt,fused", [("k4v4", False), ("k8v8", False), ("k4v4", True)])
+def test_longest_packed_sequence_the_plan_holds(fmt, fused):
     """The packed kernel at the longest plan (256 splits of 64 blocks): equal
     keys give equal scores, so the output is the mean of the dequantised
     value records (mlx-swift-lm PR #142, "Add packed paged KV formats with
     bounded workspace admission", section "Summary": attention reads the
-    packed pages directly), here a closed form over the periodic pattern."""
+    packed pages directly), here a closed form over the periodic pattern.
+    Fused, the last token (block 16383: split 255's 64th block) is quantised
+    and stored by the decode launch itself."""
     from oracle.packed import FORMATS, dequantise_records, v_records
     from synth import hadamard_signs
     n, n_kv, G, D, P = MAX_LEN, 8, 4, 64, 5
@@ -128,13 +130,19 @@ def test_longest_packed_sequence_the_plan_holds(fmt):
     S = 512
     pool = pd.SlabPool(1, BS, n_kv, D, S, n // BS // S + 1, fmt, hadamard_signs=signs)
     pool.reserve_rows(n // BS)
-    pool.write_block(0, i32(rows[0][t // BS]), i32(t % BS),
-                     to_device_bits(np.ascontiguousarray(k_bits), "bf16"),
-                     to_device_bits(np.ascontiguousarray(v_bits), "bf16"))
+    written = n - 1 if fused else n
+    pool.write_block(0, i32(rows[0][t[:written] // BS]), i32(t[:written] % BS),
+                     to_device_bits(np.ascontiguousarray(k_bits[:written]), "bf16"),
+                     to_device_bits(np.ascontiguousarray(v_bits[:written]), "bf16"))
     q = to_device_bits(q_bits(13, 0, 1, n_kv * G, D, "bf16"), "bf16")
     out = torch.empty_like(q)
-    pool.paged_decode(0, q, i32(make_block_table(rows)), i32([n]), n, 1 / 8, out,
-                      pool.workspace(1, n_kv * G, n))
+    table, lens, ws = i32(make_block_table(rows)), i32([n]), pool.workspace(1, n_kv * G, n)
+    if fused:
+        pool.paged_decode_append(0, q, to_device_bits(kvec[None], "bf16"),
+                                 to_device_bits(np.ascontiguousarray(v_bits[n - 1:]), "bf16"),
+                                 table, lens, n, 1 / 8, out, ws)
+    else:
+        pool.paged_decode(0, q, table, lens, n, 1 / 8, out, ws)
     torch.cuda.synchronize()
     assert pool.check_error() == 0
     deq = dequantise_records(v_records(pattern, vb), D, vb)  # [P, n_kv, D]

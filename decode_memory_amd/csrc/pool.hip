@@ -9,6 +9,7 @@
 // pool byte accounting sums over slabs; one slab_for_row helper is the only
 // place that maps a row to (slab, row_in_slab).
 #include <cmath>
+#include <cstdint>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -251,6 +252,15 @@ bool make_decode_plan_for(int32_t format, int32_t n_kv, int32_t D, int32_t bs, i
   plan.split = plan_splits(units, max_len, bs, target, max_bps);
   *out = plan;
   return true;
+}
+
+// Launch sizes stay in 32-bit arithmetic (grids, work ids, partial rows).
+pd_status check_decode_size(int32_t B, int32_t n_q_heads, const DecodePlan& plan) {
+  const long long rows = static_cast<long long>(B) * n_q_heads * plan.split.n_split;
+  if (rows > (1LL << 30))
+    return fail(PD_ERR_ARG, "B * n_q_heads * splits = %lld beyond 2^30 (B %d, n_q_heads %d, %d splits)", rows,
+                B, n_q_heads, plan.split.n_split);
+  return PD_OK;
 }
 
 bool make_decode_plan(const pd_pool* p, int32_t B, int32_t group, int32_t max_len, DecodePlan* out) {
@@ -627,6 +637,7 @@ pd_status pd_decode_workspace_bytes(const pd_pool* p, int32_t B, int32_t n_q_hea
   if (!make_decode_plan(p, B, n_q_heads / n_kv, max_len, &plan))
     return fail(PD_ERR_UNSUPPORTED, "no decode kernel for format %d, head_dim %d, group %d",
                 p->desc.format, p->desc.head_dim, n_q_heads / n_kv);
+  if (pd_status st = check_decode_size(B, n_q_heads, plan)) return st;
   *bytes = decode_workspace_bytes(B, n_q_heads, p->desc.head_dim, plan.split);
   return PD_OK;
 }
@@ -662,6 +673,7 @@ static pd_status decode_call(pd_pool* p, int32_t layer, int32_t B, int32_t n_q_h
   if (!make_decode_plan(p, B, group, plan_len, &plan))
     return fail(PD_ERR_UNSUPPORTED, "no decode kernel for format %d, head_dim %d, group %d",
                 p->desc.format, p->desc.head_dim, group);
+  if (pd_status st = check_decode_size(B, n_q_heads, plan)) return st;
   const size_t need = decode_workspace_bytes(B, n_q_heads, p->desc.head_dim, plan.split);
   if (workspace_bytes < need)
     return fail(PD_ERR_CAPACITY, "workspace %zu bytes, %zu needed", workspace_bytes, need);
@@ -770,6 +782,11 @@ pd_status dense_plan(const pd_dense_desc* d, int32_t B, int32_t n_q_heads, int32
                 "dense decode needs the row kernel's shapes (n_kv_heads * head_dim * 2 a multiple of "
                 "1024 bytes, head_dim 64/128/256, group 1/2/4/8); got n_kv %d, head_dim %d, group %d",
                 d->n_kv_heads, d->head_dim, group);
+  if (pd_status st = check_decode_size(B, n_q_heads, *plan)) return st;
+  // the kernels form row b * blocks + j (blocks = ceil(max_len / 32)) in 32 bits
+  const int64_t blocks = max_len > 0 ? (max_len + kDenseBlock - 1) / kDenseBlock : 1;
+  if (static_cast<int64_t>(B) * blocks > INT32_MAX)
+    return fail(PD_ERR_ARG, "B %d x %lld blocks beyond 2^31 rows", B, static_cast<long long>(blocks));
   return PD_OK;
 }
 

@@ -270,6 +270,8 @@ pd_status pd_gather_visible(pd_pool* pool, int32_t layer, int32_t B, const int32
 /*
  * Workspace bytes that pd_paged_decode needs for B sequences, n_q_heads query
  * heads and a longest sequence of at most max_len tokens (host output).
+ * B * n_q_heads * splits above 2^30 (the split kernels' partial rows, in 32
+ * bits) is PD_ERR_ARG, here and from pd_paged_decode.
  */
 pd_status pd_decode_workspace_bytes(const pd_pool* pool, int32_t B, int32_t n_q_heads,
                                     int32_t max_len, size_t* bytes);
@@ -352,7 +354,9 @@ pd_status pd_paged_decode_append(pd_pool* pool, int32_t layer, int32_t B, int32_
  * keeps them.  Shapes: those of the row kernel (n_kv_heads * head_dim * 2 a
  * multiple of 1024 bytes; head_dim 64, 128, 256; group 1, 2, 4, 8), else
  * PD_ERR_UNSUPPORTED.  There is no device error word: a length beyond
- * max_len is clamped to it.
+ * max_len is clamped to it.  B * ceil(max_len / 32) above 2^31 - 1, or B *
+ * n_q_heads * splits above 2^30, is PD_ERR_ARG (here and from
+ * pd_dense_workspace_bytes): the kernels index rows and partials in 32 bits.
  */
 typedef struct pd_dense_desc {
   int32_t format;      /* PD_FMT_FP16 or PD_FMT_BF16 */

@@ -69,6 +69,23 @@ def test_pool_create_validates_on_host(kwargs, status):
     assert e.value.status == status
 
 
+def test_dense_workspace_query_bounds_the_launch_on_host():
+    """Dense decode sizes are checked on the host: the kernels form row
+    b * ceil(max_len / 32) + j and the (sequence, query head, split) rows of
+    the workspace in 32 bits, so batches past those ranges are argument
+    errors, while a qwen3-shaped batch gets its workspace size."""
+    per_split = 8 * 16 * (128 + 2) * 4  # B x n_q x (weighted V + max, sum), fp32
+    ok = pd.dense_workspace_bytes("bf16", 8, 128, 8, 16, 4096)
+    assert ok >= per_split and ok % 4 == 0
+    with pytest.raises(pd.PagedKVError) as e:  # 131073 x 16384 rows
+        pd.dense_workspace_bytes("bf16", 8, 128, 131073, 8, 524288)
+    assert e.value.status == -1
+    with pytest.raises(pd.PagedKVError) as e:  # 131073 x 8192 query heads, one split
+        pd.dense_workspace_bytes("bf16", 1024, 64, 131073, 8192, 32)
+    assert e.value.status == -1
+    assert pd.dense_workspace_bytes("bf16", 1024, 64, 131072, 8192, 32) > 0  # 2^30 rows fit
+
+
 def test_null_pool_is_an_argument_error():
     lib = pd.lib()
     assert lib.pd_pool_stats(None, None) == -1

@@ -20,6 +20,9 @@ def test_slab_pool_overhead_is_below_one_slab():
     lengths = [4100, 4200, 4297, 4096, 4150, 4250, 4111, 4222]
     cap = slab_pool_capacity(lengths, bs, S, blk)[-1]
     rows = sum(blocks_for(n, bs) for n in lengths)
+    # growth appends whole slabs: with the bound below, the capacity is the
+    # smallest whole number of slabs that holds the rows
+    assert cap % (S * blk) == 0
     assert rows * blk <= cap < (rows + S) * blk
     assert cap > dense_bytes(lengths, blk // bs)
 

@@ -228,15 +228,27 @@ def test_copy_on_write_block_shares_then_isolates_a_block():
 
 def test_copy_block_reads_every_source_before_writing():
     """Several pairs in one call: each destination gets its source as it was
-    before the call (brute force over a tiny pool)."""
-    pool = SlabPoolModel(1, 2, 1, 4, 4, 2)
-    pool.reserve_rows(6)
-    for row in range(6):
-        rec = np.full((1, 1, 4), row + 1, np.uint8)
-        pool.write(0, [row, row], [0, 1], np.repeat(rec, 2, 0), np.repeat(rec, 2, 0))
+    before the call (brute force over a tiny pool).  The second call chains
+    pairs (a destination is a later pair's source), where copying pair by
+    pair would differ; the C ABI leaves that case unspecified, the oracle
+    reads first."""
+    def fresh():
+        pool = SlabPoolModel(1, 2, 1, 4, 4, 2)
+        pool.reserve_rows(6)
+        for row in range(6):
+            rec = np.full((1, 1, 4), row + 1, np.uint8)
+            pool.write(0, [row, row], [0, 1], np.repeat(rec, 2, 0), np.repeat(rec, 2, 0))
+        return pool
+
+    def values(pool):
+        return [int(pool.slab_for_row(0, r)[0][pool.slab_for_row(0, r)[2]][0, 0, 0]) for r in range(6)]
+
+    pool = fresh()
     pool.copy_block([0, 3, 5], [4, 1, 2])
-    got = [int(pool.slab_for_row(0, r)[0][pool.slab_for_row(0, r)[2]][0, 0, 0]) for r in range(6)]
-    assert got == [1, 4, 6, 4, 1, 6]
+    assert values(pool) == [1, 4, 6, 4, 1, 6]
+    pool = fresh()
+    pool.copy_block([0, 3, 4], [3, 4, 1])
+    assert values(pool) == [1, 5, 3, 1, 4, 6]  # pair by pair would give [1, 1, 3, 1, 1, 6]
 
 
 def test_fnv1a64_published_vectors():

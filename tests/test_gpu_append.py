@@ -204,15 +204,22 @@ def test_append_rejects_what_it_cannot_fuse(case):
     pool.close()
 
 
-def test_captured_append_step_replays_bit_equal():
+@pytest.mark.parametrize("fmt", ["bf16", "k4v4"])
+def test_captured_append_step_replays_bit_equal(fmt):
     """Every layer's append-and-attend captured into a HIP graph: each replay,
     with eager steps and synchronisations between replays, gives the eager
-    outputs bit for bit."""
-    L, B, n, n_kv, G, D, dtype = 3, 4, 700, 8, 2, 128, "bf16"
+    outputs bit for bit (a packed pool quantises the new tokens in the
+    replayed launches too)."""
+    from synth import hadamard_signs
+    packed = fmt != "bf16"
+    L, B, n, n_kv, dtype = 3, 4, 700, 8, "bf16"
+    G, D = (4, 64) if packed else (2, 128)
+    signs = hadamard_signs(71, D) if packed else None
     lengths = [n] * B
     rows = monotone_rows(lengths, BS)
     R = int(max(r.max() for r in rows)) + 1
-    pool, kv = _fill(lengths, rows, R, 8, n_kv, D, dtype, 71, n_layers=L)
+    pool, kv = _fill(lengths, rows, R, 8, n_kv, D, dtype, 71, n_layers=L, fmt=fmt if packed else None,
+                     signs=signs)
     table, lens = i32(make_block_table(rows)), i32(lengths)
     new = [_new_tokens(kv, layer, lengths, n_kv, D, dtype) for layer in range(L)]
     qs = [to_device_bits(q_bits(71, layer, B, n_kv * G, D, dtype), dtype) for layer in range(L)]
@@ -243,8 +250,13 @@ def test_captured_append_step_replays_bit_equal():
         graph.replay()
         torch.cuda.synchronize()
         assert all(torch.equal(a, b) for a, b in zip(eager, outs))
-    ref = decode_attention_bits(q_bits(71, 0, B, n_kv * G, D, dtype), [k for k, _ in kv[0]],
-                                [v for _, v in kv[0]], dtype, 1 / np.sqrt(D))
+    qb = q_bits(71, 0, B, n_kv * G, D, dtype)
+    if packed:
+        from oracle.packed import k_records, packed_decode_attention, v_records
+        ref = packed_decode_attention(qb, [k_records(k, signs, 4) for k, _ in kv[0]],
+                                      [v_records(v, 4) for _, v in kv[0]], signs, fmt, D, 1 / np.sqrt(D))
+    else:
+        ref = decode_attention_bits(qb, [k for k, _ in kv[0]], [v for _, v in kv[0]], dtype, 1 / np.sqrt(D))
     assert_decode_close(from_device_bits(outs[0]), ref, dtype)
     assert pool.check_error() == 0
     pool.close()

@@ -32,7 +32,7 @@ FORMAT_NAMES = {"fp16": FMT_FP16, "bf16": FMT_BF16, "k8v8": FMT_K8V8, "k8v4": FM
 DEVERR_WRITE_ROW, DEVERR_WRITE_SLOT, DEVERR_TABLE_ROW, DEVERR_LENGTH = 0x1, 0x2, 0x4, 0x8
 
 STATUS = {0: "PD_OK", -1: "PD_ERR_ARG", -2: "PD_ERR_RANGE", -3: "PD_ERR_CAPACITY",
-          -4: "PD_ERR_UNSUPPORTED", -5: "PD_ERR_HIP", -6: "PD_ERR_DEVICE"}
+          -4: "PD_ERR_UNSUPPORTED", -5: "PD_ERR_HIP", -6: "PD_ERR_DEVICE", -7: "PD_ERR_IDENTITY"}
 
 
 class PagedKVError(RuntimeError):

@@ -86,6 +86,13 @@ def test_dense_workspace_query_bounds_the_launch_on_host():
     assert pd.dense_workspace_bytes("bf16", 1024, 64, 131072, 8192, 32) > 0  # 2^30 rows fit
 
 
+def test_status_names_cover_the_header():
+    """Every pd_status value the header declares has its name in the binding."""
+    text = open(os.path.join(ROOT, "include", "pagedkv.h")).read()
+    declared = {int(v): n for n, v in re.findall(r"\b(PD_(?:OK|ERR_[A-Z]+))\s*=\s*(-?\d+)", text)}
+    assert declared and declared == pd.STATUS
+
+
 def test_null_pool_is_an_argument_error():
     lib = pd.lib()
     assert lib.pd_pool_stats(None, None) == -1

@@ -337,16 +337,17 @@ def dense_decode(q: torch.Tensor, k_seqs: Sequence[torch.Tensor], v_seqs: Sequen
     _require(lens, "lens", torch.int32, B)
     for t in list(k_seqs) + list(v_seqs):
         _require(t, "k/v sequence")
-    ptrs = torch.tensor([t.data_ptr() for t in k_seqs] + [t.data_ptr() for t in v_seqs],
-                        dtype=torch.int64, device=q.device)
-    _check(lib().pd_dense_decode(ctypes.byref(desc), B, n_q, _ptr(q), ptrs.data_ptr(),
-                                 ptrs.data_ptr() + 8 * B, _ptr(lens), max_len, float(scale), _ptr(out),
-                                 _ptr(workspace), workspace.numel() * workspace.element_size(),
-                                 _stream(stream)))
-    if stream is not None:
-        # the pointer array is freed on return; the allocator reuses it only
-        # after work already queued on the streams it was used on
-        ptrs.record_stream(stream)
+    s = torch.cuda.current_stream() if stream is None else stream
+    # the pointer array is copied to the device on the stream the kernel runs
+    # on, so the kernel reads it after the copy; allocated on that stream, it
+    # is reused only after the work queued there
+    with torch.cuda.stream(s):
+        ptrs = torch.tensor([t.data_ptr() for t in k_seqs] + [t.data_ptr() for t in v_seqs],
+                            dtype=torch.int64, device=q.device)
+        _check(lib().pd_dense_decode(ctypes.byref(desc), B, n_q, _ptr(q), ptrs.data_ptr(),
+                                     ptrs.data_ptr() + 8 * B, _ptr(lens), max_len, float(scale), _ptr(out),
+                                     _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                     s.cuda_stream))
 
 
 CHECKPOINT_MAGIC = b"PDKVBLK1"

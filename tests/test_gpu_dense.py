@@ -49,6 +49,14 @@ def test_dense_is_bit_identical_to_paged(D, G, n_kv, dtype, lengths):
     torch.cuda.synchronize()
     dense = from_device_bits(out)
     assert np.array_equal(dense, paged)
+    # on another stream: the per-sequence pointer array travels on that stream too
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    out_side, ws_side = torch.full_like(out, 7), torch.zeros_like(ws)
+    pd.dense_decode(qd, ks, vs, torch.tensor(lengths, dtype=torch.int32, device="cuda"), ml, scale, out_side,
+                    ws_side, stream=side)
+    side.synchronize()
+    assert torch.equal(out_side, out)
     ref = decode_attention_bits(q, seqs["k"], seqs["v"], dtype, scale)
     assert_decode_close(dense, ref, dtype, allow_output_rounding=True)
     for b, n in enumerate(lengths):

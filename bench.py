@@ -743,9 +743,24 @@ def run_packed(args, torch, pd):
         def call():
             pool.paged_decode(next(it) % copies, q, table, lens, n, scale, out, ws)
 
+        # the same call with each sequence's newest token (position n - 1)
+        # appended in the split launch: packed pools rotate and quantise it there
+        k_new = normal_device((w.seed, D, 3), (B, n_kv, D), "bf16", dev)
+        v_new = normal_device((w.seed, D, 4), (B, n_kv, D), "bf16", dev)
+
+        def call_append():
+            pool.paged_decode_append(next(it) % copies, q, k_new, v_new, table, lens, n, scale, out, ws)
+
         for _ in range(args.warmup):
             call()
-        us = timer(call, max(args.steps, copies))
+            call_append()
+        # alternate blocks of the two, so that both see the same clocks (the
+        # GPU slows by up to about 10% over the first milliseconds of load)
+        blocks, per_block = 3, max(args.steps, copies)
+        us = append_us = 0.0
+        for _ in range(blocks):
+            us += timer(call, per_block) / blocks
+            append_us += timer(call_append, per_block) / blocks
 
         def decode_call(layer, stage):
             pool.paged_decode(layer, q, table, lens, n, scale, out, ws, stage=stage)
@@ -757,7 +772,8 @@ def run_packed(args, torch, pd):
         pool.close()
         d_bytes = decode_bytes(lengths, n_kv, n_q, D, bs, k_rec + v_rec)
         return {
-            "us_per_call": round(us, 2), "split_us": round(split_us, 2),
+            "us_per_call": round(us, 2), "append_us_per_call": round(append_us, 2),
+            "split_us": round(split_us, 2),
             "combine_us": round(combine_us, 2), "kv_bytes": kv_bytes,
             "algorithmic_bytes": d_bytes,
             "bits_per_value": round(8 * (k_rec + v_rec) / (2 * D), 3),

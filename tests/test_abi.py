@@ -86,6 +86,47 @@ def test_dense_workspace_query_bounds_the_launch_on_host():
     assert pd.dense_workspace_bytes("bf16", 1024, 64, 131072, 8192, 32) > 0  # 2^30 rows fit
 
 
+C_PROGRAM = r"""
+#include <stdio.h>
+#include "pagedkv.h"
+int main(void) {
+  int32_t k = 0, v = 0;
+  uint64_t h = 0;
+  const int8_t signs[4] = {1, -1, 1, 1};
+  if (pd_record_bytes(PD_FMT_K4V4, 64, 48, &k, &v) != PD_ERR_ARG) return 2;  /* 48 does not divide 64 */
+  if (pd_record_bytes(PD_FMT_K8V4, 256, 64, &k, &v) != PD_OK) return 3;
+  if (pd_signs_hash(signs, 4, &h) != PD_OK) return 4;
+  printf("%d %d %d %llu\n", pd_version(), k, v, (unsigned long long)h);
+  return 0;
+}
+"""
+
+
+def test_header_compiles_as_c_and_the_library_links(tmp_path):
+    """The boundary is a C ABI: a plain C99 program includes pagedkv.h,
+    links libpagedkv.so and calls its host-only entry points."""
+    import shutil
+    import subprocess
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("gcc is not installed")
+    lib_dir = os.path.dirname(pd.LIB_PATH)
+    pd.lib()  # raises if the library has not been built
+    src, exe = tmp_path / "abi.c", tmp_path / "abi"
+    src.write_text(C_PROGRAM)
+    r = subprocess.run([gcc, "-std=c99", "-Wall", "-Wextra", "-Werror=implicit-function-declaration",
+                        "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(ROOT, "include"), "-I", "/opt/rocm/include",
+                        str(src), "-L", lib_dir, "-lpagedkv", f"-Wl,-rpath,{lib_dir}", "-o", str(exe)],
+                       capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr[-2000:]
+    r = subprocess.run([str(exe)], capture_output=True, text=True)
+    assert r.returncode == 0, (r.returncode, r.stderr)
+    version, k, v, h = (int(x) for x in r.stdout.split())
+    assert version == pd.version()
+    assert (k, v) == (oracle_record_bytes(256, 8, 64), oracle_record_bytes(256, 4, 64))
+    assert h == pd.signs_hash([1, -1, 1, 1])
+
+
 def test_status_names_cover_the_header():
     """Every pd_status value the header declares has its name in the binding."""
     text = open(os.path.join(ROOT, "include", "pagedkv.h")).read()

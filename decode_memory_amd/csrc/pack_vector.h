@@ -13,17 +13,14 @@
 
 namespace pagedkv {
 
-// x' = H diag(sigma) x / sqrt(D), with H the Sylvester Hadamard matrix
-// applied as the butterfly network h = 1, 2, ..., D/2, each pair (a, b) ->
-// (a + b, a - b) in fp32 (the lower index gets a + b), then one multiply by
-// 1/sqrt(D).  Stages h < 8 pair values inside a lane, the others pair lanes c
-// and c ^ (h / 8) of the vector's lane group.
+// The Sylvester Hadamard butterfly network over a D-value vector held 8
+// values per lane by D/8 lanes (lane c of the group: values 8c .. 8c+7):
+// stages h = 1, 2, ..., D/2, each pair (a, b) -> (a + b, a - b) in fp32 (the
+// lower index gets a + b).  Stages h < 8 pair values inside a lane, the
+// others pair lanes c and c ^ (h / 8) of the vector's lane group.
 template <int D>
-__device__ __forceinline__ void fwht_rotate8(float (&x)[8], const float* signs, int c,
-                                             float inv_sqrt_d) {
+__device__ __forceinline__ void fwht8(float (&x)[8], int c) {
   constexpr int LPT = D / 8;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) x[e] *= signs[8 * c + e];  // exact sign flips
 #pragma unroll
   for (int h = 1; h < 8; h <<= 1) {
     float y[8];
@@ -41,6 +38,16 @@ __device__ __forceinline__ void fwht_rotate8(float (&x)[8], const float* signs, 
       x[e] = upper ? __fsub_rn(other, x[e]) : __fadd_rn(x[e], other);
     }
   }
+}
+
+// x' = H diag(sigma) x / sqrt(D): the sign flips (exact), the butterfly
+// network above, then one multiply by 1/sqrt(D).
+template <int D>
+__device__ __forceinline__ void fwht_rotate8(float (&x)[8], const float* signs, int c,
+                                             float inv_sqrt_d) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) x[e] *= signs[8 * c + e];  // exact sign flips
+  fwht8<D>(x, c);
 #pragma unroll
   for (int e = 0; e < 8; ++e) x[e] = __fmul_rn(x[e], inv_sqrt_d);
 }

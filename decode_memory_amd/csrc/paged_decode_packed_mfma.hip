@@ -118,28 +118,6 @@ struct PShape {
 template <int D>
 constexpr int kPMinWaves = D <= 64 ? 4 : 2;
 
-// N 32-bit words at p (aligned to min(4 N, 16) bytes) with the widest loads.
-template <int N>
-__device__ __forceinline__ void load_words(const void* p, uint32_t (&w)[N]) {
-  if constexpr (N % 4 == 0) {
-#pragma unroll
-    for (int k = 0; k < N / 4; ++k) {
-      const uint4 x = reinterpret_cast<const uint4*>(p)[k];
-      w[4 * k] = x.x;
-      w[4 * k + 1] = x.y;
-      w[4 * k + 2] = x.z;
-      w[4 * k + 3] = x.w;
-    }
-  } else if constexpr (N == 2) {
-    const uint2 x = *reinterpret_cast<const uint2*>(p);
-    w[0] = x.x;
-    w[1] = x.y;
-  } else {
-    static_assert(N == 1, "1, 2 or a multiple of 4 words");
-    w[0] = *reinterpret_cast<const uint32_t*>(p);
-  }
-}
-
 __device__ __forceinline__ const char* lane_ptr(uint64_t v, int j) {
   const uint32_t lo = __builtin_amdgcn_readlane(static_cast<uint32_t>(v), j);
   const uint32_t hi = __builtin_amdgcn_readlane(static_cast<uint32_t>(v >> 32), j);
@@ -263,21 +241,30 @@ __global__ __launch_bounds__(kPThreads, kPMinWaves<D>) void paged_decode_packed_
   const int32_t* trow = a.table + static_cast<size_t>(b) * a.max_blocks;
 
   // Independent loads first: the length, the rows of this split's blocks (one
-  // per lane), this wave's query heads and the signs.  Lane l holds query
-  // values [l EPL, (l + 1) EPL) of the wave's [G][D] query.
+  // per lane), this wave's query heads and the signs.  A query head vector
+  // is held 8 values per lane by QLPT = D/8 lanes (lane c: values 8c ..
+  // 8c+7), QVPP vectors per pass of the wave; pass p, lane l holds query head
+  // p QVPP + l / QLPT of the wave's G.
   int len = a.lens[b];
   int row = -1;
   {
     const int blk = s + lane * n_split;
     if (lane < a.blocks_per_split && blk < a.max_blocks) row = trow[blk];
   }
-  constexpr int EPL = G * D / kWave;
-  uint32_t qw[(EPL + 1) / 2], sgw[EPL];  // bf16 pairs (one value: the low half); signs
+  constexpr int QLPT = D / 8, QVPP = kWave / QLPT, QPASS = (G + QVPP - 1) / QVPP;
+  const int qc = lane % QLPT;
+  uint4 qraw[QPASS];
+  float4 sg0, sg1;  // the signs of values 8 qc .. 8 qc + 7
   {
-    const uint16_t* q = static_cast<const uint16_t*>(a.q) + (static_cast<size_t>(b) * a.n_q + h * G) * D + lane * EPL;
-    if constexpr (EPL == 1) qw[0] = q[0];
-    else load_words<EPL / 2>(q, qw);
-    load_words<EPL>(a.signs + (lane * EPL) % D, sgw);
+    const uint16_t* q = static_cast<const uint16_t*>(a.q) + (static_cast<size_t>(b) * a.n_q + h * G) * D;
+#pragma unroll
+    for (int p = 0; p < QPASS; ++p) {
+      const int j = p * QVPP + lane / QLPT;
+      qraw[p] = j < G ? *reinterpret_cast<const uint4*>(q + j * D + 8 * qc) : make_uint4(0, 0, 0, 0);
+    }
+    const float4* sp4 = reinterpret_cast<const float4*>(a.signs + 8 * qc);
+    sg0 = sp4[0];
+    sg1 = sp4[1];
   }
   const int cap_len = min(a.max_blocks, n_split * a.blocks_per_split) * kPBS;
   const bool len_ok = len >= 0 && len <= cap_len;
@@ -380,25 +367,43 @@ __global__ __launch_bounds__(kPThreads, kPMinWaves<D>) void paged_decode_packed_
   };
   if (n_stages > 0) fetch(0);
 
-  // ---- query: widen, signs, fp32 Walsh-Hadamard transform (per wave, LDS) --
+  // ---- query: widen, signs, fp32 Walsh-Hadamard butterflies (in registers),
+  // then into this wave's LDS area as [G][D] -----------------------------
   float* sq = s_aux[h];
-#pragma unroll
-  for (int e = 0; e < EPL; ++e) {
-    const uint32_t qb = (e % 2) ? qw[e / 2] & 0xffff0000u : qw[e / 2] << 16;
-    sq[lane * EPL + e] = __uint_as_float(qb) * __uint_as_float(sgw[e]);
-  }
-  __syncthreads();
-  for (int hh = 1; hh < D; hh <<= 1) {
-    for (int i = lane; i < G * D / 2; i += kWave) {
-      const int j = i / (D / 2), p = i % (D / 2);
-      const int i0 = j * D + (p / hh) * 2 * hh + (p % hh);
-      const float x = sq[i0], y = sq[i0 + hh];
-      sq[i0] = x + y;
-      sq[i0 + hh] = x - y;
-    }
-    __syncthreads();
-  }
   const float qs = a.inv_sqrt_d * a.scale_log2;  // scores live in the exp2 domain
+  // and per (query head, group): the sum of q' (offset term) and 1024 times
+  // the sum of the A operand's f16 values (the bias the biased key codes
+  // add), each over the lane's 8 values and then its group's GS/8 lanes
+#pragma unroll
+  for (int p = 0; p < QPASS; ++p) {
+    const int j = p * QVPP + lane / QLPT;
+    float x[8];
+    widen8<true>(qraw[p], x);
+    x[0] *= sg0.x, x[1] *= sg0.y, x[2] *= sg0.z, x[3] *= sg0.w;  // exact sign flips
+    x[4] *= sg1.x, x[5] *= sg1.y, x[6] *= sg1.z, x[7] *= sg1.w;
+    fwht8<D>(x, qc);  // every lane takes part (lane exchanges)
+    float qsum_l = 0.f, ab_l = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      qsum_l += x[e];
+      ab_l += static_cast<float>(static_cast<_Float16>(x[e] * qs * key_q_factor<KB>(e)));
+    }
+#pragma unroll
+    for (int m = 1; m < GS / 8; m <<= 1) {
+      qsum_l += __shfl_xor(qsum_l, m, kWave);
+      ab_l += __shfl_xor(ab_l, m, kWave);
+    }
+    if (j < G) {
+      float4* dst = reinterpret_cast<float4*>(sq + j * D + 8 * qc);
+      dst[0] = make_float4(x[0], x[1], x[2], x[3]);
+      dst[1] = make_float4(x[4], x[5], x[6], x[7]);
+      if (qc % (GS / 8) == 0) {
+        s_qs[h][j * NMG + qc / (GS / 8)] = qsum_l * qs;
+        s_kb[h][j * NMG + qc / (GS / 8)] = ab_l * 1024.f;
+      }
+    }
+  }
+  __syncthreads();  // q', its group sums in LDS
   // A operands of the score products: row m = n holds query head m / 4 when
   // m % 4 == 0 (rows of absent query heads and the rest are zero), k-block J
   h8 aq[NKB];
@@ -413,22 +418,8 @@ __global__ __launch_bounds__(kPThreads, kPMinWaves<D>) void paged_decode_packed_
         aq[g][e] = static_cast<_Float16>(live ? sq[jq * D + g * 32 + v] * qs * key_q_factor<KB>(v) : 0.f);
       }
   }
-  // per (query head, group), one lane each, into LDS: the sum of q' (offset
-  // term) and 1024 times the sum of the A operand's f16 values (the bias the
-  // biased key codes add); each lane then takes those of query head J of the
-  // score layout
-  for (int i = lane; i < G * NMG; i += kWave) {
-    const float* src = sq + (i / NMG) * D + (i % NMG) * GS;
-    float acc = 0.f, ab = 0.f;
-#pragma unroll 8
-    for (int k = 0; k < GS; ++k) {
-      acc += src[k];
-      ab += static_cast<float>(static_cast<_Float16>(src[k] * qs * key_q_factor<KB>(k)));
-    }
-    s_qs[h][i] = acc * qs;
-    s_kb[h][i] = ab * 1024.f;
-  }
-  __syncthreads();  // the per-wave area is reused for p^T below
+  // each lane takes the group sums of query head J of the score layout; the
+  // stage loop's first barrier orders these LDS reads before p^T reuses the area
   float qsum[NMG], kbias[NMG];
 #pragma unroll
   for (int g = 0; g < NMG; ++g) {

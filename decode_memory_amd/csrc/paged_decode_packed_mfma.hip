@@ -411,12 +411,17 @@ __global__ __launch_bounds__(kPThreads, kPMinWaves<D>) void paged_decode_packed_
     const bool live = (n % 4) == 0 && n / 4 < G;
     const int jq = live ? n / 4 : 0;
 #pragma unroll
-    for (int g = 0; g < NKB; ++g)
+    for (int g = 0; g < NKB; ++g) {
+      // the lane's 8 values of the k-block are contiguous (4-bit codes take them permuted)
+      const float4* src = reinterpret_cast<const float4*>(sq + jq * D + g * 32 + J * 8);
+      const float4 lo = src[0], hi = src[1];
+      const float vals[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const int v = J * 8 + key_value_index<KB>(e);
-        aq[g][e] = static_cast<_Float16>(live ? sq[jq * D + g * 32 + v] * qs * key_q_factor<KB>(v) : 0.f);
+        const int v = key_value_index<KB>(e);
+        aq[g][e] = static_cast<_Float16>(live ? vals[v] * qs * key_q_factor<KB>(v) : 0.f);
       }
+    }
   }
   // each lane takes the group sums of query head J of the score layout; the
   // stage loop's first barrier orders these LDS reads before p^T reuses the area

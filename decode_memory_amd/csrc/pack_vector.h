@@ -31,11 +31,13 @@ __device__ __forceinline__ void fwht8(float (&x)[8], int c) {
   }
 #pragma unroll
   for (int hl = 1; hl < LPT; hl <<= 1) {
-    const bool upper = (c & hl) != 0;
+    // the lower lane keeps x + other, the upper other - x: one fma with a
+    // +-1 factor (exact product, one rounding) gives both
+    const float sgn = (c & hl) ? -1.f : 1.f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const float other = __shfl_xor(x[e], hl, kWave);
-      x[e] = upper ? __fsub_rn(other, x[e]) : __fadd_rn(x[e], other);
+      x[e] = __fmaf_rn(sgn, x[e], other);
     }
   }
 }
@@ -81,12 +83,15 @@ __device__ __forceinline__ void quantise_store8(const float (&x)[8], int c, int 
   }
   const float levels = static_cast<float>((1 << bits) - 1);
   const float scale = __fdiv_rn(__fsub_rn(mx, mn), levels);
+  // a constant group (scale 0) gets code 0; it divides by 1 instead, so that
+  // no lane branches
+  const bool flat = scale == 0.f;
+  const float div = flat ? 1.f : scale;
   uint32_t code[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
-    float t = 0.f;
-    if (scale != 0.f) t = fminf(fmaxf(rintf(__fdiv_rn(__fsub_rn(x[e], mn), scale)), 0.f), levels);
-    code[e] = static_cast<uint32_t>(t);
+    const float t = fminf(fmaxf(rintf(__fdiv_rn(__fsub_rn(x[e], mn), div)), 0.f), levels);
+    code[e] = flat ? 0u : static_cast<uint32_t>(t);
   }
   if (!rec) return;
   if (bits == 8) {

@@ -90,7 +90,7 @@ EXPORTS = [
     "pd_version", "pd_last_error", "pd_record_bytes", "pd_pool_create", "pd_pool_destroy",
     "pd_slab_bytes", "pd_append_slab", "pd_slabs_needed", "pd_reserve_rows", "pd_slab_for_row",
     "pd_write_block", "pd_copy_on_write_block", "pd_gather_visible", "pd_decode_workspace_bytes",
-    "pd_paged_decode", "pd_paged_decode_append",
+    "pd_paged_decode", "pd_paged_decode_noalloc", "pd_paged_decode_append",
     "pd_paged_decode_split", "pd_paged_decode_combine", "pd_pool_stats", "pd_pool_check_error",
     "pd_signs_hash", "pd_storage_identity_of", "pd_identity_check", "pd_block_bytes",
     "pd_export_blocks", "pd_import_blocks", "pd_dense_workspace_bytes", "pd_dense_decode",
@@ -120,6 +120,8 @@ def _declare(lib):
         "pd_decode_workspace_bytes": (_i32, [_vp, _i32, _i32, _i32, ctypes.POINTER(_sz)]),
         "pd_paged_decode": (_i32, [_vp, _i32, _i32, _i32, _vp, _vp, _i32, _vp, _i32,
                                    ctypes.c_float, _vp, _vp, _sz, _vp]),
+        "pd_paged_decode_noalloc": (_i32, [_vp, _i32, _i32, _i32, _vp, _vp, _i32, _vp, _i32,
+                                           ctypes.c_float, _vp, _vp]),
         "pd_paged_decode_append": (_i32, [_vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _i32, _vp, _i32,
                                    ctypes.c_float, _vp, _vp, _sz, _vp]),
         "pd_paged_decode_split": (_i32, [_vp, _i32, _i32, _i32, _vp, _vp, _i32, _vp, _i32,
@@ -418,6 +420,23 @@ def paged_decode(pool: int, layer: int, q: torch.Tensor, block_table: torch.Tens
                                  _stream(stream)))
 
 
+def paged_decode_noalloc(pool: int, layer: int, q: torch.Tensor, block_table: torch.Tensor,
+                         lens: torch.Tensor, max_len: int, scale: float, out: torch.Tensor,
+                         stream=None) -> None:
+    """pd_paged_decode_noalloc: paged_decode with the partials in the
+    library's static per-device scratch (no workspace, nothing allocated)."""
+    B, n_q, _ = q.shape
+    _require(q, "q")
+    _require(block_table, "block_table", torch.int32)
+    _require(lens, "lens", torch.int32, B)
+    _require(out, "out", q.dtype, q.numel())
+    if block_table.shape[0] != B:
+        raise ValueError("block_table rows must equal the batch size")
+    _check(lib().pd_paged_decode_noalloc(pool, layer, B, n_q, _ptr(q), _ptr(block_table),
+                                         block_table.shape[1], _ptr(lens), max_len, float(scale),
+                                         _ptr(out), _stream(stream)))
+
+
 def paged_decode_append(pool: int, layer: int, q: torch.Tensor, k_new: torch.Tensor,
                         v_new: torch.Tensor, block_table: torch.Tensor, lens: torch.Tensor,
                         max_len: int, scale: float, out: torch.Tensor, workspace: torch.Tensor,
@@ -580,6 +599,9 @@ class SlabPool:
                      stream=None, stage="all"):
         paged_decode(self.handle, layer, q, block_table, lens, max_len, scale, out, workspace,
                      stream, stage)
+
+    def paged_decode_noalloc(self, layer, q, block_table, lens, max_len, scale, out, stream=None):
+        paged_decode_noalloc(self.handle, layer, q, block_table, lens, max_len, scale, out, stream)
 
     def paged_decode_append(self, layer, q, k_new, v_new, block_table, lens, max_len, scale, out,
                             workspace, stream=None):

@@ -13,6 +13,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -53,9 +54,41 @@ struct pd_pool {
   float inv_sqrt_d = 1.f;
 };
 
+// Device scratch of pd_paged_decode_noalloc, for callers that cannot
+// allocate: the split partials of one call live here instead of in a
+// caller-provided workspace.  Each device the library runs on holds its own
+// copy until the process ends.  In host code `scratch` names a host-side
+// stand-in, never the device memory: the host reaches the memory only
+// through the address hipGetSymbolAddress returns for the current device,
+// kept per device in g_scratch.
+constexpr size_t kNoAllocScratchBytes = size_t{16} << 20;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
 namespace {
 
 thread_local std::string g_last_error;
+
+constexpr int kMaxDevices = 64;
+struct ScratchSlot {
+  bool resolved = false;  // hipGetSymbolAddress has run on this device
+  hipError_t status = hipSuccess;
+  void* ptr = nullptr;
+};
+std::mutex g_scratch_mu;
+ScratchSlot g_scratch[kMaxDevices];
+
+// Once per device, with that device current (pd_pool_create): the device
+// address of this device's copy of `scratch`.
+void resolve_scratch(int device) {
+  if (device < 0 || device >= kMaxDevices) return;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  ScratchSlot& slot = g_scratch[device];
+  if (slot.resolved) return;
+  void* ptr = nullptr;
+  slot.status = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+  slot.ptr = slot.status == hipSuccess ? ptr : nullptr;
+  slot.resolved = true;
+}
 
 pd_status fail(pd_status st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
 pd_status fail(pd_status st, const char* fmt, ...) {
@@ -332,6 +365,7 @@ pd_status pd_pool_create(const pd_pool_desc* d, pd_pool** out) {
   p->inv_sqrt_d = static_cast<float>(1.0 / std::sqrt(static_cast<double>(d->head_dim)));
 
   hipError_t e = hipGetDevice(&p->device);
+  if (e == hipSuccess) resolve_scratch(p->device);  // a failure is reported by the no-alloc call
   if (e == hipSuccess) e = hipHostMalloc(reinterpret_cast<void**>(&p->h_tables),
                                          table_entries * sizeof(void*), hipHostMallocDefault);
   if (e == hipSuccess) {
@@ -649,7 +683,8 @@ static pd_status decode_call(pd_pool* p, int32_t layer, int32_t B, int32_t n_q_h
                       const int32_t* block_table, int32_t max_blocks, const int32_t* lens,
                       int32_t max_len, float scale, void* out, void* workspace,
                       size_t workspace_bytes, hipStream_t stream, int stages,
-                      const void* k_new = nullptr, const void* v_new = nullptr) {
+                      const void* k_new = nullptr, const void* v_new = nullptr,
+                      bool use_scratch = false) {
   if (pd_status st = check_pool(p)) return st;
   if (pd_status st = check_layer(p, layer)) return st;
   if (B < 0 || max_blocks < 1 || max_len < 0) return fail(PD_ERR_ARG, "B < 0, max_blocks < 1 or max_len < 0");
@@ -658,6 +693,14 @@ static pd_status decode_call(pd_pool* p, int32_t layer, int32_t B, int32_t n_q_h
   if (n_q_heads < 1 || n_q_heads % n_kv)
     return fail(PD_ERR_ARG, "n_q_heads %d not a positive multiple of n_kv_heads %d", n_q_heads, n_kv);
   const int32_t group = n_q_heads / n_kv;
+  if (use_scratch) {
+    if (workspace) return fail(PD_ERR_ARG, "the no-alloc call takes no workspace");
+    const ScratchSlot* slot = p->device >= 0 && p->device < kMaxDevices ? &g_scratch[p->device] : nullptr;
+    if (!slot || !slot->resolved) return fail(PD_ERR_HIP, "no scratch address for device %d", p->device);
+    if (slot->status != hipSuccess) return hip_fail(slot->status, "hipGetSymbolAddress(scratch)");
+    workspace = slot->ptr;
+    workspace_bytes = kNoAllocScratchBytes;
+  }
   if (!q || !block_table || !lens || !out || !workspace) return fail(PD_ERR_ARG, "NULL device pointer");
   if ((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(out)) & 15)
     return fail(PD_ERR_ARG, "q and out must be 16-byte aligned");
@@ -675,6 +718,10 @@ static pd_status decode_call(pd_pool* p, int32_t layer, int32_t B, int32_t n_q_h
                 p->desc.format, p->desc.head_dim, group);
   if (pd_status st = check_decode_size(B, n_q_heads, plan)) return st;
   const size_t need = decode_workspace_bytes(B, n_q_heads, p->desc.head_dim, plan.split);
+  if (use_scratch && need > workspace_bytes)
+    return fail(PD_ERR_CAPACITY,
+                "this call needs %zu bytes of partials; the no-alloc scratch holds %zu "
+                "(use pd_paged_decode with a workspace)", need, workspace_bytes);
   if (workspace_bytes < need)
     return fail(PD_ERR_CAPACITY, "workspace %zu bytes, %zu needed", workspace_bytes, need);
   if (k_new || v_new) {
@@ -732,6 +779,14 @@ pd_status pd_paged_decode(pd_pool* p, int32_t layer, int32_t B, int32_t n_q_head
                           size_t workspace_bytes, hipStream_t stream) {
   return decode_call(p, layer, B, n_q_heads, q, block_table, max_blocks, lens, max_len, scale, out,
                      workspace, workspace_bytes, stream, kStageSplit | kStageCombine);
+}
+
+pd_status pd_paged_decode_noalloc(pd_pool* p, int32_t layer, int32_t B, int32_t n_q_heads,
+                                  const void* q, const int32_t* block_table, int32_t max_blocks,
+                                  const int32_t* lens, int32_t max_len, float scale, void* out,
+                                  hipStream_t stream) {
+  return decode_call(p, layer, B, n_q_heads, q, block_table, max_blocks, lens, max_len, scale, out,
+                     nullptr, 0, stream, kStageSplit | kStageCombine, nullptr, nullptr, true);
 }
 
 pd_status pd_paged_decode_append(pd_pool* p, int32_t layer, int32_t B, int32_t n_q_heads,

@@ -305,6 +305,29 @@ pd_status pd_paged_decode(pd_pool* pool, int32_t layer, int32_t B, int32_t n_q_h
                           void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * pd_paged_decode with no workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  The split partials go to a scratch
+ * array inside the library, 16 MiB per device (a file-scope device array
+ * that every device the library runs on holds until the process ends; its
+ * address is looked up once per device, in the first pd_pool_create on that
+ * device).  The call allocates nothing: no hipMalloc, hipFree or allocating
+ * library routine.  Arguments, kernels, split plan and output are those of
+ * pd_paged_decode with the same inputs, bit for bit.  A call whose partials
+ * (pd_decode_workspace_bytes for its B, n_q_heads and max_len) exceed the
+ * scratch is PD_ERR_CAPACITY and enqueues nothing.  Nothing in the scratch
+ * needs to start at zero: every partial the combine reads is written by the
+ * same call.  All calls on one device share that device's scratch, which
+ * keeps the last call's contents: calls that overlap on one device (other
+ * streams, other threads, other pools) race and give undefined outputs;
+ * order them on one stream.
+ */
+pd_status pd_paged_decode_noalloc(pd_pool* pool, int32_t layer, int32_t B, int32_t n_q_heads,
+                                  const void* q, const int32_t* block_table, int32_t max_blocks,
+                                  const int32_t* lens, int32_t max_len, float scale, void* out,
+                                  hipStream_t stream);
+
+/*
  * Append then attend, in one launch of the split kernel: mlxcel #2171
  * ("refactor: one KV storage abstraction with dense and paged backends",
  * section "Proposed Solution"): attend(q, k, v, scale, mask) takes the new

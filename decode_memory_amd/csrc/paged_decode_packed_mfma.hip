@@ -16,6 +16,17 @@
 // MFMA units take exactly in f16; q' and p * scale go in as f16 and the
 // products accumulate in fp32.
 //
+// Range and precision of the f16 operands.  q' goes in as two f16 parts (hi =
+// f16(y), lo = f16(y - hi): about 22 bits of y), in two rows of the A operand
+// that the single-token query leaves free, so the scores carry close to fp32
+// precision at no extra product.  Before the split, each query head is scaled
+// by a power of two 2^kq (kq <= 0) that keeps its largest |q'| below 2^14;
+// the scores are scaled back exactly.  p * scale goes in as f16 times a
+// power of two 2^vk per value group and wave: vk starts at 10 and is lowered
+// (the accumulator of the group rescaled by the exact ratio) whenever a step
+// holds a group scale with p * scale * 2^vk possibly above 2^15 (p <= 1), so
+// no operand overflows f16 for any finite record.
+//
 // Decomposition.  A workgroup owns (sequence, split of the token axis) and
 // all 8 kv heads, one wave per kv head; split s takes logical blocks s, s +
 // n_split, ...  Whole token rows of a block (every head, K and V) are staged
@@ -80,7 +91,6 @@ constexpr int kPThreads = kPWaves * kWave;
 constexpr int kPBS = 32;    // tokens per block
 constexpr int kPLdsSlabs = kPThreads;  // slab pointers staged in LDS
 constexpr int kSub = 16;    // tokens per MFMA sub-tile
-constexpr float kPScale = 1024.f;  // p * scale travels as (p * scale * 1024) in f16
 
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 typedef _Float16 h4 __attribute__((ext_vector_type(4)));
@@ -194,12 +204,33 @@ __device__ __forceinline__ int vdim(int i, int lane) {
   else return 2 * (lane + 64 * (i / 2)) + (i % 2);
 }
 // Scale that brings accumulator i of lane l back to sum_t p_t s_t c_t: the
-// 1024 of p * scale, and 16 more for a 4-bit high nibble taken in place.
+// prescale 2^vk of p * scale, and 16 more for a 4-bit high nibble taken in
+// place (exact powers of two).
 template <int VB, int NV>
-__device__ __forceinline__ float vacc_scale(int i, int lane) {
+__device__ __forceinline__ float vacc_scale(int i, int lane, int vk) {
   const bool high = VB == 4 && (NV == 1 ? lane >= 32 : (i % 2) == 1);
-  return high ? 1.f / (16.f * kPScale) : 1.f / kPScale;
+  return __builtin_bit_cast(float, static_cast<uint32_t>(127 - vk - (high ? 4 : 0)) << 23);
 }
+
+// 2^k as an fp32 (k in [-126, 128]; 128 gives inf)
+__device__ __forceinline__ float exp2i(int k) {
+  return __builtin_bit_cast(float, static_cast<uint32_t>(127 + k) << 23);
+}
+// floor(log2(x)) of a normal positive fp32
+__device__ __forceinline__ int exponent_of(float x) {
+  return static_cast<int>((__builtin_bit_cast(uint32_t, x) >> 23) & 0xffu) - 127;
+}
+// f16 high and low parts of y: hi = f16(y), lo = f16(y - hi) (y - hi is exact)
+__device__ __forceinline__ void split_f16(float y, _Float16& hi, _Float16& lo) {
+  hi = static_cast<_Float16>(y);
+  lo = static_cast<_Float16>(y - static_cast<float>(hi));
+}
+// Exponent kq <= 0 of the power-of-two prescale of a query head whose largest
+// |q' * qs| is mq: 0 while mq < 2^14, else the one that brings it below 2^14.
+__device__ __forceinline__ int query_prescale(float mq) {
+  return mq < 16384.f ? 0 : 13 - exponent_of(mq);
+}
+constexpr int kVk0 = 10;  // first value prescale exponent: p * scale * 1024
 
 __device__ __forceinline__ float row_max16(float v) {
   v = fmaxf(v, dpp<kDppXor1>(v));
@@ -224,6 +255,7 @@ __global__ __launch_bounds__(kPThreads, kPMinWaves<D>) void paged_decode_packed_
   __shared__ __attribute__((aligned(16))) float s_aux[kPWaves][AUX];  // q' transform, then p^T
   __shared__ float s_qs[kPWaves][G * NMG];  // sum of q' per (query head, group)
   __shared__ float s_kb[kPWaves][G * NMG];  // 1024 * sum of the f16 A operand, likewise
+  __shared__ int s_qk[kPWaves][4];          // query prescale exponent per query head
   __shared__ uint64_t s_kt[kPLdsSlabs];    // slab base pointers of the layer
   __shared__ uint64_t s_vt[kPLdsSlabs];
 
@@ -372,8 +404,9 @@ __global__ __launch_bounds__(kPThreads, kPMinWaves<D>) void paged_decode_packed_
   float* sq = s_aux[h];
   const float qs = a.inv_sqrt_d * a.scale_log2;  // scores live in the exp2 domain
   // and per (query head, group): the sum of q' (offset term) and 1024 times
-  // the sum of the A operand's f16 values (the bias the biased key codes
-  // add), each over the lane's 8 values and then its group's GS/8 lanes
+  // the sum of the A operand's f16 values, both parts (the bias the biased
+  // key codes add), each over the lane's 8 values and then its group's GS/8
+  // lanes; all of it at the query head's prescale 2^kq
 #pragma unroll
   for (int p = 0; p < QPASS; ++p) {
     const int j = p * QVPP + lane / QLPT;
@@ -382,11 +415,20 @@ __global__ __launch_bounds__(kPThreads, kPMinWaves<D>) void paged_decode_packed_
     x[0] *= sg0.x, x[1] *= sg0.y, x[2] *= sg0.z, x[3] *= sg0.w;  // exact sign flips
     x[4] *= sg1.x, x[5] *= sg1.y, x[6] *= sg1.z, x[7] *= sg1.w;
     fwht8<D>(x, qc);  // every lane takes part (lane exchanges)
+    float mq = 0.f;  // largest |q' * qs| of the query head, over its QLPT lanes
+#pragma unroll
+    for (int e = 0; e < 8; ++e) mq = fmaxf(mq, fabsf(x[e] * qs));
+#pragma unroll
+    for (int m = 1; m < QLPT; m <<= 1) mq = fmaxf(mq, __shfl_xor(mq, m, kWave));
+    const int kq = query_prescale(mq);
+    const float qsf = qs * exp2i(kq);  // exact: a power of two
     float qsum_l = 0.f, ab_l = 0.f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       qsum_l += x[e];
-      ab_l += static_cast<float>(static_cast<_Float16>(x[e] * qs * key_q_factor<KB>(e)));
+      _Float16 hi, lo;
+      split_f16(x[e] * qsf * key_q_factor<KB>(e), hi, lo);
+      ab_l += static_cast<float>(hi) + static_cast<float>(lo);
     }
 #pragma unroll
     for (int m = 1; m < GS / 8; m <<= 1) {
@@ -398,28 +440,35 @@ __global__ __launch_bounds__(kPThreads, kPMinWaves<D>) void paged_decode_packed_
       dst[0] = make_float4(x[0], x[1], x[2], x[3]);
       dst[1] = make_float4(x[4], x[5], x[6], x[7]);
       if (qc % (GS / 8) == 0) {
-        s_qs[h][j * NMG + qc / (GS / 8)] = qsum_l * qs;
+        s_qs[h][j * NMG + qc / (GS / 8)] = qsum_l * qsf;
         s_kb[h][j * NMG + qc / (GS / 8)] = ab_l * 1024.f;
       }
+      if (qc == 0) s_qk[h][j] = kq;
     }
   }
   __syncthreads();  // q', its group sums in LDS
-  // A operands of the score products: row m = n holds query head m / 4 when
-  // m % 4 == 0 (rows of absent query heads and the rest are zero), k-block J
+  // A operands of the score products, k-block J: row m = n holds the high
+  // f16 part of query head m / 4 when m % 4 == 0 and its low part when m % 4
+  // == 1 (rows of absent query heads and the rest are zero), so output
+  // registers 0 and 1 of a score lane hold the two parts' products
   h8 aq[NKB];
   {
-    const bool live = (n % 4) == 0 && n / 4 < G;
+    const int part = n % 4;
+    const bool live = part < 2 && n / 4 < G;
     const int jq = live ? n / 4 : 0;
+    const float qsf = qs * exp2i(s_qk[h][jq]);
 #pragma unroll
     for (int g = 0; g < NKB; ++g) {
       // the lane's 8 values of the k-block are contiguous (4-bit codes take them permuted)
       const float4* src = reinterpret_cast<const float4*>(sq + jq * D + g * 32 + J * 8);
-      const float4 lo = src[0], hi = src[1];
-      const float vals[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+      const float4 lo4 = src[0], hi4 = src[1];
+      const float vals[8] = {lo4.x, lo4.y, lo4.z, lo4.w, hi4.x, hi4.y, hi4.z, hi4.w};
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int v = key_value_index<KB>(e);
-        aq[g][e] = static_cast<_Float16>(live ? vals[v] * qs * key_q_factor<KB>(v) : 0.f);
+        _Float16 hi, lo;
+        split_f16(vals[v] * qsf * key_q_factor<KB>(v), hi, lo);
+        aq[g][e] = live ? (part == 0 ? hi : lo) : static_cast<_Float16>(0.f);
       }
     }
   }
@@ -431,13 +480,66 @@ __global__ __launch_bounds__(kPThreads, kPMinWaves<D>) void paged_decode_packed_
     qsum[g] = J < G ? s_qs[h][J * NMG + g] : 0.f;
     kbias[g] = J < G ? s_kb[h][J * NMG + g] : 0.f;
   }
-
-  float m_run = -INFINITY, l_run = 0.f, bias[NMG];
-  f4 acc[NV];  // lane l: dimension 64 i + l, register r: query head r
+  const float qinv = J < G ? exp2i(-s_qk[h][J]) : 1.f;  // undoes the query prescale (exact)
+  // first accumulator of each group's score products: the bias the biased
+  // key codes add, taken off inside the product (score register 0; register
+  // 1 collects the low part of q')
+  f4 cinit[NMG];
 #pragma unroll
-  for (int g = 0; g < NMG; ++g) bias[g] = 0.f;
+  for (int g = 0; g < NMG; ++g) cinit[g] = f4{-kbias[g], 0.f, 0.f, 0.f};
+
+  f4 acc[NV];  // lane l: dimension vdim(i, l), register r: query head r
 #pragma unroll
   for (int i = 0; i < NV; ++i) acc[i] = f4{0.f, 0.f, 0.f, 0.f};
+  // value prescale exponents, per group (wave-uniform)
+  int vk[NMG];
+#pragma unroll
+  for (int g = 0; g < NMG; ++g) vk[g] = kVk0;
+  // The f16 operands of a step are p * scale * 2^vk (p <= 1).  A step whose
+  // value scales (read unmasked: cheaper, and a stale invisible scale costs
+  // at most a needless look) may exceed 2^15 / 2^vk takes the slow path:
+  // each group whose largest visible scale s has s * 2^vk above 2^15 gets
+  // the exponent that brings s below 2^15, and its accumulator columns are
+  // rescaled by the exact ratio.  Then no operand can reach f16's range.
+  int vk_top = kVk0;  // max over groups of vk: the lowest threshold is 2^(15 - vk_top)
+  auto fit_value_prescale = [&](const bool (&tv)[NSUB], const float2 (&vm)[NSUB][NMG]) {
+    // scales are >= 0, so their bit patterns order as unsigned integers
+    // (a NaN or -0 only sends the step to the slow path)
+    uint32_t big = 0u;
+#pragma unroll
+    for (int u = 0; u < NSUB; ++u)
+#pragma unroll
+      for (int g = 0; g < NMG; ++g) big = max(big, __builtin_bit_cast(uint32_t, vm[u][g].x));
+    if (!__ballot(big > __builtin_bit_cast(uint32_t, exp2i(15 - vk_top)))) return;  // uniform; rare
+    vk_top = -1000;
+#pragma unroll
+    for (int g = 0; g < NMG; ++g) {
+      float mx = 0.f;
+#pragma unroll
+      for (int u = 0; u < NSUB; ++u) mx = fmaxf(mx, tv[u] ? vm[u][g].x : 0.f);
+      mx = row_max16(mx);
+      mx = fmaxf(fmaxf(__builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, mx), 0)),
+                       __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, mx), 16))),
+                 fmaxf(__builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, mx), 32)),
+                       __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, mx), 48))));
+      if (mx > exp2i(15 - vk[g])) {
+        const int knew = __builtin_amdgcn_readfirstlane(14 - exponent_of(mx));
+        const float ratio = exp2i(knew - vk[g]);
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+          const float f = vdim<VB, NV>(i, lane) / GS == g ? ratio : 1.f;
+          acc[i] *= f;
+        }
+        vk[g] = knew;
+      }
+      vk_top = max(vk_top, vk[g]);
+    }
+    vk_top = __builtin_amdgcn_readfirstlane(vk_top);
+  };
+
+  float m_run = -INFINITY, l_run = 0.f, bias[NMG];
+#pragma unroll
+  for (int g = 0; g < NMG; ++g) bias[g] = 0.f;
   // p * scale * 1024 as f16: [group][query head][token of the step]
   _Float16* sp = reinterpret_cast<_Float16*>(s_aux[h]);
 
@@ -473,7 +575,7 @@ __global__ __launch_bounds__(kPThreads, kPMinWaves<D>) void paged_decode_packed_
 #pragma unroll
         for (int mg = 0; mg < NMG; ++mg) {
           // the k-blocks of one group accumulate in one product chain
-          f4 c = f4{0.f, 0.f, 0.f, 0.f};
+          f4 c = cinit[mg];
 #pragma unroll
           for (int kk = 0; kk < KPG; ++kk) {
             const int g = mg * KPG + kk;
@@ -481,23 +583,28 @@ __global__ __launch_bounds__(kPThreads, kPMinWaves<D>) void paged_decode_packed_
             c = __builtin_amdgcn_mfma_f32_16x16x32_f16(aq[g], bk, c, 0, 0, 0);
           }
           const float2 km = *reinterpret_cast<const float2*>(krow + S::KCODE + 8 * mg);
-          sv = fmaf(c[0] - kbias[mg], km.x, fmaf(km.y, qsum[mg], sv));
+          sv = fmaf(c[0] + c[1], km.x, fmaf(km.y, qsum[mg], sv));
         }
         const bool tv = J < G && t0 + lt0 + n < nt;
+        // sv carries the query prescale: qinv takes it off (in the max, and
+        // in the exponent's fma)
         const float sc = tv ? sv : -INFINITY;
-        const float m_new = fmaxf(m_run, row_max16(sc));  // -inf while nothing is visible
+        const float m_new = fmaxf(m_run, row_max16(sc) * qinv);  // -inf while nothing is visible
         alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
-        const float p = (sc == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(sc - m_new);
+        const float p = (sc == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(fmaf(sc, qinv, -m_new));
         m_run = m_new;
         l_run = fmaf(l_run, alpha, p);
-        const float pk = p * kPScale;
         // value metadata of token n; invisible tokens add nothing even if it is garbage
         const unsigned char* vrow = s_stage + T * PK + (lt0 + n) * PV + h * VREC;
+        float2 vm[1][NMG];
+#pragma unroll
+        for (int g = 0; g < NMG; ++g) vm[0][g] = *reinterpret_cast<const float2*>(vrow + S::VCODE + 8 * g);
+        const bool ta[1] = {tv};
+        fit_value_prescale(ta, vm);
 #pragma unroll
         for (int g = 0; g < NMG; ++g) {
-          const float2 vm = *reinterpret_cast<const float2*>(vrow + S::VCODE + 8 * g);
-          bias[g] = fmaf(bias[g], alpha, tv ? p * vm.y : 0.f);
-          sp[(g * 4 + J) * STEP + n] = static_cast<_Float16>(tv ? pk * vm.x : 0.f);
+          bias[g] = fmaf(bias[g], alpha, tv ? p * vm[0][g].y : 0.f);
+          sp[(g * 4 + J) * STEP + n] = static_cast<_Float16>(tv ? (p * exp2i(vk[g])) * vm[0][g].x : 0.f);
         }
       } else {
         // scores of each sub-tile: lane (n, J) = (token n, query head J);
@@ -510,7 +617,7 @@ __global__ __launch_bounds__(kPThreads, kPMinWaves<D>) void paged_decode_packed_
           float sv = 0.f;
 #pragma unroll
           for (int mg = 0; mg < NMG; ++mg) {
-            f4 c = f4{0.f, 0.f, 0.f, 0.f};
+            f4 c = cinit[mg];
 #pragma unroll
             for (int kk = 0; kk < KPG; ++kk) {
               const int g = mg * KPG + kk;
@@ -518,20 +625,21 @@ __global__ __launch_bounds__(kPThreads, kPMinWaves<D>) void paged_decode_packed_
               c = __builtin_amdgcn_mfma_f32_16x16x32_f16(aq[g], bk, c, 0, 0, 0);
             }
             const float2 km = *reinterpret_cast<const float2*>(krow + S::KCODE + 8 * mg);
-            sv = fmaf(c[0] - kbias[mg], km.x, fmaf(km.y, qsum[mg], sv));
+            sv = fmaf(c[0] + c[1], km.x, fmaf(km.y, qsum[mg], sv));
           }
           tv[u] = J < G && t0 + lt0 + u * kSub + n < nt;
-          sc[u] = tv[u] ? sv : -INFINITY;
+          sc[u] = tv[u] ? sv : -INFINITY;  // carries the query prescale, taken off by qinv below
         }
         float mx = sc[0];
 #pragma unroll
         for (int u = 1; u < NSUB; ++u) mx = fmaxf(mx, sc[u]);
-        const float m_new = fmaxf(m_run, row_max16(mx));  // -inf while nothing is visible
+        const float m_new = fmaxf(m_run, row_max16(mx) * qinv);  // -inf while nothing is visible
         alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
         float p[NSUB];
 #pragma unroll
         for (int u = 0; u < NSUB; ++u) {
-          const float e = __builtin_amdgcn_exp2f(sc[u] - m_new);  // NaN when both are -inf: not used
+          // NaN when both are -inf: not used
+          const float e = __builtin_amdgcn_exp2f(fmaf(sc[u], qinv, -m_new));
           p[u] = (sc[u] == -INFINITY) ? 0.f : e;
         }
         m_run = m_new;
@@ -553,14 +661,16 @@ __global__ __launch_bounds__(kPThreads, kPMinWaves<D>) void paged_decode_packed_
             asm volatile("" : "+v"(vm[u][g]));
           }
         }
+        fit_value_prescale(tv, vm);
 #pragma unroll
         for (int g = 0; g < NMG; ++g) {
           float bg = fmaf(bias[g], alpha, tv[0] ? p[0] * vm[0][g].y : 0.f);
+          const float pf = exp2i(vk[g]);
 #pragma unroll
           for (int u = 0; u < NSUB; ++u) {
             if (u > 0) bg += tv[u] ? p[u] * vm[u][g].y : 0.f;
             sp[(g * 4 + J) * STEP + u * kSub + n] =
-                static_cast<_Float16>(tv[u] ? (p[u] * kPScale) * vm[u][g].x : 0.f);
+                static_cast<_Float16>(tv[u] ? (p[u] * pf) * vm[u][g].x : 0.f);
           }
           bias[g] = bg;
         }
@@ -645,9 +755,13 @@ __global__ __launch_bounds__(kPThreads, kPMinWaves<D>) void paged_decode_packed_
     for (int i = 0; i < NV; ++i) {
       const int d = vdim<VB, NV>(i, lane);
       float bsel = 0.f;
+      int ksel = kVk0;
 #pragma unroll
-      for (int g = 0; g < NMG; ++g) bsel = d / GS == g ? bq[g] : bsel;
-      part_acc[d] = fmaf(acc[i][r], vacc_scale<VB, NV>(i, lane), bsel);
+      for (int g = 0; g < NMG; ++g) {
+        bsel = d / GS == g ? bq[g] : bsel;
+        ksel = d / GS == g ? vk[g] : ksel;
+      }
+      part_acc[d] = fmaf(acc[i][r], vacc_scale<VB, NV>(i, lane, ksel), bsel);
     }
     if (lane == kSub * r) {
       a.partials[a.ml_offset + hs * 2] = m_run;

@@ -20,6 +20,7 @@ from .inputs import (  # noqa: F401
     normal_bits,
     normal_device,
     q_bits,
+    ranged_bits,
     shuffled_rows,
     workload_lengths,
 )

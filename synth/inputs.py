@@ -66,6 +66,19 @@ def normal_bits(seed_seq, shape, dtype: str) -> np.ndarray:
     raise ValueError(dtype)
 
 
+def ranged_bits(seed_seq, shape, group: int, amplitudes: Sequence[float], dtype: str = BF16) -> np.ndarray:
+    """Uniform samples from PCG64 whose value groups (``group`` consecutive
+    values along the last axis) lie in [-A, A], A = amplitudes[g % len], for
+    group g of a vector; rounded to ``dtype``; uint16 bits.  Stands in for
+    keys, values or queries far from unit scale."""
+    rng = np.random.Generator(np.random.PCG64(seed_seq))
+    x = rng.uniform(-1.0, 1.0, size=shape).astype(np.float32)
+    d = shape[-1]
+    amp = np.asarray([amplitudes[(i // group) % len(amplitudes)] for i in range(d)], dtype=np.float32)
+    x = (x * amp).astype(np.float32)
+    return f16_bits_from_f32(x) if dtype == FP16 else bf16_bits_from_f32(x)
+
+
 def kv_bits_for_sequence(seed: int, layer: int, b: int, length: int, n_kv: int,
                          head_dim: int, dtype: str):
     """K and V of one sequence in one layer: two uint16 arrays [length, n_kv, D]."""

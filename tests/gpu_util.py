@@ -105,3 +105,67 @@ def run_decode(pool, layer, q_bits, table, lengths, dtype, scale, max_len=None, 
     pool.paged_decode(layer, q, t, lens, ml, scale, out, ws)
     torch.cuda.synchronize()
     return from_device_bits(out)
+
+
+def packed_decode_bound(q_bits, k_recs, v_recs, signs, fmt, head_dim, scale, group):
+    """Per-output error bound of the packed decode kernel's arithmetic, in fp64
+    from the same records (shape [B, n_q, D]).
+
+    The kernel feeds the matrix cores f16 operands.  Value products take
+    p * scale as f16 (relative error 2^-11, or 2^-25 absolute below f16's
+    normal range, at a power-of-two prescale 2^vk that is at least
+    min(1024, 2^(14 - e)) for a largest group scale in [2^e, 2^(e+1))), so
+    the value sum is off by at most 2^-11 * sum_t p_t |v_t - offset_t| / l
+    plus the subnormal floor; twice that is allowed (fp32 accumulation).
+    Scores take q' as two f16 parts (about 22 bits) whose products accumulate
+    in fp32 around biased codes: an error below 2^-16 * scale * sum_i
+    |q'_i k_i| per score is allowed, and it moves the output by at most that
+    times sum_t p_t |v_t - o| / l.  The 2e-3 of the plain tolerance comes on
+    top."""
+    from oracle.packed import FORMATS, rotate_exact, unpack
+
+    kb, vb = FORMATS[fmt]
+    q_rot = rotate_exact(widen(q_bits, "bf16"), signs)  # [B, n_q, D]
+    B, n_q, D = q_rot.shape
+    out = np.zeros((B, n_q, D))
+    for b in range(B):
+        if k_recs[b].shape[0] == 0:
+            continue
+        kc, ks, ko = unpack(k_recs[b], head_dim, kb, group)
+        vc, vs, vo = unpack(v_recs[b], head_dim, vb, group)
+        ng = head_dim // group
+        kh = (kc.astype(np.float64).reshape(kc.shape[:-1] + (ng, group)) * ks[..., None] + ko[..., None]
+              ).reshape(kc.shape)                                   # [T, n_kv, D]
+        vd = (vc.astype(np.float64).reshape(vc.shape[:-1] + (ng, group)) * vs[..., None])
+        vd = vd.reshape(vc.shape)                                   # v - offset
+        vh = vd + np.repeat(vo.astype(np.float64), group, axis=-1)  # v
+        n_kv = kh.shape[1]
+        G = n_q // n_kv
+        T = kh.shape[0]
+        vmax = float(np.max(vs)) if vs.size else 0.0
+        e = np.floor(np.log2(vmax)) if vmax > 0 else -100
+        vf = min(1024.0, 2.0 ** (14 - e))
+        floor = T * ((1 << vb) - 1) * 2.0 ** -25 / vf
+        for h in range(n_q):
+            g = h // G
+            s = scale * (kh[:, g, :] @ q_rot[b, h])
+            s1 = scale * (np.abs(kh[:, g, :]) @ np.abs(q_rot[b, h]))
+            w = np.exp(s - s.max())
+            l = w.sum()
+            o = (w @ vh[:, g, :]) / l
+            wterm = (w @ np.abs(vd[:, g, :])) / l
+            dv = (w @ np.abs(vh[:, g, :] - o)) / l
+            out[b, h] = 2.0 * 2.0 ** -11 * wterm + floor + 2.0 ** -16 * s1.max() * dv
+    return out
+
+
+def assert_packed_close(out_bits, ref, bound, dtype="bf16", tol=TOL):
+    """|out - ref| <= tol + half an output ulp at |ref| + bound, element-wise;
+    every output finite.  Returns the largest error over its allowance."""
+    got = widen(out_bits, dtype)
+    assert np.isfinite(got).all(), "non-finite output"
+    err = np.abs(got - ref)
+    allow = tol + half_ulp(ref, dtype) + bound
+    worst = float((err / allow).max(initial=0.0))
+    assert worst <= 1.0, (worst, float(err.max()))
+    return worst

@@ -14,9 +14,9 @@ import decode_memory_amd as pd
 from oracle.packed import FORMATS, k_records, packed_decode_attention, record_bytes, v_records
 from oracle.slab_pool import SlabPoolModel
 from synth import (WORKLOADS, hadamard_signs, kv_bits_for_sequence, make_block_table,
-                   monotone_rows, q_bits, shuffled_rows)
-from tests.gpu_util import (assert_decode_close, from_device_bits, i32, to_device_bits,
-                            token_targets)
+                   monotone_rows, q_bits, ranged_bits, shuffled_rows)
+from tests.gpu_util import (assert_decode_close, assert_packed_close, from_device_bits, i32,
+                            packed_decode_bound, to_device_bits, token_targets)
 
 pytestmark = pytest.mark.gpu
 
@@ -164,3 +164,69 @@ def test_packed_workload_full_size_sampled(fmt, D, group):
     print(f"packed {fmt} D={D} group {group}: max-abs {err:.2e}")
     assert pool.check_error() == 0
     pool.close()
+
+
+def _ranged_case(fmt, D, G, group, seed, v_amps=None, q_amp=None):
+    """A packed pool over sequences of mixed lengths whose V groups alternate
+    between +-v_amps[i] (uniform) and whose query is uniform in +-q_amp (or
+    N(0, 1) when not given); returns (device output bits, oracle output,
+    per-output bound)."""
+    kb, vb = FORMATS[fmt]
+    lengths = [300, 1, 45, 0, 1024, 64]
+    B = len(lengths)
+    rows, _, R = shuffled_rows(np.random.default_rng(seed), lengths, BS, 32, spare_rows=2)
+    signs = hadamard_signs(seed, D)
+    pool = pd.SlabPool(1, BS, 8, D, 32, -(-R // 32) + 2, fmt, hadamard_signs=signs, group_size=group)
+    pool.reserve_rows(R)
+    kr, vr = [], []
+    for b, n in enumerate(lengths):
+        k, v = kv_bits_for_sequence(seed, 0, b, n, 8, D, "bf16")
+        if v_amps is not None:
+            v = ranged_bits(np.random.SeedSequence([seed, b, 7]), (n, 8, D), group, v_amps)
+        kr.append(k_records(k, signs, kb, group))
+        vr.append(v_records(v, vb, group))
+        if n:
+            r, sl = token_targets(rows[b], n, BS)
+            pool.write_block(0, i32(r), i32(sl), to_device_bits(k, "bf16"), to_device_bits(v, "bf16"))
+    if q_amp is None:
+        q = q_bits(seed, 0, B, 8 * G, D, "bf16")
+    else:
+        q = ranged_bits(np.random.SeedSequence([seed, 1 << 20]), (B, 8 * G, D), D, [q_amp])
+    scale = 1.0 / np.sqrt(D)
+    qd = to_device_bits(q, "bf16")
+    out = torch.empty_like(qd)
+    ws = pool.workspace(B, 8 * G, max(lengths))
+    pool.paged_decode(0, qd, i32(make_block_table(rows)), i32(lengths), max(lengths), scale, out, ws)
+    got = from_device_bits(out)
+    assert pool.check_error() == 0
+    pool.close()
+    ref = packed_decode_attention(q, kr, vr, signs, fmt, D, scale, group)
+    return got, ref, packed_decode_bound(q, kr, vr, signs, fmt, D, scale, group)
+
+
+@pytest.mark.parametrize("fmt", ["k8v8", "k8v4", "k4v4"])
+@pytest.mark.parametrize("amp", [600.0, 5000.0, 20000.0])
+@pytest.mark.parametrize("D,G,group", [(64, 4, 32), (256, 2, 32), (128, 4, 64)])
+def test_packed_decode_wide_value_groups(fmt, amp, D, G, group):
+    """V groups spanning +-600, +-5000 and +-20000 next to unit-scale groups
+    in the same vectors: the record format takes any finite range (fp32 scale
+    and offset per group), so the output must be finite and within the
+    arithmetic's bound of the oracle over the same records.  At 4 bits a
+    range above about 960 (8 bits: 16,300) took p * scale past f16's range
+    before the value prescale was lowered as the groups demand."""
+    got, ref, bound = _ranged_case(fmt, D, G, group, 700 + D + G + int(amp) % 97, v_amps=[amp, 1.0])
+    worst = assert_packed_close(got, ref, bound)
+    print(f"{fmt} D={D} G={G} group {group} V +-{amp:g}: error / allowance {worst:.3f}")
+
+
+@pytest.mark.parametrize("fmt", ["k8v8", "k8v4", "k4v4"])
+@pytest.mark.parametrize("q_amp", [8.0, 1.0e6])
+@pytest.mark.parametrize("D,G,group", [(64, 4, 32), (256, 4, 32), (128, 2, 64)])
+def test_packed_decode_large_norm_query(fmt, q_amp, D, G, group):
+    """Queries uniform in +-8 (a sharp softmax over near-tied scores, where
+    the scores' precision shows) and in +-1e6 (|q'| far beyond f16's range:
+    the query is prescaled by a power of two, and the softmax is one-hot).
+    Every output finite and within the arithmetic's bound of the oracle."""
+    got, ref, bound = _ranged_case(fmt, D, G, group, 800 + D + G + int(q_amp) % 89, q_amp=q_amp)
+    worst = assert_packed_close(got, ref, bound)
+    print(f"{fmt} D={D} G={G} group {group} q +-{q_amp:g}: error / allowance {worst:.3f}")

@@ -89,7 +89,8 @@ class DenseDesc(ctypes.Structure):
 EXPORTS = [
     "pd_version", "pd_last_error", "pd_record_bytes", "pd_pool_create", "pd_pool_destroy",
     "pd_slab_bytes", "pd_append_slab", "pd_slabs_needed", "pd_reserve_rows", "pd_slab_for_row",
-    "pd_write_block", "pd_copy_on_write_block", "pd_gather_visible", "pd_decode_workspace_bytes",
+    "pd_write_block", "pd_copy_on_write_block", "pd_gather_visible", "pd_split_runs",
+    "pd_decode_workspace_bytes",
     "pd_paged_decode", "pd_paged_decode_noalloc", "pd_paged_decode_append",
     "pd_paged_decode_split", "pd_paged_decode_combine", "pd_pool_stats", "pd_pool_check_error",
     "pd_signs_hash", "pd_storage_identity_of", "pd_identity_check", "pd_block_bytes",
@@ -117,6 +118,7 @@ def _declare(lib):
         "pd_write_block": (_i32, [_vp, _i32, _i32, _vp, _vp, _vp, _vp, _vp]),
         "pd_copy_on_write_block": (_i32, [_vp, _i32, _vp, _vp, _vp]),
         "pd_gather_visible": (_i32, [_vp, _i32, _i32, _vp, _i32, _vp, _i32, _vp, _vp, _vp, _vp]),
+        "pd_split_runs": (_i32, [_vp, _i32, _vp, _i32, _vp, _vp, _vp, _vp]),
         "pd_decode_workspace_bytes": (_i32, [_vp, _i32, _i32, _i32, ctypes.POINTER(_sz)]),
         "pd_paged_decode": (_i32, [_vp, _i32, _i32, _i32, _vp, _vp, _i32, _vp, _i32,
                                    ctypes.c_float, _vp, _vp, _sz, _vp]),
@@ -325,31 +327,41 @@ def dense_workspace_bytes(fmt, n_kv_heads: int, head_dim: int, B: int, n_q_heads
     return n.value
 
 
-def dense_decode(q: torch.Tensor, k_seqs: Sequence[torch.Tensor], v_seqs: Sequence[torch.Tensor],
-                 lens: torch.Tensor, max_len: int, scale: float, out: torch.Tensor,
-                 workspace: torch.Tensor, stream=None) -> None:
-    """Decode over per-sequence contiguous K/V [len_b, n_kv, D] (the dense
-    backend): bit-identical to paged_decode over the same tokens."""
-    B, n_q, D = q.shape
-    n_kv = k_seqs[0].shape[1] if B else 1
-    fmt = FMT_FP16 if q.dtype == torch.float16 else FMT_BF16
-    desc = DenseDesc(fmt, n_kv, D)
-    _require(q, "q")
-    _require(out, "out")
-    _require(lens, "lens", torch.int32, B)
+def dense_pointers(k_seqs: Sequence[torch.Tensor], v_seqs: Sequence[torch.Tensor],
+                   device=None) -> torch.Tensor:
+    """The device pointer table dense_decode reads: int64 [2, B], row 0 the
+    K and row 1 the V base address of each sequence.  Build it once, when the
+    sequences are placed, and keep it (and the sequences) alive while calls
+    use it: dense_decode itself allocates nothing."""
     for t in list(k_seqs) + list(v_seqs):
         _require(t, "k/v sequence")
-    s = torch.cuda.current_stream() if stream is None else stream
-    # the pointer array is copied to the device on the stream the kernel runs
-    # on, so the kernel reads it after the copy; allocated on that stream, it
-    # is reused only after the work queued there
-    with torch.cuda.stream(s):
-        ptrs = torch.tensor([t.data_ptr() for t in k_seqs] + [t.data_ptr() for t in v_seqs],
-                            dtype=torch.int64, device=q.device)
-        _check(lib().pd_dense_decode(ctypes.byref(desc), B, n_q, _ptr(q), ptrs.data_ptr(),
-                                     ptrs.data_ptr() + 8 * B, _ptr(lens), max_len, float(scale), _ptr(out),
-                                     _ptr(workspace), workspace.numel() * workspace.element_size(),
-                                     s.cuda_stream))
+    if len(k_seqs) != len(v_seqs):
+        raise ValueError("k_seqs and v_seqs differ in length")
+    dev = device if device is not None else (k_seqs[0].device if len(k_seqs) else "cuda")
+    return torch.tensor([[t.data_ptr() for t in k_seqs], [t.data_ptr() for t in v_seqs]],
+                        dtype=torch.int64, device=dev).reshape(2, len(k_seqs))
+
+
+def dense_decode(q: torch.Tensor, ptrs: torch.Tensor, n_kv_heads: int, lens: torch.Tensor,
+                 max_len: int, scale: float, out: torch.Tensor, workspace: torch.Tensor,
+                 stream=None) -> None:
+    """Decode over per-sequence contiguous K/V [len_b, n_kv, D] (the dense
+    backend), reached through `ptrs` (dense_pointers): bit-identical to
+    paged_decode over the same tokens.  Nothing is allocated per call."""
+    B, n_q, D = q.shape
+    fmt = FMT_FP16 if q.dtype == torch.float16 else FMT_BF16
+    if q.dtype not in (torch.float16, torch.bfloat16):
+        raise ValueError(f"q must be fp16 or bf16, got {q.dtype}")
+    desc = DenseDesc(fmt, n_kv_heads, D)
+    _require(q, "q")
+    _require(out, "out", q.dtype, q.numel())
+    _require(lens, "lens", torch.int32, B)
+    _require(ptrs, "ptrs", torch.int64, 2 * B)
+    _require(workspace, "workspace")
+    _check(lib().pd_dense_decode(ctypes.byref(desc), B, n_q, _ptr(q), ptrs.data_ptr(),
+                                 ptrs.data_ptr() + 8 * B, _ptr(lens), max_len, float(scale), _ptr(out),
+                                 _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                 _stream(stream)))
 
 
 CHECKPOINT_MAGIC = b"PDKVBLK1"
@@ -392,6 +404,19 @@ def gather_visible(pool: int, layer: int, block_table: torch.Tensor, lens: torch
         _require(n_runs_out, "n_runs_out", torch.int32, B)
     _check(lib().pd_gather_visible(pool, layer, B, _ptr(block_table), max_blocks, _ptr(lens), t_out,
                                    _ptr(k_out), _ptr(v_out), _ptr(n_runs_out), _stream(stream)))
+
+
+def split_runs(pool: int, block_table: torch.Tensor, lens: torch.Tensor, runs_out: torch.Tensor,
+               n_runs_out: torch.Tensor, stream=None) -> None:
+    """pd_split_runs: (slab, first block, blocks) of each same-slab run, per
+    sequence, into runs_out [B, max_blocks, 3] and the counts into n_runs_out [B]."""
+    B, max_blocks = block_table.shape
+    _require(block_table, "block_table", torch.int32)
+    _require(lens, "lens", torch.int32, B)
+    _require(runs_out, "runs_out", torch.int32, B * max_blocks * 3)
+    _require(n_runs_out, "n_runs_out", torch.int32, B)
+    _check(lib().pd_split_runs(pool, B, _ptr(block_table), max_blocks, _ptr(lens), _ptr(runs_out),
+                               _ptr(n_runs_out), _stream(stream)))
 
 
 def decode_workspace_bytes(pool: int, B: int, n_q_heads: int, max_len: int) -> int:
@@ -542,7 +567,33 @@ class SlabPool:
     def slab_for_row(self, layer: int, row: int):
         return slab_for_row(self.handle, layer, row)
 
+    # -- argument checks the C ABI cannot make (it sees raw pointers only) --
+
+    def _check_tokens(self, name, t, n):
+        """t holds n token rows [n, n_kv_heads, head_dim] in the pool's dtype."""
+        _require(t, name, self.dtype)
+        if t.numel() != n * self.n_kv_heads * self.head_dim:
+            raise ValueError(f"{name} must be [{n}, {self.n_kv_heads}, {self.head_dim}] "
+                             f"({n * self.n_kv_heads * self.head_dim} values), got {tuple(t.shape)}")
+
+    def _check_query(self, q, out=None):
+        _require(q, "q", self.dtype)
+        if q.dim() != 3 or q.shape[2] != self.head_dim or q.shape[1] % self.n_kv_heads:
+            raise ValueError(f"q must be [B, n_q_heads, {self.head_dim}] with n_q_heads a multiple of "
+                             f"{self.n_kv_heads}, got {tuple(q.shape)}")
+        if out is not None:
+            _require(out, "out", self.dtype, q.numel())
+
+    def _check_table(self, block_table, lens, B):
+        _require(block_table, "block_table", torch.int32)
+        if block_table.dim() != 2 or block_table.shape[0] != B:
+            raise ValueError(f"block_table must be [{B}, max_blocks], got {tuple(block_table.shape)}")
+        _require(lens, "lens", torch.int32, B)
+
     def write_block(self, layer, rows, slots, k_src, v_src, stream=None):
+        n = rows.numel()
+        self._check_tokens("k_src", k_src, n)
+        self._check_tokens("v_src", v_src, n)
         write_block(self.handle, layer, rows, slots, k_src, v_src, stream)
 
     def copy_on_write_block(self, src_rows, dst_rows, stream=None):
@@ -587,8 +638,26 @@ class SlabPool:
 
     def gather_visible(self, layer, block_table, lens, t_out, k_out, v_out, n_runs_out=None,
                        stream=None):
+        B = block_table.shape[0] if block_table.dim() == 2 else -1
+        self._check_table(block_table, lens, B)
+        for name, t, rec in (("k_out", k_out, self.k_record_bytes), ("v_out", v_out, self.v_record_bytes)):
+            _require(t, name)
+            need = B * self.n_kv_heads * int(t_out) * rec
+            if t.numel() * t.element_size() < need:
+                raise ValueError(f"{name} holds {t.numel() * t.element_size()} bytes; "
+                                 f"[{B}, {self.n_kv_heads}, {t_out}] records need {need}")
         gather_visible(self.handle, layer, block_table, lens, t_out, k_out, v_out, n_runs_out,
                        stream)
+
+    def split_runs(self, block_table, lens, stream=None):
+        """The same-slab runs of each sequence: (runs [B, max_blocks, 3] with
+        -1 past each sequence's count, n_runs [B]), on the device."""
+        B = block_table.shape[0] if block_table.dim() == 2 else -1
+        self._check_table(block_table, lens, B)
+        runs = torch.full((B, block_table.shape[1], 3), -1, dtype=torch.int32, device=self.device)
+        n = torch.empty((B,), dtype=torch.int32, device=self.device)
+        split_runs(self.handle, block_table, lens, runs, n, stream)
+        return runs, n
 
     def workspace(self, B: int, n_q_heads: int, max_len: int) -> torch.Tensor:
         """A decode workspace for up to B sequences of at most max_len tokens."""
@@ -597,16 +666,22 @@ class SlabPool:
 
     def paged_decode(self, layer, q, block_table, lens, max_len, scale, out, workspace,
                      stream=None, stage="all"):
+        self._check_query(q, out)
+        self._check_table(block_table, lens, q.shape[0])
         paged_decode(self.handle, layer, q, block_table, lens, max_len, scale, out, workspace,
                      stream, stage)
 
     def paged_decode_noalloc(self, layer, q, block_table, lens, max_len, scale, out, stream=None):
+        self._check_query(q, out)
+        self._check_table(block_table, lens, q.shape[0])
         paged_decode_noalloc(self.handle, layer, q, block_table, lens, max_len, scale, out, stream)
 
     def paged_decode_append(self, layer, q, k_new, v_new, block_table, lens, max_len, scale, out,
                             workspace, stream=None):
-        if k_new.numel() != q.shape[0] * self.n_kv_heads * self.head_dim:
-            raise ValueError("k_new must be [B, n_kv_heads, head_dim]")
+        self._check_query(q, out)
+        self._check_table(block_table, lens, q.shape[0])
+        self._check_tokens("k_new", k_new, q.shape[0])
+        self._check_tokens("v_new", v_new, q.shape[0])
         paged_decode_append(self.handle, layer, q, k_new, v_new, block_table, lens, max_len, scale,
                             out, workspace, stream)
 

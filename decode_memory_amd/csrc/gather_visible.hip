@@ -12,9 +12,12 @@
 //
 // Decomposition: one workgroup per (sequence, chunk of kChunk logical
 // blocks; one block measured fastest: more, shorter workgroups keep the
-// memory system busier than fewer, longer ones).  Lane i of the first wave resolves block i of the chunk: its row,
-// the row's slab and that slab's base pointer (blocks of one same-slab run
-// resolve to the same base).  The workgroup then copies the chunk's blocks in
+// memory system busier than fewer, longer ones).  The copy does not walk the
+// runs: lane i of the first wave resolves block i of the chunk itself -- its
+// row, the row's slab and that slab's base pointer (the blocks of one
+// same-slab run resolve to the same base, a table entry that stays in L2) --
+// so every block of every run is copied at once.  The run list is
+// split_runs_kernel's output (pd_split_runs).  The workgroup then copies the chunk's blocks in
 // logical order as 16-byte vectors: each block's source is one contiguous
 // row [block_size, n_kv, record]; the destination is n_kv contiguous pieces
 // of block_size records.  A block's K row and V row form one range of
@@ -174,7 +177,71 @@ __global__ __launch_bounds__(kThreads) void gather_kernel(GatherArgs a, GatherDi
 
 
 
+// The run split itself (mlxcel #235, "Proposed solution", touch point 3):
+// one wave per sequence walks its visible blocks 64 at a time.  Lane i takes
+// block c0 + i and its slab (row / slab_blocks; -1 for a row outside the
+// pool, which also sets the error word); a block starts a run when it is
+// the first or its slab differs from the previous block's.  A start lane
+// writes its run's (slab, first block) at the run's index (the starts before
+// it, counted with a ballot) and closes the previous run's count; the chunk
+// carries the run count, the last start and the last slab to the next.
+constexpr int kRunWaves = 4;
+
+__global__ __launch_bounds__(kRunWaves * kWave) void split_runs_kernel(RunArgs a) {
+  const int lane = threadIdx.x % kWave;
+  const int b = blockIdx.x * kRunWaves + threadIdx.x / kWave;
+  if (b >= a.B) return;
+  const LayerView& lv = a.lv;
+  const int bs = lv.block_size;
+  int len = a.lens[b];
+  const int cap_len = a.max_blocks * bs;
+  if (len < 0 || len > cap_len) {
+    if (lane == 0) set_error(lv.err, PD_DEVERR_LENGTH);
+    len = len < 0 ? 0 : cap_len;
+  }
+  const int nb = (len + bs - 1) / bs;
+  const int32_t* trow = a.table + static_cast<size_t>(b) * a.max_blocks;
+  int32_t* runs = a.runs + static_cast<size_t>(b) * a.max_blocks * 3;
+  int n_runs = 0, last_first = -1, last_slab = 0;
+  for (int c0 = 0; c0 < nb; c0 += kWave) {
+    const int blk = c0 + lane;
+    const bool valid = blk < nb;
+    int slab = -2;
+    if (valid) {
+      slab = slab_of(trow[blk], lv);
+      if (slab < 0) set_error(lv.err, PD_DEVERR_TABLE_ROW);
+    }
+    int prev = __shfl_up(slab, 1, kWave);
+    if (lane == 0) prev = last_slab;
+    const bool start = valid && (blk == 0 || slab != prev);
+    const uint64_t mask = __ballot(start);
+    const uint64_t below = mask & ((uint64_t{1} << lane) - 1);
+    if (start) {
+      const int k = n_runs + __popcll(below);
+      runs[3 * k] = slab;
+      runs[3 * k + 1] = blk;
+      // the previous run ends here: its first block is the highest start below this lane
+      const int prev_first = below ? c0 + 63 - __clzll(below) : last_first;
+      if (k > 0) runs[3 * (k - 1) + 2] = blk - prev_first;
+    }
+    n_runs += __popcll(mask);
+    if (mask) last_first = c0 + 63 - __clzll(mask);
+    last_slab = __shfl(slab, kWave - 1, kWave);
+  }
+  if (lane == 0) {
+    if (n_runs > 0) runs[3 * (n_runs - 1) + 2] = nb - last_first;
+    if (a.n_runs) a.n_runs[b] = n_runs;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_split_runs(const RunArgs& a, hipStream_t s) {
+  if (a.B <= 0) return hipSuccess;
+  const int grid = (a.B + kRunWaves - 1) / kRunWaves;
+  hipLaunchKernelGGL(split_runs_kernel, dim3(grid), dim3(kRunWaves * kWave), 0, s, a);
+  return hipGetLastError();
+}
 
 hipError_t launch_gather(const GatherArgs& a, hipStream_t s) {
   const int bs = a.lv.block_size;

@@ -70,6 +70,17 @@ struct GatherArgs {
   int32_t* n_runs_out;
 };
 
+// The run split of a block table (split_runs).
+struct RunArgs {
+  LayerView lv;
+  int32_t B;
+  const int32_t* table;
+  int32_t max_blocks;
+  const int32_t* lens;
+  int32_t* runs;    // [B][max_blocks][3]: (slab, first logical block, blocks)
+  int32_t* n_runs;  // [B]
+};
+
 struct DecodeArgs {
   LayerView lv;
   int32_t B;
@@ -97,12 +108,28 @@ struct DecodeArgs {
   float inv_sqrt_d;
 };
 
+// An append of new slabs, as one launch per up to kAppendMaxPairs (slab,
+// layer) pairs: the launch records each pair's K and V slab base pointers in
+// the device tables and zero-fills both slabs.  Passed by value, so the host
+// arrays can be reused as soon as the launch is queued.
+constexpr int kAppendMaxPairs = 96;
+struct AppendArgs {
+  void** tables;               // device [n_layers][2][max_slabs]
+  int32_t max_slabs;
+  int32_t n_pairs;             // pairs in this launch
+  int64_t k_bytes, v_bytes;    // bytes of one K slab, one V slab
+  int32_t entry[kAppendMaxPairs];  // table index of the pair's K pointer (V: + max_slabs)
+  void* k_mem[kAppendMaxPairs];
+  void* v_mem[kAppendMaxPairs];
+};
+
 // Launchers (return the hipError_t of the launch; hipErrorInvalidValue when
 // no kernel exists for the shape).
-hipError_t launch_zero_fill(void* p, size_t bytes, hipStream_t s);
+hipError_t launch_append_slabs(const AppendArgs& a, hipStream_t s);
 hipError_t launch_write_block(const WriteArgs& a, int32_t format, hipStream_t s);
 hipError_t launch_row_move(const RowMoveArgs& a, int mode, hipStream_t s);
 hipError_t launch_gather(const GatherArgs& a, hipStream_t s);
+hipError_t launch_split_runs(const RunArgs& a, hipStream_t s);
 hipError_t launch_paged_decode_column(const DecodeArgs& a, bool bf16, int32_t head_dim,
                                       int32_t group, hipStream_t s);
 hipError_t launch_paged_decode_row(const DecodeArgs& a, bool bf16, int32_t head_dim, int32_t group,

@@ -174,34 +174,34 @@ pd_status append_slabs(pd_pool* p, int32_t n, void* const* k_mem, void* const* v
   }
   hipError_t e = hipSetDevice(p->device);
   if (e != hipSuccess) return hip_fail(e, "hipSetDevice");
-  // zero the new memory first; nothing is recorded until every launch is queued
-  for (int64_t i = 0; i < static_cast<int64_t>(n) * L; ++i) {
-    if ((e = launch_zero_fill(k_mem[i], p->k_slab_bytes, stream)) != hipSuccess)
-      return hip_fail(e, "zero fill");
-    if ((e = launch_zero_fill(v_mem[i], p->v_slab_bytes, stream)) != hipSuccess)
-      return hip_fail(e, "zero fill");
-  }
+  // One launch per kAppendMaxPairs (slab, layer) pairs records the new base
+  // pointers in the device tables and zero-fills the new slabs (one launch
+  // for a single slab in up to 96 layers).  Nothing is recorded on the host
+  // until every launch is queued.
   const int ms = p->desc.max_slabs;
+  const int64_t pairs = static_cast<int64_t>(n) * L;
+  AppendArgs a{};
+  a.tables = p->d_tables;
+  a.max_slabs = ms;
+  a.k_bytes = static_cast<int64_t>(p->k_slab_bytes);
+  a.v_bytes = static_cast<int64_t>(p->v_slab_bytes);
+  for (int64_t i0 = 0; i0 < pairs; i0 += kAppendMaxPairs) {
+    a.n_pairs = static_cast<int32_t>(pairs - i0 < kAppendMaxPairs ? pairs - i0 : kAppendMaxPairs);
+    for (int j = 0; j < a.n_pairs; ++j) {
+      const int64_t i = i0 + j;  // slab-major, as k_mem / v_mem
+      const int64_t slab = p->n_slabs + i / L;
+      const int64_t l = i % L;
+      a.entry[j] = static_cast<int32_t>(l * 2 * ms + slab);
+      a.k_mem[j] = k_mem[i];
+      a.v_mem[j] = v_mem[i];
+    }
+    if ((e = launch_append_slabs(a, stream)) != hipSuccess) return hip_fail(e, "append_slabs launch");
+  }
   for (int s = 0; s < n; ++s) {
     const int64_t slab = p->n_slabs + s;
     for (int l = 0; l < L; ++l) {
       p->h_tables[static_cast<size_t>(l) * 2 * ms + slab] = k_mem[static_cast<size_t>(s) * L + l];
       p->h_tables[static_cast<size_t>(l) * 2 * ms + ms + slab] = v_mem[static_cast<size_t>(s) * L + l];
-    }
-  }
-  // copy the new entries (one contiguous range per layer and K/V table)
-  for (int l = 0; l < L; ++l) {
-    for (int kv = 0; kv < 2; ++kv) {
-      const size_t base = static_cast<size_t>(l) * 2 * ms + kv * ms + p->n_slabs;
-      e = hipMemcpyAsync(p->d_tables + base, p->h_tables + base, sizeof(void*) * n,
-                         hipMemcpyHostToDevice, stream);
-      if (e != hipSuccess) {
-        for (int s = 0; s < n; ++s)  // roll the host mirror back: nothing recorded
-          for (int ll = 0; ll < L; ++ll)
-            for (int kk = 0; kk < 2; ++kk)
-              p->h_tables[static_cast<size_t>(ll) * 2 * ms + kk * ms + p->n_slabs + s] = nullptr;
-        return hip_fail(e, "table update");
-      }
     }
   }
   p->n_slabs += n;
@@ -337,6 +337,10 @@ pd_status pd_pool_create(const pd_pool_desc* d, pd_pool** out) {
     return fail(PD_ERR_UNSUPPORTED, "block_size %d (supported: 16, 32, 64)", d->block_size);
   if (is_packed(d->format) && d->block_size != 32)
     return fail(PD_ERR_UNSUPPORTED, "packed formats use block_size 32");
+  // the packed decode kernel gives one wave to each of 8 kv heads: a pool it
+  // could not decode is refused here, before anything is written to it
+  if (is_packed(d->format) && d->n_kv_heads != 8)
+    return fail(PD_ERR_UNSUPPORTED, "packed formats need n_kv_heads 8 (got %d)", d->n_kv_heads);
   if (is_native(d->format) && d->group_size != 0)
     return fail(PD_ERR_ARG, "group_size %d: 16-bit formats have no groups (pass 0)", d->group_size);
   if (is_packed(d->format) && packed_group_or_zero(d->group_size, d->head_dim) == 0)
@@ -653,6 +657,27 @@ pd_status pd_gather_visible(pd_pool* p, int32_t layer, int32_t B, const int32_t*
   a.n_runs_out = n_runs_out;
   hipError_t e = launch_gather(a, stream);
   if (e != hipSuccess) return hip_fail(e, "gather_visible launch");
+  return PD_OK;
+}
+
+pd_status pd_split_runs(pd_pool* p, int32_t B, const int32_t* block_table, int32_t max_blocks,
+                        const int32_t* lens, int32_t* runs_out, int32_t* n_runs_out, hipStream_t stream) {
+  if (pd_status st = check_pool(p)) return st;
+  if (B < 0 || max_blocks < 1) return fail(PD_ERR_ARG, "B < 0 or max_blocks < 1");
+  if (B == 0) return PD_OK;
+  if (!block_table || !lens || !runs_out || !n_runs_out) return fail(PD_ERR_ARG, "NULL device pointer");
+  if (static_cast<int64_t>(max_blocks) * p->desc.block_size > INT32_MAX)
+    return fail(PD_ERR_ARG, "max_blocks * block_size beyond 2^31");
+  RunArgs a{};
+  a.lv = layer_view(p, 0);
+  a.B = B;
+  a.table = block_table;
+  a.max_blocks = max_blocks;
+  a.lens = lens;
+  a.runs = runs_out;
+  a.n_runs = n_runs_out;
+  hipError_t e = launch_split_runs(a, stream);
+  if (e != hipSuccess) return hip_fail(e, "split_runs launch");
   return PD_OK;
 }
 

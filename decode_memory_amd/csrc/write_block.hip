@@ -23,7 +23,17 @@ namespace {
 
 constexpr int kThreads = 256;
 
-__global__ __launch_bounds__(kThreads) void zero_fill_kernel(uint4* p, size_t n16) {
+// Growth (one launch per append): workgroup row y takes slab y of the launch
+// -- pair y / 2, K when y is even, V when odd -- records its base pointer in
+// the device table (workgroup column 0) and zero-fills it with the other
+// columns' help, 16 bytes per store.
+__global__ __launch_bounds__(kThreads) void append_slabs_kernel(AppendArgs a) {
+  const int y = blockIdx.y;
+  const int pair = y >> 1, kv = y & 1;
+  void* mem = kv ? a.v_mem[pair] : a.k_mem[pair];
+  if (blockIdx.x == 0 && threadIdx.x == 0) a.tables[a.entry[pair] + kv * a.max_slabs] = mem;
+  const size_t n16 = static_cast<size_t>(kv ? a.v_bytes : a.k_bytes) / 16;
+  uint4* p = static_cast<uint4*>(mem);
   const size_t stride = static_cast<size_t>(gridDim.x) * kThreads;
   for (size_t i = static_cast<size_t>(blockIdx.x) * kThreads + threadIdx.x; i < n16; i += stride)
     p[i] = make_uint4(0, 0, 0, 0);
@@ -288,13 +298,16 @@ __global__ __launch_bounds__(kThreads) void write_block_packed_kernel(WriteArgs 
 
 }  // namespace
 
-hipError_t launch_zero_fill(void* p, size_t bytes, hipStream_t s) {
-  const size_t n16 = bytes / 16;
-  if (n16 == 0) return hipSuccess;
-  size_t blocks = (n16 + kThreads - 1) / kThreads;
-  if (blocks > 4096) blocks = 4096;
-  hipLaunchKernelGGL(zero_fill_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, s,
-                     static_cast<uint4*>(p), n16);
+hipError_t launch_append_slabs(const AppendArgs& a, hipStream_t s) {
+  if (a.n_pairs <= 0) return hipSuccess;
+  if (a.n_pairs > kAppendMaxPairs) return hipErrorInvalidValue;
+  // columns per slab: about 4 stores per thread per column, at most 64
+  const size_t n16 = static_cast<size_t>(a.k_bytes > a.v_bytes ? a.k_bytes : a.v_bytes) / 16;
+  size_t cols = (n16 + 4 * kThreads - 1) / (4 * kThreads);
+  if (cols < 1) cols = 1;
+  if (cols > 64) cols = 64;
+  hipLaunchKernelGGL(append_slabs_kernel, dim3(static_cast<unsigned>(cols), 2 * a.n_pairs), dim3(kThreads), 0, s,
+                     a);
   return hipGetLastError();
 }
 

@@ -87,7 +87,7 @@ typedef enum pd_format {
 typedef struct pd_pool_desc {
   int32_t n_layers;      /* >= 1                                                */
   int32_t block_size;    /* tokens per block (row): 16, 32 or 64                */
-  int32_t n_kv_heads;    /* >= 1                                                */
+  int32_t n_kv_heads;    /* >= 1; packed formats: 8                             */
   int32_t head_dim;      /* 64, 128 or 256                                      */
   int32_t slab_blocks;   /* POOL_SLAB_BLOCKS: rows per slab, >= 1               */
   int32_t max_slabs;     /* capacity of the slab-pointer tables, >= 1           */
@@ -160,7 +160,10 @@ pd_status pd_record_bytes(int32_t format, int32_t head_dim, int32_t group_size, 
  * pool tensor.  Allocates the device slab-pointer tables
  * (n_layers * 2 * max_slabs pointers) and the device error word.
  * out: host, receives the handle.  Errors: PD_ERR_ARG, PD_ERR_UNSUPPORTED,
- * PD_ERR_HIP.
+ * PD_ERR_HIP.  Packed pools are refused (PD_ERR_UNSUPPORTED) unless the
+ * packed decode kernel can read them: block_size 32, n_kv_heads 8, head_dim
+ * 64/128/256, group_size 32 (or 64 with head_dim 128, 256).  Their decode
+ * calls take 8, 16 or 32 query heads (1, 2 or 4 per kv head).
  */
 pd_status pd_pool_create(const pd_pool_desc* desc, pd_pool** out);
 
@@ -250,8 +253,10 @@ pd_status pd_copy_on_write_block(pd_pool* pool, int32_t n, const int32_t* src_ro
 /*
  * gather_visible (mlxcel #235, "Proposed solution", touch point 3): copy each
  * sequence's visible K and V out of the pool into contiguous, transposed
- * tensors.  The row list of a sequence is split into maximal same-slab runs
- * in logical order; each run is read from its slab's base pointer.
+ * tensors: the same bytes the page's take-per-run, concatenate, reshape,
+ * slice and transpose produce.  The kernel reads every block from the slab
+ * its row names (the blocks of one same-slab run share that slab's base), so
+ * all runs are copied at once; pd_split_runs returns the runs themselves.
  *   block_table: device int32 [B, max_blocks]; entry (b, i) is the physical
  *     row of logical block i of sequence b; entries past the sequence's block
  *     count are ignored.
@@ -266,6 +271,23 @@ pd_status pd_copy_on_write_block(pd_pool* pool, int32_t n, const int32_t* src_ro
 pd_status pd_gather_visible(pd_pool* pool, int32_t layer, int32_t B, const int32_t* block_table,
                             int32_t max_blocks, const int32_t* lens, int32_t t_out, void* k_out,
                             void* v_out, int32_t* n_runs_out, hipStream_t stream);
+
+/*
+ * split_runs (mlxcel #235, "Proposed solution", touch point 3): the maximal
+ * same-slab runs of each sequence's visible blocks, in logical order.
+ *   block_table, lens: as pd_gather_visible (max_blocks * block_size < 2^31).
+ *   runs_out: device int32 [B, max_blocks, 3]; run k of sequence b is
+ *     (slab, first logical block, number of blocks) at runs_out[b][k]; the
+ *     entries past the sequence's run count are left as they were.
+ *   n_runs_out: device int32 [B], the run count of each sequence (0 for an
+ *     empty sequence).
+ * A row outside [0, capacity_rows) counts as slab -1 (consecutive such rows
+ * form one run) and sets PD_DEVERR_TABLE_ROW; a length outside [0,
+ * max_blocks * block_size] is clamped and sets PD_DEVERR_LENGTH.  Layer
+ * independent: rows name the same slab in every layer.
+ */
+pd_status pd_split_runs(pd_pool* pool, int32_t B, const int32_t* block_table, int32_t max_blocks,
+                        const int32_t* lens, int32_t* runs_out, int32_t* n_runs_out, hipStream_t stream);
 
 /*
  * Workspace bytes that pd_paged_decode needs for B sequences, n_q_heads query
@@ -298,6 +320,17 @@ pd_status pd_decode_workspace_bytes(const pd_pool* pool, int32_t B, int32_t n_q_
  * splits of each (sequence, kv head) in split order.
  * The result is bit-identical from run to run and independent of which
  * physical rows and slabs hold the data.
+ * Packed pools: the matrix cores take f16 operands.  The rotated query goes
+ * in as high and low f16 parts after a power-of-two scaling that keeps it in
+ * f16 range (any finite query); p * scale goes in as f16 at a power-of-two
+ * prescale per value group that the kernel lowers whenever a group's scale
+ * demands it (any finite record).  Admitted inputs: finite values whose
+ * rotated keys, group ranges (max - min), scores and outputs stay finite in
+ * fp32 and in bf16 (every bf16 input with |x| <= 2^100 and a finite
+ * output).  Error against exact arithmetic over the same records: at most
+ * 2^-11 of sum_t p_t |v_t - offset_t| / sum_t p_t per output (f16 value
+ * operands) plus what a score error of about 2^-18 of scale * sum_i |q'_i
+ * k_i| moves, before the final rounding to bf16.
  */
 pd_status pd_paged_decode(pd_pool* pool, int32_t layer, int32_t B, int32_t n_q_heads,
                           const void* q, const int32_t* block_table, int32_t max_blocks,

@@ -59,6 +59,11 @@ def test_version_and_record_bytes():
     (dict(fmt=pd.FMT_K4V4, head_dim=64, hadamard_signs=[1] * 64, group_size=64), -4),  # 40-byte records
     (dict(fmt=pd.FMT_K8V8, head_dim=128, hadamard_signs=[1] * 128, group_size=16), -4),
     (dict(fmt=pd.FMT_BF16, group_size=32), -1),  # 16-bit formats have no groups
+    # the packed decode kernel takes 8 kv heads: other head counts are refused
+    # at create, before anything could be written into a pool it cannot read
+    (dict(fmt=pd.FMT_K8V8, n_kv_heads=4, hadamard_signs=[1] * 128), -4),
+    (dict(fmt=pd.FMT_K4V4, n_kv_heads=16, hadamard_signs=[1] * 128), -4),
+    (dict(fmt=pd.FMT_K8V4, n_kv_heads=1, hadamard_signs=[1] * 128), -4),
 ])
 def test_pool_create_validates_on_host(kwargs, status):
     args = dict(n_layers=2, block_size=32, n_kv_heads=8, head_dim=128, slab_blocks=4,

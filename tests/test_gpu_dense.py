@@ -45,16 +45,17 @@ def test_dense_is_bit_identical_to_paged(D, G, n_kv, dtype, lengths):
     out = torch.empty_like(qd)
     ml = max(lengths)
     ws = torch.zeros(pd.dense_workspace_bytes(dtype, n_kv, D, B, n_q, ml), dtype=torch.uint8, device="cuda")
-    pd.dense_decode(qd, ks, vs, torch.tensor(lengths, dtype=torch.int32, device="cuda"), ml, scale, out, ws)
+    ptrs = pd.dense_pointers(ks, vs)  # built once; the calls allocate nothing
+    lens = torch.tensor(lengths, dtype=torch.int32, device="cuda")
+    pd.dense_decode(qd, ptrs, n_kv, lens, ml, scale, out, ws)
     torch.cuda.synchronize()
     dense = from_device_bits(out)
     assert np.array_equal(dense, paged)
-    # on another stream: the per-sequence pointer array travels on that stream too
+    # on another stream, with the same pointer table
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     out_side, ws_side = torch.full_like(out, 7), torch.zeros_like(ws)
-    pd.dense_decode(qd, ks, vs, torch.tensor(lengths, dtype=torch.int32, device="cuda"), ml, scale, out_side,
-                    ws_side, stream=side)
+    pd.dense_decode(qd, ptrs, n_kv, lens, ml, scale, out_side, ws_side, stream=side)
     side.synchronize()
     assert torch.equal(out_side, out)
     ref = decode_attention_bits(q, seqs["k"], seqs["v"], dtype, scale)
@@ -73,3 +74,13 @@ def test_dense_rejects_shapes_without_the_row_kernel():
     with pytest.raises(pd.PagedKVError) as e:
         pd.dense_workspace_bytes("k4v4", 8, 64, 1, 32, 100)
     assert e.value.status == -4
+
+
+def test_dense_decode_checks_its_pointer_table():
+    q = torch.zeros((2, 16, 128), dtype=torch.bfloat16, device="cuda")
+    out = torch.empty_like(q)
+    lens = torch.tensor([5, 5], dtype=torch.int32, device="cuda")
+    ws = torch.zeros(pd.dense_workspace_bytes("bf16", 8, 128, 2, 16, 5), dtype=torch.uint8, device="cuda")
+    bad = torch.zeros(3, dtype=torch.int64, device="cuda")  # [2, B] needs 4 pointers
+    with pytest.raises(ValueError):
+        pd.dense_decode(q, bad, 8, lens, 5, 0.1, out, ws)

@@ -85,3 +85,71 @@ def test_misaligned_slab_memory_is_rejected():
     assert e.value.status == -1
     assert p.stats()["n_slabs"] == 0
     p.close()
+
+
+def test_append_over_many_layers_records_every_table_entry():
+    """An append records each new slab's base pointer in the device tables and
+    zero-fills it in one launch per 96 (slab, layer) pairs: 40 layers x 3
+    slabs take two launches.  Garbage memory comes back zero, and a token
+    written to the last slab of the last layer gathers back through the
+    device table entry the second launch wrote."""
+    L, n = 40, 3
+    p = _pool(n_layers=L, max_slabs=4)
+    ks = [torch.full((p.k_slab_bytes,), 0xAB, dtype=torch.uint8, device="cuda") for _ in range(n * L)]
+    vs = [torch.full((p.v_slab_bytes,), 0xCD, dtype=torch.uint8, device="cuda") for _ in range(n * L)]
+    assert pd.reserve_rows(p.handle, 12, ks, vs, n) == n
+    p._adopt(ks, vs, n)
+    torch.cuda.synchronize()
+    assert all(int(t.count_nonzero()) == 0 for t in ks + vs)
+    for layer in (0, L - 1):
+        for row in (0, 11):
+            kb, vb, r = p.slab_for_row(layer, row)
+            assert kb == p.k_slabs[layer][row // 4].data_ptr() and r == row % 4
+    k = torch.arange(8 * 128, dtype=torch.float32, device="cuda").view(1, 8, 128).to(torch.bfloat16)
+    p.write_block(L - 1, torch.tensor([11], dtype=torch.int32, device="cuda"),
+                  torch.tensor([5], dtype=torch.int32, device="cuda"), k, -k)
+    table = torch.full((1, 12), -1, dtype=torch.int32, device="cuda")
+    table[0, 0] = 11
+    out_k = torch.zeros((1, 8, 6, 256), dtype=torch.uint8, device="cuda")
+    out_v = torch.zeros_like(out_k)
+    p.gather_visible(L - 1, table, torch.tensor([6], dtype=torch.int32, device="cuda"), 6, out_k, out_v)
+    torch.cuda.synchronize()
+    assert torch.equal(out_k[0, :, 5].view(torch.bfloat16), k[0])
+    assert torch.equal(out_v[0, :, 5].view(torch.bfloat16), -k[0])
+    assert int(out_k[0, :, :5].count_nonzero()) == 0            # zeroed slots before it
+    assert p.check_error() == 0
+    p.close()
+
+
+def test_allocation_failure_mid_append_leaves_pool_unchanged(monkeypatch):
+    """The slab memory of an append is allocated by the caller before the
+    library is called; an allocation that fails part-way (the fourth of six
+    slab tensors here) raises before anything is appended, and the pool's
+    counters, addresses and contents are as before.  A later append works."""
+    p = _pool(n_layers=3, max_slabs=5)
+    p.reserve_rows(4)
+    p.k_slabs[1][0].fill_(9)
+    st = p.stats()
+    addr = [p.slab_for_row(l, 3) for l in range(3)]
+    real_empty = torch.empty
+    calls = {"n": 0}
+
+    def failing_empty(*a, **kw):
+        calls["n"] += 1
+        if calls["n"] == 4:
+            raise RuntimeError("HIP out of memory (injected)")
+        return real_empty(*a, **kw)
+
+    monkeypatch.setattr(torch, "empty", failing_empty)
+    with pytest.raises(RuntimeError, match="injected"):
+        p.reserve_rows(8)
+    monkeypatch.setattr(torch, "empty", real_empty)
+    assert p.stats() == st
+    assert [p.slab_for_row(l, 3) for l in range(3)] == addr
+    with pytest.raises(pd.PagedKVError):
+        p.slab_for_row(0, 4)                                   # no slab was added
+    torch.cuda.synchronize()
+    assert bool((p.k_slabs[1][0] == 9).all())
+    assert p.reserve_rows(8) == 1                              # growth still works
+    assert p.stats()["n_slabs"] == 2
+    p.close()

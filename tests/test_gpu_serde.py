@@ -132,7 +132,9 @@ def test_incompatible_identity_is_rejected_before_anything_happens(change):
     elif change == "n_layers":
         kw["n_layers"] = 3
     else:
-        kw["n_kv"] = 4
+        # packed pools hold 8 kv heads (the packed decode kernel's shape), so
+        # blocks of another head count arrive as a foreign checkpoint header
+        ident.n_kv_heads = 4
     target = pd.SlabPool(kw["n_layers"], kw["block_size"], kw["n_kv"], kw["D"], 4, 16, kw["fmt"],
                          hadamard_signs=kw["signs"], group_size=kw["group"])
     target.reserve_rows(8)
@@ -144,7 +146,8 @@ def test_incompatible_identity_is_rejected_before_anything_happens(change):
     import tempfile, os
     with tempfile.TemporaryDirectory() as d:
         path = os.path.join(d, "blocks.pdkv")
-        pool.save_checkpoint(path, i32(blocks))
+        torch.cuda.synchronize()
+        pd.write_checkpoint(path, ident, payload)  # the (possibly foreign) identity the blocks carry
         slabs_before = target.stats()["n_slabs"]
         with pytest.raises(pd.PagedKVError) as e:
             target.restore_checkpoint(path, i32(np.arange(40, 40 + len(blocks), dtype=np.int32)))

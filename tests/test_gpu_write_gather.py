@@ -221,3 +221,63 @@ def test_copy_on_write_block_moves_packed_records(fmt, D):
             assert np.array_equal(pool.slab_view(layer, slab, "v").cpu().numpy(), model.v_slabs[layer][slab])
     assert pool.check_error() == 0
     pool.close()
+
+
+def _expected_runs(model, rows, lengths, bs):
+    out = []
+    for r, n in zip(rows, lengths):
+        nb = -(-int(n) // bs)
+        out.append(model.split_runs([int(x) for x in r[:nb]]))
+    return out
+
+
+@pytest.mark.parametrize("case", ["monotone_4k", "offset_5_runs", "shuffled_long", "one_row_slabs"])
+def test_split_runs_lists_every_run(case):
+    """pd_split_runs against the oracle's run split (maximal same-slab runs in
+    logical order, as (slab, first block, blocks)): the monotone 8 x 4096
+    layout gives exactly 4 runs per sequence, an offset of 16 rows 5, and
+    shuffled rows over sequences longer than one 64-block chunk (runs carried
+    across chunks) about one run per block; empty sequences have none."""
+    bs, n_kv, D = 32, 8, 128
+    if case == "monotone_4k":
+        lengths, S = [4096] * 8, 32
+        rows = monotone_rows(lengths, bs)
+    elif case == "offset_5_runs":
+        lengths, S = [4096] * 3, 32
+        rows = monotone_rows(lengths, bs, offset=16)
+    elif case == "shuffled_long":
+        lengths, S = [0, 1, 31, 33, 64 * 32, 64 * 32 + 1, 150 * 32 + 5, 7000], 4
+        rows, _, _ = shuffled_rows(np.random.default_rng(5), lengths, bs, S, spare_rows=9)
+    else:
+        lengths, S = [3000, 200, 0, 4096], 1
+        rows, _, _ = shuffled_rows(np.random.default_rng(6), lengths, bs, S, spare_rows=2)
+    cap = max(int(r.max()) + 1 for r in rows if len(r))
+    pool = pd.SlabPool(1, bs, n_kv, D, S, -(-cap // S) + 1, "bf16")
+    pool.reserve_rows(cap)
+    table = make_block_table(rows, max_blocks=max(len(r) for r in rows) + 3)
+    runs, n = pool.split_runs(i32(table), i32(lengths))
+    runs, n = runs.cpu().numpy(), n.cpu().numpy()
+    model = SlabPoolModel(1, bs, n_kv, 2 * D, 2 * D, S)
+    expect = _expected_runs(model, rows, lengths, bs)
+    for b, e in enumerate(expect):
+        assert n[b] == len(e), (case, b)
+        assert [tuple(int(x) for x in t) for t in runs[b, :n[b]]] == e, (case, b)
+        assert (runs[b, n[b]:] == -1).all()                     # left as they were
+    if case == "monotone_4k":
+        assert list(n) == [4] * 8
+    if case == "offset_5_runs":
+        assert list(n) == [5] * 3
+    assert pool.check_error() == 0
+    pool.close()
+
+
+def test_split_runs_flags_rows_outside_the_pool():
+    pool = pd.SlabPool(1, 32, 8, 128, 4, 2, "bf16")
+    pool.reserve_rows(8)
+    table = i32(np.array([[0, 1, 99, 100, 5, -3]], dtype=np.int32))
+    runs, n = pool.split_runs(table, i32([6 * 32]))
+    assert int(n[0]) == 4
+    assert [tuple(int(x) for x in t) for t in runs[0, :4].cpu().numpy()] == [(0, 0, 2), (-1, 2, 2), (1, 4, 1),
+                                                                             (-1, 5, 1)]
+    assert pool.check_error() == pd.DEVERR_TABLE_ROW
+    pool.close()

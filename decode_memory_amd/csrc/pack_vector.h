@@ -87,11 +87,30 @@ __device__ __forceinline__ void quantise_store8(const float (&x)[8], int c, int 
   // no lane branches
   const bool flat = scale == 0.f;
   const float div = flat ? 1.f : scale;
+  // The code is rint of the correctly rounded quotient q = RN(d / div), d =
+  // RN(x - mn) >= 0.  One correctly rounded reciprocal r = RN(1 / div) per
+  // lane and a product q' = RN(d * r) give q' within 2.5 ulp(q) of q, and for
+  // q < 256 that is below 2^-14.6, so rint(q') = rint(q) unless q' lies
+  // within 2^-14 of a half-integer.  Such a value (about 1 in 8000) sends the
+  // whole wave through the correctly rounded divisions.
+  const float r = __fdiv_rn(1.f, div);
+  float t[8];
+  bool near = false;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float q = __fmul_rn(__fsub_rn(x[e], mn), r);
+    near |= fabsf(__fsub_rn(q, floorf(q)) - 0.5f) <= 6.103515625e-05f;  // 2^-14
+    t[e] = rintf(q);
+  }
+  if (__ballot(near)) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) t[e] = rintf(__fdiv_rn(__fsub_rn(x[e], mn), div));
+  }
   uint32_t code[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
-    const float t = fminf(fmaxf(rintf(__fdiv_rn(__fsub_rn(x[e], mn), div)), 0.f), levels);
-    code[e] = flat ? 0u : static_cast<uint32_t>(t);
+    const float c = fminf(fmaxf(t[e], 0.f), levels);
+    code[e] = flat ? 0u : static_cast<uint32_t>(c);
   }
   if (!rec) return;
   if (bits == 8) {

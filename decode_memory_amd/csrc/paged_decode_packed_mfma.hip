@@ -491,10 +491,14 @@ __global__ __launch_bounds__(kPThreads, kPMinWaves<D>) void paged_decode_packed_
   f4 acc[NV];  // lane l: dimension vdim(i, l), register r: query head r
 #pragma unroll
   for (int i = 0; i < NV; ++i) acc[i] = f4{0.f, 0.f, 0.f, 0.f};
-  // value prescale exponents, per group (wave-uniform)
+  // value prescale exponents per group, and the factors 2^vk (wave-uniform)
   int vk[NMG];
+  float pf[NMG];
 #pragma unroll
-  for (int g = 0; g < NMG; ++g) vk[g] = kVk0;
+  for (int g = 0; g < NMG; ++g) {
+    vk[g] = kVk0;
+    pf[g] = exp2i(kVk0);
+  }
   // The f16 operands of a step are p * scale * 2^vk (p <= 1).  A step whose
   // value scales (read unmasked: cheaper, and a stale invisible scale costs
   // at most a needless look) may exceed 2^15 / 2^vk takes the slow path:
@@ -531,6 +535,7 @@ __global__ __launch_bounds__(kPThreads, kPMinWaves<D>) void paged_decode_packed_
           acc[i] *= f;
         }
         vk[g] = knew;
+        pf[g] = exp2i(knew);
       }
       vk_top = max(vk_top, vk[g]);
     }
@@ -604,7 +609,7 @@ __global__ __launch_bounds__(kPThreads, kPMinWaves<D>) void paged_decode_packed_
 #pragma unroll
         for (int g = 0; g < NMG; ++g) {
           bias[g] = fmaf(bias[g], alpha, tv ? p * vm[0][g].y : 0.f);
-          sp[(g * 4 + J) * STEP + n] = static_cast<_Float16>(tv ? (p * exp2i(vk[g])) * vm[0][g].x : 0.f);
+          sp[(g * 4 + J) * STEP + n] = static_cast<_Float16>(tv ? (p * pf[g]) * vm[0][g].x : 0.f);
         }
       } else {
         // scores of each sub-tile: lane (n, J) = (token n, query head J);
@@ -665,12 +670,11 @@ __global__ __launch_bounds__(kPThreads, kPMinWaves<D>) void paged_decode_packed_
 #pragma unroll
         for (int g = 0; g < NMG; ++g) {
           float bg = fmaf(bias[g], alpha, tv[0] ? p[0] * vm[0][g].y : 0.f);
-          const float pf = exp2i(vk[g]);
 #pragma unroll
           for (int u = 0; u < NSUB; ++u) {
             if (u > 0) bg += tv[u] ? p[u] * vm[u][g].y : 0.f;
             sp[(g * 4 + J) * STEP + u * kSub + n] =
-                static_cast<_Float16>(tv[u] ? (p[u] * pf) * vm[u][g].x : 0.f);
+                static_cast<_Float16>(tv[u] ? (p[u] * pf[g]) * vm[u][g].x : 0.f);
           }
           bias[g] = bg;
         }

@@ -61,6 +61,7 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0  # MI355X published HBM3E bandwidth
 CALIB_COPY_BYTES = 256 << 20
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "paged_decode_qwen3_0p6b_8x4k_traffic.md")
+TRACE_PROFILE = os.path.join(ROOT, "profiles", "paged_decode_qwen3_0p6b_8x4k_kernel_trace.md")
 DECODE_SOURCES = ("paged_decode_row.hip", "device_common.h")
 METRIC = "paged_decode achieved HBM GB/s (% of peak) + KV tokens attended/sec"
 MALL_BYTES = 256 << 20  # last-level cache of the MI355X
@@ -93,6 +94,26 @@ def measured_traffic():
         return int(fields["hbm_bytes_per_launch"])
     except (KeyError, ValueError):
         return None
+
+
+def traced_launch_us(kernel_prefix: str):
+    """Average duration of `kernel_prefix` in the committed rocprofv3 kernel
+    trace of this benchmark, or None when the trace is missing or was taken
+    from another version of the decode kernel's source."""
+    try:
+        text = open(TRACE_PROFILE).read()
+    except OSError:
+        return None
+    if f"source hash `{decode_source_hash()}`" not in text:
+        return None
+    for line in text.splitlines():
+        cells = [c.strip().strip("`") for c in line.split("|")]
+        if len(cells) > 4 and cells[1].startswith(kernel_prefix):
+            try:
+                return float(cells[3])
+            except ValueError:
+                return None
+    return None
 
 
 PACKED_TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "paged_decode_packed_16x16k_traffic.md")
@@ -464,6 +485,14 @@ def run_qwen3_0p6b(args, torch, pd):
     rl = roofline(d_bytes, split_us, "paged_decode_row_kernel<128,2,true,2> (split stage)",
                   measured_traffic())
     rl["kernel_source_sha256"] = decode_source_hash()
+    # the whole paged_decode call (split + combine) against the same bytes
+    rl["frac_call"] = round(d_bytes / ((split_us + combine_us) * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)
+    # the same kernel in the committed rocprofv3 trace of this benchmark
+    # (another box, the same command; null when the kernel changed since)
+    t_us = traced_launch_us("paged_decode_row_kernel<128, 2, true, 2>")
+    rl["trace"] = None if t_us is None else {
+        "avg_launch_us": t_us, "frac": round(d_bytes / (t_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+        "profile": os.path.relpath(TRACE_PROFILE, ROOT)}
     result.update({
         "pct_of_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
         "kv_tokens_attended_per_s": round(sum(lengths) * L / (step_ms * 1e-3), 1),
@@ -832,11 +861,17 @@ def run_packed(args, torch, pd):
 
 def run_footprint(args, torch, pd):
     """Peak HBM of the KV cache over 8 distinct prompts of ~4.2k tokens
-    prefilled one after another (qwen3-0.6b KV shape, 28 layers): the slab
-    pool, which grows by appending slabs as each prompt extends it, against
-    the dense backend, which holds each sequence in K/V tensors of exactly
-    its length.  Both phases write the same tokens from the same transient
-    per-layer sources; peaks come from the torch allocator."""
+    (qwen3-0.6b KV shape, 28 layers), three ways, each measured on the torch
+    allocator (peak reserved bytes):
+      - dense: each sequence in K/V tensors of exactly its length;
+      - slab pool: grows by appending slabs as the prompts extend it;
+      - growth by copy (the pool before slabs, mlxcel #235 "Problem"): one
+        tensor per layer for K and one for V, grown to the rows in use
+        rounded up to 32 blocks by allocating a larger zeroed tensor, copying
+        and freeing the old one, so the allocator keeps the freed ladder.
+    Twice: prefilled one after another (sequential), and concurrently (every
+    round extends all 8 prompts by up to 512 tokens, so rows interleave).
+    All arms write the same tokens from the same transient per-layer sources."""
     from synth import WORKLOADS, normal_device, workload_lengths
 
     w = WORKLOADS["footprint_8x4k"]
@@ -844,6 +879,7 @@ def run_footprint(args, torch, pd):
     L, bs, S, n_kv, D = w.n_layers, w.block_size, w.slab_blocks, w.n_kv_heads, w.head_dim
     lengths = [int(x) for x in workload_lengths(w)]
     token_bytes = L * n_kv * D * 2 * 2  # K + V, every layer
+    chunk_tokens, grow_blocks = 512, 32
 
     def measure(fn):
         torch.cuda.synchronize()
@@ -858,64 +894,122 @@ def run_footprint(args, torch, pd):
         peak_r = torch.cuda.max_memory_reserved() - base_r
         return keep, peak_a, peak_r, dt
 
-    def source(i, layer, n):
-        return (normal_device((w.seed, layer, i, 0), (n, n_kv, D), w.dtype, dev),
-                normal_device((w.seed, layer, i, 1), (n, n_kv, D), w.dtype, dev))
+    def source(i, layer, t0, t1):
+        """Tokens [t0, t1) of prompt i in `layer` (drawn whole, then sliced)."""
+        n = lengths[i]
+        ks = normal_device((w.seed, layer, i, 0), (n, n_kv, D), w.dtype, dev)[t0:t1].contiguous()
+        vs = normal_device((w.seed, layer, i, 1), (n, n_kv, D), w.dtype, dev)[t0:t1].contiguous()
+        return ks, vs
 
-    def dense():
+    def spans(concurrent):
+        """(prompt, first token, end token) in the order the prefills write them."""
+        if not concurrent:
+            return [(i, 0, n) for i, n in enumerate(lengths)]
+        out, t = [], 0
+        while t < max(lengths):
+            out += [(i, t, min(n, t + chunk_tokens)) for i, n in enumerate(lengths) if t < n]
+            t += chunk_tokens
+        return out
+
+    def dense(concurrent):
         cache = []
         for i, n in enumerate(lengths):
             k = torch.empty((L, n, n_kv, D), dtype=torch.bfloat16, device=dev)
-            v = torch.empty_like(k)
+            cache.append((k, torch.empty_like(k)))
+        for i, t0, t1 in spans(concurrent):
             for layer in range(L):
-                ks, vs = source(i, layer, n)
-                k[layer].copy_(ks)
-                v[layer].copy_(vs)
+                ks, vs = source(i, layer, t0, t1)
+                cache[i][0][layer, t0:t1].copy_(ks)
+                cache[i][1][layer, t0:t1].copy_(vs)
                 del ks, vs
-            cache.append((k, v))
         return cache
 
-    def slab():
+    def slab(concurrent):
         pool = pd.SlabPool(L, bs, n_kv, D, S, 64, "bf16", device=dev)
-        rows = 0
-        for i, n in enumerate(lengths):
-            nb = -(-n // bs)
-            pool.reserve_rows(rows + nb)  # presize for the span: whole slabs appended
-            t = np.arange(n)
-            r = torch.as_tensor((rows + t // bs).astype(np.int32), device=dev)
+        rows = [[] for _ in lengths]
+        next_row = 0
+        for i, t0, t1 in spans(concurrent):
+            nb_have, nb_need = len(rows[i]), -(-t1 // bs)
+            rows[i] += list(range(next_row, next_row + nb_need - nb_have))
+            next_row += nb_need - nb_have
+            pool.reserve_rows(next_row)  # presize for the span: whole slabs appended
+            t = np.arange(t0, t1)
+            r = torch.as_tensor(np.asarray(rows[i], np.int32)[t // bs], device=dev)
             sl = torch.as_tensor((t % bs).astype(np.int32), device=dev)
             for layer in range(L):
-                ks, vs = source(i, layer, n)
+                ks, vs = source(i, layer, t0, t1)
                 pool.write_block(layer, r, sl, ks, vs)
                 del ks, vs
-            rows += nb
         return pool
 
-    cache, dense_a, dense_r, dense_s = measure(dense)
-    dense_storage = sum(k.numel() * 2 * 2 for k, _ in cache)
-    del cache
-    pool, slab_a, slab_r, slab_s = measure(slab)
-    if pool.check_error():
-        raise RuntimeError("device error during the prefills")
-    st = pool.stats()
-    pool.close()
-    del pool
-    ratio = slab_r / dense_r
+    def by_copy(concurrent):
+        # K and V of every layer in one tensor each, [capacity blocks, bs, n_kv, D]
+        cap = 0
+        pool = [[None, None] for _ in range(L)]
+        rows = [[] for _ in lengths]
+        next_row = 0
+        for i, t0, t1 in spans(concurrent):
+            nb_have, nb_need = len(rows[i]), -(-t1 // bs)
+            rows[i] += list(range(next_row, next_row + nb_need - nb_have))
+            next_row += nb_need - nb_have
+            need = -(-next_row // grow_blocks) * grow_blocks
+            if need > cap:
+                for layer in range(L):
+                    for kv in range(2):
+                        new = torch.zeros((need, bs, n_kv, D), dtype=torch.bfloat16, device=dev)
+                        if cap:
+                            new[:cap].copy_(pool[layer][kv])
+                        pool[layer][kv] = new  # the old tensor is freed into the allocator's cache
+                        del new
+                cap = need
+            t = np.arange(t0, t1)
+            r = torch.as_tensor(np.asarray(rows[i], np.int64)[t // bs], device=dev)
+            sl = torch.as_tensor(t % bs, device=dev)
+            for layer in range(L):
+                ks, vs = source(i, layer, t0, t1)
+                pool[layer][0][r, sl] = ks
+                pool[layer][1][r, sl] = vs
+                del ks, vs
+        return pool
+
+    arms = {}
+    for mode in ("sequential", "concurrent"):
+        conc = mode == "concurrent"
+        cache, dense_a, dense_r, _ = measure(lambda: dense(conc))
+        dense_storage = sum(k.numel() * 2 * 2 for k, _ in cache)
+        del cache
+        pool, slab_a, slab_r, slab_s = measure(lambda: slab(conc))
+        if pool.check_error():
+            raise RuntimeError("device error during the prefills")
+        st = pool.stats()
+        pool.close()
+        del pool
+        grown, copy_a, copy_r, _ = measure(lambda: by_copy(conc))
+        del grown
+        arms[mode] = {
+            "dense": {"storage_bytes": dense_storage, "peak_allocated_bytes": dense_a,
+                      "peak_reserved_bytes": dense_r},
+            "slab_pool": {"bytes_reserved": st["bytes_reserved"], "n_slabs": st["n_slabs"],
+                          "slab_append_events": st["slab_append_events"],
+                          "bytes_copied_on_growth": st["bytes_copied_on_growth"],
+                          "peak_allocated_bytes": slab_a, "peak_reserved_bytes": slab_r,
+                          "prefill_s": round(slab_s, 3)},
+            "growth_by_copy": {"peak_allocated_bytes": copy_a, "peak_reserved_bytes": copy_r},
+            "ratio_reserved": round(slab_r / dense_r, 4),
+            "ratio_allocated": round(slab_a / dense_a, 4),
+            "growth_by_copy_ratio_reserved": round(copy_r / dense_r, 4),
+        }
+    seq = arms["sequential"]
     result = {
-        "metric": "peak KV-cache HBM of 8 sequential distinct ~4.2k-token prefills, slab pool / dense",
-        "value": round(ratio, 4), "unit": "x", "n_gpus": 1, "steps": 1, "warmup": 0,
-        "ms_per_step": round(slab_s * 1e3, 2), "higher_is_better": False, "scaling": "weak",
-        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": "footprint: 8 distinct prompts U{4096..4300} tokens, prefilled one after another",
+        "metric": "peak KV-cache HBM of 8 distinct ~4.2k-token prefills, slab pool / dense",
+        "value": seq["ratio_reserved"], "unit": "x", "n_gpus": 1, "steps": 1, "warmup": 0,
+        "ms_per_step": round(seq["slab_pool"]["prefill_s"] * 1e3, 2), "higher_is_better": False,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "footprint: 8 distinct prompts U{4096..4300} tokens, prefilled one after another "
+                               "(value) and concurrently in 512-token rounds",
                    "layers": L, "block_size": bs, "slab_blocks": S, "n_kv_heads": n_kv, "head_dim": D,
-                   "lengths": lengths},
-        "dense": {"storage_bytes": dense_storage, "peak_allocated_bytes": dense_a,
-                  "peak_reserved_bytes": dense_r},
-        "slab_pool": {"bytes_reserved": st["bytes_reserved"], "n_slabs": st["n_slabs"],
-                      "slab_append_events": st["slab_append_events"],
-                      "bytes_copied_on_growth": st["bytes_copied_on_growth"],
-                      "peak_allocated_bytes": slab_a, "peak_reserved_bytes": slab_r},
-        "ratio_reserved": round(ratio, 4), "ratio_allocated": round(slab_a / dense_a, 4),
+                   "lengths": lengths, "growth_chunk_blocks": grow_blocks, "concurrent_chunk_tokens": chunk_tokens},
+        "sequential": seq, "concurrent": arms["concurrent"],
         "gate": "within about 1.15x of the dense backend",
         "token_bytes_all_layers": token_bytes,
     }

@@ -37,6 +37,7 @@ struct WriteArgs {
   int32_t qgroup;      // values per (scale, offset) pair: 32 or 64
   const float* signs;  // device [head_dim] of +-1 (packed only)
   float inv_sqrt_d;
+  uint32_t m_slab;     // reciprocal_u32(slab_blocks) when every row / slab_blocks is exact with it, else 0
 };
 
 // Whole block rows moved between two pool rows (copy_on_write_block), from

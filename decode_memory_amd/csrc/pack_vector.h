@@ -54,6 +54,16 @@ __device__ __forceinline__ void fwht_rotate8(float (&x)[8], const float* signs, 
   for (int e = 0; e < 8; ++e) x[e] = __fmul_rn(x[e], inv_sqrt_d);
 }
 
+// The same with the lane's 8 signs already in registers.
+template <int D>
+__device__ __forceinline__ void fwht_rotate8(float (&x)[8], const float (&sg)[8], int c, float inv_sqrt_d) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) x[e] *= sg[e];  // exact sign flips
+  fwht8<D>(x, c);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) x[e] = __fmul_rn(x[e], inv_sqrt_d);
+}
+
 // Quantise the lane's 8 values (values 8c .. 8c+7 of the vector) with the
 // (scale, offset) of their group of GS values, all in fp32: mn = min, mx =
 // max, scale = (mx - mn) / (2^bits - 1), offset = mn, code = clamp(rint((x -

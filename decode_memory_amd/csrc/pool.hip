@@ -17,6 +17,7 @@
 #include <string>
 #include <vector>
 
+#include "index_math.h"
 #include "internal.h"
 
 using namespace pagedkv;
@@ -487,6 +488,11 @@ pd_status pd_write_block(pd_pool* p, int32_t layer, int32_t n, const int32_t* ro
   a.qgroup = p->qgroup;
   a.signs = p->d_signs;
   a.inv_sqrt_d = p->inv_sqrt_d;
+  // the high multiply is exact for every row below capacity while
+  // capacity_rows < 2^32 / slab_blocks
+  const uint64_t S = static_cast<uint64_t>(p->desc.slab_blocks);
+  a.m_slab = static_cast<uint64_t>(a.lv.capacity_rows) * S < (uint64_t{1} << 32) ? reciprocal_u32(static_cast<uint32_t>(S)) : 0u;
+  if (S == 1) a.m_slab = 0;  // 0 means divide (by one)
   hipError_t e = launch_write_block(a, p->desc.format, stream);
   if (e == hipErrorInvalidValue) return fail(PD_ERR_UNSUPPORTED, "no write_block kernel for this shape");
   if (e != hipSuccess) return hip_fail(e, "write_block launch");

@@ -22,6 +22,7 @@ namespace pagedkv {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int kPackedKv = 8;  // kv heads of a packed pool (pd_pool_create refuses others)
 
 // Growth (one launch per append): workgroup row y takes slab y of the launch
 // -- pair y / 2, K when y is even, V when odd -- records its base pointer in
@@ -248,49 +249,57 @@ __global__ __launch_bounds__(kThreads) void write_block_packed_kernel(WriteArgs 
   constexpr int VPW = kWave / LPT;  // vectors per wave
   const int lane = threadIdx.x % kWave;
   const int c = lane % LPT;         // values 8c .. 8c+7 of the vector
-  const int n_vec = a.n * a.lv.n_kv;  // K vectors; as many V vectors follow
+  const int n_vec = a.n * kPackedKv;  // K vectors; as many V vectors follow
   const int waves = gridDim.x * (kThreads / kWave);
+  float sg[8];  // the signs of values 8c .. 8c+7 (the same for every vector)
+  {
+    const float4* sp4 = reinterpret_cast<const float4*>(a.signs + 8 * c);
+    const float4 s0 = sp4[0], s1 = sp4[1];
+    sg[0] = s0.x, sg[1] = s0.y, sg[2] = s0.z, sg[3] = s0.w;
+    sg[4] = s1.x, sg[5] = s1.y, sg[6] = s1.z, sg[7] = s1.w;
+  }
   for (int w0 = (blockIdx.x * (kThreads / kWave) + threadIdx.x / kWave) * VPW; w0 < 2 * n_vec;
        w0 += waves * VPW) {
     const int job = w0 + lane / LPT;
     const bool live = job < 2 * n_vec;
     const bool is_v = job >= n_vec;
     const int th = is_v ? job - n_vec : job;
-    const int i = th / a.lv.n_kv, head = th % a.lv.n_kv;
-    bool ok = false;
-    int slab = 0;
-    size_t tok = 0;
+    const int i = th / kPackedKv, head = th % kPackedKv;
+    // the loads that depend on nothing go out together: the lane's 16 bytes
+    // of the source vector, the token's row and slot
+    uint4 u = make_uint4(0, 0, 0, 0);
+    int32_t row = -1, slot = -1;
     if (live) {
-      const int32_t row = a.rows[i], slot = a.slots[i];
-      ok = valid_target(a.lv, row, slot, c == 0 && !is_v && head == 0);
-      if (ok) tok = token_in_slab(a.lv, row, slot, &slab);
+      u = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(is_v ? a.v_src : a.k_src) +
+                                          static_cast<size_t>(th) * D + 8 * c);
+      row = a.rows[i];
+      slot = a.slots[i];
+    }
+    const bool ok = live && valid_target(a.lv, row, slot, c == 0 && !is_v && head == 0);
+    // the record's address (one dependent read: its slab's base) before the
+    // arithmetic, so that read is in flight meanwhile
+    char* rec = nullptr;
+    if (ok) {
+      // row / slab_blocks as one high multiply when the host found it exact
+      const int slab =
+          a.m_slab ? static_cast<int>(div_by(static_cast<uint32_t>(row), a.m_slab)) : row / a.lv.slab_blocks;
+      const size_t tok = static_cast<size_t>(row - slab * a.lv.slab_blocks) * a.lv.block_size + slot;
+      const int rec_bytes = is_v ? a.lv.v_rec : a.lv.k_rec;
+      rec = static_cast<char*>(const_cast<void*>(is_v ? a.lv.v_tab[slab] : a.lv.k_tab[slab])) +
+            (tok * kPackedKv + head) * rec_bytes;
     }
     float x[8];
-    {
-      uint4 u = make_uint4(0, 0, 0, 0);
-      if (ok) {
-        const uint16_t* src = static_cast<const uint16_t*>(is_v ? a.v_src : a.k_src) +
-                              static_cast<size_t>(th) * D + 8 * c;
-        u = *reinterpret_cast<const uint4*>(src);
-      }
-      widen8<true>(u, x);
-    }
+    widen8<true>(u, x);  // a token that is not written is still quantised, and not stored
     // every lane takes part in the cross-lane stages; V vectors keep x
     if (__ballot(live && !is_v)) {
       float y[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) y[e] = x[e];
-      fwht_rotate8<D>(y, a.signs, c, a.inv_sqrt_d);
+      fwht_rotate8<D>(y, sg, c, a.inv_sqrt_d);
       if (!is_v) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) x[e] = y[e];
       }
-    }
-    char* rec = nullptr;
-    if (ok) {
-      const int rec_bytes = is_v ? a.lv.v_rec : a.lv.k_rec;
-      rec = static_cast<char*>(const_cast<void*>(is_v ? a.lv.v_tab[slab] : a.lv.k_tab[slab])) +
-            (tok * a.lv.n_kv + head) * rec_bytes;
     }
     quantise_store8<D, GS>(x, c, is_v ? a.v_bits : a.k_bits, rec);
   }
@@ -346,6 +355,7 @@ hipError_t launch_write_block(const WriteArgs& a, int32_t format, hipStream_t s)
                        reciprocal_u32(static_cast<uint32_t>(upt)));
     return hipGetLastError();
   }
+  if (a.lv.n_kv != kPackedKv) return hipErrorInvalidValue;  // packed pools hold 8 kv heads
   const long long waves = (2LL * a.n * a.lv.n_kv * (a.head_dim / 8) + kWave - 1) / kWave;
   long long grid = (waves + kThreads / kWave - 1) / (kThreads / kWave);
   if (grid > 65536) grid = 65536;

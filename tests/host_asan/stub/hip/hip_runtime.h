@@ -29,8 +29,13 @@ typedef enum hipMemcpyKind {
 #define __device__
 #define __host__
 #define __global__
+#define __forceinline__ inline
 #define __align__(n) __attribute__((aligned(n)))
 #define HIP_SYMBOL(x) (reinterpret_cast<const void*>(&(x)))
+
+inline unsigned int __umulhi(unsigned int a, unsigned int b) {
+  return static_cast<unsigned int>((static_cast<unsigned long long>(a) * b) >> 32);
+}
 
 const char* hipGetErrorString(hipError_t e);
 hipError_t hipGetDevice(int* device);

@@ -13,55 +13,83 @@
 
 namespace pagedkv {
 
+// Every rounding below is the one the packed format's definition states, in
+// fp32.  Each function turns contraction off and uses plain operators (HIP's
+// __fmul_rn and the like are plain operators in a header that allows
+// contraction), so no product is fused into a following sum unless the code
+// says so with an fma whose product is exact.
+
 // The Sylvester Hadamard butterfly network over a D-value vector held 8
 // values per lane by D/8 lanes (lane c of the group: values 8c .. 8c+7):
 // stages h = 1, 2, ..., D/2, each pair (a, b) -> (a + b, a - b) in fp32 (the
 // lower index gets a + b).  Stages h < 8 pair values inside a lane, the
-// others pair lanes c and c ^ (h / 8) of the vector's lane group.
+// others pair lanes c and c ^ (h / 8) of the vector's lane group.  The values
+// are first multiplied by the signs sg (exact), and that product is fused
+// into the first stage: fma(s, x, b) = RN(s x + b).
 template <int D>
-__device__ __forceinline__ void fwht8(float (&x)[8], int c) {
+__device__ __forceinline__ void signed_fwht8(float (&x)[8], int c, const float (&sg)[8]) {
+  #pragma clang fp contract(off)
   constexpr int LPT = D / 8;
 #pragma unroll
-  for (int h = 1; h < 8; h <<= 1) {
+  for (int e = 0; e < 8; e += 2) {
+    const float a = x[e];
+    const float b = x[e + 1] * sg[e + 1];
+    x[e] = __builtin_fmaf(sg[e], a, b);
+    x[e + 1] = __builtin_fmaf(sg[e], a, -b);
+  }
+#pragma unroll
+  for (int h = 2; h < 8; h <<= 1) {
     float y[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) y[e] = (e & h) ? __fsub_rn(x[e ^ h], x[e]) : __fadd_rn(x[e], x[e ^ h]);
+    for (int e = 0; e < 8; ++e) y[e] = (e & h) ? x[e ^ h] - x[e] : x[e] + x[e ^ h];
 #pragma unroll
     for (int e = 0; e < 8; ++e) x[e] = y[e];
   }
+  const int lane = static_cast<int>(__lane_id());
 #pragma unroll
   for (int hl = 1; hl < LPT; hl <<= 1) {
     // the lower lane keeps x + other, the upper other - x: one fma with a
     // +-1 factor (exact product, one rounding) gives both
     const float sgn = (c & hl) ? -1.f : 1.f;
+    const int from = (lane ^ hl) * 4;  // byte address of the partner lane
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const float other = __shfl_xor(x[e], hl, kWave);
-      x[e] = __fmaf_rn(sgn, x[e], other);
+      const float other = __int_as_float(__builtin_amdgcn_ds_bpermute(from, __float_as_int(x[e])));
+      x[e] = __builtin_fmaf(sgn, x[e], other);
     }
   }
 }
 
 // x' = H diag(sigma) x / sqrt(D): the sign flips (exact), the butterfly
-// network above, then one multiply by 1/sqrt(D).
+// network above, then one multiply by 1/sqrt(D).  sg holds the lane's signs
+// sigma[8c .. 8c+7].
 template <int D>
-__device__ __forceinline__ void fwht_rotate8(float (&x)[8], const float* signs, int c,
-                                             float inv_sqrt_d) {
+__device__ __forceinline__ void fwht_rotate8_held(float (&x)[8], const float (&sg)[8], int c, float inv_sqrt_d) {
+  #pragma clang fp contract(off)
+  signed_fwht8<D>(x, c, sg);
 #pragma unroll
-  for (int e = 0; e < 8; ++e) x[e] *= signs[8 * c + e];  // exact sign flips
-  fwht8<D>(x, c);
-#pragma unroll
-  for (int e = 0; e < 8; ++e) x[e] = __fmul_rn(x[e], inv_sqrt_d);
+  for (int e = 0; e < 8; ++e) x[e] = x[e] * inv_sqrt_d;
 }
 
-// The same with the lane's 8 signs already in registers.
+// The same with the signs read from the D-value sign vector.
 template <int D>
-__device__ __forceinline__ void fwht_rotate8(float (&x)[8], const float (&sg)[8], int c, float inv_sqrt_d) {
+__device__ __forceinline__ void fwht_rotate8(float (&x)[8], const float* signs, int c, float inv_sqrt_d) {
+  float sg[8];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) x[e] *= sg[e];  // exact sign flips
-  fwht8<D>(x, c);
-#pragma unroll
-  for (int e = 0; e < 8; ++e) x[e] = __fmul_rn(x[e], inv_sqrt_d);
+  for (int e = 0; e < 8; ++e) sg[e] = signs[8 * c + e];
+  fwht_rotate8_held<D>(x, sg, c, inv_sqrt_d);
+}
+
+// RN(a / b) for b = 15 or 255 and every finite a >= 0: q0 = RN(a * RN(1/b)),
+// then one correction with the exact remainder a - q0 * b (an fma).  For
+// these two divisors this equals the correctly rounded quotient for all 2^31
+// - 2^23 finite non-negative fp32 a (checked exhaustively against IEEE
+// division on the host); a = inf gives inf.
+__device__ __forceinline__ float div_levels_rn(float a, float levels, float inv_levels) {
+  #pragma clang fp contract(off)
+  const float q0 = a * inv_levels;
+  const float q1 = __builtin_fmaf(__builtin_fmaf(-q0, levels, a), inv_levels, q0);
+  return a < __builtin_inff() ? q1 : a;
 }
 
 // Quantise the lane's 8 values (values 8c .. 8c+7 of the vector) with the
@@ -73,6 +101,7 @@ __device__ __forceinline__ void fwht_rotate8(float (&x)[8], const float (&sg)[8]
 // offset) pair are stored into the record rec of a D-value vector.
 template <int D, int GS>
 __device__ __forceinline__ void quantise_store8(const float (&x)[8], int c, int bits, char* rec) {
+  #pragma clang fp contract(off)
   static_assert(GS == 32 || GS == 64, "groups of 32 or 64 values");
   constexpr int LPG = GS / 8;  // lanes per group
   // min and max in the lane, then across the lane quad, then (groups of 64)
@@ -91,46 +120,50 @@ __device__ __forceinline__ void quantise_store8(const float (&x)[8], int c, int 
     mn = fminf(mn, dpp<kDppHalfMirror>(mn));
     mx = fmaxf(mx, dpp<kDppHalfMirror>(mx));
   }
-  const float levels = static_cast<float>((1 << bits) - 1);
-  const float scale = __fdiv_rn(__fsub_rn(mx, mn), levels);
-  // a constant group (scale 0) gets code 0; it divides by 1 instead, so that
-  // no lane branches
-  const bool flat = scale == 0.f;
-  const float div = flat ? 1.f : scale;
-  // The code is rint of the correctly rounded quotient q = RN(d / div), d =
-  // RN(x - mn) >= 0.  One correctly rounded reciprocal r = RN(1 / div) per
-  // lane and a product q' = RN(d * r) give q' within 2.5 ulp(q) of q, and for
-  // q < 256 that is below 2^-14.6, so rint(q') = rint(q) unless q' lies
-  // within 2^-14 of a half-integer.  Such a value (about 1 in 8000) sends the
-  // whole wave through the correctly rounded divisions.
-  const float r = __fdiv_rn(1.f, div);
-  float t[8];
-  bool near = false;
+  const bool eight = bits == 8;
+  const float levels = eight ? 255.f : 15.f;
+  const float scale = div_levels_rn(mx - mn, levels, eight ? 1.f / 255.f : 1.f / 15.f);
+  // a constant group (scale 0) divides by 1 instead: every x - mn is then
+  // below half the smallest subnormal times 2^bits, so its code is 0
+  const float div = scale == 0.f ? 1.f : scale;
+  // The code is rint(q), q = RN(d / div), d = RN(x - mn) >= 0.  With div
+  // normal, the hardware reciprocal estimate and one Newton step give r with
+  // relative error below 2^-24 + 2^-40, so q' = RN(d * r) lies within 2.01
+  // ulp(q) of q, below 2^-14.9 as q < 256, and t = rint(q') is rint(q)
+  // unless q' lies within 2^-14 of a half-integer (about 1 value in 8000).
+  // Such a value, or a divisor below 2^-125 or not finite, sends the whole
+  // wave through the correctly rounded divisions, clamped (a subnormal scale
+  // can give q > 2^bits - 1).  The fast path needs no clamp: q' <= (2^bits -
+  // 1)(1 + 2^-21) for a normal scale.  A NaN value gets an unspecified code.
+  const float r0 = __builtin_amdgcn_rcpf(div);
+  const float r = __builtin_fmaf(__builtin_fmaf(-div, r0, 1.f), r0, r0);
+  float d[8], t[8], worst = 0.f;
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
-    const float q = __fmul_rn(__fsub_rn(x[e], mn), r);
-    near |= fabsf(__fsub_rn(q, floorf(q)) - 0.5f) <= 6.103515625e-05f;  // 2^-14
+    d[e] = x[e] - mn;
+    const float q = d[e] * r;
     t[e] = rintf(q);
+    worst = fmaxf(worst, fabsf(q - t[e]));
   }
-  if (__ballot(near)) {
+  const bool slow = !(div >= 0x1p-125f && div <= 0x1.fffffep127f && worst < 0.49993896484375f);
+  if (__ballot(slow)) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) t[e] = rintf(__fdiv_rn(__fsub_rn(x[e], mn), div));
-  }
-  uint32_t code[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const float c = fminf(fmaxf(t[e], 0.f), levels);
-    code[e] = flat ? 0u : static_cast<uint32_t>(c);
+    for (int e = 0; e < 8; ++e) t[e] = fminf(rintf(d[e] / div), levels);
   }
   if (!rec) return;
-  if (bits == 8) {
-    *reinterpret_cast<uint2*>(rec + 8 * c) =
-        make_uint2(code[0] | (code[1] << 8) | (code[2] << 16) | (code[3] << 24),
-                   code[4] | (code[5] << 8) | (code[6] << 16) | (code[7] << 24));
+  // codes to bytes (each t is an integer in 0 .. 255: the conversion is exact)
+  uint32_t lo = 0, hi = 0;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    lo = __builtin_amdgcn_cvt_pk_u8_f32(t[e], e, lo);
+    hi = __builtin_amdgcn_cvt_pk_u8_f32(t[4 + e], e, hi);
+  }
+  if (eight) {
+    *reinterpret_cast<uint2*>(rec + 8 * c) = make_uint2(lo, hi);
   } else {
-    *reinterpret_cast<uint32_t*>(rec + 4 * c) =
-        (code[0] | (code[1] << 4)) | ((code[2] | (code[3] << 4)) << 8) |
-        ((code[4] | (code[5] << 4)) << 16) | ((code[6] | (code[7] << 4)) << 24);
+    // nibbles: byte 0 of w | w >> 4 is v0 | v1 << 4, byte 2 is v2 | v3 << 4
+    const uint32_t lw = lo | (lo >> 4), hw = hi | (hi >> 4);
+    *reinterpret_cast<uint32_t*>(rec + 4 * c) = __builtin_amdgcn_perm(hw, lw, 0x06040200u);
   }
   if (c % LPG == 0) {
     float* meta = reinterpret_cast<float*>(rec + D * bits / 8) + 2 * (c / LPG);

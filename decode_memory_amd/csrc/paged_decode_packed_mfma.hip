@@ -412,9 +412,8 @@ __global__ __launch_bounds__(kPThreads, kPMinWaves<D>) void paged_decode_packed_
     const int j = p * QVPP + lane / QLPT;
     float x[8];
     widen8<true>(qraw[p], x);
-    x[0] *= sg0.x, x[1] *= sg0.y, x[2] *= sg0.z, x[3] *= sg0.w;  // exact sign flips
-    x[4] *= sg1.x, x[5] *= sg1.y, x[6] *= sg1.z, x[7] *= sg1.w;
-    fwht8<D>(x, qc);  // every lane takes part (lane exchanges)
+    const float sgq[8] = {sg0.x, sg0.y, sg0.z, sg0.w, sg1.x, sg1.y, sg1.z, sg1.w};
+    signed_fwht8<D>(x, qc, sgq);  // exact sign flips, then the butterflies; every lane takes part
     float mq = 0.f;  // largest |q' * qs| of the query head, over its QLPT lanes
 #pragma unroll
     for (int e = 0; e < 8; ++e) mq = fmaxf(mq, fabsf(x[e] * qs));

@@ -239,9 +239,42 @@ __global__ __launch_bounds__(kThreads) void row_move_kernel(RowMoveArgs a) {
 
 // ---- packed pools -------------------------------------------------------------
 // A lane holds 8 consecutive values of a vector (one token-head of K or V),
-// D/8 lanes hold the vector, and a wave works on 64/(D/8) vectors at once.
-// Jobs are ordered all K vectors first, then all V vectors, so a wave rarely
-// mixes the two.
+// D/8 lanes hold the vector, and a wave works on 64/(D/8) vectors at once, all
+// K or all V: the wave tasks are the K vectors in wave-sized runs, then the V
+// vectors likewise.
+
+// One wave task: the VPW = 64/(D/8) vectors v0 .. v0 + VPW - 1 of K (IS_V
+// false, rotated) or of V.  VPW divides the 8 kv heads and v0 is a multiple
+// of VPW, so the task's vectors are heads of one token: its row, slot and
+// slab are the same in every lane and are resolved once per wave.
+template <int D, int GS, bool IS_V>
+__device__ __forceinline__ void pack_task(const WriteArgs& a, int v0, int lane, int c, const float (&sg)[8]) {
+  constexpr int LPT = D / 8;
+  const int i = v0 / kPackedKv;                          // the token
+  const int head = v0 % kPackedKv + lane / LPT;
+  // the lane's 16 bytes of the source vector (vector v0 + lane / LPT, values
+  // 8c .. 8c+7) and the token's row and slot go out together
+  const uint4 u = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(IS_V ? a.v_src : a.k_src) +
+                                                  static_cast<size_t>(v0) * D + 8 * lane);
+  const int32_t row = __builtin_amdgcn_readfirstlane(a.rows[i]);
+  const int32_t slot = __builtin_amdgcn_readfirstlane(a.slots[i]);
+  // the record's address (one dependent read: its slab's base) before the
+  // arithmetic, so that read is in flight meanwhile
+  char* rec = nullptr;
+  if (valid_target(a.lv, row, slot, lane == 0 && !IS_V && v0 % kPackedKv == 0)) {
+    // row / slab_blocks as one high multiply when the host found it exact
+    const int slab =
+        a.m_slab ? static_cast<int>(div_by(static_cast<uint32_t>(row), a.m_slab)) : row / a.lv.slab_blocks;
+    const size_t tok = static_cast<size_t>(row - slab * a.lv.slab_blocks) * a.lv.block_size + slot;
+    const int rec_bytes = IS_V ? a.lv.v_rec : a.lv.k_rec;
+    rec = static_cast<char*>(const_cast<void*>(IS_V ? a.lv.v_tab[slab] : a.lv.k_tab[slab])) +
+          tok * kPackedKv * rec_bytes + head * rec_bytes;
+  }
+  float x[8];
+  widen8<true>(u, x);  // a token that is not written is still quantised, and not stored
+  if constexpr (!IS_V) fwht_rotate8_held<D>(x, sg, c, a.inv_sqrt_d);  // every lane takes part
+  quantise_store8<D, GS>(x, c, IS_V ? a.v_bits : a.k_bits, rec);
+}
 
 template <int D, int GS>
 __global__ __launch_bounds__(kThreads) void write_block_packed_kernel(WriteArgs a) {
@@ -249,7 +282,8 @@ __global__ __launch_bounds__(kThreads) void write_block_packed_kernel(WriteArgs 
   constexpr int VPW = kWave / LPT;  // vectors per wave
   const int lane = threadIdx.x % kWave;
   const int c = lane % LPT;         // values 8c .. 8c+7 of the vector
-  const int n_vec = a.n * kPackedKv;  // K vectors; as many V vectors follow
+  const int n_vec = a.n * kPackedKv;  // K vectors; as many V vectors
+  const int tasks = (n_vec + VPW - 1) / VPW;
   const int waves = gridDim.x * (kThreads / kWave);
   float sg[8];  // the signs of values 8c .. 8c+7 (the same for every vector)
   {
@@ -258,50 +292,13 @@ __global__ __launch_bounds__(kThreads) void write_block_packed_kernel(WriteArgs 
     sg[0] = s0.x, sg[1] = s0.y, sg[2] = s0.z, sg[3] = s0.w;
     sg[4] = s1.x, sg[5] = s1.y, sg[6] = s1.z, sg[7] = s1.w;
   }
-  for (int w0 = (blockIdx.x * (kThreads / kWave) + threadIdx.x / kWave) * VPW; w0 < 2 * n_vec;
-       w0 += waves * VPW) {
-    const int job = w0 + lane / LPT;
-    const bool live = job < 2 * n_vec;
-    const bool is_v = job >= n_vec;
-    const int th = is_v ? job - n_vec : job;
-    const int i = th / kPackedKv, head = th % kPackedKv;
-    // the loads that depend on nothing go out together: the lane's 16 bytes
-    // of the source vector, the token's row and slot
-    uint4 u = make_uint4(0, 0, 0, 0);
-    int32_t row = -1, slot = -1;
-    if (live) {
-      u = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(is_v ? a.v_src : a.k_src) +
-                                          static_cast<size_t>(th) * D + 8 * c);
-      row = a.rows[i];
-      slot = a.slots[i];
-    }
-    const bool ok = live && valid_target(a.lv, row, slot, c == 0 && !is_v && head == 0);
-    // the record's address (one dependent read: its slab's base) before the
-    // arithmetic, so that read is in flight meanwhile
-    char* rec = nullptr;
-    if (ok) {
-      // row / slab_blocks as one high multiply when the host found it exact
-      const int slab =
-          a.m_slab ? static_cast<int>(div_by(static_cast<uint32_t>(row), a.m_slab)) : row / a.lv.slab_blocks;
-      const size_t tok = static_cast<size_t>(row - slab * a.lv.slab_blocks) * a.lv.block_size + slot;
-      const int rec_bytes = is_v ? a.lv.v_rec : a.lv.k_rec;
-      rec = static_cast<char*>(const_cast<void*>(is_v ? a.lv.v_tab[slab] : a.lv.k_tab[slab])) +
-            (tok * kPackedKv + head) * rec_bytes;
-    }
-    float x[8];
-    widen8<true>(u, x);  // a token that is not written is still quantised, and not stored
-    // every lane takes part in the cross-lane stages; V vectors keep x
-    if (__ballot(live && !is_v)) {
-      float y[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) y[e] = x[e];
-      fwht_rotate8<D>(y, sg, c, a.inv_sqrt_d);
-      if (!is_v) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) x[e] = y[e];
-      }
-    }
-    quantise_store8<D, GS>(x, c, is_v ? a.v_bits : a.k_bits, rec);
+  const int wave = __builtin_amdgcn_readfirstlane(blockIdx.x * (kThreads / kWave) + threadIdx.x / kWave);
+  static_assert(kPackedKv % VPW == 0, "a wave task covers heads of one token");
+  for (int t = wave; t < 2 * tasks; t += waves) {
+    if (t < tasks)
+      pack_task<D, GS, false>(a, t * VPW, lane, c, sg);
+    else
+      pack_task<D, GS, true>(a, (t - tasks) * VPW, lane, c, sg);
   }
 }
 

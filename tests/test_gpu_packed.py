@@ -13,7 +13,7 @@ import torch
 import decode_memory_amd as pd
 from oracle.packed import FORMATS, k_records, packed_decode_attention, record_bytes, v_records
 from oracle.slab_pool import SlabPoolModel
-from synth import (WORKLOADS, hadamard_signs, kv_bits_for_sequence, make_block_table,
+from synth import (WORKLOADS, bf16_bits_from_f32, hadamard_signs, kv_bits_for_sequence, make_block_table,
                    monotone_rows, q_bits, ranged_bits, shuffled_rows)
 from tests.gpu_util import (assert_decode_close, assert_packed_close, from_device_bits, i32,
                             packed_decode_bound, to_device_bits, token_targets)
@@ -71,6 +71,61 @@ def test_quantising_write_and_gather_are_bit_exact(fmt, D, group):
     pool.gather_visible(0, i32(table), i32(lengths), t_out, gk, gv)
     ek, ev = model.gather_batched(0, table, lengths, t_out)
     assert np.array_equal(gk.cpu().numpy(), ek) and np.array_equal(gv.cpu().numpy(), ev)
+    assert pool.check_error() == 0
+    pool.close()
+
+
+def _extreme_vectors(seed, n_tok, D, group, levels):
+    """[n_tok, 8, D] float32 vectors whose groups probe the quantiser's edges:
+    uniform groups at amplitudes from subnormal (1e-40) through 1e-37 (scale
+    below 2^-125 or subnormal) to 1e35 (the rotation of 256 such values stays
+    finite), constant groups (0.75 and +0), groups
+    one bf16 ulp wide, and groups of exact half-integer quotients (min 0, max
+    2^bits - 1, so scale is 1 and round-half-even decides)."""
+    rng = np.random.default_rng(seed)
+    amps = [1e-40, 1e-39, 4e-39, 2e-38, 1e-37, 1.0, 1e35]
+    x = rng.uniform(-1.0, 1.0, size=(n_tok, 8, D // group, group)).astype(np.float32)
+    kind = rng.integers(0, len(amps) + 4, size=(n_tok, 8, D // group))
+    for k, a in enumerate(amps):
+        x[kind == k] *= np.float32(a)
+    x[kind == len(amps)] = np.float32(0.75)
+    x[kind == len(amps) + 1] = np.float32(0.0)
+    ulp = kind == len(amps) + 2                       # 1.0 and the next bf16 value
+    x[ulp] = np.where(rng.random(x[ulp].shape) < 0.5, np.float32(1.0), np.float32(1.0078125))
+    ties = kind == len(amps) + 3
+    top = min(levels, 127)                            # k + 1/2 exact in bf16 for k < 128
+    halves = rng.integers(0, top, size=x[ties].shape).astype(np.float32) + np.float32(0.5)
+    halves[:, 0], halves[:, 1] = 0.0, float(levels)
+    x[ties] = halves
+    return x.reshape(n_tok, 8, D)
+
+
+@pytest.mark.parametrize("fmt", ["k8v8", "k8v4", "k4v4"])
+@pytest.mark.parametrize("D,group", [(64, 32), (256, 32), (128, 64)])
+def test_quantising_write_extreme_ranges_bit_exact(fmt, D, group):
+    """The quantising write at the edges of fp32: subnormal inputs and scales
+    (whose reciprocal overflows, so the codes come from the correctly rounded
+    division), wide groups, constant and one-ulp groups and exact ties.  The
+    records equal the oracle's byte for byte."""
+    kb, vb = FORMATS[fmt]
+    n = 300
+    k = bf16_bits_from_f32(_extreme_vectors(900 + D, n, D, group, (1 << kb) - 1))
+    v = bf16_bits_from_f32(_extreme_vectors(901 + D, n, D, group, (1 << vb) - 1))
+    signs = hadamard_signs(77, D)
+    rows = monotone_rows([n], BS)[0]
+    R = len(rows)
+    pool = pd.SlabPool(1, BS, 8, D, 4, -(-R // 4) + 1, fmt, hadamard_signs=signs, group_size=group)
+    pool.reserve_rows(R)
+    r, sl = token_targets(rows, n, BS)
+    pool.write_block(0, i32(r), i32(sl), to_device_bits(k, "bf16"), to_device_bits(v, "bf16"))
+    torch.cuda.synchronize()
+    krec, vrec = record_bytes(D, kb, group), record_bytes(D, vb, group)
+    model = SlabPoolModel(1, BS, 8, krec, vrec, 4)
+    model.reserve_rows(R)
+    model.write(0, r, sl, k_records(k, signs, kb, group), v_records(v, vb, group))
+    for slab in range(model.n_slabs):
+        assert np.array_equal(pool.slab_view(0, slab, "k").cpu().numpy(), model.k_slabs[0][slab]), (fmt, D, "K", slab)
+        assert np.array_equal(pool.slab_view(0, slab, "v").cpu().numpy(), model.v_slabs[0][slab]), (fmt, D, "V", slab)
     assert pool.check_error() == 0
     pool.close()
 

@@ -22,6 +22,31 @@ __device__ __forceinline__ float f16_hi(uint32_t w) {
   return __half2float(__ushort_as_half(static_cast<unsigned short>(w >> 16)));
 }
 
+// ---- global-memory access through table pointers ----------------------------
+// Slab tables hold generic pointers, so a plain access through one compiles
+// to a FLAT instruction, which also counts against the LDS wait counter and
+// so holds up unrelated LDS waits; these cast the pointer to the global
+// address space first (every slab lives in device global memory).
+
+typedef unsigned int gw2 __attribute__((ext_vector_type(2)));
+typedef unsigned int gw4 __attribute__((ext_vector_type(4)));
+template <int N> struct GlobalWords;
+template <> struct GlobalWords<4> { typedef unsigned int type; };
+template <> struct GlobalWords<8> { typedef gw2 type; };
+template <> struct GlobalWords<16> { typedef gw4 type; };
+
+template <class T>
+__device__ __forceinline__ void store_global(void* p, const T& v) {
+  typedef typename GlobalWords<sizeof(T)>::type W;
+  *(__attribute__((address_space(1))) W*)p = __builtin_bit_cast(W, v);
+}
+
+template <class T>
+__device__ __forceinline__ T load_global(const void* p) {
+  typedef typename GlobalWords<sizeof(T)>::type W;
+  return __builtin_bit_cast(T, *(const __attribute__((address_space(1))) W*)p);
+}
+
 // Widen 8 packed 16-bit values (one 16-byte vector) to fp32.
 template <bool BF16>
 __device__ __forceinline__ void widen8(const uint4& v, float (&x)[8]) {

@@ -25,15 +25,16 @@ namespace pagedkv {
 // lower index gets a + b).  Stages h < 8 pair values inside a lane, the
 // others pair lanes c and c ^ (h / 8) of the vector's lane group.  The values
 // are first multiplied by the signs sg (exact), and that product is fused
-// into the first stage: fma(s, x, b) = RN(s x + b).
-template <int D>
+// into the first stage: fma(s, x, b) = RN(s x + b).  With ODD_SIGNED the odd
+// values x[1], x[3], ... carry their signs already.
+template <int D, bool ODD_SIGNED = false>
 __device__ __forceinline__ void signed_fwht8(float (&x)[8], int c, const float (&sg)[8]) {
   #pragma clang fp contract(off)
   constexpr int LPT = D / 8;
 #pragma unroll
   for (int e = 0; e < 8; e += 2) {
     const float a = x[e];
-    const float b = x[e + 1] * sg[e + 1];
+    const float b = ODD_SIGNED ? x[e + 1] : x[e + 1] * sg[e + 1];
     x[e] = __builtin_fmaf(sg[e], a, b);
     x[e + 1] = __builtin_fmaf(sg[e], a, -b);
   }
@@ -78,6 +79,24 @@ __device__ __forceinline__ void fwht_rotate8(float (&x)[8], const float* signs, 
 #pragma unroll
   for (int e = 0; e < 8; ++e) sg[e] = signs[8 * c + e];
   fwht_rotate8_held<D>(x, sg, c, inv_sqrt_d);
+}
+
+// The rotation straight from the lane's 16 bytes of bf16 values: each odd
+// value's sign flip is folded into the mask that widens it (an exact flip of
+// the sign bit, odd_sign[i] = sign bit of sigma[8c + 2i + 1]).
+template <int D>
+__device__ __forceinline__ void widen_rotate8(const uint4& u, const uint32_t (&odd_sign)[4], const float (&sg)[8],
+                                              int c, float inv_sqrt_d, float (&x)[8]) {
+  #pragma clang fp contract(off)
+  const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    x[2 * i] = __uint_as_float(w[i] << 16);
+    x[2 * i + 1] = __uint_as_float((w[i] & 0xffff0000u) ^ odd_sign[i]);
+  }
+  signed_fwht8<D, true>(x, c, sg);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) x[e] = x[e] * inv_sqrt_d;
 }
 
 // RN(a / b) for b = 15 or 255 and every finite a >= 0: q0 = RN(a * RN(1/b)),
@@ -129,8 +148,9 @@ __device__ __forceinline__ void quantise_store8(const float (&x)[8], int c, int 
   // The code is rint(q), q = RN(d / div), d = RN(x - mn) >= 0.  With div
   // normal, the hardware reciprocal estimate and one Newton step give r with
   // relative error below 2^-24 + 2^-40, so q' = RN(d * r) lies within 2.01
-  // ulp(q) of q, below 2^-14.9 as q < 256, and t = rint(q') is rint(q)
-  // unless q' lies within 2^-14 of a half-integer (about 1 value in 8000).
+  // ulp(q) of q (below 2^-14.9 at 8 bits, q < 256; below 2^-18.9 at 4 bits,
+  // q < 16), and t = rint(q') is rint(q) unless q' lies within 2^-14 (4 bits:
+  // 2^-18) of a half-integer, about 1 value in 8000 (4 bits: 1 in 130000).
   // Such a value, or a divisor below 2^-125 or not finite, sends the whole
   // wave through the correctly rounded divisions, clamped (a subnormal scale
   // can give q > 2^bits - 1).  The fast path needs no clamp: q' <= (2^bits -
@@ -145,7 +165,7 @@ __device__ __forceinline__ void quantise_store8(const float (&x)[8], int c, int 
     t[e] = rintf(q);
     worst = fmaxf(worst, fabsf(q - t[e]));
   }
-  const bool slow = !(div >= 0x1p-125f && div <= 0x1.fffffep127f && worst < 0.49993896484375f);
+  const bool slow = !(div >= 0x1p-125f && div <= 0x1.fffffep127f && worst < (eight ? 0.49993896484375f : 0.4999961853027344f));
   if (__ballot(slow)) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) t[e] = fminf(rintf(d[e] / div), levels);
@@ -159,15 +179,14 @@ __device__ __forceinline__ void quantise_store8(const float (&x)[8], int c, int 
     hi = __builtin_amdgcn_cvt_pk_u8_f32(t[4 + e], e, hi);
   }
   if (eight) {
-    *reinterpret_cast<uint2*>(rec + 8 * c) = make_uint2(lo, hi);
+    store_global(rec + 8 * c, make_uint2(lo, hi));
   } else {
     // nibbles: byte 0 of w | w >> 4 is v0 | v1 << 4, byte 2 is v2 | v3 << 4
     const uint32_t lw = lo | (lo >> 4), hw = hi | (hi >> 4);
-    *reinterpret_cast<uint32_t*>(rec + 4 * c) = __builtin_amdgcn_perm(hw, lw, 0x06040200u);
+    store_global(rec + 4 * c, __builtin_amdgcn_perm(hw, lw, 0x06040200u));
   }
   if (c % LPG == 0) {
-    float* meta = reinterpret_cast<float*>(rec + D * bits / 8) + 2 * (c / LPG);
-    *reinterpret_cast<float2*>(meta) = make_float2(scale, mn);
+    store_global(rec + D * bits / 8 + 8 * (c / LPG), make_float2(scale, mn));
   }
 }
 

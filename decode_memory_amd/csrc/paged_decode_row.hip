@@ -226,8 +226,8 @@ __global__ __launch_bounds__(kRowThreads, PAGEDKV_ROW_WAVES_PER_SIMD) void paged
         const uint32_t off = lane_off + static_cast<uint32_t>(p % kBS) * tok_bytes;
         const uint4 kn = *reinterpret_cast<const uint4*>(static_cast<const char*>(a.k_new) + src);
         const uint4 vn = *reinterpret_cast<const uint4*>(static_cast<const char*>(a.v_new) + src);
-        *reinterpret_cast<uint4*>(const_cast<char*>(lane_ptr(kaddr, jj)) + off) = kn;
-        *reinterpret_cast<uint4*>(const_cast<char*>(lane_ptr(vaddr, jj)) + off) = vn;
+        store_global(const_cast<char*>(lane_ptr(kaddr, jj)) + off, kn);
+        store_global(const_cast<char*>(lane_ptr(vaddr, jj)) + off, vn);
       }
       __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the stores have reached L2
       __syncthreads();

@@ -82,8 +82,8 @@ __global__ __launch_bounds__(kThreads) void write_block_native_kernel(WriteArgs 
     uint4* vd = reinterpret_cast<uint4*>(static_cast<char*>(const_cast<void*>(a.lv.v_tab[slab])) +
                                          tok * tok_bytes);
     for (int j = threadIdx.x; j < n16; j += kThreads) {
-      kd[j] = ks[j];
-      vd[j] = vs[j];
+      store_global(kd + j, ks[j]);
+      store_global(vd + j, vs[j]);
     }
   }
 }
@@ -140,7 +140,7 @@ __global__ __launch_bounds__(kThreads) void write_block_native_multi_kernel(Writ
         const int r = f - t * upt;
         const bool is_v = r >= n16;
         char* d = is_v ? s_vd[t] : s_kd[t];
-        if (d) *reinterpret_cast<uint4*>(d + static_cast<size_t>(is_v ? r - n16 : r) * 16) = v[j];
+        if (d) store_global(d + static_cast<size_t>(is_v ? r - n16 : r) * 16, v[j]);
       }
     }
   };
@@ -214,16 +214,14 @@ __global__ __launch_bounds__(kThreads) void row_move_kernel(RowMoveArgs a) {
         continue;
       }
       if (lane_in)
-        *reinterpret_cast<uint4*>(pool_row(a, layer, kv, dst) + off) =
-            *reinterpret_cast<const uint4*>(pool_row(a, layer, kv, src) + off);
+        store_global(pool_row(a, layer, kv, dst) + off, load_global<uint4>(pool_row(a, layer, kv, src) + off));
     } else if constexpr (MODE == kMoveExport) {
       const int32_t src = a.src_rows[i];
       const bool ok = src >= 0 && src < a.capacity_rows;
       if (!ok && report) set_error(a.err, PD_DEVERR_TABLE_ROW);
       if (lane_in)
         *reinterpret_cast<uint4*>(a.dst_buf + buf_offset(a, i, layer, kv) + off) =
-            ok ? *reinterpret_cast<const uint4*>(pool_row(a, layer, kv, src) + off)
-               : make_uint4(0, 0, 0, 0);
+            ok ? load_global<uint4>(pool_row(a, layer, kv, src) + off) : make_uint4(0, 0, 0, 0);
     } else {
       const int32_t dst = a.dst_rows[i];
       if (dst < 0 || dst >= a.capacity_rows) {
@@ -231,8 +229,8 @@ __global__ __launch_bounds__(kThreads) void row_move_kernel(RowMoveArgs a) {
         continue;
       }
       if (lane_in)
-        *reinterpret_cast<uint4*>(pool_row(a, layer, kv, dst) + off) =
-            *reinterpret_cast<const uint4*>(a.src_buf + buf_offset(a, i, layer, kv) + off);
+        store_global(pool_row(a, layer, kv, dst) + off,
+                     *reinterpret_cast<const uint4*>(a.src_buf + buf_offset(a, i, layer, kv) + off));
     }
   }
 }
@@ -248,7 +246,8 @@ __global__ __launch_bounds__(kThreads) void row_move_kernel(RowMoveArgs a) {
 // of VPW, so the task's vectors are heads of one token: its row, slot and
 // slab are the same in every lane and are resolved once per wave.
 template <int D, int GS, bool IS_V>
-__device__ __forceinline__ void pack_task(const WriteArgs& a, int v0, int lane, int c, const float (&sg)[8]) {
+__device__ __forceinline__ void pack_task(const WriteArgs& a, int v0, int lane, int c, const float (&sg)[8],
+                                          const uint32_t (&odd_sign)[4]) {
   constexpr int LPT = D / 8;
   const int i = v0 / kPackedKv;                          // the token
   const int head = v0 % kPackedKv + lane / LPT;
@@ -270,9 +269,11 @@ __device__ __forceinline__ void pack_task(const WriteArgs& a, int v0, int lane, 
     rec = static_cast<char*>(const_cast<void*>(IS_V ? a.lv.v_tab[slab] : a.lv.k_tab[slab])) +
           tok * kPackedKv * rec_bytes + head * rec_bytes;
   }
-  float x[8];
-  widen8<true>(u, x);  // a token that is not written is still quantised, and not stored
-  if constexpr (!IS_V) fwht_rotate8_held<D>(x, sg, c, a.inv_sqrt_d);  // every lane takes part
+  float x[8];  // a token that is not written is still quantised, and not stored
+  if constexpr (IS_V)
+    widen8<true>(u, x);
+  else
+    widen_rotate8<D>(u, odd_sign, sg, c, a.inv_sqrt_d, x);  // every lane takes part
   quantise_store8<D, GS>(x, c, IS_V ? a.v_bits : a.k_bits, rec);
 }
 
@@ -292,13 +293,16 @@ __global__ __launch_bounds__(kThreads) void write_block_packed_kernel(WriteArgs 
     sg[0] = s0.x, sg[1] = s0.y, sg[2] = s0.z, sg[3] = s0.w;
     sg[4] = s1.x, sg[5] = s1.y, sg[6] = s1.z, sg[7] = s1.w;
   }
+  uint32_t odd_sign[4];  // sign bits of the odd values' signs
+#pragma unroll
+  for (int i = 0; i < 4; ++i) odd_sign[i] = __float_as_uint(sg[2 * i + 1]) & 0x80000000u;
   const int wave = __builtin_amdgcn_readfirstlane(blockIdx.x * (kThreads / kWave) + threadIdx.x / kWave);
   static_assert(kPackedKv % VPW == 0, "a wave task covers heads of one token");
   for (int t = wave; t < 2 * tasks; t += waves) {
     if (t < tasks)
-      pack_task<D, GS, false>(a, t * VPW, lane, c, sg);
+      pack_task<D, GS, false>(a, t * VPW, lane, c, sg, odd_sign);
     else
-      pack_task<D, GS, true>(a, (t - tasks) * VPW, lane, c, sg);
+      pack_task<D, GS, true>(a, (t - tasks) * VPW, lane, c, sg, odd_sign);
   }
 }
 
@@ -355,7 +359,7 @@ hipError_t launch_write_block(const WriteArgs& a, int32_t format, hipStream_t s)
   if (a.lv.n_kv != kPackedKv) return hipErrorInvalidValue;  // packed pools hold 8 kv heads
   const long long waves = (2LL * a.n * a.lv.n_kv * (a.head_dim / 8) + kWave - 1) / kWave;
   long long grid = (waves + kThreads / kWave - 1) / (kThreads / kWave);
-  if (grid > 65536) grid = 65536;
+  if (grid > 16384) grid = 16384;  // a few wave tasks per wave: its set-up is shared
   const int key = a.head_dim * 100 + a.qgroup;
   switch (key) {
     case 6432:

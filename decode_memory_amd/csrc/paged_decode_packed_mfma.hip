@@ -548,6 +548,18 @@ __global__ __launch_bounds__(kPThreads, kPMinWaves<D>) void paged_decode_packed_
   _Float16* sp = reinterpret_cast<_Float16*>(s_aux[h]);
 
   for (int i = 0; i < n_stages; ++i) {
+    if constexpr (kPMinWaves<D> >= 4) {
+      // Two workgroups share a CU here, and the older one's waves win issue
+      // ties, so it finished its stages well before the younger one.  A
+      // workgroup's priority falls as it advances (3 at the start, 0 in the
+      // last quarter), so one that is behind gets the ties instead (K8V8 at
+      // head_dim 64: 58.1-58.6 -> 55.9 us).
+      const int pr = 3 - (4 * i) / n_stages;
+      if (pr == 3) __builtin_amdgcn_s_setprio(3);
+      else if (pr == 2) __builtin_amdgcn_s_setprio(2);
+      else if (pr == 1) __builtin_amdgcn_s_setprio(1);
+      else __builtin_amdgcn_s_setprio(0);
+    }
     __syncthreads();  // every wave is done with the previous stage
 #pragma unroll
     for (int r = 0; r < S::UPT; ++r) {

@@ -188,13 +188,13 @@ def test_packed_decode_with_more_slabs_than_its_lds_table(fmt, D, G):
 def test_packed_workload_full_size_sampled(fmt, D, group):
     """The packed workload at full size (16 x 16384 tokens, 8 kv heads, GQA 4):
     every sequence is written and decoded on the device; the oracle checks the
-    records and outputs of sequences 0 and 15.  Groups of 64 (K4/V4 at five
-    bits per value) run at the same size."""
+    records and outputs of sequences 0, 5, 10 and 15.  Groups of 64 (K4/V4 at
+    five bits per value) run at the same size."""
     w = WORKLOADS["packed_16x16k"]
     lengths = [w.length] * w.batch
     rows = monotone_rows(lengths, BS)
     cap = int(rows[-1].max()) + 1
-    sample = (0, w.batch - 1)
+    sample = (0, 5, 10, w.batch - 1)
     pool, recs, signs = _packed_pool(fmt, D, lengths, rows, w.seed, cap, keep=sample, group=group)
     q = q_bits(w.seed, 0, w.batch, w.n_q_heads, D, "bf16")
     scale = 1.0 / np.sqrt(D)
@@ -206,9 +206,9 @@ def test_packed_workload_full_size_sampled(fmt, D, group):
     got = from_device_bits(out)
     # sampled records, through gather_visible of the sampled sequences
     sub = table[list(sample)]
-    gk = torch.empty((2, 8, w.length, pool.k_record_bytes), dtype=torch.uint8, device="cuda")
-    gv = torch.empty((2, 8, w.length, pool.v_record_bytes), dtype=torch.uint8, device="cuda")
-    pool.gather_visible(0, i32(sub), i32([w.length] * 2), w.length, gk, gv)
+    gk = torch.empty((len(sample), 8, w.length, pool.k_record_bytes), dtype=torch.uint8, device="cuda")
+    gv = torch.empty((len(sample), 8, w.length, pool.v_record_bytes), dtype=torch.uint8, device="cuda")
+    pool.gather_visible(0, i32(sub), i32([w.length] * len(sample)), w.length, gk, gv)
     gk, gv = gk.cpu().numpy(), gv.cpu().numpy()
     for i, b in enumerate(sample):
         assert np.array_equal(gk[i], recs[b][0].transpose(1, 0, 2)), (fmt, D, b)

@@ -30,6 +30,8 @@ FORMAT_NAMES = {"fp16": FMT_FP16, "bf16": FMT_BF16, "k8v8": FMT_K8V8, "k8v4": FM
                 "k4v4": FMT_K4V4}
 
 DEVERR_WRITE_ROW, DEVERR_WRITE_SLOT, DEVERR_TABLE_ROW, DEVERR_LENGTH = 0x1, 0x2, 0x4, 0x8
+DEVERR_DUPLICATE = 0x10
+DEBUG_DUPLICATE_WRITES = 0x1
 
 STATUS = {0: "PD_OK", -1: "PD_ERR_ARG", -2: "PD_ERR_RANGE", -3: "PD_ERR_CAPACITY",
           -4: "PD_ERR_UNSUPPORTED", -5: "PD_ERR_HIP", -6: "PD_ERR_DEVICE", -7: "PD_ERR_IDENTITY"}
@@ -93,6 +95,7 @@ EXPORTS = [
     "pd_decode_workspace_bytes",
     "pd_paged_decode", "pd_paged_decode_noalloc", "pd_paged_decode_append",
     "pd_paged_decode_split", "pd_paged_decode_combine", "pd_pool_stats", "pd_pool_check_error",
+    "pd_pool_set_debug",
     "pd_signs_hash", "pd_storage_identity_of", "pd_identity_check", "pd_block_bytes",
     "pd_export_blocks", "pd_import_blocks", "pd_dense_workspace_bytes", "pd_dense_decode",
 ]
@@ -132,6 +135,7 @@ def _declare(lib):
                                            ctypes.c_float, _vp, _vp, _sz, _vp]),
         "pd_pool_stats": (_i32, [_vp, ctypes.POINTER(PoolStats)]),
         "pd_pool_check_error": (_i32, [_vp, _vp, _p_i32]),
+        "pd_pool_set_debug": (_i32, [_vp, ctypes.c_uint32]),
         "pd_signs_hash": (_i32, [ctypes.POINTER(ctypes.c_int8), _i32, ctypes.POINTER(ctypes.c_uint64)]),
         "pd_storage_identity_of": (_i32, [_vp, ctypes.POINTER(StorageIdentity)]),
         "pd_identity_check": (_i32, [_vp, ctypes.POINTER(StorageIdentity)]),
@@ -490,6 +494,14 @@ def pool_stats(pool: int) -> dict:
     return s.as_dict()
 
 
+def pool_set_debug(pool: int, flags: int) -> None:
+    """Turn the library's debug checks on or off (DEBUG_* bits; 0: all off).
+    DEBUG_DUPLICATE_WRITES makes write_block flag DEVERR_DUPLICATE when two
+    tokens of one call target the same (row, slot).  Turning it on allocates
+    and synchronises: call it at set-up."""
+    _check(lib().pd_pool_set_debug(_vp(pool), ctypes.c_uint32(int(flags))))
+
+
 def pool_check_error(pool: int, stream=None) -> int:
     """Synchronise and return (and clear) the device error bits; never raises for them."""
     bits = ctypes.c_int32(0)
@@ -690,6 +702,9 @@ class SlabPool:
 
     def check_error(self, stream=None) -> int:
         return pool_check_error(self.handle, stream)
+
+    def set_debug(self, flags: int) -> None:
+        pool_set_debug(self.handle, flags)
 
     def close(self) -> None:
         if getattr(self, "handle", None):

@@ -124,8 +124,24 @@ struct AppendArgs {
   void* v_mem[kAppendMaxPairs];
 };
 
+// Duplicate-write check of write_block (pd_pool_set_debug): bit row *
+// block_size + slot of `bits` per token of the call.
+struct DupArgs {
+  const int32_t* rows;
+  const int32_t* slots;
+  int32_t n;
+  int64_t capacity_rows;
+  int32_t block_size;
+  uint32_t* bits;
+  int32_t* err;
+};
+
 // Launchers (return the hipError_t of the launch; hipErrorInvalidValue when
 // no kernel exists for the shape).
+// mark == true: set each token's bit and flag PD_DEVERR_DUPLICATE where it
+// was set already; mark == false: clear the words the tokens touched.
+hipError_t launch_dup_check(const DupArgs& a, bool mark, hipStream_t s);
+
 hipError_t launch_append_slabs(const AppendArgs& a, hipStream_t s);
 hipError_t launch_write_block(const WriteArgs& a, int32_t format, hipStream_t s);
 hipError_t launch_row_move(const RowMoveArgs& a, int mode, hipStream_t s);

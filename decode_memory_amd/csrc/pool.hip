@@ -53,6 +53,8 @@ struct pd_pool {
   float* d_signs = nullptr;  // packed: [head_dim] of +-1
   uint64_t signs_hash = 0;   // packed: pd_signs_hash of the signs
   float inv_sqrt_d = 1.f;
+  uint32_t debug = 0;          // PD_DEBUG_* bits
+  uint32_t* d_dup = nullptr;   // duplicate-write bitmap, one bit per slot of max capacity
 };
 
 // Device scratch of pd_paged_decode_noalloc, for callers that cannot
@@ -405,6 +407,7 @@ pd_status pd_pool_destroy(pd_pool* p) {
   if (p->d_tables) hipFree(p->d_tables);
   if (p->d_err) hipFree(p->d_err);
   if (p->d_signs) hipFree(p->d_signs);
+  if (p->d_dup) hipFree(p->d_dup);
   if (p->h_tables) hipHostFree(p->h_tables);
   hipSetDevice(cur);
   delete p;
@@ -493,9 +496,44 @@ pd_status pd_write_block(pd_pool* p, int32_t layer, int32_t n, const int32_t* ro
   const uint64_t S = static_cast<uint64_t>(p->desc.slab_blocks);
   a.m_slab = static_cast<uint64_t>(a.lv.capacity_rows) * S < (uint64_t{1} << 32) ? reciprocal_u32(static_cast<uint32_t>(S)) : 0u;
   if (S == 1) a.m_slab = 0;  // 0 means divide (by one)
+  const bool dup = (p->debug & PD_DEBUG_DUPLICATE_WRITES) != 0;
+  DupArgs d{rows, slots, n, a.lv.capacity_rows, p->desc.block_size, p->d_dup, p->d_err};
+  if (dup) {
+    if (hipError_t e = launch_dup_check(d, true, stream)) return hip_fail(e, "duplicate-write check launch");
+  }
   hipError_t e = launch_write_block(a, p->desc.format, stream);
-  if (e == hipErrorInvalidValue) return fail(PD_ERR_UNSUPPORTED, "no write_block kernel for this shape");
+  if (e == hipErrorInvalidValue) e = hipErrorNotSupported;
+  // the bitmap is cleared even when the write could not launch, so it is all
+  // zero again for the next call
+  if (dup) {
+    if (hipError_t ec = launch_dup_check(d, false, stream)) return hip_fail(ec, "duplicate-write clear launch");
+  }
+  if (e == hipErrorNotSupported) return fail(PD_ERR_UNSUPPORTED, "no write_block kernel for this shape");
   if (e != hipSuccess) return hip_fail(e, "write_block launch");
+  return PD_OK;
+}
+
+pd_status pd_pool_set_debug(pd_pool* p, uint32_t flags) {
+  if (pd_status st = check_pool(p)) return st;
+  if (flags & ~PD_DEBUG_DUPLICATE_WRITES) return fail(PD_ERR_ARG, "unknown debug flag bits 0x%x", flags);
+  if ((flags & PD_DEBUG_DUPLICATE_WRITES) && !p->d_dup) {
+    const uint64_t bits = static_cast<uint64_t>(p->desc.max_slabs) * p->desc.slab_blocks * p->desc.block_size;
+    const size_t bytes = static_cast<size_t>((bits + 31) / 32) * 4;
+    int cur = 0;
+    hipGetDevice(&cur);
+    hipSetDevice(p->device);
+    void* mem = nullptr;
+    hipError_t e = hipMalloc(&mem, bytes);
+    if (e == hipSuccess) e = hipMemset(mem, 0, bytes);
+    if (e == hipSuccess) e = hipDeviceSynchronize();
+    hipSetDevice(cur);
+    if (e != hipSuccess) {
+      if (mem) hipFree(mem);
+      return hip_fail(e, "duplicate-write bitmap");
+    }
+    p->d_dup = static_cast<uint32_t*>(mem);
+  }
+  p->debug = flags;
   return PD_OK;
 }
 

@@ -306,6 +306,28 @@ __global__ __launch_bounds__(kThreads) void write_block_packed_kernel(WriteArgs 
   }
 }
 
+// ---- duplicate-write check (debug) ----------------------------------------------
+// A token whose (row, slot) is outside the pool is left to the write, which
+// reports it.  Marking uses a vector atomic OR per token; the clear stores
+// zero to each touched word (every bit set in it belongs to this call, since
+// the bitmap is all zero between calls).
+
+template <bool MARK>
+__global__ __launch_bounds__(kThreads) void dup_check_kernel(DupArgs a) {
+  for (int i = blockIdx.x * kThreads + threadIdx.x; i < a.n; i += gridDim.x * kThreads) {
+    const int32_t row = a.rows[i], slot = a.slots[i];
+    if (row < 0 || row >= a.capacity_rows || slot < 0 || slot >= a.block_size) continue;
+    const uint64_t bit = static_cast<uint64_t>(row) * a.block_size + slot;
+    uint32_t* word = a.bits + (bit >> 5);
+    if constexpr (MARK) {
+      const uint32_t m = 1u << (bit & 31);
+      if (atomicOr(word, m) & m) set_error(a.err, PD_DEVERR_DUPLICATE);
+    } else {
+      *word = 0u;
+    }
+  }
+}
+
 }  // namespace
 
 hipError_t launch_append_slabs(const AppendArgs& a, hipStream_t s) {
@@ -318,6 +340,17 @@ hipError_t launch_append_slabs(const AppendArgs& a, hipStream_t s) {
   if (cols > 64) cols = 64;
   hipLaunchKernelGGL(append_slabs_kernel, dim3(static_cast<unsigned>(cols), 2 * a.n_pairs), dim3(kThreads), 0, s,
                      a);
+  return hipGetLastError();
+}
+
+hipError_t launch_dup_check(const DupArgs& a, bool mark, hipStream_t s) {
+  if (a.n <= 0) return hipSuccess;
+  long long grid = (a.n + kThreads - 1) / kThreads;
+  if (grid > 4096) grid = 4096;
+  if (mark)
+    hipLaunchKernelGGL(dup_check_kernel<true>, dim3(static_cast<unsigned>(grid)), dim3(kThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL(dup_check_kernel<false>, dim3(static_cast<unsigned>(grid)), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 

@@ -83,6 +83,11 @@ typedef enum pd_format {
 #define PD_DEVERR_TABLE_ROW   0x4  /* a block-table row outside the pool          */
 #define PD_DEVERR_LENGTH      0x8  /* lens[b] < 0, or beyond max_blocks*block_size,
                                       t_out (gather) or max_len (decode)        */
+#define PD_DEVERR_DUPLICATE   0x10 /* write_block, duplicate-write check on: two
+                                      tokens of one call target one (row, slot) */
+
+/* Debug checks (pd_pool_set_debug). */
+#define PD_DEBUG_DUPLICATE_WRITES 0x1u
 
 typedef struct pd_pool_desc {
   int32_t n_layers;      /* >= 1                                                */
@@ -229,6 +234,25 @@ pd_status pd_slab_for_row(const pd_pool* pool, int32_t layer, int64_t row, void*
 pd_status pd_write_block(pd_pool* pool, int32_t layer, int32_t n, const int32_t* rows,
                          const int32_t* slots, const void* k_src, const void* v_src,
                          hipStream_t stream);
+
+/*
+ * pool_set_debug: turn debug checks on or off for the calls that follow.
+ * PD_DEBUG_DUPLICATE_WRITES checks the scatter of pd_write_block (mlxcel
+ * #235, "Proposed solution", touch point 1: new K/V rows land in the row's
+ * slab): two tokens of one call that target the same (row, slot) leave which
+ * one is stored unspecified, so with the check on such a call sets
+ * PD_DEVERR_DUPLICATE in the device error word (the call still writes).  The
+ * check marks one bit per token in a device bitmap of one bit per slot of
+ * the pool's largest capacity (max_slabs * slab_blocks * block_size bits,
+ * allocated here the first time the check is turned on, freed by
+ * pd_pool_destroy), and clears its bits again after the write: two more
+ * launches per pd_write_block on `stream`.  Turning the check on allocates
+ * and synchronises the device, so it is for set-up, not for graph capture;
+ * calls that run at once on several streams of one pool share the bitmap.
+ *   flags: a combination of PD_DEBUG_* bits; 0 turns every check off.
+ * Errors: PD_ERR_ARG (unknown flag bits), PD_ERR_HIP (allocation).
+ */
+pd_status pd_pool_set_debug(pd_pool* pool, uint32_t flags);
 
 /*
  * copy_on_write_block (mlxcel #235, "Proposed solution", touch point 2):

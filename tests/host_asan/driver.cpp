@@ -21,6 +21,7 @@ static int g_fail_host_malloc = 0;   // fail the next hipHostMalloc
 static int g_launch_fail_at = -1;    // fail the append launch with this index
 static int g_append_launches = 0;
 static int g_other_launches = 0;
+static int g_dup_launches = 0;       // duplicate-write check launches (mark, clear)
 static void** g_tables = nullptr;    // the device tables the last append wrote
 
 const char* hipGetErrorString(hipError_t e) { return e == hipSuccess ? "no error" : "stand-in error"; }
@@ -58,6 +59,23 @@ hipError_t launch_append_slabs(const AppendArgs& a, hipStream_t) {
   return hipSuccess;
 }
 hipError_t launch_write_block(const WriteArgs&, int32_t, hipStream_t) { ++g_other_launches; return hipSuccess; }
+// the duplicate-write check on host memory: rows and slots are host arrays here
+hipError_t launch_dup_check(const DupArgs& a, bool mark, hipStream_t) {
+  ++g_dup_launches;
+  for (int i = 0; i < a.n; ++i) {
+    const int32_t row = a.rows[i], slot = a.slots[i];
+    if (row < 0 || row >= a.capacity_rows || slot < 0 || slot >= a.block_size) continue;
+    const uint64_t bit = static_cast<uint64_t>(row) * a.block_size + slot;
+    if (mark) {
+      const uint32_t m = 1u << (bit & 31);
+      if (a.bits[bit >> 5] & m) *a.err |= PD_DEVERR_DUPLICATE;
+      a.bits[bit >> 5] |= m;
+    } else {
+      a.bits[bit >> 5] = 0u;
+    }
+  }
+  return hipSuccess;
+}
 hipError_t launch_row_move(const RowMoveArgs&, int, hipStream_t) { ++g_other_launches; return hipSuccess; }
 hipError_t launch_gather(const GatherArgs&, hipStream_t) { ++g_other_launches; return hipSuccess; }
 hipError_t launch_split_runs(const RunArgs&, hipStream_t) { ++g_other_launches; return hipSuccess; }
@@ -229,6 +247,37 @@ int main() {
     d.n_kv_heads = 4;  // the packed decode kernel takes 8 kv heads
     pd_pool* q = nullptr;
     CHECK(pd_pool_create(&d, &q) == PD_ERR_UNSUPPORTED && q == nullptr);
+    CHECK(pd_pool_destroy(p) == PD_OK);
+  }
+  // the duplicate-write check: off by default; on, a call with two tokens on
+  // one (row, slot) flags the error word, the bitmap is all zero after each
+  // call (no false report on the next), and destroy frees it
+  {
+    pd_pool_desc d = desc(1, 4, 3);
+    pd_pool* p = nullptr;
+    CHECK(pd_pool_create(&d, &p) == PD_OK);
+    size_t kb = 0, vb = 0;
+    CHECK(pd_slab_bytes(p, &kb, &vb) == PD_OK);
+    void* k[1] = {mem.get(kb, 0)};
+    void* v[1] = {mem.get(vb, 0)};
+    int32_t idx = -1;
+    CHECK(pd_append_slab(p, k, v, nullptr, &idx) == PD_OK && idx == 0);  // rows 0 .. 3
+    int32_t rows[3] = {0, 1, 0}, slots[3] = {5, 5, 5}, good_slots[3] = {5, 5, 6};
+    static char src[3 * 4096] __attribute__((aligned(16)));
+    const int l0 = g_dup_launches;
+    CHECK(pd_pool_set_debug(p, 0x80u) == PD_ERR_ARG);
+    CHECK(pd_write_block(p, 0, 3, rows, slots, src, src, nullptr) == PD_OK);
+    CHECK(g_dup_launches == l0);                 // off: no check
+    CHECK(pd_pool_set_debug(p, PD_DEBUG_DUPLICATE_WRITES) == PD_OK);
+    CHECK(pd_write_block(p, 0, 3, rows, slots, src, src, nullptr) == PD_OK);
+    CHECK(g_dup_launches == l0 + 2);             // mark before the write, clear after
+    int32_t err = 0;
+    CHECK(pd_pool_check_error(p, nullptr, &err) == PD_ERR_DEVICE && (err & PD_DEVERR_DUPLICATE));
+    CHECK(pd_write_block(p, 0, 3, rows, good_slots, src, src, nullptr) == PD_OK);
+    CHECK(pd_pool_check_error(p, nullptr, &err) == PD_OK && err == 0);
+    CHECK(pd_pool_set_debug(p, 0) == PD_OK);
+    CHECK(pd_write_block(p, 0, 3, rows, slots, src, src, nullptr) == PD_OK);
+    CHECK(g_dup_launches == l0 + 4);
     CHECK(pd_pool_destroy(p) == PD_OK);
   }
   // a failed host allocation inside create leaves nothing behind

@@ -12,7 +12,8 @@ typedef enum hipError_t {
   hipErrorInvalidValue = 1,
   hipErrorOutOfMemory = 2,
   hipErrorInvalidDevice = 101,
-  hipErrorLaunchFailure = 719
+  hipErrorLaunchFailure = 719,
+  hipErrorNotSupported = 801
 } hipError_t;
 
 typedef struct ihipStream_t* hipStream_t;

@@ -281,3 +281,43 @@ def test_split_runs_flags_rows_outside_the_pool():
                                                                              (-1, 5, 1)]
     assert pool.check_error() == pd.DEVERR_TABLE_ROW
     pool.close()
+
+
+@pytest.mark.parametrize("fmt,D", [("bf16", 128), ("k4v4", 64)])
+def test_duplicate_write_check(fmt, D):
+    """With the debug check on, a write_block whose tokens share a (row,
+    slot) sets DEVERR_DUPLICATE (which token is stored is unspecified; the
+    page's scatter never generates such calls); distinct targets, a target
+    outside the pool (reported as such, not as a duplicate) and the check
+    turned off leave the bit clear, and the check's bitmap is clear again
+    after every call."""
+    from synth import hadamard_signs
+    extra = {} if fmt == "bf16" else {"hadamard_signs": hadamard_signs(5, D)}
+    pool = pd.SlabPool(1, 32, 8, D, 32, 5, fmt, **extra)
+    pool.reserve_rows(128)
+    dt = torch.bfloat16
+    n = 4096
+    gen = torch.Generator(device="cuda").manual_seed(3)
+    k = torch.randn((n + 1, 8, D), generator=gen, device="cuda").to(dt)
+    v = torch.randn((n + 1, 8, D), generator=gen, device="cuda").to(dt)
+    t = np.arange(n)
+    rows, slots = (t // 32).astype(np.int32), (t % 32).astype(np.int32)   # rows 0..127
+    with pytest.raises(pd.PagedKVError):
+        pool.set_debug(0x80)
+    pool.write_block(0, i32(rows[:3]), i32([5, 5, 5]), k[:3], v[:3])   # off: not checked
+    assert pool.check_error() == 0
+    pool.set_debug(pd.DEBUG_DUPLICATE_WRITES)
+    pool.write_block(0, i32(rows[:n]), i32(slots[:n]), k[:n], v[:n])   # 4096 distinct targets
+    assert pool.check_error() == 0
+    dup_rows = np.concatenate([rows, rows[1234:1235]])
+    dup_slots = np.concatenate([slots, slots[1234:1235]])
+    pool.write_block(0, i32(dup_rows), i32(dup_slots), k, v)             # token n repeats token 1234
+    assert pool.check_error() == pd.DEVERR_DUPLICATE
+    pool.write_block(0, i32(rows[:n]), i32(slots[:n]), k[:n], v[:n])   # the bitmap was cleared
+    assert pool.check_error() == 0
+    pool.write_block(0, i32([1000, 1000]), i32([0, 0]), k[:2], v[:2])  # outside the pool
+    assert pool.check_error() == pd.DEVERR_WRITE_ROW
+    pool.set_debug(0)
+    pool.write_block(0, i32(dup_rows), i32(dup_slots), k, v)
+    assert pool.check_error() == 0
+    pool.close()

@@ -9,7 +9,7 @@ import torch
 
 import decode_memory_amd as pd
 from oracle.slab_pool import SlabPoolModel, records_from_u16
-from synth import WORKLOADS, make_block_table, monotone_rows, shuffled_rows, workload_lengths
+from synth import WORKLOADS, make_block_table, monotone_rows, normal_device, shuffled_rows, workload_lengths
 from tests.gpu_util import build_pool, from_device_bits, i32, to_device_bits, token_targets
 
 pytestmark = pytest.mark.gpu
@@ -118,6 +118,43 @@ def test_fragmented_workload_gather_is_byte_identical():
     assert list(runs) == expect_runs
     nbs = [len(r) for r in rows]
     assert sum(expect_runs) > 0.8 * sum(nbs)            # worst-case fragmentation
+    pool.close()
+
+
+def test_fragmented_workload_gather_full_size():
+    """The fragmented pool at its full size (64 sequences U{512..16384},
+    536,438 tokens, 8 kv heads, head_dim 128, shuffled free list): every
+    gathered record equals the dense source the pool was written from, the
+    padding past each length is zero, and each sequence's run count equals
+    the oracle's run split of its row list."""
+    w = WORKLOADS["fragmented_64"]
+    lengths = workload_lengths(w).astype(np.int64)
+    B, bs, S, n_kv, D = len(lengths), w.block_size, w.slab_blocks, w.n_kv_heads, w.head_dim
+    rng = np.random.default_rng(np.random.SeedSequence([w.seed, 1 << 24]))
+    rows, _, R = shuffled_rows(rng, lengths, bs, S)
+    pool = pd.SlabPool(1, bs, n_kv, D, S, R // S + 2, w.dtype)
+    pool.reserve_rows(R)
+    dense_k, dense_v = [], []
+    for b, n in enumerate(lengths):
+        k = normal_device((w.seed, 1 << 24, b, 0), (int(n), n_kv, D), w.dtype, "cuda")
+        v = normal_device((w.seed, 1 << 24, b, 1), (int(n), n_kv, D), w.dtype, "cuda")
+        r, sl = token_targets(rows[b], int(n), bs)
+        pool.write_block(0, i32(r), i32(sl), k, v)
+        dense_k.append(k)
+        dense_v.append(v)
+    t_out = int(lengths.max())
+    gk = torch.full((B, n_kv, t_out, D), 7, dtype=torch.int16, device="cuda")
+    gv = torch.full_like(gk, 7)
+    runs = torch.full((B,), -1, dtype=torch.int32, device="cuda")
+    pool.gather_visible(0, i32(make_block_table(rows)), i32(lengths), t_out, gk, gv, runs)
+    for b, n in enumerate(lengths):
+        n = int(n)
+        assert torch.equal(gk[b, :, :n], dense_k[b].transpose(0, 1).view(torch.int16)), b
+        assert torch.equal(gv[b, :, :n], dense_v[b].transpose(0, 1).view(torch.int16)), b
+        assert not bool(gk[b, :, n:].any()) and not bool(gv[b, :, n:].any()), b
+    model = SlabPoolModel(1, bs, n_kv, 2 * D, 2 * D, S)
+    assert runs.cpu().tolist() == [len(model.split_runs(r)) for r in rows]
+    assert pool.check_error() == 0
     pool.close()
 
 

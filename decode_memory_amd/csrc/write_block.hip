@@ -1,6 +1,7 @@
 // write_block: token-granular scatter of new K/V into the slab of their row;
-// whole-row moves (copy_on_write_block, block export and import); and the
-// zero fill that backs append_slab.
+// whole-row moves (copy_on_write_block, block export and import); the zero
+// fill that backs append_slab; and the duplicate-write check of the debug
+// mode.
 //
 // mlxcel issue #235 ("perf(core): chunked slab storage for the paged pool to
 // eliminate growth reallocation entirely"), section "Proposed solution:

@@ -164,7 +164,7 @@ int row_kernel_heads_per_workgroup(int32_t head_dim, int hgw);
 
 // Split policy shared by the workspace query and the launch.
 constexpr int kMaxBlocksPerSplit = 64;
-constexpr int kMaxSplits = 256;
+constexpr int kMaxSplits = 1024;
 inline int64_t max_decode_len(int32_t block_size) {
   return static_cast<int64_t>(kMaxBlocksPerSplit) * kMaxSplits * block_size;
 }

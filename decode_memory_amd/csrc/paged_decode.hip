@@ -290,10 +290,11 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
-template <int D, bool BF16>
+// KM: (max, sum) pairs a lane holds, splits / 64 rounded up (the launch
+// picks the smallest that covers the call's splits)
+template <int D, bool BF16, int KM>
 __global__ __launch_bounds__(kCWaves * kWave) void combine_kernel(DecodeArgs a) {
   constexpr int CH = D / kWave;  // 64-column chunks per query head
-  constexpr int KM = kMaxSplits / kWave;
   const int lane = threadIdx.x % kWave;
   // the split kernel's work ids are (sequence, head set, split) in order and
   // XCD x runs a contiguous range of them; the same mapping here gives XCD x
@@ -373,7 +374,18 @@ template <int D, bool BF16>
 hipError_t launch_combine_typed(const DecodeArgs& a, hipStream_t s) {
   const long long waves = static_cast<long long>(a.B) * a.n_q * (D / kWave);
   const int grid = round_up(static_cast<int>((waves + kCWaves - 1) / kCWaves), kXcds);
-  hipLaunchKernelGGL((combine_kernel<D, BF16>), dim3(grid), dim3(kCWaves * kWave), 0, s, a);
+  static_assert(kMaxSplits <= 16 * kWave, "combine holds at most 16 (max, sum) pairs per lane");
+  const int km = (a.n_split + kWave - 1) / kWave;
+  if (km <= 1)
+    hipLaunchKernelGGL((combine_kernel<D, BF16, 1>), dim3(grid), dim3(kCWaves * kWave), 0, s, a);
+  else if (km <= 2)
+    hipLaunchKernelGGL((combine_kernel<D, BF16, 2>), dim3(grid), dim3(kCWaves * kWave), 0, s, a);
+  else if (km <= 4)
+    hipLaunchKernelGGL((combine_kernel<D, BF16, 4>), dim3(grid), dim3(kCWaves * kWave), 0, s, a);
+  else if (km <= 8)
+    hipLaunchKernelGGL((combine_kernel<D, BF16, 8>), dim3(grid), dim3(kCWaves * kWave), 0, s, a);
+  else
+    hipLaunchKernelGGL((combine_kernel<D, BF16, 16>), dim3(grid), dim3(kCWaves * kWave), 0, s, a);
   return hipGetLastError();
 }
 

@@ -332,7 +332,9 @@ pd_status pd_decode_workspace_bytes(const pd_pool* pool, int32_t B, int32_t n_q_
  *     packed pools; the kernel applies the Hadamard rotation itself).
  *   block_table, lens: as pd_gather_visible; tokens >= lens[b] are not read.
  *   max_len: host, >= max(lens); sizes the split of the token axis without a
- *     host-device synchronisation.
+ *     host-device synchronisation.  At most 65,536 blocks (1024 splits of 64
+ *     blocks: 2,097,152 tokens at block_size 32); beyond that
+ *     PD_ERR_UNSUPPORTED.
  *   scale: multiplies q.k (typically 1/sqrt(head_dim)).
  *   out: device [B, n_q_heads, head_dim], same dtype as q, rounded to nearest
  *     even once at the end.  A sequence with lens[b] == 0 gets zeros.

@@ -1,10 +1,10 @@
 """The limits of paged_decode: the longest sequence the split plan holds, and
 lengths beyond what a call can read.
 
-At block_size 32 the plan holds 64 blocks per split and 256 splits, 524,288
-tokens: the only length at which the row kernel and the packed kernel read
-64 blocks per split (the last lane's row and the top bit of the block mask)
-and the combine merges 256 splits.  Keys are all equal there, so the softmax is uniform and
+At block_size 32 the plan holds 64 blocks per split and 1024 splits,
+2,097,152 tokens: the only length at which the row kernel and the packed
+kernel read 64 blocks per split (the last lane's row and the top bit of the
+block mask) and the combine merges 1024 splits (16 per lane).  Keys are all equal there, so the softmax is uniform and
 the output is the plain mean of the values, a closed form over the periodic
 value pattern (mlxcel #2171, "Proposed Solution": attend(q, k, v, scale,
 mask) with one query token; with equal scores it reduces to the mean)."""
@@ -21,7 +21,7 @@ from tests.gpu_util import assert_decode_close, from_device_bits, i32, to_device
 pytestmark = pytest.mark.gpu
 
 BS = 32
-MAX_LEN = 64 * 256 * BS  # blocks per split x splits x block_size
+MAX_LEN = 64 * 1024 * BS  # blocks per split x splits x block_size
 
 
 def _bf16(x):
@@ -107,12 +107,12 @@ def test_lengths_beyond_the_call_are_clamped_and_flagged():
 
 @pytest.mark.parametrize("fmt,fused", [("k4v4", False), ("k8v8", False), ("k4v4", True)])
 def test_longest_packed_sequence_the_plan_holds(fmt, fused):
-    """The packed kernel at the longest plan (256 splits of 64 blocks): equal
+    """The packed kernel at the longest plan (1024 splits of 64 blocks): equal
     keys give equal scores, so the output is the mean of the dequantised
     value records (mlx-swift-lm PR #142, "Add packed paged KV formats with
     bounded workspace admission", section "Summary": attention reads the
     packed pages directly), here a closed form over the periodic pattern.
-    Fused, the last token (block 16383: split 255's 64th block) is quantised
+    Fused, the last token (block 65535: split 1023's 64th block) is quantised
     and stored by the decode launch itself."""
     from oracle.packed import FORMATS, dequantise_records, v_records
     from synth import hadamard_signs

@@ -134,11 +134,12 @@ __device__ __forceinline__ void quantise_store8(const float (&x)[8], int c, int 
   // Each step is one DPP min and one DPP max: the lane exchange rides in the
   // instruction, where a separate DPP move would also need the compiler's
   // canonicalising max of the moved value (both inputs here are results of
-  // min/max, so the plain IEEE min/max is the same operation).  s_nop 1 gives
-  // the two wait states a DPP read of a just-written register needs.  Records
-  // unchanged; the packed write measured 1-6% faster.
+  // min/max, so the plain IEEE min/max is the same operation).  s_nop 4 gives
+  // the wait states a DPP instruction needs after a VALU write of its source
+  // register (2) or of EXEC (5), whatever the compiler placed before it.
+  // Records unchanged; the packed write measured 1-6% faster.
 #define PD_DPP_MINMAX(CTRL)                                                                      \
-  asm("s_nop 1\n\tv_min_f32_dpp %0, %2, %2 " CTRL " row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t" \
+  asm("s_nop 4\n\tv_min_f32_dpp %0, %2, %2 " CTRL " row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t" \
       "v_max_f32_dpp %1, %3, %3 " CTRL " row_mask:0xf bank_mask:0xf bound_ctrl:1"                 \
       : "=&v"(mn), "=&v"(mx)                                                                    \
       : "v"(mn), "v"(mx))

@@ -78,6 +78,39 @@ def test_noalloc_matches_workspace_call_twice_shrinking(fmt_case):
     pool2.close()
 
 
+@pytest.mark.parametrize("fmt,D,G", [("k4v4", 64, 4), ("k8v8", 256, 2)])
+def test_noalloc_packed_matches_workspace_call_twice_shrinking(fmt, D, G):
+    """The same for packed pools (the matrix-core kernel's partials in the
+    scratch): bit for bit the workspace call's output, on a larger call and
+    then a smaller one."""
+    from synth import hadamard_signs, monotone_rows
+    for step, lengths in enumerate(([3000, 1, 777, 0, 2048, 64], [500, 33])):
+        _say(f"noalloc {fmt} D={D} G={G}: call {step + 1}, B={len(lengths)}")
+        rows = monotone_rows(lengths, 32)
+        cap = max(int(r.max()) + 1 for r in rows if len(r))
+        pool = pd.SlabPool(1, 32, 8, D, 8, -(-cap // 8) + 1, fmt, hadamard_signs=hadamard_signs(61 + step, D))
+        pool.reserve_rows(cap)
+        gen = torch.Generator(device="cuda").manual_seed(100 + step)
+        for b, n in enumerate(lengths):
+            if n == 0:
+                continue
+            t = np.arange(n)
+            k = torch.randn((n, 8, D), generator=gen, device="cuda").to(torch.bfloat16)
+            v = torch.randn((n, 8, D), generator=gen, device="cuda").to(torch.bfloat16)
+            pool.write_block(0, i32(rows[b][t // 32]), i32(t % 32), k, v)
+        q = torch.randn((len(lengths), 8 * G, D), generator=gen, device="cuda").to(torch.bfloat16)
+        t_, lens, ml = i32(make_block_table(rows)), i32(lengths), max(lengths)
+        out_na = torch.full_like(q, float("nan"))
+        pd.paged_decode_noalloc(pool.handle, 0, q, t_, lens, ml, 1 / np.sqrt(D), out_na)
+        out_ws = torch.full_like(q, float("nan"))
+        pool.paged_decode(0, q, t_, lens, ml, 1 / np.sqrt(D), out_ws, pool.workspace(len(lengths), 8 * G, ml))
+        torch.cuda.synchronize()
+        assert torch.equal(out_na.view(torch.int16), out_ws.view(torch.int16))
+        assert bool(torch.isfinite(out_na).all())
+        assert pool.check_error() == 0
+        pool.close()
+
+
 def test_noalloc_refuses_calls_beyond_the_scratch():
     """256 sequences x 32 query heads x 16384 tokens (16 splits) need 68 MB
     of partials, more than the 16 MiB scratch: refused with PD_ERR_CAPACITY

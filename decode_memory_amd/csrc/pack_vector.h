@@ -159,24 +159,29 @@ __device__ __forceinline__ void quantise_store8(const float (&x)[8], int c, int 
   // ulp(q) of q (below 2^-14.9 at 8 bits, q < 256; below 2^-18.9 at 4 bits,
   // q < 16), and t = rint(q') is rint(q) unless q' lies within 2^-14 (4 bits:
   // 2^-18) of a half-integer, about 1 value in 8000 (4 bits: 1 in 130000).
-  // Such a value, or a divisor below 2^-125 or not finite, sends the whole
-  // wave through the correctly rounded divisions, clamped (a subnormal scale
-  // can give q > 2^bits - 1).  The fast path needs no clamp: q' <= (2^bits -
-  // 1)(1 + 2^-21) for a normal scale.  A NaN value gets an unspecified code.
+  // Such a value takes the correctly rounded division, clamped (a subnormal
+  // scale can give q > 2^bits - 1): for each of the lane's 8 positions, the
+  // wave divides at that position when any of its lanes has a value there in
+  // the band.  Bf16 data put values exactly at a code midpoint often (the
+  // middle of a group's range is q = 7.5 at 4 bits), so about 1 position in
+  // 8 of a wave needs it, while a whole-wave fallback would divide all 8 in
+  // most wave tasks.  A divisor below 2^-125 or not finite sends every
+  // position through the division.  The fast path needs no clamp: q' <=
+  // (2^bits - 1)(1 + 2^-21) for a normal scale.  A NaN value gets an
+  // unspecified code.
   const float r0 = __builtin_amdgcn_rcpf(div);
   const float r = __builtin_fmaf(__builtin_fmaf(-div, r0, 1.f), r0, r0);
-  float d[8], t[8], worst = 0.f;
+  // (a divisor out of range makes the threshold -1, which every position
+  // fails; so does a NaN quotient)
+  const float band = eight ? 0.49993896484375f : 0.4999961853027344f;
+  const float thr = (div >= 0x1p-125f && div <= 0x1.fffffep127f) ? band : -1.f;
+  float t[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
-    d[e] = x[e] - mn;
-    const float q = d[e] * r;
+    const float d = x[e] - mn;
+    const float q = d * r;
     t[e] = rintf(q);
-    worst = fmaxf(worst, fabsf(q - t[e]));
-  }
-  const bool slow = !(div >= 0x1p-125f && div <= 0x1.fffffep127f && worst < (eight ? 0.49993896484375f : 0.4999961853027344f));
-  if (__ballot(slow)) {
-#pragma unroll
-    for (int e = 0; e < 8; ++e) t[e] = fminf(rintf(d[e] / div), levels);
+    if (__ballot(!(fabsf(q - t[e]) < thr))) t[e] = fminf(rintf(d / div), levels);
   }
   if (!rec) return;
   // codes to bytes (each t is an integer in 0 .. 255: the conversion is exact)

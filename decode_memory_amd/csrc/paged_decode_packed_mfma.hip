@@ -193,14 +193,26 @@ __device__ __forceinline__ float key_q_factor(int v) {
   return (KB == 4 && (v & 1)) ? 0.0625f : 1.f;
 }
 
-// Value dimension that accumulator i of lane l holds.  8-bit codes: 64 i +
-// l.  4-bit codes: lanes take code bytes, whose two nibbles are dimensions
-// 2 byte and 2 byte + 1 -- with 64 dimensions byte l % 32 and nibble l / 32,
-// otherwise byte l + 64 (i / 2) and nibble i % 2.
+// Value accumulators per lane: one per 64 dimensions, two at head_dim 64.
+template <int NV>
+constexpr int kNAcc = NV == 1 ? 2 : NV;
+// Head_dim 64 reads the value code bytes with LDS transpose loads
+// (ds_read_b64_tr_b8): within each 16-lane group, lane i receives byte
+// column i % 8 of the 8 rows named by lanes 2m + (i % 16) / 8, m = 0..7.  With
+// lanes naming tokens as below, lane l holds byte column tr_col(l) of 8
+// consecutive tokens, and lanes l and l + 8 of a group hold the two halves of
+// 16 tokens (their sums are added at the end).
+__device__ __forceinline__ int tr_col(int lane) { return 8 * (lane / 16) + lane % 8; }
+__device__ __forceinline__ int tr_token(int lane) { return (lane % 16) / 2 + 8 * (lane % 2); }
+// Value dimension that accumulator i of lane l holds.  Head_dim 64: 8-bit
+// codes, tr_col(l) + 32 i; 4-bit codes, nibble i of byte tr_col(l), that is
+// 2 tr_col(l) + i.  Otherwise 8-bit codes: 64 i + l; 4-bit codes: lanes take
+// code bytes l + 64 (i / 2), whose two nibbles are dimensions 2 byte and 2
+// byte + 1 (nibble i % 2).
 template <int VB, int NV>
 __device__ __forceinline__ int vdim(int i, int lane) {
-  if constexpr (VB == 8) return 64 * i + lane;
-  else if constexpr (NV == 1) return 2 * (lane % 32) + lane / 32;
+  if constexpr (NV == 1) return VB == 8 ? tr_col(lane) + 32 * i : 2 * tr_col(lane) + i;
+  else if constexpr (VB == 8) return 64 * i + lane;
   else return 2 * (lane + 64 * (i / 2)) + (i % 2);
 }
 // Scale that brings accumulator i of lane l back to sum_t p_t s_t c_t: the
@@ -208,8 +220,15 @@ __device__ __forceinline__ int vdim(int i, int lane) {
 // place (exact powers of two).
 template <int VB, int NV>
 __device__ __forceinline__ float vacc_scale(int i, int lane, int vk) {
-  const bool high = VB == 4 && (NV == 1 ? lane >= 32 : (i % 2) == 1);
+  const bool high = VB == 4 && (i % 2) == 1;
   return __builtin_bit_cast(float, static_cast<uint32_t>(127 - vk - (high ? 4 : 0)) << 23);
+}
+
+typedef int v2i __attribute__((ext_vector_type(2)));
+// 8 bytes per lane from LDS, transposed across each 16-lane group as above
+__device__ __forceinline__ uint2 lds_read_tr8(const unsigned char* p) {
+  const v2i r = __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) v2i*)(p));
+  return make_uint2(static_cast<uint32_t>(r.x), static_cast<uint32_t>(r.y));
 }
 
 // 2^k as an fp32 (k in [-126, 128]; 128 gives inf)
@@ -246,7 +265,8 @@ __global__ __launch_bounds__(kPThreads, kPMinWaves<D>) void paged_decode_packed_
   constexpr int NKB = S::NKB, NMG = S::NMG, KPG = S::KPG, T = S::T, PK = S::PK, PV = S::PV;
   constexpr int NSUB = S::NSUB, STEP = S::STEP;
   constexpr int KREC = S::KREC, VREC = S::VREC, KROW = S::KROW, VROW = S::VROW;
-  constexpr int NV = D / 64;  // value accumulators (64 dimensions each, one per lane)
+  constexpr int NV = D / 64;  // 64-dimension blocks of a value
+  constexpr int NACC = kNAcc<NV>;
   // floats per wave: the q' transform, then p^T as f16 [group][4][STEP]
   constexpr int AUX = (G * D > NMG * 2 * STEP) ? G * D : NMG * 2 * STEP;
   static_assert(G <= 4, "query heads of a kv head take rows 0, 4, 8, 12");
@@ -487,9 +507,9 @@ __global__ __launch_bounds__(kPThreads, kPMinWaves<D>) void paged_decode_packed_
 #pragma unroll
   for (int g = 0; g < NMG; ++g) cinit[g] = f4{-kbias[g], 0.f, 0.f, 0.f};
 
-  f4 acc[NV];  // lane l: dimension vdim(i, l), register r: query head r
+  f4 acc[NACC];  // lane l: dimension vdim(i, l), register r: query head r
 #pragma unroll
-  for (int i = 0; i < NV; ++i) acc[i] = f4{0.f, 0.f, 0.f, 0.f};
+  for (int i = 0; i < NACC; ++i) acc[i] = f4{0.f, 0.f, 0.f, 0.f};
   // value prescale exponents per group, and the factors 2^vk (wave-uniform)
   int vk[NMG];
   float pf[NMG];
@@ -529,7 +549,7 @@ __global__ __launch_bounds__(kPThreads, kPMinWaves<D>) void paged_decode_packed_
         const int knew = __builtin_amdgcn_readfirstlane(14 - exponent_of(mx));
         const float ratio = exp2i(knew - vk[g]);
 #pragma unroll
-        for (int i = 0; i < NV; ++i) {
+        for (int i = 0; i < NACC; ++i) {
           const float f = vdim<VB, NV>(i, lane) / GS == g ? ratio : 1.f;
           acc[i] *= f;
         }
@@ -696,7 +716,7 @@ __global__ __launch_bounds__(kPThreads, kPMinWaves<D>) void paged_decode_packed_
         for (int r = 0; r < G; ++r) {
           const float ar = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, alpha), kSub * r));
 #pragma unroll
-          for (int i = 0; i < NV; ++i) acc[i][r] *= ar;
+          for (int i = 0; i < NACC; ++i) acc[i][r] *= ar;
         }
       }
       __builtin_amdgcn_wave_barrier();
@@ -704,8 +724,39 @@ __global__ __launch_bounds__(kPThreads, kPMinWaves<D>) void paged_decode_packed_
       // head lane % 4 (rows of absent query heads hold zeros); the B/C column
       // of lane l is dimension vdim(i, l)
       const int qa = lane % 4;
-      // 4-bit codes, 64 dimensions: the nibble of this lane, in place
-      const uint32_t nib_mask = lane < 32 ? 0x000f000fu : 0x00f000f0u;
+      if constexpr (NV == 1) {
+        // head_dim 64: one transpose load per 16 tokens and 32 code bytes
+        // gives lane l byte column tr_col(l) of the 8 tokens t8 .. t8 + 7;
+        // each dword of it (4 tokens) feeds the products of its dimensions
+        const int col = tr_col(lane);
+        const int t8 = 8 * ((lane % 16) / 8);
+        const unsigned char* vcol = s_stage + T * PK + (lt0 + tr_token(lane)) * PV + h * VREC + 8 * (lane / 16);
+#pragma unroll
+        for (int u = 0; u < NSUB; ++u) {
+#pragma unroll
+          for (int rd = 0; rd < VB / 4; ++rd) {  // 8-bit codes: bytes 0-31, then 32-63
+            const uint2 w = lds_read_tr8(vcol + u * kSub * PV + 32 * rd);
+#pragma unroll
+            for (int dw = 0; dw < 2; ++dw) {
+              const uint32_t x = dw ? w.y : w.x;
+              const int tq0 = u * kSub + t8 + 4 * dw;  // the dword's first token in the step
+              const uint32_t p01 = bytes_biased(x, kSelB01), p23 = bytes_biased(x, kSelB23);
+              if constexpr (VB == 8) {
+                const h4 ap = *reinterpret_cast<const h4*>(sp + ((col + 32 * rd) / GS * 4 + qa) * STEP + tq0);
+                const uint32_t u2[2] = {unbias(p01), unbias(p23)};
+                acc[rd] = __builtin_amdgcn_mfma_f32_4x4x4f16(ap, __builtin_bit_cast(h4, u2), acc[rd], 0, 0, 0);
+              } else {
+                // low nibbles as 1024 + code, high nibbles in place as 1024 + 16 code
+                const h4 ap = *reinterpret_cast<const h4*>(sp + (2 * col / GS * 4 + qa) * STEP + tq0);
+                const uint32_t ul[2] = {unbias(p01 & 0xff0fff0fu), unbias(p23 & 0xff0fff0fu)};
+                const uint32_t uh[2] = {unbias(p01 & 0xfff0fff0u), unbias(p23 & 0xfff0fff0u)};
+                acc[0] = __builtin_amdgcn_mfma_f32_4x4x4f16(ap, __builtin_bit_cast(h4, ul), acc[0], 0, 0, 0);
+                acc[1] = __builtin_amdgcn_mfma_f32_4x4x4f16(ap, __builtin_bit_cast(h4, uh), acc[1], 0, 0, 0);
+              }
+            }
+          }
+        }
+      } else {
 #pragma unroll
       for (int tq = 0; tq < STEP / 4; ++tq) {
         const unsigned char* vtok = s_stage + T * PK + (lt0 + 4 * tq) * PV + h * VREC;
@@ -719,15 +770,6 @@ __global__ __launch_bounds__(kPThreads, kPMinWaves<D>) void paged_decode_packed_
             const uint32_t u2[2] = {unbias(x01 | kBias2), unbias(x23 | kBias2)};
             acc[i] = __builtin_amdgcn_mfma_f32_4x4x4f16(ap, __builtin_bit_cast(h4, u2), acc[i], 0, 0, 0);
           }
-        } else if constexpr (NV == 1) {
-          // 4-bit codes, 64 dimensions: lane l takes code byte l % 32 of the 4
-          // tokens and its low (l < 32) or high nibble: dimension vdim(0, l)
-          const int bi = lane % 32;
-          const h4 ap = *reinterpret_cast<const h4*>(sp + (bi / (GS / 2) * 4 + qa) * STEP + 4 * tq);
-          uint32_t x01, x23;
-          byte_column<PV>(vtok + bi, x01, x23);
-          const uint32_t u2[2] = {unbias((x01 & nib_mask) | kBias2), unbias((x23 & nib_mask) | kBias2)};
-          acc[0] = __builtin_amdgcn_mfma_f32_4x4x4f16(ap, __builtin_bit_cast(h4, u2), acc[0], 0, 0, 0);
         } else {
           // 4-bit codes: lane l takes code byte l + 64 k of the 4 tokens, whose
           // low nibbles are dimension 2 (l + 64 k) and high nibbles the next
@@ -748,12 +790,22 @@ __global__ __launch_bounds__(kPThreads, kPMinWaves<D>) void paged_decode_packed_
         // registers the scheduler would otherwise spend hoisting them)
         if constexpr (NV >= PAGEDKV_PMFMA_QUAD_BARRIER_NV) __builtin_amdgcn_sched_barrier(0);
       }
+      }
       __builtin_amdgcn_wave_barrier();
     }
   }
 
   // partials: (max, sum) and the group offsets' sums are uniform over score
-  // row r; lane l holds dimension 64 i + l of query head r in register r
+  // row r; lane l holds dimension vdim(i, l) of query head r in register r
+  // (head_dim 64: lanes l and l + 8 of a 16-lane group hold the two token
+  // halves of the same dimensions, added here; the lower lane writes)
+  if constexpr (NV == 1) {
+#pragma unroll
+    for (int i = 0; i < NACC; ++i)
+#pragma unroll
+      for (int r = 0; r < G; ++r) acc[i][r] += __shfl_down(acc[i][r], 8, 16);
+  }
+  const bool writer = NV > 1 || lane % 16 < 8;
   const float l_tot = group_sum<kSub>(l_run);
   float btot[NMG];
 #pragma unroll
@@ -767,7 +819,7 @@ __global__ __launch_bounds__(kPThreads, kPMinWaves<D>) void paged_decode_packed_
     for (int g = 0; g < NMG; ++g)
       bq[g] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, btot[g]), kSub * r));
 #pragma unroll
-    for (int i = 0; i < NV; ++i) {
+    for (int i = 0; i < NACC; ++i) {
       const int d = vdim<VB, NV>(i, lane);
       float bsel = 0.f;
       int ksel = kVk0;
@@ -776,7 +828,7 @@ __global__ __launch_bounds__(kPThreads, kPMinWaves<D>) void paged_decode_packed_
         bsel = d / GS == g ? bq[g] : bsel;
         ksel = d / GS == g ? vk[g] : ksel;
       }
-      part_acc[d] = fmaf(acc[i][r], vacc_scale<VB, NV>(i, lane, ksel), bsel);
+      if (writer) part_acc[d] = fmaf(acc[i][r], vacc_scale<VB, NV>(i, lane, ksel), bsel);
     }
     if (lane == kSub * r) {
       a.partials[a.ml_offset + hs * 2] = m_run;

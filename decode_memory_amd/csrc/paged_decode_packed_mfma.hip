@@ -80,10 +80,11 @@ namespace {
 #ifndef PAGEDKV_PMFMA_STEP_TOKENS
 #define PAGEDKV_PMFMA_STEP_TOKENS 32
 #endif
-// Token quads of the value products are scheduled one at a time (a
-// scheduling barrier after each) from this many value accumulators up.
-#ifndef PAGEDKV_PMFMA_QUAD_BARRIER_NV
-#define PAGEDKV_PMFMA_QUAD_BARRIER_NV 1
+// The value products of one transpose load are scheduled together (a
+// scheduling barrier after each load's products) from this many loads per
+// 16 tokens up.
+#ifndef PAGEDKV_PMFMA_TR_BARRIER_NRD
+#define PAGEDKV_PMFMA_TR_BARRIER_NRD 4
 #endif
 
 constexpr int kPWaves = 8;  // one wave per kv head; packed pools have 8
@@ -95,7 +96,6 @@ constexpr int kSub = 16;    // tokens per MFMA sub-tile
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 typedef _Float16 h4 __attribute__((ext_vector_type(4)));
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
-typedef unsigned short us2 __attribute__((ext_vector_type(2)));
 typedef float f4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(1))) u32x4 gu32x4;
@@ -141,21 +141,11 @@ __device__ __forceinline__ uint32_t bytes_biased(uint32_t w, uint32_t sel) {
 }
 constexpr uint32_t kSelB01 = 0x04010400u;  // bytes 0, 1 -> (lo, hi) halves
 constexpr uint32_t kSelB23 = 0x04030402u;  // bytes 2, 3
-constexpr uint32_t kBias2 = 0x64006400u;   // f16 pair (1024, 1024)
 
 // An f16 pair (1024 + x, 1024 + y) less 1024 each, exactly.
 __device__ __forceinline__ uint32_t unbias(uint32_t v) {
   const h2 x = __builtin_bit_cast(h2, v) - h2{static_cast<_Float16>(1024.f), static_cast<_Float16>(1024.f)};
   return __builtin_bit_cast(uint32_t, x);
-}
-
-// Byte c of the 4 token rows at p, PITCH apart, as two 16-bit pairs
-// (token 0 | token 1 << 16, token 2 | token 3 << 16).
-template <int PITCH>
-__device__ __forceinline__ void byte_column(const unsigned char* p, uint32_t& x01, uint32_t& x23) {
-  const us2 a{p[0], p[PITCH]}, b{p[2 * PITCH], p[3 * PITCH]};
-  x01 = __builtin_bit_cast(uint32_t, a);
-  x23 = __builtin_bit_cast(uint32_t, b);
 }
 
 // B operand of a score product: 8 codes of one token and group as biased
@@ -193,33 +183,27 @@ __device__ __forceinline__ float key_q_factor(int v) {
   return (KB == 4 && (v & 1)) ? 0.0625f : 1.f;
 }
 
-// Value accumulators per lane: one per 64 dimensions, two at head_dim 64.
-template <int NV>
-constexpr int kNAcc = NV == 1 ? 2 : NV;
-// Head_dim 64 reads the value code bytes with LDS transpose loads
-// (ds_read_b64_tr_b8): within each 16-lane group, lane i receives byte
-// column i % 8 of the 8 rows named by lanes 2m + (i % 16) / 8, m = 0..7.  With
-// lanes naming tokens as below, lane l holds byte column tr_col(l) of 8
-// consecutive tokens, and lanes l and l + 8 of a group hold the two halves of
-// 16 tokens (their sums are added at the end).
+// The value code bytes are read with LDS transpose loads (ds_read_b64_tr_b8):
+// within each 16-lane group, lane i receives byte column i % 8 of the 8 rows
+// named by lanes 2m + (i % 16) / 8, m = 0..7.  With lanes naming tokens as
+// below, one load gives lane l byte column tr_col(l) (of 32) of 8 consecutive
+// tokens, and lanes l and l + 8 of a group hold the two halves of 16 tokens
+// (their sums are added at the end).  A value takes D * VB / 256 such loads
+// per 16 tokens (32 code bytes each) and D / 32 accumulators per lane.
 __device__ __forceinline__ int tr_col(int lane) { return 8 * (lane / 16) + lane % 8; }
 __device__ __forceinline__ int tr_token(int lane) { return (lane % 16) / 2 + 8 * (lane % 2); }
-// Value dimension that accumulator i of lane l holds.  Head_dim 64: 8-bit
-// codes, tr_col(l) + 32 i; 4-bit codes, nibble i of byte tr_col(l), that is
-// 2 tr_col(l) + i.  Otherwise 8-bit codes: 64 i + l; 4-bit codes: lanes take
-// code bytes l + 64 (i / 2), whose two nibbles are dimensions 2 byte and 2
-// byte + 1 (nibble i % 2).
-template <int VB, int NV>
+// Value dimension that accumulator i of lane l holds: 8-bit codes, byte
+// tr_col(l) of load i, dimension 32 i + tr_col(l); 4-bit codes, nibble i % 2
+// of byte tr_col(l) of load i / 2, dimension 64 (i / 2) + 2 tr_col(l) + i % 2.
+template <int VB>
 __device__ __forceinline__ int vdim(int i, int lane) {
-  if constexpr (NV == 1) return VB == 8 ? tr_col(lane) + 32 * i : 2 * tr_col(lane) + i;
-  else if constexpr (VB == 8) return 64 * i + lane;
-  else return 2 * (lane + 64 * (i / 2)) + (i % 2);
+  return VB == 8 ? 32 * i + tr_col(lane) : 64 * (i / 2) + 2 * tr_col(lane) + i % 2;
 }
 // Scale that brings accumulator i of lane l back to sum_t p_t s_t c_t: the
 // prescale 2^vk of p * scale, and 16 more for a 4-bit high nibble taken in
 // place (exact powers of two).
-template <int VB, int NV>
-__device__ __forceinline__ float vacc_scale(int i, int lane, int vk) {
+template <int VB>
+__device__ __forceinline__ float vacc_scale(int i, int vk) {
   const bool high = VB == 4 && (i % 2) == 1;
   return __builtin_bit_cast(float, static_cast<uint32_t>(127 - vk - (high ? 4 : 0)) << 23);
 }
@@ -265,8 +249,8 @@ __global__ __launch_bounds__(kPThreads, kPMinWaves<D>) void paged_decode_packed_
   constexpr int NKB = S::NKB, NMG = S::NMG, KPG = S::KPG, T = S::T, PK = S::PK, PV = S::PV;
   constexpr int NSUB = S::NSUB, STEP = S::STEP;
   constexpr int KREC = S::KREC, VREC = S::VREC, KROW = S::KROW, VROW = S::VROW;
-  constexpr int NV = D / 64;  // 64-dimension blocks of a value
-  constexpr int NACC = kNAcc<NV>;
+  constexpr int NACC = D / 32;      // value accumulators per lane
+  constexpr int NRD = D * VB / 256;  // transpose loads per 16 tokens of a value
   // floats per wave: the q' transform, then p^T as f16 [group][4][STEP]
   constexpr int AUX = (G * D > NMG * 2 * STEP) ? G * D : NMG * 2 * STEP;
   static_assert(G <= 4, "query heads of a kv head take rows 0, 4, 8, 12");
@@ -550,7 +534,7 @@ __global__ __launch_bounds__(kPThreads, kPMinWaves<D>) void paged_decode_packed_
         const float ratio = exp2i(knew - vk[g]);
 #pragma unroll
         for (int i = 0; i < NACC; ++i) {
-          const float f = vdim<VB, NV>(i, lane) / GS == g ? ratio : 1.f;
+          const float f = vdim<VB>(i, lane) / GS == g ? ratio : 1.f;
           acc[i] *= f;
         }
         vk[g] = knew;
@@ -724,17 +708,17 @@ __global__ __launch_bounds__(kPThreads, kPMinWaves<D>) void paged_decode_packed_
       // head lane % 4 (rows of absent query heads hold zeros); the B/C column
       // of lane l is dimension vdim(i, l)
       const int qa = lane % 4;
-      if constexpr (NV == 1) {
-        // head_dim 64: one transpose load per 16 tokens and 32 code bytes
-        // gives lane l byte column tr_col(l) of the 8 tokens t8 .. t8 + 7;
-        // each dword of it (4 tokens) feeds the products of its dimensions
+      {
+        // one transpose load per 16 tokens and 32 code bytes gives lane l byte
+        // column tr_col(l) of the 8 tokens t8 .. t8 + 7; each dword of it (4
+        // tokens) feeds the products of its dimensions
         const int col = tr_col(lane);
         const int t8 = 8 * ((lane % 16) / 8);
         const unsigned char* vcol = s_stage + T * PK + (lt0 + tr_token(lane)) * PV + h * VREC + 8 * (lane / 16);
 #pragma unroll
         for (int u = 0; u < NSUB; ++u) {
 #pragma unroll
-          for (int rd = 0; rd < VB / 4; ++rd) {  // 8-bit codes: bytes 0-31, then 32-63
+          for (int rd = 0; rd < NRD; ++rd) {
             const uint2 w = lds_read_tr8(vcol + u * kSub * PV + 32 * rd);
 #pragma unroll
             for (int dw = 0; dw < 2; ++dw) {
@@ -742,54 +726,24 @@ __global__ __launch_bounds__(kPThreads, kPMinWaves<D>) void paged_decode_packed_
               const int tq0 = u * kSub + t8 + 4 * dw;  // the dword's first token in the step
               const uint32_t p01 = bytes_biased(x, kSelB01), p23 = bytes_biased(x, kSelB23);
               if constexpr (VB == 8) {
-                const h4 ap = *reinterpret_cast<const h4*>(sp + ((col + 32 * rd) / GS * 4 + qa) * STEP + tq0);
+                const h4 ap = *reinterpret_cast<const h4*>(sp + ((32 * rd + col) / GS * 4 + qa) * STEP + tq0);
                 const uint32_t u2[2] = {unbias(p01), unbias(p23)};
                 acc[rd] = __builtin_amdgcn_mfma_f32_4x4x4f16(ap, __builtin_bit_cast(h4, u2), acc[rd], 0, 0, 0);
               } else {
                 // low nibbles as 1024 + code, high nibbles in place as 1024 + 16 code
-                const h4 ap = *reinterpret_cast<const h4*>(sp + (2 * col / GS * 4 + qa) * STEP + tq0);
+                const h4 ap = *reinterpret_cast<const h4*>(sp + ((64 * rd + 2 * col) / GS * 4 + qa) * STEP + tq0);
                 const uint32_t ul[2] = {unbias(p01 & 0xff0fff0fu), unbias(p23 & 0xff0fff0fu)};
                 const uint32_t uh[2] = {unbias(p01 & 0xfff0fff0u), unbias(p23 & 0xfff0fff0u)};
-                acc[0] = __builtin_amdgcn_mfma_f32_4x4x4f16(ap, __builtin_bit_cast(h4, ul), acc[0], 0, 0, 0);
-                acc[1] = __builtin_amdgcn_mfma_f32_4x4x4f16(ap, __builtin_bit_cast(h4, uh), acc[1], 0, 0, 0);
+                acc[2 * rd] = __builtin_amdgcn_mfma_f32_4x4x4f16(ap, __builtin_bit_cast(h4, ul), acc[2 * rd], 0, 0, 0);
+                acc[2 * rd + 1] =
+                    __builtin_amdgcn_mfma_f32_4x4x4f16(ap, __builtin_bit_cast(h4, uh), acc[2 * rd + 1], 0, 0, 0);
               }
             }
+            // keep each load next to its products (bounds the registers the
+            // scheduler would otherwise spend hoisting loads)
+            if constexpr (NRD >= PAGEDKV_PMFMA_TR_BARRIER_NRD) __builtin_amdgcn_sched_barrier(0);
           }
         }
-      } else {
-#pragma unroll
-      for (int tq = 0; tq < STEP / 4; ++tq) {
-        const unsigned char* vtok = s_stage + T * PK + (lt0 + 4 * tq) * PV + h * VREC;
-        if constexpr (VB == 8) {
-#pragma unroll
-          for (int i = 0; i < NV; ++i) {
-            const int d = 64 * i + lane;
-            const h4 ap = *reinterpret_cast<const h4*>(sp + (d / GS * 4 + qa) * STEP + 4 * tq);
-            uint32_t x01, x23;
-            byte_column<PV>(vtok + d, x01, x23);
-            const uint32_t u2[2] = {unbias(x01 | kBias2), unbias(x23 | kBias2)};
-            acc[i] = __builtin_amdgcn_mfma_f32_4x4x4f16(ap, __builtin_bit_cast(h4, u2), acc[i], 0, 0, 0);
-          }
-        } else {
-          // 4-bit codes: lane l takes code byte l + 64 k of the 4 tokens, whose
-          // low nibbles are dimension 2 (l + 64 k) and high nibbles the next
-          // one -- two products (accumulators 2k, 2k + 1), one A operand
-#pragma unroll
-          for (int k = 0; k < NV / 2; ++k) {
-            const int bi = lane + 64 * k;
-            const h4 ap = *reinterpret_cast<const h4*>(sp + (bi / (GS / 2) * 4 + qa) * STEP + 4 * tq);
-            uint32_t x01, x23;
-            byte_column<PV>(vtok + bi, x01, x23);
-            const uint32_t ul[2] = {unbias((x01 & 0x000f000fu) | kBias2), unbias((x23 & 0x000f000fu) | kBias2)};
-            const uint32_t uh[2] = {unbias((x01 & 0x00f000f0u) | kBias2), unbias((x23 & 0x00f000f0u) | kBias2)};
-            acc[2 * k] = __builtin_amdgcn_mfma_f32_4x4x4f16(ap, __builtin_bit_cast(h4, ul), acc[2 * k], 0, 0, 0);
-            acc[2 * k + 1] = __builtin_amdgcn_mfma_f32_4x4x4f16(ap, __builtin_bit_cast(h4, uh), acc[2 * k + 1], 0, 0, 0);
-          }
-        }
-        // keep each token quad's loads next to their products (bounds the
-        // registers the scheduler would otherwise spend hoisting them)
-        if constexpr (NV >= PAGEDKV_PMFMA_QUAD_BARRIER_NV) __builtin_amdgcn_sched_barrier(0);
-      }
       }
       __builtin_amdgcn_wave_barrier();
     }
@@ -797,15 +751,13 @@ __global__ __launch_bounds__(kPThreads, kPMinWaves<D>) void paged_decode_packed_
 
   // partials: (max, sum) and the group offsets' sums are uniform over score
   // row r; lane l holds dimension vdim(i, l) of query head r in register r
-  // (head_dim 64: lanes l and l + 8 of a 16-lane group hold the two token
-  // halves of the same dimensions, added here; the lower lane writes)
-  if constexpr (NV == 1) {
+  // (lanes l and l + 8 of a 16-lane group hold the two token halves of the
+  // same dimensions, added here; the lower lane writes)
 #pragma unroll
-    for (int i = 0; i < NACC; ++i)
+  for (int i = 0; i < NACC; ++i)
 #pragma unroll
-      for (int r = 0; r < G; ++r) acc[i][r] += __shfl_down(acc[i][r], 8, 16);
-  }
-  const bool writer = NV > 1 || lane % 16 < 8;
+    for (int r = 0; r < G; ++r) acc[i][r] += __shfl_down(acc[i][r], 8, 16);
+  const bool writer = lane % 16 < 8;
   const float l_tot = group_sum<kSub>(l_run);
   float btot[NMG];
 #pragma unroll
@@ -820,7 +772,7 @@ __global__ __launch_bounds__(kPThreads, kPMinWaves<D>) void paged_decode_packed_
       bq[g] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, btot[g]), kSub * r));
 #pragma unroll
     for (int i = 0; i < NACC; ++i) {
-      const int d = vdim<VB, NV>(i, lane);
+      const int d = vdim<VB>(i, lane);
       float bsel = 0.f;
       int ksel = kVk0;
 #pragma unroll
@@ -828,7 +780,7 @@ __global__ __launch_bounds__(kPThreads, kPMinWaves<D>) void paged_decode_packed_
         bsel = d / GS == g ? bq[g] : bsel;
         ksel = d / GS == g ? vk[g] : ksel;
       }
-      if (writer) part_acc[d] = fmaf(acc[i][r], vacc_scale<VB, NV>(i, lane, ksel), bsel);
+      if (writer) part_acc[d] = fmaf(acc[i][r], vacc_scale<VB>(i, ksel), bsel);
     }
     if (lane == kSub * r) {
       a.partials[a.ml_offset + hs * 2] = m_run;

@@ -40,14 +40,14 @@
 //     the score of (query head j, token n) lands in lane n + 16 j, so the
 //     online softmax runs on every lane and its reductions over tokens are
 //     16-lane DPP row operations;
-//   values: p * scale * 1024 goes through a small per-wave LDS area into the
-//     A operand of 4x4x4 products (16 independent blocks per instruction:
-//     4 query heads x 4 tokens times 4 tokens x 4 dimensions), so lane l
-//     accumulates one value dimension of every query head in its four
-//     registers per 64 dimensions; the B operand is that dimension of 4
-//     tokens, read byte by byte from the staged rows (4-bit codes: one byte
-//     feeds the two dimensions of its nibbles); the offsets add
-//     sum_t p_t offset_t per group.
+//   values: p * scale * 2^vk goes through a small per-wave LDS area into
+//     the A operand of 4x4x4 products (16 independent blocks per
+//     instruction: 4 query heads x 4 tokens times 4 tokens x 4 dimensions),
+//     so a lane accumulates value dimensions of every query head in the four
+//     registers of each accumulator; the B operand is one code byte column
+//     of 4 tokens, which LDS transpose loads (ds_read_b64_tr_b8) deliver 8
+//     tokens at a time (4-bit codes: one byte feeds the two dimensions of
+//     its nibbles); the offsets add sum_t p_t offset_t per group.
 // Codes become f16 exactly: a byte placed under the exponent bits 0x64 is
 // 1024 + byte.  Key products take these biased codes as they are and drop
 // 1024 * sum(q') per group afterwards; value codes get one packed f16 add of

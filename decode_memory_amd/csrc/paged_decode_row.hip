@@ -21,9 +21,10 @@
 // output columns per query head) stays in the lane group: the only
 // cross-lane operation per token is the DPP reduction that finishes each dot
 // product.  Each wave keeps PAGEDKV_ROW_TILES_IN_FLIGHT tiles of K/V loads in
-// flight (tile i + 2 is requested before tile i is consumed); with one
-// 8-wave workgroup per CU that is 128-192 KiB of reads outstanding per CU,
-// several times what HBM3E needs to run at its streaming rate.
+// flight (tile i + 1 is requested before tile i is consumed); with one
+// 8-wave workgroup per CU that is 64-128 KiB of reads outstanding per CU.
+// Deeper queues measured slower: with every CU streaming at once, more
+// requests in flight only add contention.
 //
 // A block's address costs one dependent global read: the layer's slab
 // pointer tables are staged in LDS while the block-table reads are in
@@ -40,7 +41,7 @@ namespace pagedkv {
 namespace {
 
 #ifndef PAGEDKV_ROW_TILES_IN_FLIGHT
-#define PAGEDKV_ROW_TILES_IN_FLIGHT 3
+#define PAGEDKV_ROW_TILES_IN_FLIGHT 2
 #endif
 #ifndef PAGEDKV_ROW_WAVES
 #define PAGEDKV_ROW_WAVES 8
@@ -52,10 +53,13 @@ namespace {
 #ifndef PAGEDKV_ROW_WAVES_PER_SIMD
 #define PAGEDKV_ROW_WAVES_PER_SIMD 2
 #endif
+#ifndef PAGEDKV_ROW_TILE_TOKENS
+#define PAGEDKV_ROW_TILE_TOKENS 4
+#endif
 
 constexpr int kRowWaves = PAGEDKV_ROW_WAVES;  // waves per workgroup
 constexpr int kRowThreads = kRowWaves * kWave;
-constexpr int kTile = 4;                     // tokens per wave per tile
+constexpr int kTile = PAGEDKV_ROW_TILE_TOKENS;  // tokens per wave per tile
 constexpr int kBuf = PAGEDKV_ROW_TILES_IN_FLIGHT;  // tiles a wave keeps in flight
 constexpr int kBS = 32;                      // tokens per block
 constexpr int kLdsSlabs = 2 * kRowThreads;   // slab pointers staged in LDS
@@ -238,15 +242,22 @@ __global__ __launch_bounds__(kRowThreads, PAGEDKV_ROW_WAVES_PER_SIMD) void paged
   // [0, kTile) with k = i % NT -- at any moment the slices of a head group
   // read one contiguous run of tokens.  Tokens past the visible length are
   // clamped to the last visible token (in bounds) and masked.
+  // A tile past the last one (i >= n_tiles) is still requested -- see the
+  // pipeline below -- but every lane reads the same 16 bytes at the start of
+  // the query (valid memory of at least 128 bytes); its registers are never
+  // used.
+  const char* const dummy = static_cast<const char*>(a.q);
   auto load_tile = [&](Tile& t, int i) {
-    const int j = i / NT, k = i % NT;
-    const char* kb = lane_ptr(kaddr, j);
-    const char* vb = lane_ptr(vaddr, j);
+    const bool live = i < n_tiles;  // uniform over the wave
+    const int ic = live ? i : 0;
+    const int j = ic / NT, k = ic % NT;
+    const char* kb = live ? lane_ptr(kaddr, j) : dummy;
+    const char* vb = live ? lane_ptr(vaddr, j) : dummy;
     const int nt = min(kBS, len - (s + j * n_split) * kBS);
     const int t0 = (k * SLICES + slice) * kTile;
 #pragma unroll
     for (int u = 0; u < kTile; ++u) {
-      const uint32_t off = lane_off + min(t0 + u, nt - 1) * tok_bytes;
+      const uint32_t off = live ? lane_off + min(t0 + u, nt - 1) * tok_bytes : 0u;
       t.k[u] = gload16(kb, off);
       t.v[u] = gload16(vb, off);
     }
@@ -294,20 +305,28 @@ __global__ __launch_bounds__(kRowThreads, PAGEDKV_ROW_WAVES_PER_SIMD) void paged
     }
   };
 
-  // kBuf tiles in flight: tile i + kBuf - 1 is requested before tile i is
-  // consumed (the buffer index is static after unrolling by kBuf).
-  Tile buf[kBuf];
+  // NB tiles in flight: tile i + NB - 1 is requested before tile i is
+  // consumed (the buffer index is static after unrolling by NB); eight
+  // query heads per kv head keep at most two, their state leaves no room
+  // for three.
+  //
+  // No load sits behind a branch.  The compiler places its wait for a
+  // loaded register from the loads it knows were issued after it, taking the
+  // fewest over every path into the wait; a branch around the loads of the
+  // last tiles would make every wait assume the later tiles were never
+  // requested and drain the loads in flight down to one tile.  So the
+  // prologue and every pass request a tile (the ones past the end read the
+  // dummy word above) and only the arithmetic is conditional.
+  constexpr int NB = G >= 8 && kBuf > 2 ? 2 : kBuf;
+  Tile buf[NB];
 #pragma unroll
-  for (int r = 0; r < kBuf - 1; ++r)
-    if (r < n_tiles) load_tile(buf[r], r);
-  for (int i0 = 0; i0 < n_tiles; i0 += kBuf) {
+  for (int r = 0; r < kBuf - 1; ++r) load_tile(buf[r], r);
+  for (int i0 = 0; i0 < n_tiles; i0 += NB) {
 #pragma unroll
-    for (int r = 0; r < kBuf; ++r) {
+    for (int r = 0; r < NB; ++r) {
       const int i = i0 + r;
-      if (i < n_tiles) {
-        if (i + kBuf - 1 < n_tiles) load_tile(buf[(r + kBuf - 1) % kBuf], i + kBuf - 1);
-        compute_tile(buf[r], i);
-      }
+      load_tile(buf[(r + NB - 1) % NB], i + NB - 1);
+      if (i < n_tiles) compute_tile(buf[r], i);
     }
   }
 
@@ -367,11 +386,17 @@ __global__ __launch_bounds__(kRowThreads, PAGEDKV_ROW_WAVES_PER_SIMD) void paged
 template <int D, int G, bool BF16, int HGW>
 hipError_t launch_row(const DecodeArgs& a, hipStream_t s) {
   constexpr int HG = (kWave / (D / 8)) * HGW;
-  const int total = a.B * (a.lv.n_kv / HG) * a.n_split;
-  const int grid = round_up(total, kXcds);
-  hipLaunchKernelGGL((paged_decode_row_kernel<D, G, BF16, HGW>), dim3(grid), dim3(kRowThreads), 0,
-                     s, a);
-  return hipGetLastError();
+  // the slices of a head group must tile a block exactly
+  constexpr bool kFits = kRowWaves % HGW == 0 && kBS % ((kRowWaves / HGW) * kTile) == 0;
+  if constexpr (!kFits) {
+    return hipErrorInvalidValue;
+  } else {
+    const int total = a.B * (a.lv.n_kv / HG) * a.n_split;
+    const int grid = round_up(total, kXcds);
+    hipLaunchKernelGGL((paged_decode_row_kernel<D, G, BF16, HGW>), dim3(grid), dim3(kRowThreads), 0,
+                       s, a);
+    return hipGetLastError();
+  }
 }
 
 template <int D, bool BF16, int HGW>
@@ -411,7 +436,7 @@ int row_kernel_kpl(int32_t n_kv, int32_t head_dim, int32_t group, int32_t block_
   const int n_groups = n_kv / hpl;
   for (int hgw : {4, 2, 1})  // as many head groups per workgroup as allowed
     if (hgw <= PAGEDKV_ROW_MAX_HEAD_GROUPS && hgw <= kRowWaves && kRowWaves % hgw == 0 &&
-        n_groups % hgw == 0 && (kRowWaves / hgw) * kTile <= kBS)
+        n_groups % hgw == 0 && kBS % ((kRowWaves / hgw) * kTile) == 0)
       return hgw;
   return 0;
 }

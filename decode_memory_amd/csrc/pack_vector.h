@@ -114,12 +114,18 @@ __device__ __forceinline__ float div_levels_rn(float a, float levels, float inv_
 // Quantise the lane's 8 values (values 8c .. 8c+7 of the vector) with the
 // (scale, offset) of their group of GS values, all in fp32: mn = min, mx =
 // max, scale = (mx - mn) / (2^bits - 1), offset = mn, code = clamp(rint((x -
-// mn) / scale)) with round-half-even, and a constant group gets code 0.  When
-// rec is not null the codes (8-bit: one byte per value; 4-bit: value 2i in
-// the low nibble of byte i) and, from the group's first lane, the (scale,
-// offset) pair are stored into the record rec of a D-value vector.
+// mn) / scale)) with round-half-even, and a constant group gets code 0.  The
+// codes are packed as a record holds them (8-bit: one byte per value; 4-bit:
+// value 2i in the low nibble of byte i).
+// The lane's codes packed as they are stored (8-bit: bytes 0-3 in lo, 4-7 in
+// hi; 4-bit: the nibble pairs in lo), and its group's (scale, offset).
+struct Codes8 {
+  uint32_t lo, hi;
+  float scale, offset;
+};
+
 template <int D, int GS>
-__device__ __forceinline__ void quantise_store8(const float (&x)[8], int c, int bits, char* rec) {
+__device__ __forceinline__ Codes8 quantise8(const float (&x)[8], int c, int bits) {
   #pragma clang fp contract(off)
   static_assert(GS == 32 || GS == 64, "groups of 32 or 64 values");
   constexpr int LPG = GS / 8;  // lanes per group
@@ -183,7 +189,6 @@ __device__ __forceinline__ void quantise_store8(const float (&x)[8], int c, int 
     t[e] = rintf(q);
     if (__ballot(!(fabsf(q - t[e]) < thr))) t[e] = fminf(rintf(d / div), levels);
   }
-  if (!rec) return;
   // codes to bytes (each t is an integer in 0 .. 255: the conversion is exact)
   uint32_t lo = 0, hi = 0;
 #pragma unroll
@@ -191,16 +196,32 @@ __device__ __forceinline__ void quantise_store8(const float (&x)[8], int c, int 
     lo = __builtin_amdgcn_cvt_pk_u8_f32(t[e], e, lo);
     hi = __builtin_amdgcn_cvt_pk_u8_f32(t[4 + e], e, hi);
   }
-  if (eight) {
-    store_global(rec + 8 * c, make_uint2(lo, hi));
-  } else {
+  if (!eight) {
     // nibbles: byte 0 of w | w >> 4 is v0 | v1 << 4, byte 2 is v2 | v3 << 4
     const uint32_t lw = lo | (lo >> 4), hw = hi | (hi >> 4);
-    store_global(rec + 4 * c, __builtin_amdgcn_perm(hw, lw, 0x06040200u));
+    lo = __builtin_amdgcn_perm(hw, lw, 0x06040200u);
   }
-  if (c % LPG == 0) {
-    store_global(rec + D * bits / 8 + 8 * (c / LPG), make_float2(scale, mn));
-  }
+  return Codes8{lo, hi, scale, mn};
+}
+
+// Store the lane's codes, and from the group's first lane the (scale, offset)
+// pair, into the record rec of a D-value vector.
+template <int D, int GS>
+__device__ __forceinline__ void store_codes8(const Codes8& q, int c, int bits, char* rec) {
+  constexpr int LPG = GS / 8;  // lanes per group
+  if (bits == 8)
+    store_global(rec + 8 * c, make_uint2(q.lo, q.hi));
+  else
+    store_global(rec + 4 * c, q.lo);
+  if (c % LPG == 0) store_global(rec + D * bits / 8 + 8 * (c / LPG), make_float2(q.scale, q.offset));
+}
+
+// Quantise the lane's 8 values and, when rec is not null, store them (see
+// quantise8 and store_codes8).
+template <int D, int GS>
+__device__ __forceinline__ void quantise_store8(const float (&x)[8], int c, int bits, char* rec) {
+  const Codes8 q = quantise8<D, GS>(x, c, bits);
+  if (rec) store_codes8<D, GS>(q, c, bits, rec);
 }
 
 }  // namespace pagedkv

@@ -242,42 +242,68 @@ __global__ __launch_bounds__(kThreads) void row_move_kernel(RowMoveArgs a) {
 // K or all V: the wave tasks are the K vectors in wave-sized runs, then the V
 // vectors likewise.
 
-// One wave task: the VPW = 64/(D/8) vectors v0 .. v0 + VPW - 1 of K (IS_V
-// false, rotated) or of V.  VPW divides the 8 kv heads and v0 is a multiple
-// of VPW, so the task's vectors are heads of one token: its row, slot and
-// slab are the same in every lane and are resolved once per wave.
-template <int D, int GS, bool IS_V>
-__device__ __forceinline__ void pack_task(const WriteArgs& a, int v0, int lane, int c, const float (&sg)[8],
-                                          const uint32_t (&odd_sign)[4]) {
-  constexpr int LPT = D / 8;
-  const int i = v0 / kPackedKv;                          // the token
-  const int head = v0 % kPackedKv + lane / LPT;
-  // the lane's 16 bytes of the source vector (vector v0 + lane / LPT, values
-  // 8c .. 8c+7) and the token's row and slot go out together
-  const uint4 u = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(IS_V ? a.v_src : a.k_src) +
-                                                  static_cast<size_t>(v0) * D + 8 * lane);
-  const int32_t row = __builtin_amdgcn_readfirstlane(a.rows[i]);
-  const int32_t slot = __builtin_amdgcn_readfirstlane(a.slots[i]);
-  // the record's address (one dependent read: its slab's base) before the
-  // arithmetic, so that read is in flight meanwhile
-  char* rec = nullptr;
-  if (valid_target(a.lv, row, slot, lane == 0 && !IS_V && v0 % kPackedKv == 0)) {
-    // row / slab_blocks as one high multiply when the host found it exact
-    const int slab =
-        a.m_slab ? static_cast<int>(div_by(static_cast<uint32_t>(row), a.m_slab)) : row / a.lv.slab_blocks;
-    const size_t tok = static_cast<size_t>(row - slab * a.lv.slab_blocks) * a.lv.block_size + slot;
-    const int rec_bytes = IS_V ? a.lv.v_rec : a.lv.k_rec;
-    rec = static_cast<char*>(const_cast<void*>(IS_V ? a.lv.v_tab[slab] : a.lv.k_tab[slab])) +
-          tok * kPackedKv * rec_bytes + head * rec_bytes;
-  }
-  float x[8];  // a token that is not written is still quantised, and not stored
-  if constexpr (IS_V)
-    widen8<true>(u, x);
-  else
-    widen_rotate8<D>(u, odd_sign, sg, c, a.inv_sqrt_d, x);  // every lane takes part
-  quantise_store8<D, GS>(x, c, IS_V ? a.v_bits : a.k_bits, rec);
+// One wave task: the VPW = 64/(D/8) vectors v0 .. v0 + VPW - 1 of K (task t <
+// tasks, rotated) or of V (t - tasks).  VPW divides the 8 kv heads and v0 is
+// a multiple of VPW, so the task's vectors are heads of one token: its row,
+// slot and slab are the same in every lane and are resolved once per wave.
+struct PackIn {
+  uint4 u;       // the lane's 16 bytes of the source vector (values 8c .. 8c+7)
+  int32_t row, slot;
+  int v0;        // first vector of the task (K or V numbering)
+  bool is_v;
+};
+
+template <int D>
+__device__ __forceinline__ PackIn pack_load(const WriteArgs& a, int t, int tasks, int lane) {
+  constexpr int VPW = kWave / (D / 8);
+  PackIn in;
+  in.is_v = t >= tasks;
+  in.v0 = (in.is_v ? t - tasks : t) * VPW;
+  const uint16_t* src = static_cast<const uint16_t*>(in.is_v ? a.v_src : a.k_src);
+  in.u = *reinterpret_cast<const uint4*>(src + static_cast<size_t>(in.v0) * D + 8 * lane);
+  const int i = in.v0 / kPackedKv;  // the token
+  in.row = __builtin_amdgcn_readfirstlane(a.rows[i]);
+  in.slot = __builtin_amdgcn_readfirstlane(a.slots[i]);
+  return in;
 }
 
+// The record of the lane's vector.  A token whose (row, slot) is outside the
+// pool gets ok = false and the record address of row 0, slot 0 (its slab
+// base is still read, so no load depends on the check).
+template <int D>
+__device__ __forceinline__ char* pack_record(const WriteArgs& a, const PackIn& in, int lane, bool& ok) {
+  constexpr int LPT = D / 8;
+  ok = in.row >= 0 && in.row < a.lv.capacity_rows && in.slot >= 0 && in.slot < a.lv.block_size;
+  const int32_t row = ok ? in.row : 0, slot = ok ? in.slot : 0;
+  // row / slab_blocks as one high multiply when the host found it exact
+  const int slab =
+      a.m_slab ? static_cast<int>(div_by(static_cast<uint32_t>(row), a.m_slab)) : row / a.lv.slab_blocks;
+  const size_t tok = static_cast<size_t>(row - slab * a.lv.slab_blocks) * a.lv.block_size + slot;
+  const int rec_bytes = in.is_v ? a.lv.v_rec : a.lv.k_rec;
+  const int head = in.v0 % kPackedKv + lane / LPT;
+  const void* const* tab = in.is_v ? a.lv.v_tab : a.lv.k_tab;
+  return static_cast<char*>(const_cast<void*>(tab[slab])) + tok * kPackedKv * rec_bytes + head * rec_bytes;
+}
+
+template <int D, int GS>
+__device__ __forceinline__ Codes8 pack_codes(const WriteArgs& a, const PackIn& in, int c, const float (&sg)[8],
+                                             const uint32_t (&odd_sign)[4]) {
+  float x[8];  // a token that is not written is still quantised, and not stored
+  if (in.is_v) {
+    widen8<true>(in.u, x);
+    return quantise8<D, GS>(x, c, a.v_bits);
+  }
+  widen_rotate8<D>(in.u, odd_sign, sg, c, a.inv_sqrt_d, x);  // every lane takes part
+  return quantise8<D, GS>(x, c, a.k_bits);
+}
+
+// A wave takes two consecutive tasks per pass, and every load of both (the
+// sources, rows and slots, then the slab bases) goes out before the first
+// task's arithmetic: one task's loads alone leave too few bytes in flight per
+// CU to cover the memory latency.  The stores of both come last.  The second
+// load of the last pass of an odd task count repeats the first and stores
+// nothing.  No load sits behind a branch, so the compiler's waits for the
+// loaded registers count the loads issued after them exactly.
 template <int D, int GS>
 __global__ __launch_bounds__(kThreads) void write_block_packed_kernel(WriteArgs a) {
   constexpr int LPT = D / 8;        // lanes per vector
@@ -286,6 +312,7 @@ __global__ __launch_bounds__(kThreads) void write_block_packed_kernel(WriteArgs 
   const int c = lane % LPT;         // values 8c .. 8c+7 of the vector
   const int n_vec = a.n * kPackedKv;  // K vectors; as many V vectors
   const int tasks = (n_vec + VPW - 1) / VPW;
+  const int total = 2 * tasks;
   const int waves = gridDim.x * (kThreads / kWave);
   float sg[8];  // the signs of values 8c .. 8c+7 (the same for every vector)
   {
@@ -299,11 +326,20 @@ __global__ __launch_bounds__(kThreads) void write_block_packed_kernel(WriteArgs 
   for (int i = 0; i < 4; ++i) odd_sign[i] = __float_as_uint(sg[2 * i + 1]) & 0x80000000u;
   const int wave = __builtin_amdgcn_readfirstlane(blockIdx.x * (kThreads / kWave) + threadIdx.x / kWave);
   static_assert(kPackedKv % VPW == 0, "a wave task covers heads of one token");
-  for (int t = wave; t < 2 * tasks; t += waves) {
-    if (t < tasks)
-      pack_task<D, GS, false>(a, t * VPW, lane, c, sg, odd_sign);
-    else
-      pack_task<D, GS, true>(a, (t - tasks) * VPW, lane, c, sg, odd_sign);
+  for (int t = 2 * wave; t < total; t += 2 * waves) {
+    const bool has_b = t + 1 < total;  // uniform over the wave
+    const PackIn ia = pack_load<D>(a, t, tasks, lane);
+    const PackIn ib = pack_load<D>(a, has_b ? t + 1 : t, tasks, lane);
+    bool oka, okb;
+    char* const ra = pack_record<D>(a, ia, lane, oka);
+    char* const rb = pack_record<D>(a, ib, lane, okb);
+    const Codes8 qa = pack_codes<D, GS>(a, ia, c, sg, odd_sign);
+    const Codes8 qb = pack_codes<D, GS>(a, ib, c, sg, odd_sign);
+    if (oka) store_codes8<D, GS>(qa, c, ia.is_v ? a.v_bits : a.k_bits, ra);
+    if (has_b && okb) store_codes8<D, GS>(qb, c, ib.is_v ? a.v_bits : a.k_bits, rb);
+    // a token outside the pool is reported once, by the wave holding its first K vectors
+    if (!oka && lane == 0 && !ia.is_v && ia.v0 % kPackedKv == 0) valid_target(a.lv, ia.row, ia.slot, true);
+    if (has_b && !okb && lane == 0 && !ib.is_v && ib.v0 % kPackedKv == 0) valid_target(a.lv, ib.row, ib.slot, true);
   }
 }
 
@@ -391,7 +427,8 @@ hipError_t launch_write_block(const WriteArgs& a, int32_t format, hipStream_t s)
     return hipGetLastError();
   }
   if (a.lv.n_kv != kPackedKv) return hipErrorInvalidValue;  // packed pools hold 8 kv heads
-  const long long waves = (2LL * a.n * a.lv.n_kv * (a.head_dim / 8) + kWave - 1) / kWave;
+  // one wave per two tasks (a task is one wave-wide pass over 64 lanes' values)
+  const long long waves = ((2LL * a.n * a.lv.n_kv * (a.head_dim / 8) + kWave - 1) / kWave + 1) / 2;
   long long grid = (waves + kThreads / kWave - 1) / (kThreads / kWave);
   if (grid > 16384) grid = 16384;  // a few wave tasks per wave: its set-up is shared
   const int key = a.head_dim * 100 + a.qgroup;

@@ -28,11 +28,11 @@
 //
 // A block's address costs one dependent global read: the layer's slab
 // pointer tables are staged in LDS while the block-table reads are in
-// flight.  At the end each wave stages its state in LDS and the last wave of
-// each head group to finish merges the group's slices in slice order (so the
-// result does not depend on which wave that is) and writes one partial (max,
-// sum, weighted V) per query head and split; a combine kernel merges the
-// splits.
+// flight.  At the end each wave stages its state in LDS and, after one
+// workgroup barrier, the waves of each head group merge the group's slices
+// together, each wave a share of the columns, in slice order, and write one
+// partial (max, sum, weighted V) per query head and split; a combine kernel
+// merges the splits.
 #include "device_common.h"
 #include "internal.h"
 
@@ -101,7 +101,6 @@ __global__ __launch_bounds__(kRowThreads, PAGEDKV_ROW_WAVES_PER_SIMD) void paged
   __shared__ float s_acc[kRowWaves][HPL * G][D];
   __shared__ uint64_t s_kt[kLdsSlabs];  // slab base pointers of the layer
   __shared__ uint64_t s_vt[kLdsSlabs];
-  __shared__ int s_done[HGW];           // waves of each head group that finished
 
   const int lane = threadIdx.x % kWave;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -169,7 +168,6 @@ __global__ __launch_bounds__(kRowThreads, PAGEDKV_ROW_WAVES_PER_SIMD) void paged
       s_kt[t1] = k1;
       s_vt[t1] = v1;
     }
-    if (threadIdx.x < HGW) s_done[threadIdx.x] = 0;
   }
   __syncthreads();
   uint64_t kaddr = 0, vaddr = 0;
@@ -279,16 +277,19 @@ __global__ __launch_bounds__(kRowThreads, PAGEDKV_ROW_WAVES_PER_SIMD) void paged
       float mx = sc[0];
 #pragma unroll
       for (int u = 1; u < kTile; ++u) mx = fmaxf(mx, sc[u]);
-      // running max; while nothing is visible it stays -inf and every weight is 0
+      // Running max.  While nothing is visible it stays -inf; the exponents
+      // are then taken against 0 instead, so every weight (and alpha, with l
+      // and acc still 0) is exp2(-inf) = 0 with no test per token.
       const float m_new = fmaxf(m[jq], mx);
-      const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m[jq] - m_new);
+      const float m_ref = (m_new == -INFINITY) ? 0.f : m_new;
+      const float alpha = __builtin_amdgcn_exp2f(m[jq] - m_ref);
       m[jq] = m_new;
       l[jq] *= alpha;
 #pragma unroll
       for (int e = 0; e < 8; ++e) acc[jq][e] *= alpha;
 #pragma unroll
       for (int u = 0; u < kTile; ++u) {
-        p[jq][u] = (sc[u] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(sc[u] - m_new);
+        p[jq][u] = __builtin_amdgcn_exp2f(sc[u] - m_ref);
         l[jq] += p[jq][u];
       }
     }
@@ -331,10 +332,11 @@ __global__ __launch_bounds__(kRowThreads, PAGEDKV_ROW_WAVES_PER_SIMD) void paged
   }
 
   // Stage each wave's state in LDS (lane c of group lg holds columns
-  // c*8..c*8+7 of its kv head's query heads).  The last wave of a head group
-  // to get here merges the group's slices in slice order -- the result does
-  // not depend on which wave that is -- and writes the partial; the others
-  // are done.
+  // c*8..c*8+7 of its kv head's query heads), then the waves of each head
+  // group merge its slices together: slice sl's wave takes columns [sl W,
+  // (sl + 1) W) of every query head of the group, W = D / SLICES, EPL
+  // consecutive columns per lane, and merges the slices in slice order, so
+  // the result does not depend on which wave finished last.
 #pragma unroll
   for (int jq = 0; jq < G; ++jq) {
     const int hq = lg * G + jq;
@@ -345,41 +347,43 @@ __global__ __launch_bounds__(kRowThreads, PAGEDKV_ROW_WAVES_PER_SIMD) void paged
       s_l[wave][hq] = l[jq];
     }
   }
-  int arrived = 0;
-  if (lane == 0)
-    arrived = __hip_atomic_fetch_add(&s_done[hgw], 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_WORKGROUP);
-  arrived = __builtin_amdgcn_readfirstlane(arrived);
-  if (arrived != SLICES - 1) return;
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+  __syncthreads();
 
-  float* part_acc = a.partials;
-  float* part_ml = a.partials + a.ml_offset;
+  constexpr int W = D / SLICES;        // columns per wave
+  constexpr int EPL = 8 * G / SLICES;  // columns per lane
+  constexpr int LR = W / EPL;          // lanes per query head
+  static_assert(EPL >= 1 && W % EPL == 0 && LR * HPL * G == kWave, "merge layout");
+  const int r = lane / LR;                        // query head inside the head group
+  const int col = slice * W + (lane % LR) * EPL;  // first column of the lane
+  float M = -INFINITY;
 #pragma unroll
-  for (int jq = 0; jq < G; ++jq) {
-    const int hq = lg * G + jq;
-    float M = -INFINITY;
+  for (int sl = 0; sl < SLICES; ++sl) M = fmaxf(M, s_m[sl * HGW + hgw][r]);
+  float L = 0.f, A[EPL];
 #pragma unroll
-    for (int sl = 0; sl < SLICES; ++sl) M = fmaxf(M, s_m[sl * HGW + hgw][hq]);
-    float L = 0.f, A[8];
+  for (int e = 0; e < EPL; ++e) A[e] = 0.f;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) A[e] = 0.f;
+  for (int sl = 0; sl < SLICES; ++sl) {
+    const int wv = sl * HGW + hgw;
+    const float mw = s_m[wv][r];
+    const float f = (mw == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mw - M);
+    L = fmaf(s_l[wv][r], f, L);
 #pragma unroll
-    for (int sl = 0; sl < SLICES; ++sl) {
-      const int wv = sl * HGW + hgw;
-      const float mw = s_m[wv][hq];
-      const float f = (mw == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mw - M);
-      L = fmaf(s_l[wv][hq], f, L);
+    for (int e = 0; e < EPL; ++e) A[e] = fmaf(s_acc[wv][r][col + e], f, A[e]);
+  }
+  const size_t hs = (static_cast<size_t>(b) * a.n_q + (hset * HG + hgw * HPL) * G + r) * n_split + s;
+  float* dst = a.partials + hs * D + col;
+  if constexpr (EPL % 4 == 0) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) A[e] = fmaf(s_acc[wv][hq][c * 8 + e], f, A[e]);
-    }
-    const size_t hs = (static_cast<size_t>(b) * a.n_q + kvh * G + jq) * n_split + s;
-    float4* dst = reinterpret_cast<float4*>(part_acc + hs * D + c * 8);
-    dst[0] = make_float4(A[0], A[1], A[2], A[3]);
-    dst[1] = make_float4(A[4], A[5], A[6], A[7]);
-    if (c == 0) {
-      part_ml[hs * 2] = M;
-      part_ml[hs * 2 + 1] = L;
-    }
+    for (int e = 0; e < EPL; e += 4)
+      *reinterpret_cast<float4*>(dst + e) = make_float4(A[e], A[e + 1], A[e + 2], A[e + 3]);
+  } else {
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) dst[e] = A[e];
+  }
+  if (slice == 0 && lane % LR == 0) {
+    float* part_ml = a.partials + a.ml_offset;
+    part_ml[hs * 2] = M;
+    part_ml[hs * 2 + 1] = L;
   }
 }
 

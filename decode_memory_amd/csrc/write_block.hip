@@ -297,13 +297,13 @@ __device__ __forceinline__ Codes8 pack_codes(const WriteArgs& a, const PackIn& i
   return quantise8<D, GS>(x, c, a.k_bits);
 }
 
-// A wave takes two consecutive tasks per pass, and every load of both (the
-// sources, rows and slots, then the slab bases) goes out before the first
-// task's arithmetic: one task's loads alone leave too few bytes in flight per
-// CU to cover the memory latency.  The stores of both come last.  The second
-// load of the last pass of an odd task count repeats the first and stores
-// nothing.  No load sits behind a branch, so the compiler's waits for the
-// loaded registers count the loads issued after them exactly.
+// A wave takes two consecutive tasks per pass (the task count, K tasks then
+// as many V tasks, is even), and every load of both (the sources, rows and
+// slots, then the slab bases) goes out before the first task's arithmetic:
+// one task's loads alone leave too few bytes in flight per CU to cover the
+// memory latency.  The stores of both come last.  No load sits behind a
+// branch, so the compiler's waits for the loaded registers count the loads
+// issued after them exactly.
 template <int D, int GS>
 __global__ __launch_bounds__(kThreads) void write_block_packed_kernel(WriteArgs a) {
   constexpr int LPT = D / 8;        // lanes per vector
@@ -312,7 +312,7 @@ __global__ __launch_bounds__(kThreads) void write_block_packed_kernel(WriteArgs 
   const int c = lane % LPT;         // values 8c .. 8c+7 of the vector
   const int n_vec = a.n * kPackedKv;  // K vectors; as many V vectors
   const int tasks = (n_vec + VPW - 1) / VPW;
-  const int total = 2 * tasks;
+  const int total = 2 * tasks;  // even: every pass below holds tasks t and t + 1
   const int waves = gridDim.x * (kThreads / kWave);
   float sg[8];  // the signs of values 8c .. 8c+7 (the same for every vector)
   {
@@ -327,19 +327,18 @@ __global__ __launch_bounds__(kThreads) void write_block_packed_kernel(WriteArgs 
   const int wave = __builtin_amdgcn_readfirstlane(blockIdx.x * (kThreads / kWave) + threadIdx.x / kWave);
   static_assert(kPackedKv % VPW == 0, "a wave task covers heads of one token");
   for (int t = 2 * wave; t < total; t += 2 * waves) {
-    const bool has_b = t + 1 < total;  // uniform over the wave
     const PackIn ia = pack_load<D>(a, t, tasks, lane);
-    const PackIn ib = pack_load<D>(a, has_b ? t + 1 : t, tasks, lane);
+    const PackIn ib = pack_load<D>(a, t + 1, tasks, lane);
     bool oka, okb;
     char* const ra = pack_record<D>(a, ia, lane, oka);
     char* const rb = pack_record<D>(a, ib, lane, okb);
     const Codes8 qa = pack_codes<D, GS>(a, ia, c, sg, odd_sign);
     const Codes8 qb = pack_codes<D, GS>(a, ib, c, sg, odd_sign);
     if (oka) store_codes8<D, GS>(qa, c, ia.is_v ? a.v_bits : a.k_bits, ra);
-    if (has_b && okb) store_codes8<D, GS>(qb, c, ib.is_v ? a.v_bits : a.k_bits, rb);
+    if (okb) store_codes8<D, GS>(qb, c, ib.is_v ? a.v_bits : a.k_bits, rb);
     // a token outside the pool is reported once, by the wave holding its first K vectors
     if (!oka && lane == 0 && !ia.is_v && ia.v0 % kPackedKv == 0) valid_target(a.lv, ia.row, ia.slot, true);
-    if (has_b && !okb && lane == 0 && !ib.is_v && ib.v0 % kPackedKv == 0) valid_target(a.lv, ib.row, ib.slot, true);
+    if (!okb && lane == 0 && !ib.is_v && ib.v0 % kPackedKv == 0) valid_target(a.lv, ib.row, ib.slot, true);
   }
 }
 

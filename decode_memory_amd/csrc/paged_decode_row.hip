@@ -26,9 +26,8 @@
 // Deeper queues measured slower: with every CU streaming at once, more
 // requests in flight only add contention.
 //
-// A block's address costs one dependent global read: the layer's slab
-// pointer tables are staged in LDS while the block-table reads are in
-// flight.  At the end each wave stages its state in LDS and, after one
+// A block's address costs two dependent global reads: its row in the block
+// table, then its slab's base pointer.  At the end each wave stages its state in LDS and, after one
 // workgroup barrier, the waves of each head group merge the group's slices
 // together, each wave a share of the columns, in slice order, and write one
 // partial (max, sum, weighted V) per query head and split; a combine kernel
@@ -62,7 +61,6 @@ constexpr int kRowThreads = kRowWaves * kWave;
 constexpr int kTile = PAGEDKV_ROW_TILE_TOKENS;  // tokens per wave per tile
 constexpr int kBuf = PAGEDKV_ROW_TILES_IN_FLIGHT;  // tiles a wave keeps in flight
 constexpr int kBS = 32;                      // tokens per block
-constexpr int kLdsSlabs = 2 * kRowThreads;   // slab pointers staged in LDS
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 // K/V bytes are read once per call: non-temporal loads keep them from
@@ -99,8 +97,6 @@ __global__ __launch_bounds__(kRowThreads, PAGEDKV_ROW_WAVES_PER_SIMD) void paged
   __shared__ float s_m[kRowWaves][HPL * G];
   __shared__ float s_l[kRowWaves][HPL * G];
   __shared__ float s_acc[kRowWaves][HPL * G][D];
-  __shared__ uint64_t s_kt[kLdsSlabs];  // slab base pointers of the layer
-  __shared__ uint64_t s_vt[kLdsSlabs];
 
   const int lane = threadIdx.x % kWave;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -145,46 +141,18 @@ __global__ __launch_bounds__(kRowThreads, PAGEDKV_ROW_WAVES_PER_SIMD) void paged
   const size_t row_bytes = static_cast<size_t>(kBS) * tok_bytes;
   const bool row_ok = row >= 0 && row < lv.capacity_rows;
 
-  // The layer's slab pointer tables go to LDS while the block-table reads
-  // are in flight, so a block's address costs one global read (its row), not
-  // two; slabs past kLdsSlabs are looked up in global memory.
-  {
-    const int n_slabs = static_cast<int>(lv.capacity_rows / lv.slab_blocks);
-    const int t0 = threadIdx.x, t1 = threadIdx.x + kRowThreads;
-    uint64_t k0 = 0, v0 = 0, k1 = 0, v1 = 0;
-    if (t0 < n_slabs && t0 < kLdsSlabs) {
-      k0 = reinterpret_cast<uint64_t>(lv.k_tab[t0]);
-      v0 = reinterpret_cast<uint64_t>(lv.v_tab[t0]);
-    }
-    if (t1 < n_slabs && t1 < kLdsSlabs) {
-      k1 = reinterpret_cast<uint64_t>(lv.k_tab[t1]);
-      v1 = reinterpret_cast<uint64_t>(lv.v_tab[t1]);
-    }
-    if (t0 < kLdsSlabs) {
-      s_kt[t0] = k0;
-      s_vt[t0] = v0;
-    }
-    if (t1 < kLdsSlabs) {
-      s_kt[t1] = k1;
-      s_vt[t1] = v1;
-    }
-  }
-  __syncthreads();
+  // The block's address: its slab's base pointer, read from the layer's
+  // table as soon as the row is known (each lane its own block), plus the
+  // row's offset in the slab.  Reading the pointers straight from global
+  // memory beat staging the whole table in LDS behind a workgroup barrier.
   uint64_t kaddr = 0, vaddr = 0;
-  {
+  if (lv.capacity_rows > 0) {
     // a row outside the pool is read as row 0 of slab 0 and masked below
     const int r = row_ok ? row : 0;
     const int slab = r / lv.slab_blocks;
     const size_t off = (r - slab * lv.slab_blocks) * row_bytes;
-    if (lv.capacity_rows > 0) {
-      if (slab < kLdsSlabs) {
-        kaddr = s_kt[slab] + off;
-        vaddr = s_vt[slab] + off;
-      } else {
-        kaddr = reinterpret_cast<uint64_t>(lv.k_tab[slab]) + off;
-        vaddr = reinterpret_cast<uint64_t>(lv.v_tab[slab]) + off;
-      }
-    }
+    kaddr = reinterpret_cast<uint64_t>(lv.k_tab[slab]) + off;
+    vaddr = reinterpret_cast<uint64_t>(lv.v_tab[slab]) + off;
   }
 
   const int cap_len = min(a.max_blocks, n_split * a.blocks_per_split) * kBS;

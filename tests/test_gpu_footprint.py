@@ -4,6 +4,8 @@ extend the pool should peak within about 1.15x of the dense backend; growth
 appends slabs and copies nothing).  The expected byte counts come from the
 oracle's accounting of the same lengths."""
 
+import gc
+
 import numpy as np
 import pytest
 import torch
@@ -24,6 +26,9 @@ def test_sequential_distinct_prefills_stay_within_the_gate():
     block_bytes = bs * token_bytes
     expect = slab_pool_capacity(lengths, bs, S, block_bytes)
 
+    # tensors of earlier tests that only the cycle collector frees would
+    # otherwise be freed during this test and come off the measured footprint
+    gc.collect()
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
     base = torch.cuda.memory_allocated()

@@ -89,6 +89,42 @@ __global__ __launch_bounds__(kThreads) void write_block_native_kernel(WriteArgs 
   }
 }
 
+// The same copy when a token is exactly UPL units per lane (unit f < n16 a
+// piece of K, the rest of V; 8 kv heads at head_dim 128 are one unit per
+// lane): every lane's source loads go out first -- they do not depend on the
+// target -- and the token's row, slot and slab base are read behind them, so
+// the lookup chain overlaps the loads instead of preceding them.
+template <int UPL>
+__global__ __launch_bounds__(kThreads) void write_block_native_exact_kernel(WriteArgs a) {
+  const size_t tok_bytes = static_cast<size_t>(a.lv.n_kv) * a.lv.k_rec;  // == V bytes
+  const int n16 = static_cast<int>(tok_bytes / 16);                      // 2 n16 == UPL * kThreads
+  for (int i = blockIdx.x; i < a.n; i += gridDim.x) {
+    const char* ks = static_cast<const char*>(a.k_src) + i * tok_bytes;
+    const char* vs = static_cast<const char*>(a.v_src) + i * tok_bytes;
+    uint4 v[UPL];
+#pragma unroll
+    for (int r = 0; r < UPL; ++r) {
+      const int f = threadIdx.x + r * kThreads;
+      v[r] = *reinterpret_cast<const uint4*>(f < n16 ? ks + static_cast<size_t>(f) * 16
+                                                     : vs + static_cast<size_t>(f - n16) * 16);
+    }
+    const int32_t row = a.rows[i], slot = a.slots[i];
+    // an empty asm with a memory clobber (no instruction) keeps the loads
+    // above from being moved under the target check below
+    asm volatile("" ::: "memory");
+    if (!valid_target(a.lv, row, slot, threadIdx.x == 0)) continue;
+    int slab;
+    const size_t tok = token_in_slab(a.lv, row, slot, &slab);
+    char* kd = static_cast<char*>(const_cast<void*>(a.lv.k_tab[slab])) + tok * tok_bytes;
+    char* vd = static_cast<char*>(const_cast<void*>(a.lv.v_tab[slab])) + tok * tok_bytes;
+#pragma unroll
+    for (int r = 0; r < UPL; ++r) {
+      const int f = threadIdx.x + r * kThreads;
+      store_global(f < n16 ? kd + static_cast<size_t>(f) * 16 : vd + static_cast<size_t>(f - n16) * 16, v[r]);
+    }
+  }
+}
+
 // 16-bit pools whose tokens are small (fewer than kWbMultiBelow 16-byte units
 // of K per token): a workgroup copies a chunk of consecutive tokens, each
 // token's n_kv records of K and of V (contiguous in the source and in the
@@ -410,8 +446,16 @@ hipError_t launch_write_block(const WriteArgs& a, int32_t format, hipStream_t s)
   if (format == PD_FMT_FP16 || format == PD_FMT_BF16) {
     const long long upt = 2LL * a.lv.n_kv * a.lv.k_rec / 16;  // 16-byte units per token
     if (upt / 2 >= kWbMultiBelow) {
+      // the exact kernel takes one token per workgroup (a workgroup that loops
+      // would wait for its previous token's stores before reusing registers)
+      const int grid_exact = a.n < (1 << 22) ? a.n : (1 << 22);
       const int grid = a.n < 65536 ? a.n : 65536;
-      hipLaunchKernelGGL(write_block_native_kernel, dim3(grid), dim3(kThreads), 0, s, a);
+      if (upt == kThreads)
+        hipLaunchKernelGGL(write_block_native_exact_kernel<1>, dim3(grid_exact), dim3(kThreads), 0, s, a);
+      else if (upt == 2 * kThreads)
+        hipLaunchKernelGGL(write_block_native_exact_kernel<2>, dim3(grid_exact), dim3(kThreads), 0, s, a);
+      else
+        hipLaunchKernelGGL(write_block_native_kernel, dim3(grid), dim3(kThreads), 0, s, a);
       return hipGetLastError();
     }
     int tpw = static_cast<int>(kThreads * kWbLoads / upt);

@@ -158,8 +158,12 @@ def test_fragmented_workload_gather_full_size():
     pool.close()
 
 
-def test_write_block_overwrites_and_rejects_out_of_range_targets():
-    bs, S, n_kv, D = 32, 2, 2, 64
+# (n_kv, D): tokens of 256 B of K (several tokens per workgroup), exactly one
+# and two 16-byte units per lane (8 kv heads at head_dim 128 and 256), and
+# 1.5 units per lane (the looping one-token kernel)
+@pytest.mark.parametrize("n_kv,D", [(2, 64), (8, 128), (8, 256), (12, 128)])
+def test_write_block_overwrites_and_rejects_out_of_range_targets(n_kv, D):
+    bs, S = 32, 2
     pool = pd.SlabPool(1, bs, n_kv, D, S, 4, "bf16")
     pool.reserve_rows(4)
     src = torch.arange(3 * n_kv * D, dtype=torch.int16, device="cuda").view(torch.bfloat16)

@@ -48,13 +48,17 @@
 //     of 4 tokens, which LDS transpose loads (ds_read_b64_tr_b8) deliver 8
 //     tokens at a time (4-bit codes: one byte feeds the two dimensions of
 //     its nibbles); the offsets add sum_t p_t offset_t per group.
-// Codes become f16 exactly: a byte placed under the exponent bits 0x64 is
-// 1024 + byte.  Key products take these biased codes as they are and drop
-// 1024 * sum(q') per group afterwards; value codes get one packed f16 add of
-// -1024 first (their sums run over the whole split, where the cancellation
-// would cost accuracy).  A 4-bit high nibble is taken in place, as 16 * code,
-// and scaled back by an exact power of two (keys: in q', values: in the
-// accumulator).
+// Codes become f16 exactly.  Key codes: a byte placed under the exponent
+// bits 0x64 is 1024 + byte; the products take these biased codes as they are
+// and the first accumulator of each group's chain starts at -1024 * sum(q').
+// Value codes: a byte zero-extended to 16 bits is the f16 subnormal byte *
+// 2^-24 (the matrix cores take subnormal f16 operands), so no bias is added
+// or taken off, and 2^24 is applied once at the end; the value sums run over
+// the whole split, where a bias would cancel at a cost in accuracy.  A 4-bit
+// key's high nibble is taken in place, as 16 * code, and scaled back by an
+// exact power of two in q'.  A 4-bit value byte enters whole (lo + 16 hi)
+// for its high nibble and masked (lo) for its low one; the low nibble's sum
+// is taken off the high one's at the end.
 // Partials go to the same workspace layout as the 16-bit kernels and the same
 // combine kernel merges them.
 #include "device_common.h"
@@ -142,10 +146,10 @@ __device__ __forceinline__ uint32_t bytes_biased(uint32_t w, uint32_t sel) {
 constexpr uint32_t kSelB01 = 0x04010400u;  // bytes 0, 1 -> (lo, hi) halves
 constexpr uint32_t kSelB23 = 0x04030402u;  // bytes 2, 3
 
-// An f16 pair (1024 + x, 1024 + y) less 1024 each, exactly.
-__device__ __forceinline__ uint32_t unbias(uint32_t v) {
-  const h2 x = __builtin_bit_cast(h2, v) - h2{static_cast<_Float16>(1024.f), static_cast<_Float16>(1024.f)};
-  return __builtin_bit_cast(uint32_t, x);
+// Two bytes of w (selected by SEL) zero-extended to 16 bits: the f16
+// subnormals byte * 2^-24
+__device__ __forceinline__ uint32_t bytes_subnormal(uint32_t w, uint32_t sel) {
+  return __builtin_amdgcn_perm(0u, w, sel);
 }
 
 // B operand of a score product: 8 codes of one token and group as biased
@@ -199,14 +203,15 @@ template <int VB>
 __device__ __forceinline__ int vdim(int i, int lane) {
   return VB == 8 ? 32 * i + tr_col(lane) : 64 * (i / 2) + 2 * tr_col(lane) + i % 2;
 }
-// Scale that brings accumulator i of lane l back to sum_t p_t s_t c_t: the
-// prescale 2^vk of p * scale, and 16 more for a 4-bit high nibble taken in
-// place (exact powers of two).
+// Scale that brings accumulator i of lane l, times 2^24 (the subnormal
+// codes), back to sum_t p_t s_t c_t: the prescale 2^vk of p * scale, and 16
+// more for a 4-bit high nibble taken in place (exact powers of two).
 template <int VB>
 __device__ __forceinline__ float vacc_scale(int i, int vk) {
   const bool high = VB == 4 && (i % 2) == 1;
   return __builtin_bit_cast(float, static_cast<uint32_t>(127 - vk - (high ? 4 : 0)) << 23);
 }
+constexpr float kSubnormalUnit = 16777216.f;  // 2^24: a subnormal code's unit back to 1
 
 typedef int v2i __attribute__((ext_vector_type(2)));
 // 8 bytes per lane from LDS, transposed across each 16-lane group as above
@@ -724,16 +729,17 @@ __global__ __launch_bounds__(kPThreads, kPMinWaves<D>) void paged_decode_packed_
             for (int dw = 0; dw < 2; ++dw) {
               const uint32_t x = dw ? w.y : w.x;
               const int tq0 = u * kSub + t8 + 4 * dw;  // the dword's first token in the step
-              const uint32_t p01 = bytes_biased(x, kSelB01), p23 = bytes_biased(x, kSelB23);
+              const uint32_t p01 = bytes_subnormal(x, kSelB01), p23 = bytes_subnormal(x, kSelB23);
               if constexpr (VB == 8) {
                 const h4 ap = *reinterpret_cast<const h4*>(sp + ((32 * rd + col) / GS * 4 + qa) * STEP + tq0);
-                const uint32_t u2[2] = {unbias(p01), unbias(p23)};
+                const uint32_t u2[2] = {p01, p23};
                 acc[rd] = __builtin_amdgcn_mfma_f32_4x4x4f16(ap, __builtin_bit_cast(h4, u2), acc[rd], 0, 0, 0);
               } else {
-                // low nibbles as 1024 + code, high nibbles in place as 1024 + 16 code
+                // low nibbles masked (code), high nibbles with the low one
+                // beside them (lo + 16 hi; the low sum comes off at the end)
                 const h4 ap = *reinterpret_cast<const h4*>(sp + ((64 * rd + 2 * col) / GS * 4 + qa) * STEP + tq0);
-                const uint32_t ul[2] = {unbias(p01 & 0xff0fff0fu), unbias(p23 & 0xff0fff0fu)};
-                const uint32_t uh[2] = {unbias(p01 & 0xfff0fff0u), unbias(p23 & 0xfff0fff0u)};
+                const uint32_t ul[2] = {p01 & 0x000f000fu, p23 & 0x000f000fu};
+                const uint32_t uh[2] = {p01, p23};
                 acc[2 * rd] = __builtin_amdgcn_mfma_f32_4x4x4f16(ap, __builtin_bit_cast(h4, ul), acc[2 * rd], 0, 0, 0);
                 acc[2 * rd + 1] =
                     __builtin_amdgcn_mfma_f32_4x4x4f16(ap, __builtin_bit_cast(h4, uh), acc[2 * rd + 1], 0, 0, 0);
@@ -757,6 +763,10 @@ __global__ __launch_bounds__(kPThreads, kPMinWaves<D>) void paged_decode_packed_
   for (int i = 0; i < NACC; ++i)
 #pragma unroll
     for (int r = 0; r < G; ++r) acc[i][r] += __shfl_down(acc[i][r], 8, 16);
+  if constexpr (VB == 4) {  // a high nibble's sum holds its low nibble's
+#pragma unroll
+    for (int i = 1; i < NACC; i += 2) acc[i] -= acc[i - 1];
+  }
   const bool writer = lane % 16 < 8;
   const float l_tot = group_sum<kSub>(l_run);
   float btot[NMG];
@@ -780,7 +790,7 @@ __global__ __launch_bounds__(kPThreads, kPMinWaves<D>) void paged_decode_packed_
         bsel = d / GS == g ? bq[g] : bsel;
         ksel = d / GS == g ? vk[g] : ksel;
       }
-      if (writer) part_acc[d] = fmaf(acc[i][r], vacc_scale<VB>(i, ksel), bsel);
+      if (writer) part_acc[d] = fmaf(acc[i][r] * kSubnormalUnit, vacc_scale<VB>(i, ksel), bsel);
     }
     if (lane == kSub * r) {
       a.partials[a.ml_offset + hs * 2] = m_run;

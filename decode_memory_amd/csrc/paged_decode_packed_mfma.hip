@@ -156,24 +156,32 @@ __device__ __forceinline__ uint32_t bytes_subnormal(uint32_t w, uint32_t sel) {
 // f16, in the element order the A operand (q') uses.  8-bit codes: 1024 +
 // value e of the k-block; 4-bit codes: 1024 + values 0, 2, 4, 6 (low
 // nibbles), then 1024 + 16 * values 1, 3, 5, 7 (high nibbles in place).
+// The code bytes of one token and k-block (8 bytes, or 4 for 4-bit codes)
 template <int KB>
-__device__ __forceinline__ h8 key_codes(const unsigned char* p) {
+__device__ __forceinline__ uint2 key_load(const unsigned char* p) {
+  if constexpr (KB == 8) return *reinterpret_cast<const uint2*>(p);
+  else return make_uint2(*reinterpret_cast<const uint32_t*>(p), 0u);
+}
+template <int KB>
+__device__ __forceinline__ h8 key_unpack(uint2 w) {
   uint32_t r[4];
   if constexpr (KB == 8) {
-    const uint2 w = *reinterpret_cast<const uint2*>(p);
     r[0] = bytes_biased(w.x, kSelB01);
     r[1] = bytes_biased(w.x, kSelB23);
     r[2] = bytes_biased(w.y, kSelB01);
     r[3] = bytes_biased(w.y, kSelB23);
   } else {
-    const uint32_t w = *reinterpret_cast<const uint32_t*>(p);
-    const uint32_t lo = w & 0x0f0f0f0fu, hi = w & 0xf0f0f0f0u;
+    const uint32_t lo = w.x & 0x0f0f0f0fu, hi = w.x & 0xf0f0f0f0u;
     r[0] = bytes_biased(lo, kSelB01);
     r[1] = bytes_biased(lo, kSelB23);
     r[2] = bytes_biased(hi, kSelB01);
     r[3] = bytes_biased(hi, kSelB23);
   }
   return __builtin_bit_cast(h8, r);
+}
+template <int KB>
+__device__ __forceinline__ h8 key_codes(const unsigned char* p) {
+  return key_unpack<KB>(key_load<KB>(p));
 }
 
 template <int KB>
@@ -633,25 +641,49 @@ __global__ __launch_bounds__(kPThreads, kPMinWaves<D>) void paged_decode_packed_
         }
       } else {
         // scores of each sub-tile: lane (n, J) = (token n, query head J);
-        // sub-tiles past the length are computed and masked
+        // sub-tiles past the length are computed and masked.  Every LDS read
+        // of the step goes out first (key codes and metadata, then the value
+        // metadata), then the sub-tiles' product chains, which are
+        // independent, so that one chain's latency hides behind the others.
+        uint2 kr[NSUB][NKB];
+        float2 km[NSUB][NMG], vm[NSUB][NMG];
+#pragma unroll
+        for (int u = 0; u < NSUB; ++u) {
+          const unsigned char* krow = s_stage + (lt0 + u * kSub + n) * PK + h * KREC;
+#pragma unroll
+          for (int g = 0; g < NKB; ++g) kr[u][g] = key_load<KB>(krow + g * (32 * KB / 8) + J * KB);
+#pragma unroll
+          for (int mg = 0; mg < NMG; ++mg) km[u][mg] = *reinterpret_cast<const float2*>(krow + S::KCODE + 8 * mg);
+        }
+        // value metadata of the step's tokens; invisible tokens add nothing
+        // even if it is garbage
+#pragma unroll
+        for (int u = 0; u < NSUB; ++u) {
+          const unsigned char* vrow = s_stage + T * PK + (lt0 + u * kSub + n) * PV + h * VREC;
+#pragma unroll
+          for (int g = 0; g < NMG; ++g) vm[u][g] = *reinterpret_cast<const float2*>(vrow + S::VCODE + 8 * g);
+        }
+        f4 c[NSUB][NMG];
+#pragma unroll
+        for (int u = 0; u < NSUB; ++u)
+#pragma unroll
+          for (int mg = 0; mg < NMG; ++mg) c[u][mg] = cinit[mg];
+#pragma unroll
+        for (int kk = 0; kk < KPG; ++kk)
+#pragma unroll
+          for (int u = 0; u < NSUB; ++u)
+#pragma unroll
+            for (int mg = 0; mg < NMG; ++mg) {
+              const int g = mg * KPG + kk;
+              c[u][mg] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aq[g], key_unpack<KB>(kr[u][g]), c[u][mg], 0, 0, 0);
+            }
         float sc[NSUB];
         bool tv[NSUB];
 #pragma unroll
         for (int u = 0; u < NSUB; ++u) {
-          const unsigned char* krow = s_stage + (lt0 + u * kSub + n) * PK + h * KREC;
           float sv = 0.f;
 #pragma unroll
-          for (int mg = 0; mg < NMG; ++mg) {
-            f4 c = cinit[mg];
-#pragma unroll
-            for (int kk = 0; kk < KPG; ++kk) {
-              const int g = mg * KPG + kk;
-              const h8 bk = key_codes<KB>(krow + g * (32 * KB / 8) + J * KB);
-              c = __builtin_amdgcn_mfma_f32_16x16x32_f16(aq[g], bk, c, 0, 0, 0);
-            }
-            const float2 km = *reinterpret_cast<const float2*>(krow + S::KCODE + 8 * mg);
-            sv = fmaf(c[0] + c[1], km.x, fmaf(km.y, qsum[mg], sv));
-          }
+          for (int mg = 0; mg < NMG; ++mg) sv = fmaf(c[u][mg][0] + c[u][mg][1], km[u][mg].x, fmaf(km[u][mg].y, qsum[mg], sv));
           tv[u] = J < G && t0 + lt0 + u * kSub + n < nt;
           sc[u] = tv[u] ? sv : -INFINITY;  // carries the query prescale, taken off by qinv below
         }
@@ -671,21 +703,6 @@ __global__ __launch_bounds__(kPThreads, kPMinWaves<D>) void paged_decode_packed_
         l_run = fmaf(l_run, alpha, p[0]);
 #pragma unroll
         for (int u = 1; u < NSUB; ++u) l_run += p[u];
-        // value metadata of the step's tokens, all read before any p^T store
-        // (so the reads go out together); invisible tokens add nothing even if
-        // it is garbage
-        float2 vm[NSUB][NMG];
-#pragma unroll
-        for (int u = 0; u < NSUB; ++u) {
-          const unsigned char* vrow = s_stage + T * PK + (lt0 + u * kSub + n) * PV + h * VREC;
-#pragma unroll
-          for (int g = 0; g < NMG; ++g) {
-            vm[u][g] = *reinterpret_cast<const float2*>(vrow + S::VCODE + 8 * g);
-            // every lane reads (the compiler would otherwise move reads used
-            // only for visible tokens behind a branch)
-            asm volatile("" : "+v"(vm[u][g]));
-          }
-        }
         fit_value_prescale(tv, vm);
 #pragma unroll
         for (int g = 0; g < NMG; ++g) {

@@ -156,6 +156,50 @@ def test_packed_decode_matches_oracle(fmt, D, G, group):
     pool.close()
 
 
+@pytest.mark.parametrize("fmt,D,G", [("k4v4", 64, 4), ("k8v4", 64, 2), ("k4v4", 256, 1)])
+def test_packed_decode_skips_blocks_whose_row_is_outside_the_pool(fmt, D, G):
+    """A block whose table row is outside the pool adds nothing (its tokens
+    are left out) and the call flags PD_DEVERR_TABLE_ROW; the other blocks of
+    its split, before and after it, still count.  16 sequences of at most 125
+    blocks plan 32 splits, and split s takes blocks s, s + 32, s + 64, s + 96;
+    K4V4 at head_dim 64 stages a split's blocks two at a time, so the bad
+    rows of sequence 0 sit first (5, 77) and second (38, 98, 124) in a stage
+    and alone in a split's last stage (94: split 30 has three blocks)."""
+    lengths = [4000, 700, 100, 33, 17, 0, 64, 5, 300, 1, 2, 90, 45, 31, 32, 200]
+    rows, _, R = shuffled_rows(np.random.default_rng(31 + D), lengths, BS, 32, spare_rows=4)
+    pool, recs, signs = _packed_pool(fmt, D, lengths, rows, 70 + D, R)
+    table = make_block_table(rows)
+    bad = {0: [5, 38, 77, 98, 94, 124], 1: [21], 2: [3]}
+    for b, blocks in bad.items():
+        for j in blocks:
+            table[b, j] = -1 if j % 2 else 1_000_000
+    B = len(lengths)
+    kr, vr = [], []
+    for b in range(B):
+        if b not in recs:
+            kr.append(np.zeros((0, 8, pool.k_record_bytes), np.uint8))
+            vr.append(np.zeros((0, 8, pool.v_record_bytes), np.uint8))
+            continue
+        keep = np.ones(lengths[b], bool)
+        for j in bad.get(b, []):
+            keep[j * BS:(j + 1) * BS] = False
+        kr.append(recs[b][0][keep])
+        vr.append(recs[b][1][keep])
+    q = q_bits(70 + D, 0, B, 8 * G, D, "bf16")
+    scale = 1.0 / np.sqrt(D)
+    ref = packed_decode_attention(q, kr, vr, signs, fmt, D, scale)
+    qd = to_device_bits(q, "bf16")
+    out = torch.empty_like(qd)
+    ws = pool.workspace(B, 8 * G, max(lengths))
+    pool.paged_decode(0, qd, i32(table), i32(lengths), max(lengths), scale, out, ws)
+    got = from_device_bits(out)
+    assert pool.check_error() == pd.DEVERR_TABLE_ROW
+    assert_decode_close(got, ref, "bf16", allow_output_rounding=True)
+    assert_decode_close(got[[0, 1, 8, 15]], ref[[0, 1, 8, 15]], "bf16")
+    assert not got[5].any()
+    pool.close()
+
+
 @pytest.mark.parametrize("fmt,D,G", [("k8v4", 64, 4), ("k4v4", 256, 2)])
 def test_packed_decode_with_more_slabs_than_its_lds_table(fmt, D, G):
     """The packed kernel stages the first 512 slab base pointers of a layer in

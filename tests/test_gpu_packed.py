@@ -160,11 +160,12 @@ def test_packed_decode_matches_oracle(fmt, D, G, group):
 def test_packed_decode_skips_blocks_whose_row_is_outside_the_pool(fmt, D, G):
     """A block whose table row is outside the pool adds nothing (its tokens
     are left out) and the call flags PD_DEVERR_TABLE_ROW; the other blocks of
-    its split, before and after it, still count.  16 sequences of at most 125
-    blocks plan 32 splits, and split s takes blocks s, s + 32, s + 64, s + 96;
-    K4V4 at head_dim 64 stages a split's blocks two at a time, so the bad
-    rows of sequence 0 sit first (5, 77) and second (38, 98, 124) in a stage
-    and alone in a split's last stage (94: split 30 has three blocks)."""
+    its split, before and after it, still count.  At head_dim 64, 16
+    sequences of at most 125 blocks plan 32 splits (split s takes blocks s,
+    s + 32, s + 64, s + 96), so the bad rows of sequence 0 are the first (5),
+    second (38), third (77, 94) and fourth (98, 124) block of their splits,
+    94 the last of a split of three; at head_dim 256 the plan has 16 splits of
+    up to 8 blocks."""
     lengths = [4000, 700, 100, 33, 17, 0, 64, 5, 300, 1, 2, 90, 45, 31, 32, 200]
     rows, _, R = shuffled_rows(np.random.default_rng(31 + D), lengths, BS, 32, spare_rows=4)
     pool, recs, signs = _packed_pool(fmt, D, lengths, rows, 70 + D, R)
